@@ -1,0 +1,17 @@
+"""MI355X (gfx950) layout-aware reduce-scatter and all-gather placement for FSDP parameter groups.
+
+The compute path is the C-ABI library ``libtide.so`` (hand-written HIP kernels); this package only
+marshals arguments to it.  Importing the package does not load the library; the first call does,
+and fails loudly if it has not been built (``python -m all_gather_placement_amd.build``).
+"""
+from .tide import (  # noqa: F401
+    TIDE_AG_KERNEL,
+    TIDE_AG_SDMA,
+    Layout,
+    TideError,
+    library_path,
+    load_library,
+    tide_ag_place,
+    tide_layout_create,
+    tide_rs_bf16_to_fp32,
+)

@@ -1,0 +1,278 @@
+// Layout creation and queries: geometry of one FSDP parameter group and its work-item tables.
+//
+// Geometry follows [Endgame] Table 2 (padded per-rank rows, row length, per-rank shard size,
+// prefix offset, per-rank packed shard size) and Figure 1 (per-parameter storage on one side of
+// FSDP2's contract boundary, flat rank-major shards on the other):
+//   L_p = product of shape_p[1:], m_p = ceil(rows_p / R), e_p = m_p * L_p, o_p = sum_{q<p} e_q,
+//   v(p, r) = clamp(rows_p - r * m_p, 0, m_p).
+// The segment (p, r) is the contiguous run of v * L_p elements at element r * m_p * L_p of
+// parameter p, whose home is element o_p of rank r's shard, followed there by (m_p - v) * L_p
+// padding elements.  Segments are cut into work items whose interior boundaries sit on 16-byte
+// source boundaries, so the kernels need no per-element lookup.
+#include <hip/hip_runtime_api.h>
+
+#include <cstring>
+#include <new>
+
+#include "../../include/tide.h"
+#include "layout.h"
+
+namespace tide {
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+
+inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Cut [0, n) of a segment whose first element sits at absolute source offset `src0` into pieces
+// whose interior boundaries are at absolute offsets align_down(src0, 8) + k * chunk.
+template <typename F>
+void cut(int64_t src0, int64_t n, int64_t chunk, F&& emit) {
+  const int64_t base = src0 & ~int64_t(7);
+  int64_t pos = 0;
+  while (pos < n) {
+    const int64_t s = src0 + pos;
+    const int64_t k = (s - base) / chunk + 1;
+    const int64_t end = base + k * chunk;  // next boundary strictly after s
+    const int64_t len = (end - s) < (n - pos) ? (end - s) : (n - pos);
+    emit(pos, len);
+    pos += len;
+  }
+}
+
+thread_local int g_last_hip_error = 0;
+
+}  // namespace
+
+void set_last_hip_error(int err) { g_last_hip_error = err; }
+
+int device_state(const tide_layout* layout, DeviceState** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto it = layout->devices.find(dev);
+  if (it != layout->devices.end()) {
+    *out = &it->second;
+    return hipSuccess;
+  }
+  DeviceState st;
+  const size_t rs_bytes = layout->rs_chunks.size() * sizeof(RsChunk);
+  const size_t ag_bytes = layout->ag_chunks.size() * sizeof(AgChunk);
+  if (rs_bytes) {
+    if ((e = hipMalloc(reinterpret_cast<void**>(&st.rs), rs_bytes)) != hipSuccess) return e;
+    if ((e = hipMemcpy(st.rs, layout->rs_chunks.data(), rs_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+      (void)hipFree(st.rs);
+      return e;
+    }
+  }
+  if (ag_bytes) {
+    if ((e = hipMalloc(reinterpret_cast<void**>(&st.ag), ag_bytes)) != hipSuccess) {
+      if (st.rs) (void)hipFree(st.rs);
+      return e;
+    }
+    if ((e = hipMemcpy(st.ag, layout->ag_chunks.data(), ag_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
+      if (st.rs) (void)hipFree(st.rs);
+      (void)hipFree(st.ag);
+      return e;
+    }
+  }
+  auto res = layout->devices.emplace(dev, st);
+  *out = &res.first->second;
+  return hipSuccess;
+}
+
+}  // namespace tide
+
+using tide::AgChunk;
+using tide::ParamGeom;
+using tide::RsChunk;
+
+extern "C" {
+
+tide_status tide_layout_create(int32_t num_params, const int32_t* ndims, const int64_t* dims,
+                               int32_t num_ranks, tide_layout** out) {
+  if (out == nullptr || ndims == nullptr || dims == nullptr || num_params < 1 || num_ranks < 1)
+    return TIDE_ERR_INVALID;
+  tide_layout* L = new (std::nothrow) tide_layout();
+  if (L == nullptr) return TIDE_ERR_NOMEM;
+  try {
+    L->P = num_params;
+    L->R = num_ranks;
+    L->params.resize(num_params);
+    int64_t di = 0, o = 0;
+    for (int32_t p = 0; p < num_params; ++p) {
+      const int32_t nd = ndims[p];
+      if (nd < 1 || nd > 64) {
+        delete L;
+        return TIDE_ERR_INVALID;
+      }
+      int64_t rows = dims[di];
+      int64_t len = 1;
+      bool bad = rows < 0;
+      for (int32_t k = 1; k < nd; ++k) {
+        const int64_t d = dims[di + k];
+        if (d < 0) bad = true;
+        else if (d > 0 && len > tide::kMaxElems / d) bad = true;
+        else len *= d;
+      }
+      di += nd;
+      if (bad) {
+        delete L;
+        return TIDE_ERR_INVALID;
+      }
+      ParamGeom g;
+      g.rows = rows;
+      g.L = len;
+      g.m = (rows + num_ranks - 1) / num_ranks;
+      if (g.L > 0 && g.m > tide::kMaxElems / g.L / num_ranks) {
+        delete L;
+        return TIDE_ERR_INVALID;
+      }
+      g.e = g.m * g.L;
+      g.numel = rows * len;
+      g.o = o;
+      o += g.e;
+      if (o > tide::kMaxElems / num_ranks) {
+        delete L;
+        return TIDE_ERR_INVALID;
+      }
+      L->params[p] = g;
+    }
+    L->S = o;
+
+    // Work items.  Order: parameter-major, then rank, then position, so consecutive workgroups
+    // stream consecutive addresses of each contributor's tensor.
+    for (int32_t p = 0; p < num_params; ++p) {
+      const ParamGeom& g = L->params[p];
+      for (int32_t r = 0; r < num_ranks; ++r) {
+        const int64_t v = tide::clamp64(g.rows - int64_t(r) * g.m, 0, g.m);
+        const int64_t nvalid = v * g.L, npad = (g.m - v) * g.L;
+        const int64_t src0 = int64_t(r) * g.m * g.L;
+        tide::cut(src0, nvalid, tide::kRsChunk, [&](int64_t pos, int64_t len) {
+          L->rs_chunks.push_back(RsChunk{src0 + pos, g.o + pos, p, r, int32_t(len), 0});
+        });
+        for (int64_t pos = 0; pos < npad; pos += tide::kRsChunk) {
+          const int64_t len = (npad - pos) < tide::kRsChunk ? (npad - pos) : tide::kRsChunk;
+          L->rs_chunks.push_back(RsChunk{0, g.o + nvalid + pos, p, r, 0, int32_t(len)});
+        }
+        const int64_t stage0 = int64_t(r) * L->S + g.o;
+        tide::cut(stage0, nvalid, tide::kAgChunk, [&](int64_t pos, int64_t len) {
+          L->ag_chunks.push_back(AgChunk{stage0 + pos, src0 + pos, p, int32_t(len), 0});
+        });
+      }
+    }
+  } catch (const std::bad_alloc&) {
+    delete L;
+    return TIDE_ERR_NOMEM;
+  }
+  *out = L;
+  return TIDE_OK;
+}
+
+void tide_layout_destroy(tide_layout* layout) {
+  if (layout == nullptr) return;
+  int cur = 0;
+  // No HIP call at all for a layout that never reached a device (host-only use).
+  const bool have_dev = !layout->devices.empty() && hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : layout->devices) {
+    if (hipSetDevice(kv.first) != hipSuccess) continue;
+    tide::DeviceState& st = kv.second;
+    for (auto& s : st.slots) {
+      if (s.done) {
+        if (s.pending) (void)hipEventSynchronize(s.done);
+        (void)hipEventDestroy(s.done);
+      }
+      if (s.dev) (void)hipFree(s.dev);
+      if (s.host) (void)hipHostFree(s.host);
+    }
+    if (st.rs) (void)hipFree(st.rs);
+    if (st.ag) (void)hipFree(st.ag);
+  }
+  if (have_dev && !layout->devices.empty()) (void)hipSetDevice(cur);
+  delete layout;
+}
+
+tide_status tide_layout_prepare(const tide_layout* layout) {
+  if (layout == nullptr) return TIDE_ERR_INVALID;
+  std::lock_guard<std::mutex> lock(layout->mu);
+  tide::DeviceState* st = nullptr;
+  const int e = tide::device_state(layout, &st);
+  if (e == hipErrorOutOfMemory) return TIDE_ERR_NOMEM;
+  if (e != hipSuccess) {
+    tide::set_last_hip_error(e);
+    return TIDE_ERR_HIP;
+  }
+  return TIDE_OK;
+}
+
+int32_t tide_layout_num_params(const tide_layout* layout) { return layout ? layout->P : -1; }
+int32_t tide_layout_num_ranks(const tide_layout* layout) { return layout ? layout->R : -1; }
+int64_t tide_layout_shard_numel(const tide_layout* layout) { return layout ? layout->S : -1; }
+int64_t tide_layout_num_rs_chunks(const tide_layout* layout) {
+  return layout ? int64_t(layout->rs_chunks.size()) : -1;
+}
+int64_t tide_layout_num_ag_chunks(const tide_layout* layout) {
+  return layout ? int64_t(layout->ag_chunks.size()) : -1;
+}
+
+tide_status tide_layout_param(const tide_layout* layout, int32_t p, int64_t* rows, int64_t* row_len,
+                              int64_t* padded_rows, int64_t* offset) {
+  if (layout == nullptr || p < 0 || p >= layout->P) return TIDE_ERR_INVALID;
+  const ParamGeom& g = layout->params[p];
+  if (rows) *rows = g.rows;
+  if (row_len) *row_len = g.L;
+  if (padded_rows) *padded_rows = g.m;
+  if (offset) *offset = g.o;
+  return TIDE_OK;
+}
+
+tide_status tide_layout_segment(const tide_layout* layout, int32_t p, int32_t r, int64_t* src_offset,
+                                int64_t* valid, int64_t* dst_offset, int64_t* pad) {
+  if (layout == nullptr || p < 0 || p >= layout->P || r < 0 || r >= layout->R) return TIDE_ERR_INVALID;
+  const ParamGeom& g = layout->params[p];
+  const int64_t v = tide::clamp64(g.rows - int64_t(r) * g.m, 0, g.m);
+  if (src_offset) *src_offset = int64_t(r) * g.m * g.L;
+  if (valid) *valid = v * g.L;
+  if (dst_offset) *dst_offset = g.o;
+  if (pad) *pad = (g.m - v) * g.L;
+  return TIDE_OK;
+}
+
+tide_status tide_layout_copy_rs_items(const tide_layout* layout, int64_t first, int64_t n, int64_t* out) {
+  if (layout == nullptr || out == nullptr || first < 0 || n < 0 ||
+      first + n > int64_t(layout->rs_chunks.size()))
+    return TIDE_ERR_INVALID;
+  for (int64_t i = 0; i < n; ++i) {
+    const RsChunk& c = layout->rs_chunks[first + i];
+    int64_t* o = out + 6 * i;
+    o[0] = c.p; o[1] = c.r; o[2] = c.src; o[3] = c.dst; o[4] = c.nvalid; o[5] = c.npad;
+  }
+  return TIDE_OK;
+}
+
+tide_status tide_layout_copy_ag_items(const tide_layout* layout, int64_t first, int64_t n, int64_t* out) {
+  if (layout == nullptr || out == nullptr || first < 0 || n < 0 ||
+      first + n > int64_t(layout->ag_chunks.size()))
+    return TIDE_ERR_INVALID;
+  for (int64_t i = 0; i < n; ++i) {
+    const AgChunk& c = layout->ag_chunks[first + i];
+    int64_t* o = out + 4 * i;
+    o[0] = c.p; o[1] = c.src; o[2] = c.dst; o[3] = c.n;
+  }
+  return TIDE_OK;
+}
+
+const char* tide_status_str(int32_t status) {
+  switch (status) {
+    case TIDE_OK: return "TIDE_OK";
+    case TIDE_ERR_INVALID: return "TIDE_ERR_INVALID";
+    case TIDE_ERR_NOMEM: return "TIDE_ERR_NOMEM";
+    case TIDE_ERR_HIP: return "TIDE_ERR_HIP";
+    case TIDE_ERR_UNSUPPORTED: return "TIDE_ERR_UNSUPPORTED";
+    default: return "unknown";
+  }
+}
+
+int32_t tide_last_hip_error(void) { return tide::g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Host-side layout object: geometry, segment work-item tables, per-device state.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "tide_internal.h"
+
+namespace tide {
+
+struct ParamGeom {
+  int64_t rows;  // dim 0
+  int64_t L;     // row length: product of the trailing dims
+  int64_t m;     // padded per-rank rows: ceil(rows / R)
+  int64_t e;     // per-rank shard elements: m * L
+  int64_t o;     // prefix offset inside a rank's flat shard
+  int64_t numel; // rows * L
+};
+
+// A ring of device pointer tables.  Each RS/AG call needs its C*P + R (or P) device pointers in
+// device memory; a slot is refilled from pinned host memory with one stream-ordered copy, and a
+// call whose pointers equal the previous call's on the same stream reuses that slot with no copy.
+struct PtrSlot {
+  void** host = nullptr;  // pinned
+  void** dev = nullptr;
+  size_t cap = 0;         // pointers
+  size_t n = 0;           // pointers currently held
+  hipEvent_t done = nullptr;
+  hipStream_t stream = nullptr;
+  bool pending = false;   // `done` has been recorded after the slot's last use
+};
+
+constexpr int kPtrSlots = 8;
+
+struct DeviceState {
+  RsChunk* rs = nullptr;
+  AgChunk* ag = nullptr;
+  PtrSlot slots[kPtrSlots];
+  int next = 0;
+  int last = -1;
+};
+
+}  // namespace tide
+
+struct tide_layout {
+  int32_t P = 0;
+  int32_t R = 0;
+  int64_t S = 0;
+  std::vector<tide::ParamGeom> params;
+  std::vector<tide::RsChunk> rs_chunks;
+  std::vector<tide::AgChunk> ag_chunks;
+  mutable std::mutex mu;
+  mutable std::map<int, tide::DeviceState> devices;
+};
+
+namespace tide {
+// Returns the device state for the current device, uploading the tables on first use.
+// Must be called with layout->mu held.  Returns a hipError_t.
+int device_state(const tide_layout* layout, DeviceState** out);
+void set_last_hip_error(int err);
+}  // namespace tide

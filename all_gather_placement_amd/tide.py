@@ -1,0 +1,259 @@
+"""ctypes binding of libtide.so (include/tide.h).  Argument marshalling only.
+
+Every entry point of the C ABI is exposed under its own name; :class:`Layout` wraps a layout
+handle for convenience.  Tensors are torch tensors on the current HIP device (torch provides the
+device memory and the stream); the binding passes their data pointers and the stream handle and
+raises :class:`TideError` on any non-OK status.  There is no fallback: if the library is missing,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libtide.so"
+
+TIDE_OK = 0
+TIDE_ERR_INVALID = 1
+TIDE_ERR_NOMEM = 2
+TIDE_ERR_HIP = 3
+TIDE_ERR_UNSUPPORTED = 4
+TIDE_AG_KERNEL = 0
+TIDE_AG_SDMA = 1
+
+_lib = None
+
+
+class TideError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        name = _lib.tide_status_str(status).decode() if _lib is not None else str(status)
+        extra = f" (hipError {hip_error})" if status == TIDE_ERR_HIP else ""
+        super().__init__(f"{where}: {name}{extra}")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load_library(path: str | None = None):
+    """Load libtide.so (once).  Raises if it is not built: there is no other implementation."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m all_gather_placement_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P_i32, P_i64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    sig = {
+        "tide_layout_create": (i32, [i32, P_i32, P_i64, i32, ctypes.POINTER(vp)]),
+        "tide_layout_destroy": (None, [vp]),
+        "tide_layout_prepare": (i32, [vp]),
+        "tide_layout_num_params": (i32, [vp]),
+        "tide_layout_num_ranks": (i32, [vp]),
+        "tide_layout_shard_numel": (i64, [vp]),
+        "tide_layout_num_rs_chunks": (i64, [vp]),
+        "tide_layout_num_ag_chunks": (i64, [vp]),
+        "tide_layout_param": (i32, [vp, i32, P_i64, P_i64, P_i64, P_i64]),
+        "tide_layout_segment": (i32, [vp, i32, i32, P_i64, P_i64, P_i64, P_i64]),
+        "tide_rs_bf16_to_fp32": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]),
+        "tide_ag_place": (i32, [vp, vp, ctypes.POINTER(vp), i32, i32, vp]),
+        "tide_layout_copy_rs_items": (i32, [vp, i64, i64, P_i64]),
+        "tide_layout_copy_ag_items": (i32, [vp, i64, i64, P_i64]),
+        "tide_status_str": (ctypes.c_char_p, [i32]),
+        "tide_last_hip_error": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == library_path():
+        _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != TIDE_OK:
+        raise TideError(status, where, _lib.tide_last_hip_error() if status == TIDE_ERR_HIP else 0)
+
+
+def _ptr(x) -> int | None:
+    """Device address of a torch tensor (or a raw int address); None for None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------------------------------------
+# Entry points under their C names
+# ------------------------------------------------------------------------------------------------
+
+def tide_layout_create(shapes: Sequence[Sequence[int]], R: int) -> int:
+    """Create a layout for parameter shapes over R ranks; returns the raw handle."""
+    lib = load_library()
+    shapes = [tuple(int(d) for d in s) for s in shapes]
+    P = len(shapes)
+    ndims = (ctypes.c_int32 * max(P, 1))(*[len(s) for s in shapes])
+    flat = [d for s in shapes for d in s]
+    dims = (ctypes.c_int64 * max(len(flat), 1))(*flat)
+    out = ctypes.c_void_p()
+    _check(lib.tide_layout_create(P, ndims, dims, int(R), ctypes.byref(out)), "tide_layout_create")
+    return out.value
+
+
+def tide_rs_bf16_to_fp32(layout: int, grads, shards, cu_budget: int = 0, stream=None):
+    """grads: C lists of P bf16 tensors (or addresses); shards: R fp32 tensors (or addresses)."""
+    lib = load_library()
+    C = len(grads)
+    flat = [_ptr(g) for row in grads for g in row]
+    g_arr = (ctypes.c_void_p * max(len(flat), 1))(*flat)
+    s_list = [_ptr(s) for s in shards]
+    s_arr = (ctypes.c_void_p * max(len(s_list), 1))(*s_list)
+    _check(lib.tide_rs_bf16_to_fp32(layout, C, g_arr, s_arr, int(cu_budget), _stream_handle(stream)),
+           "tide_rs_bf16_to_fp32")
+
+
+def tide_ag_place(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0, stream=None):
+    """stage: R*S bf16 tensor (or address); params: P bf16 tensors (or addresses)."""
+    lib = load_library()
+    p_list = [_ptr(p) for p in params]
+    p_arr = (ctypes.c_void_p * max(len(p_list), 1))(*p_list)
+    _check(lib.tide_ag_place(layout, _ptr(stage), p_arr, int(mode), int(cu_budget), _stream_handle(stream)),
+           "tide_ag_place")
+
+
+class Layout:
+    """Owning wrapper of a tide_layout handle for one parameter group over R ranks."""
+
+    def __init__(self, shapes: Sequence[Sequence[int]], R: int):
+        self._lib = load_library()
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.R = int(R)
+        self.handle = tide_layout_create(self.shapes, self.R)
+        self.P = self._lib.tide_layout_num_params(self.handle)
+        self.S = self._lib.tide_layout_shard_numel(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self._lib.tide_layout_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # geometry --------------------------------------------------------------------------------
+    def param(self, p: int):
+        """(rows_p, L_p, m_p, o_p)."""
+        v = [ctypes.c_int64() for _ in range(4)]
+        _check(self._lib.tide_layout_param(self.handle, int(p), *[ctypes.byref(x) for x in v]), "tide_layout_param")
+        return tuple(x.value for x in v)
+
+    def segment(self, p: int, r: int):
+        """(src_offset, valid, dst_offset, pad) of rank r's slice of parameter p."""
+        v = [ctypes.c_int64() for _ in range(4)]
+        _check(self._lib.tide_layout_segment(self.handle, int(p), int(r), *[ctypes.byref(x) for x in v]),
+               "tide_layout_segment")
+        return tuple(x.value for x in v)
+
+    @property
+    def num_rs_chunks(self) -> int:
+        return self._lib.tide_layout_num_rs_chunks(self.handle)
+
+    @property
+    def num_ag_chunks(self) -> int:
+        return self._lib.tide_layout_num_ag_chunks(self.handle)
+
+    def rs_items(self):
+        """RS work items as an (n, 6) int64 array: p, r, src_offset, dst_offset, nvalid, npad."""
+        import numpy as np
+
+        n = self.num_rs_chunks
+        out = np.zeros((max(n, 1), 6), dtype=np.int64)
+        _check(self._lib.tide_layout_copy_rs_items(self.handle, 0, n, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+               "tide_layout_copy_rs_items")
+        return out[:n]
+
+    def ag_items(self):
+        """AG work items as an (n, 4) int64 array: p, stage_offset, param_offset, n."""
+        import numpy as np
+
+        n = self.num_ag_chunks
+        out = np.zeros((max(n, 1), 4), dtype=np.int64)
+        _check(self._lib.tide_layout_copy_ag_items(self.handle, 0, n, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+               "tide_layout_copy_ag_items")
+        return out[:n]
+
+    def prepare(self):
+        _check(self._lib.tide_layout_prepare(self.handle), "tide_layout_prepare")
+
+    # collectives -----------------------------------------------------------------------------
+    def rs_bf16_to_fp32(self, grads, shards, cu_budget: int = 0, stream=None):
+        _check_shapes_rs(self, grads, shards)
+        tide_rs_bf16_to_fp32(self.handle, grads, shards, cu_budget, stream)
+
+    def ag_place(self, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0, stream=None):
+        _check_shapes_ag(self, stage, params)
+        tide_ag_place(self.handle, stage, params, mode, cu_budget, stream)
+
+
+def _is_tensor(x) -> bool:
+    return hasattr(x, "data_ptr") and hasattr(x, "dtype")
+
+
+def _check_shapes_rs(L: Layout, grads, shards):
+    """Host-side shape/dtype checks of torch arguments (the C ABI sees only addresses)."""
+    import torch
+
+    if len(shards) != L.R:
+        raise ValueError(f"expected {L.R} shards, got {len(shards)}")
+    for row in grads:
+        if len(row) != L.P:
+            raise ValueError(f"each contributor needs {L.P} gradients, got {len(row)}")
+        for g, shape in zip(row, L.shapes):
+            if _is_tensor(g):
+                if g.dtype != torch.bfloat16 or not g.is_cuda or not g.is_contiguous() or tuple(g.shape) != shape:
+                    raise ValueError(f"gradient must be a contiguous cuda bf16 tensor of shape {shape}")
+    for s in shards:
+        if _is_tensor(s):
+            if s.dtype != torch.float32 or not s.is_cuda or not s.is_contiguous() or s.numel() != L.S:
+                raise ValueError(f"shard must be a contiguous cuda fp32 tensor of {L.S} elements")
+
+
+def _check_shapes_ag(L: Layout, stage, params):
+    import torch
+
+    if len(params) != L.P:
+        raise ValueError(f"expected {L.P} parameters, got {len(params)}")
+    if _is_tensor(stage):
+        if stage.dtype != torch.bfloat16 or not stage.is_cuda or not stage.is_contiguous() or stage.numel() != L.R * L.S:
+            raise ValueError(f"stage must be a contiguous cuda bf16 tensor of R*S = {L.R * L.S} elements")
+    for q, shape in zip(params, L.shapes):
+        if _is_tensor(q):
+            if q.dtype != torch.bfloat16 or not q.is_cuda or not q.is_contiguous() or tuple(q.shape) != shape:
+                raise ValueError(f"parameter must be a contiguous cuda bf16 tensor of shape {shape}")

@@ -1,0 +1,251 @@
+"""Benchmark of the layout-aware bf16->fp32 reduce-scatter + all-gather placement on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cu-budget B] [--ag-mode kernel|sdma]
+
+One step = one pass of the whole hot path over one parameter group already resident in HBM: the
+in-place reduce-scatter (C bf16 contributors -> R fp32 shards) followed by the all-gather placement
+(rank-major bf16 stage -> per-parameter storage).  The JSON line reports:
+
+  value       effective HBM GB/s of the step: algorithmic bytes of RS and AG / step time;
+  roofline    the RS kernel (the dominant one): algorithmic bytes per launch / its mean duration,
+              measured with HIP events on the launch stream, against the 8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload (same byte formula).
+
+Algorithmic bytes: RS = 2*C*numel (bf16 reads) + 4*R*S (fp32 writes, padding included);
+AG = 2*numel (reads) + 2*numel (writes).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "RS effective HBM GB/s (bf16 in + fp32 out) and % of 8 TB/s peak, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_1_8b_layer")
+    ap.add_argument("--cu-budget", type=int, default=0)
+    ap.add_argument("--ag-mode", choices=["kernel", "sdma"], default="kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain torch device copy of this many MiB per step (counter calibration)")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "tide_internal.h"):
+        with open(os.path.join(ROOT, "all_gather_placement_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per RS launch from the committed counter summary, if it matches this kernel."""
+    path = os.path.join(ROOT, "profiles", f"rs_kernel_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_b) or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(cfg, log):
+    """Time the oracle on a bounded sample of the workload: the first few parameters' RS and AG."""
+    import numpy as np
+
+    import oracle
+    from oracle.geometry import group_geometry
+    from workloads import normal_bf16_bits
+
+    # a sample of about 10-30 s of single-core numpy work: parameters in storage order up to ~40M
+    # elements (Llama-3.1-8B: q, k, v, o)
+    shapes, total = [], 0
+    for s in cfg.shapes:
+        n = int(np.prod(s))
+        if total and total + n > 45_000_000:
+            break
+        shapes.append(s)
+        total += n
+    grads = [[normal_bf16_bits(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(shapes)] for c in range(cfg.C)]
+    _, S = group_geometry(shapes, cfg.R)
+    stage = normal_bf16_bits((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
+    t0 = time.perf_counter()
+    oracle.reduce_scatter(grads, shapes, cfg.R)
+    t_rs = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.all_gather_place(stage, shapes, cfg.R)
+    t_ag = time.perf_counter() - t0
+    rs_bytes = 2 * cfg.C * total + 4 * cfg.R * S
+    ag_bytes = 4 * total
+    log(f"cpu oracle sample: {len(shapes)} params, {total} elems: RS {t_rs:.2f} s, AG {t_ag:.2f} s")
+    return {
+        "value": round((rs_bytes + ag_bytes) / (t_rs + t_ag) / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{cfg.name}: parameters {[n for n, _ in cfg.params[:len(shapes)]]} "
+                   f"({total} elements, R={cfg.R}, C={cfg.C}); numpy pack-then-sum RS + copy-out AG, "
+                   f"one RS and one AG pass, single-threaded numpy; {t_rs + t_ag:.1f} s"),
+        "rs_gbps": round(rs_bytes / t_rs / 1e9, 3),
+        "ag_gbps": round(ag_bytes / t_ag / 1e9, 3),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the node-local level on one GPU only; runs on more than one GPU "
+              "(--gpus > 1) are not part of this build.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    def log(msg):
+        if not args.quiet:
+            print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    import torch
+
+    from all_gather_placement_amd import Layout, TIDE_AG_KERNEL, TIDE_AG_SDMA
+    from oracle.geometry import group_geometry  # sizes only, for the byte formulas
+    from workloads import CONFIGS, normal_bf16_cuda
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {cfg.name}: P={cfg.P} R={cfg.R} C={cfg.C}")
+
+    numel = cfg.numel()
+    _, S = group_geometry(cfg.shapes, cfg.R)
+    rs_bytes = 2 * cfg.C * numel + 4 * cfg.R * S
+    ag_bytes = 4 * numel
+
+    grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
+             for c in range(cfg.C)]
+    shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
+    stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
+    params = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in cfg.shapes]
+    calib_src = calib_dst = None
+    if args.calib_copy_mib:
+        calib_src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        calib_dst = torch.empty_like(calib_src)
+    ag_mode = TIDE_AG_KERNEL if args.ag_mode == "kernel" else TIDE_AG_SDMA
+
+    L = Layout(cfg.shapes, cfg.R)
+    L.prepare()
+    stream = torch.cuda.current_stream()
+
+    def step(ev_rs=None, ev_ag=None):
+        if ev_rs:
+            ev_rs[0].record(stream)
+        L.rs_bf16_to_fp32(grads, shards, cu_budget=args.cu_budget, stream=stream)
+        if ev_rs:
+            ev_rs[1].record(stream)
+        if ev_ag:
+            ev_ag[0].record(stream)
+        L.ag_place(stage, params, mode=ag_mode, cu_budget=args.cu_budget, stream=stream)
+        if ev_ag:
+            ev_ag[1].record(stream)
+        if calib_src is not None:
+            calib_dst.copy_(calib_src)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rs_ev = [(ev(), ev()) for _ in range(K)]
+    ag_ev = [(ev(), ev()) for _ in range(K)]
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        step(rs_ev[i], ag_ev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    rs_ms = [a.elapsed_time(b) for a, b in rs_ev]
+    ag_ms = [a.elapsed_time(b) for a, b in ag_ev]
+    ms_per_step = total_ms / K
+    rs_mean = sum(rs_ms) / K
+    ag_mean = sum(ag_ms) / K
+    rs_sorted, ag_sorted = sorted(rs_ms), sorted(ag_ms)
+    log(f"{K} steps: {total_ms:.3f} ms GPU ({t_wall * 1e3:.1f} ms wall); RS mean {rs_mean:.4f} ms "
+        f"min {rs_sorted[0]:.4f} med {rs_sorted[K // 2]:.4f}; AG mean {ag_mean:.4f} ms min {ag_sorted[0]:.4f}")
+
+    value = (rs_bytes + ag_bytes) / (ms_per_step * 1e-3) / 1e9
+    rs_gbps = rs_bytes / (rs_mean * 1e-3) / 1e9
+    ag_gbps = ag_bytes / (ag_mean * 1e-3) / 1e9
+    traffic = read_traffic(cfg.name) if args.cu_budget == 0 else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name} RS+AG step (R={cfg.R}, C={cfg.C}, P={cfg.P})",
+            "R": cfg.R, "C": cfg.C, "P": cfg.P, "numel": numel, "S": S,
+            "cu_budget": args.cu_budget, "ag_mode": args.ag_mode,
+            "rs_bytes": rs_bytes, "ag_bytes": ag_bytes, "parallelism": "none (1 GPU, node-local level)",
+        },
+        "rs_gbps": round(rs_gbps, 2),
+        "rs_frac_of_peak": round(rs_gbps / HBM_PEAK_GBPS, 4),
+        "rs_ms_mean": round(rs_mean, 5),
+        "rs_ms_min_median": [round(rs_sorted[0], 5), round(rs_sorted[K // 2], 5)],
+        "ag_gbps": round(ag_gbps, 2),
+        "ag_frac_of_peak": round(ag_gbps / HBM_PEAK_GBPS, 4),
+        "ag_ms_mean": round(ag_mean, 5),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "rs_kernel<8,vec>",
+            "achieved": round(rs_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(rs_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    L.close()
+    del grads, shards, stage, params
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, log)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

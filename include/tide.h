@@ -1,0 +1,167 @@
+/*
+ * tide.h -- C ABI of the MI355X (gfx950) layout-aware reduce-scatter and all-gather placement.
+ *
+ * Method: "The Endgame of FSDP Communication: Layout-Aware Collectives on Copy Engines, RDMA, and
+ * NVSwitch" (arXiv 2610.38228; [Endgame] below).  FSDP2 keeps parameters and gradients as
+ * per-parameter tensors while its collectives work on flat rank-major buffers; TIDE folds the
+ * layout conversion into the collectives' addressing so that every piece is written once, at its
+ * final address ([Endgame] abstract; Figure 1).  This library implements, on one GPU, the
+ * node-local level of that idea:
+ *
+ *   - reduce-scatter (RS): C contributors' per-parameter bf16 gradients are read in place (no
+ *     full-group pack; [Endgame] Table 1 "In-Place Read"), summed in fp32 (the mixed-precision mode
+ *     of the abstract; Figure 6a's node-local fp32 partials) and written into R flat fp32 shards;
+ *   - all-gather placement (AG): a rank-major bf16 stage buffer is landed directly into
+ *     per-parameter storage ([Endgame] Figure 5b, one strided copy per parameter).
+ *
+ * Geometry ([Endgame] Table 2; symbols were lost in the text we have, names are ours):
+ *   parameter p has shape (rows_p, d1, d2, ...); row length L_p = d1*d2*... (1 for 1-D);
+ *   padded per-rank rows m_p = ceil(rows_p / R); per-rank shard elements e_p = m_p * L_p;
+ *   prefix offset o_p = sum_{q<p} e_q; per-rank packed shard elements S = sum_p e_p.
+ *   Rank r holds rows [r*m_p, r*m_p + v) of p with v = clamp(rows_p - r*m_p, 0, m_p); the other
+ *   (m_p - v) rows of its slice are padding.  Offsets are in elements; the byte offset is x2 in a
+ *   bf16 buffer and x4 in an fp32 buffer.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device addresses on the current device; host arrays are read only
+ *     during the call and may be freed as soon as it returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  RS and AG calls are
+ *     stream-ordered and asynchronous: they return after enqueueing, results are valid once the
+ *     stream reaches that point.  Inputs are never written.
+ *   - Errors are returned as tide_status; nothing is printed and nothing is thrown.  On an error
+ *     other than TIDE_ERR_HIP no work has been enqueued.  tide_last_hip_error() gives the HIP error
+ *     code behind the calling thread's most recent TIDE_ERR_HIP.
+ *   - A layout is immutable after creation and may be used from several streams and threads at
+ *     once.  The library owns it; the caller owns every buffer and stream.
+ */
+#ifndef TIDE_H
+#define TIDE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tide_layout tide_layout;
+
+typedef enum tide_status {
+  TIDE_OK = 0,
+  TIDE_ERR_INVALID = 1,     /* bad argument: null pointer, bad size, misalignment, overlap */
+  TIDE_ERR_NOMEM = 2,       /* host or device allocation failed */
+  TIDE_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  TIDE_ERR_UNSUPPORTED = 4  /* valid request this build cannot serve */
+} tide_status;
+
+/* Placement engines for tide_ag_place. */
+enum {
+  TIDE_AG_KERNEL = 0, /* hand-written copy kernel (bandwidth path; uses CUs) */
+  TIDE_AG_SDMA = 1    /* one 2-D DMA copy per parameter + one tail copy, no compute units */
+};
+
+/*
+ * Build the layout of one parameter group ([Endgame] Table 2; Figure 1).
+ *   num_params   P >= 1
+ *   ndims        host [P]; ndims[p] >= 1 is the rank of parameter p's shape
+ *   dims         host, the P shapes concatenated (sum of ndims entries), each entry >= 0
+ *   num_ranks    R >= 1
+ *   out          receives the new layout (unchanged on error)
+ * Host-only: no HIP call is made.  Device tables are uploaded on first use per device, or by
+ * tide_layout_prepare().  Errors: TIDE_ERR_INVALID (bad argument, or S or any offset beyond 2^62),
+ * TIDE_ERR_NOMEM.
+ */
+tide_status tide_layout_create(int32_t num_params, const int32_t* ndims, const int64_t* dims,
+                               int32_t num_ranks, tide_layout** out);
+
+/* Free a layout and its device tables.  Every stream that used it must have been synchronised.
+ * NULL is ignored. */
+void tide_layout_destroy(tide_layout* layout);
+
+/* Upload the layout's device tables to the current device (idempotent).  After this, RS and AG
+ * calls on that device allocate nothing except when a call passes more pointers than any earlier
+ * one.  Errors: TIDE_ERR_INVALID (null), TIDE_ERR_NOMEM, TIDE_ERR_HIP. */
+tide_status tide_layout_prepare(const tide_layout* layout);
+
+/* Geometry queries (host only).  Return -1 for a NULL layout. */
+int32_t tide_layout_num_params(const tide_layout* layout);  /* P */
+int32_t tide_layout_num_ranks(const tide_layout* layout);   /* R */
+int64_t tide_layout_shard_numel(const tide_layout* layout); /* S */
+int64_t tide_layout_num_rs_chunks(const tide_layout* layout); /* work items of one RS call */
+int64_t tide_layout_num_ag_chunks(const tide_layout* layout); /* work items of one AG call */
+
+/* Per-parameter geometry: rows_p, L_p, m_p, o_p (any output pointer may be NULL).
+ * Errors: TIDE_ERR_INVALID (null layout or p out of range). */
+tide_status tide_layout_param(const tide_layout* layout, int32_t p, int64_t* rows, int64_t* row_len,
+                              int64_t* padded_rows, int64_t* offset);
+
+/* Segment (p, r): rank r's slice of parameter p.
+ *   src_offset  first element of the slice inside parameter p's storage (r * m_p * L_p)
+ *   valid       elements that carry data (v * L_p)
+ *   dst_offset  first element of the slice inside rank r's flat shard (o_p)
+ *   pad         padding elements that follow the valid ones in the shard ((m_p - v) * L_p)
+ * Errors: TIDE_ERR_INVALID. */
+tide_status tide_layout_segment(const tide_layout* layout, int32_t p, int32_t r, int64_t* src_offset,
+                                int64_t* valid, int64_t* dst_offset, int64_t* pad);
+
+/* Work-item tables, for tests and tools (host only).  Copies items [first, first + n) into `out`:
+ * RS items as 6 int64 each (p, r, src_offset, dst_offset, nvalid, npad) -- nvalid summed elements
+ * of parameter p from src_offset land in shard r at dst_offset, then npad zeros; AG items as 4
+ * int64 each (p, stage_offset, param_offset, n).  Errors: TIDE_ERR_INVALID (null, range). */
+tide_status tide_layout_copy_rs_items(const tide_layout* layout, int64_t first, int64_t n, int64_t* out);
+tide_status tide_layout_copy_ag_items(const tide_layout* layout, int64_t first, int64_t n, int64_t* out);
+
+/*
+ * Reduce-scatter, bf16 in, fp32 out ([Endgame] abstract: per-parameter bf16 gradients reduced
+ * into fp32 shards; Figure 6a: node-local fp32 sums; Table 1: In-Place Read; Figure 1: each piece
+ * written once at its final address).
+ *   C          number of contributors, >= 1
+ *   grads      host [C*P]: grads[c*P + p] is contributor c's gradient of parameter p, a contiguous
+ *              row-major bf16 device tensor of rows_p * L_p elements, 2-byte aligned (NULL allowed
+ *              only for empty parameters).  Read in place, never written.
+ *   shards     host [R]: shards[r] is rank r's flat fp32 device shard of S elements, 4-byte aligned.
+ *   cu_budget  0: one launch, one short-lived workgroup per work item, as wide as the device runs.
+ *              B > 0: at most B workgroups (256 threads each) resident at a time; each processes a
+ *              few work items and exits, and the call issues as many launches as needed.
+ *   stream     hipStream_t as void*.
+ * Result, for every r, p and element k of the slice: shards[r][o_p + k] =
+ *   x_0 (+) x_1 (+) ... (+) x_{C-1}, x_c = grads[c*P+p][r*m_p*L_p + k] widened exactly to fp32,
+ *   (+) an IEEE binary32 add with round-to-nearest-even, applied in ascending c, for k < v*L_p;
+ *   +0.0 for the padding elements v*L_p <= k < e_p.  Every shard element is written exactly once,
+ *   independently of cu_budget; fp32 denormals are kept.
+ * 16-byte-aligned grads and shards take the vector path; any other legal alignment takes a
+ * slower element path with identical results.
+ * Errors: TIDE_ERR_INVALID (null layout/arrays, C < 1, cu_budget < 0, null or misaligned pointer,
+ * any shard overlapping another shard or any gradient), TIDE_ERR_NOMEM, TIDE_ERR_HIP.
+ */
+tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* grads,
+                                 float* const* shards, int32_t cu_budget, void* stream);
+
+/*
+ * All-gather placement ([Endgame] Figure 5b: one strided copy per parameter from the stage slots
+ * into parameter storage; abstract: shards delivered directly to parameter storage).
+ *   stage      device, R*S bf16 elements, rank-major: rank r's shard starts at element r*S.
+ *   params     host [P]: params[p] is parameter p's contiguous bf16 device storage of rows_p * L_p
+ *              elements (NULL allowed only for empty parameters).
+ *   mode       TIDE_AG_KERNEL or TIDE_AG_SDMA.
+ *   cu_budget  as for the RS (ignored by TIDE_AG_SDMA).
+ * Result: params[p][r*m_p*L_p + k] = stage[r*S + o_p + k] for every r and k < v*L_p, copied as
+ * bits; stage padding is never read into a parameter; every parameter element is written once.
+ * All pointers must be 2-byte aligned; 16-byte alignment selects the vector path.
+ * Errors: TIDE_ERR_INVALID (null/misaligned pointer, bad mode, a parameter overlapping the stage
+ * or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a compute-unit-free copy),
+ * TIDE_ERR_HIP.
+ */
+tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params,
+                          int32_t mode, int32_t cu_budget, void* stream);
+
+/* Static, NUL-terminated name of a status code ("TIDE_OK", ...; "unknown" otherwise). */
+const char* tide_status_str(int32_t status);
+
+/* HIP error code (hipError_t value) behind the calling thread's last TIDE_ERR_HIP, 0 if none. */
+int32_t tide_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIDE_H */

@@ -1,0 +1,274 @@
+"""Host-only tests of the C-ABI library (no GPU, no compute calls).
+
+* the library loads and exports every function that include/tide.h declares;
+* layout geometry equals the oracle's independent geometry on every workload and on random tiny
+  groups;
+* the work-item tables tile every shard element and every placed parameter element exactly once,
+  and every kernel access they imply stays inside its buffer (checked here, before any launch);
+* argument validation returns TIDE_ERR_INVALID before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import all_gather_placement_amd as tide
+from all_gather_placement_amd import tide as tb
+from oracle import geometry as ogeo
+from workloads import ORDERED, TINY
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "tide.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(tide_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tb.load_library()
+    names = _declared_functions()
+    assert "tide_rs_bf16_to_fp32" in names and "tide_ag_place" in names and "tide_layout_create" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/tide.h but not exported"
+    # and the binding exposes the three entry points under the same names
+    for n in ("tide_layout_create", "tide_rs_bf16_to_fp32", "tide_ag_place"):
+        assert callable(getattr(tide, n))
+
+
+def test_status_strings():
+    lib = tb.load_library()
+    assert lib.tide_status_str(0) == b"TIDE_OK"
+    assert lib.tide_status_str(1) == b"TIDE_ERR_INVALID"
+    assert lib.tide_status_str(4) == b"TIDE_ERR_UNSUPPORTED"
+    assert lib.tide_status_str(99) == b"unknown"
+    assert lib.tide_last_hip_error() == 0
+
+
+def _check_geometry(shapes, R):
+    geo, S = ogeo.group_geometry(shapes, R)
+    with tide.Layout(shapes, R) as L:
+        assert L.S == S and L.P == len(shapes)
+        for p, g in enumerate(geo):
+            assert L.param(p) == (g.rows, g.L, g.m, g.o)
+            for r in range(R):
+                v = ogeo.valid_rows(g.rows, g.m, r)
+                assert L.segment(p, r) == (r * g.m * g.L, v * g.L, g.o, (g.m - v) * g.L)
+
+
+@pytest.mark.parametrize("cfg", ORDERED, ids=lambda c: c.name)
+def test_layout_geometry_matches_oracle(cfg):
+    if cfg.P > 50:
+        # segment queries over 391 x 16 are fine but slow through ctypes; sample them
+        geo, S = ogeo.group_geometry(cfg.shapes, cfg.R)
+        with tide.Layout(cfg.shapes, cfg.R) as L:
+            assert L.S == S
+            for p in list(range(0, cfg.P, 37)) + [cfg.P - 1]:
+                g = geo[p]
+                assert L.param(p) == (g.rows, g.L, g.m, g.o)
+        return
+    _check_geometry(cfg.shapes, cfg.R)
+
+
+@st.composite
+def groups(draw):
+    R = draw(st.integers(1, 70))
+    P = draw(st.integers(1, 6))
+    shapes = []
+    for _ in range(P):
+        nd = draw(st.integers(1, 4))
+        rows = draw(st.integers(0, 300))
+        rest = [draw(st.integers(0, 9)) for _ in range(nd - 1)]
+        shapes.append(tuple([rows] + rest))
+    return shapes, R
+
+
+@settings(max_examples=80, deadline=None)
+@given(groups())
+def test_layout_geometry_hypothesis(g):
+    shapes, R = g
+    _check_geometry(shapes, R)
+
+
+def check_items_tile_exactly(shapes, R, rs_items, ag_items, rs_chunk=16384, ag_chunk=32768):
+    """Every shard element written once, every parameter element placed once, all in bounds."""
+    geo, S = ogeo.group_geometry(shapes, R)
+    numel = [g.rows * g.L for g in geo]
+    # --- RS: bounds
+    p, r, src, dst, nv, npad = (rs_items[:, i] for i in range(6))
+    assert np.all((p >= 0) & (p < len(shapes)) & (r >= 0) & (r < R))
+    assert np.all((nv >= 0) & (npad >= 0) & (nv + npad > 0) & (nv <= rs_chunk) & (npad <= rs_chunk))
+    assert np.all(dst >= 0) and np.all(dst + nv + npad <= S)
+    nz = nv > 0
+    numel_p = np.array(numel, dtype=np.int64)[p]
+    assert np.all(src[nz] >= 0) and np.all(src[nz] + nv[nz] <= numel_p[nz])
+    # --- RS: each (r, k) written once; valid outputs read the right source element
+    cover = np.zeros((R, S), dtype=np.int32)
+    for i in range(len(rs_items)):
+        cover[r[i], dst[i]: dst[i] + nv[i] + npad[i]] += 1
+    assert np.all(cover == 1)
+    for q, g in enumerate(geo):
+        for rr in range(R):
+            v = ogeo.valid_rows(g.rows, g.m, rr)
+            sel = (p == q) & (r == rr) & nz
+            # valid items of this segment are contiguous in both spaces with the same offset delta
+            assert np.all(src[sel] - r[sel] * g.m * g.L == dst[sel] - g.o)
+            assert int(nv[sel].sum()) == v * g.L
+            assert int(npad[(p == q) & (r == rr)].sum()) == (g.m - v) * g.L
+    # interior item boundaries on 16-byte (8-element) source boundaries
+    starts_inside = nz & (src % 8 != 0)
+    for i in np.nonzero(starts_inside)[0]:
+        q, rr = p[i], r[i]
+        assert src[i] == rr * geo[q].m * geo[q].L, "only a segment's first item may start unaligned"
+    # --- AG
+    if len(ag_items):
+        ap, asrc, adst, an = (ag_items[:, i] for i in range(4))
+        assert np.all((an > 0) & (an <= ag_chunk))
+        assert np.all(asrc >= 0) and np.all(asrc + an <= R * S)
+        anumel = np.array(numel, dtype=np.int64)[ap]
+        assert np.all(adst >= 0) and np.all(adst + an <= anumel)
+        for q, g in enumerate(geo):
+            pc = np.zeros(numel[q], dtype=np.int32)
+            for i in np.nonzero(ap == q)[0]:
+                pc[adst[i]: adst[i] + an[i]] += 1
+                # stage slot rank and the destination row agree
+                rr = asrc[i] // S
+                assert asrc[i] - rr * S - g.o == adst[i] - rr * g.m * g.L
+                assert 0 <= asrc[i] - rr * S - g.o and asrc[i] - rr * S - g.o + an[i] <= g.e
+            assert np.all(pc == 1)
+    else:
+        assert sum(numel) == 0
+
+
+@settings(max_examples=60, deadline=None)
+@given(groups())
+def test_work_items_tile_hypothesis(g):
+    shapes, R = g
+    with tide.Layout(shapes, R) as L:
+        check_items_tile_exactly(shapes, R, L.rs_items(), L.ag_items())
+
+
+def test_work_items_tile_tiny():
+    with tide.Layout(TINY.shapes, TINY.R) as L:
+        check_items_tile_exactly(TINY.shapes, TINY.R, L.rs_items(), L.ag_items())
+
+
+@pytest.mark.parametrize("cfg", [c for c in ORDERED if c.name != "tiny"], ids=lambda c: c.name)
+def test_work_items_full_configs_in_bounds(cfg):
+    """Full workloads: bounds and exact coverage, checked with interval sums (no dense arrays)."""
+    geo, S = ogeo.group_geometry(cfg.shapes, cfg.R)
+    with tide.Layout(cfg.shapes, cfg.R) as L:
+        it = L.rs_items()
+        ag = L.ag_items()
+    p, r, src, dst, nv, npad = (it[:, i] for i in range(6))
+    numel = np.array([g.rows * g.L for g in geo], dtype=np.int64)
+    assert np.all(src >= 0) and np.all(src + nv <= numel[p])
+    assert np.all(dst >= 0) and np.all(dst + nv + npad <= S)
+    # per shard: items sorted by dst tile [0, S) with no gap or overlap
+    for rr in range(cfg.R):
+        sel = r == rr
+        order = np.argsort(dst[sel])
+        d = dst[sel][order]
+        n = (nv + npad)[sel][order]
+        assert d[0] == 0 and np.all(d[1:] == d[:-1] + n[:-1]) and d[-1] + n[-1] == S
+    # every source element of every parameter is read by exactly one item
+    assert int(nv.sum()) == cfg.numel()
+    # all large workloads are 16-byte aligned everywhere: the vector path covers everything
+    assert np.all(src % 8 == 0) and np.all(dst % 4 == 0)
+    ap, asrc, adst, an = (ag[:, i] for i in range(4))
+    assert np.all(asrc + an <= cfg.R * S) and np.all(adst + an <= numel[ap])
+    assert int(an.sum()) == cfg.numel()
+    assert np.all((asrc - adst) % 8 == 0)
+
+
+# ------------------------------------------------------------------------------------------------
+# Argument validation: every case returns before any HIP call
+# ------------------------------------------------------------------------------------------------
+
+def _vp_array(vals):
+    return (ctypes.c_void_p * max(len(vals), 1))(*vals)
+
+
+def test_layout_create_rejects_bad_arguments():
+    lib = tb.load_library()
+    out = ctypes.c_void_p()
+    nd = (ctypes.c_int32 * 1)(2)
+    dims = (ctypes.c_int64 * 2)(4, 4)
+    assert lib.tide_layout_create(0, nd, dims, 4, ctypes.byref(out)) == tb.TIDE_ERR_INVALID
+    assert lib.tide_layout_create(1, nd, dims, 0, ctypes.byref(out)) == tb.TIDE_ERR_INVALID
+    assert lib.tide_layout_create(1, None, dims, 4, ctypes.byref(out)) == tb.TIDE_ERR_INVALID
+    assert lib.tide_layout_create(1, nd, dims, 4, None) == tb.TIDE_ERR_INVALID
+    nd0 = (ctypes.c_int32 * 1)(0)
+    assert lib.tide_layout_create(1, nd0, dims, 4, ctypes.byref(out)) == tb.TIDE_ERR_INVALID
+    neg = (ctypes.c_int64 * 2)(4, -1)
+    assert lib.tide_layout_create(1, nd, neg, 4, ctypes.byref(out)) == tb.TIDE_ERR_INVALID
+    huge = (ctypes.c_int64 * 2)(1 << 40, 1 << 40)
+    assert lib.tide_layout_create(1, nd, huge, 4, ctypes.byref(out)) == tb.TIDE_ERR_INVALID
+    assert out.value is None
+    assert lib.tide_layout_num_params(None) == -1 and lib.tide_layout_shard_numel(None) == -1
+    lib.tide_layout_destroy(None)
+
+
+def test_query_rejects_out_of_range():
+    lib = tb.load_library()
+    with tide.Layout(TINY.shapes, TINY.R) as L:
+        x = ctypes.c_int64()
+        assert lib.tide_layout_param(L.handle, 3, ctypes.byref(x), None, None, None) == tb.TIDE_ERR_INVALID
+        assert lib.tide_layout_param(L.handle, -1, None, None, None, None) == tb.TIDE_ERR_INVALID
+        assert lib.tide_layout_segment(L.handle, 0, 4, None, None, None, None) == tb.TIDE_ERR_INVALID
+        buf = (ctypes.c_int64 * 6)()
+        assert lib.tide_layout_copy_rs_items(L.handle, L.num_rs_chunks, 1, buf) == tb.TIDE_ERR_INVALID
+
+
+def _fake_rs_args(L, C, base=1 << 32, g_step=1 << 20, s_step=1 << 20):
+    grads = [base + (c * L.P + p) * g_step for c in range(C) for p in range(L.P)]
+    shards = [base + (1 << 30) + r * s_step for r in range(L.R)]
+    return grads, shards
+
+
+def test_rs_rejects_bad_arguments_before_any_hip_call():
+    lib = tb.load_library()
+    with tide.Layout(TINY.shapes, TINY.R) as L:
+        g, s = _fake_rs_args(L, 4)
+        call = lambda gg, ss, C=4, budget=0: lib.tide_rs_bf16_to_fp32(L.handle, C, _vp_array(gg), _vp_array(ss), budget, None)
+        INV = tb.TIDE_ERR_INVALID
+        assert lib.tide_rs_bf16_to_fp32(None, 4, _vp_array(g), _vp_array(s), 0, None) == INV
+        assert lib.tide_rs_bf16_to_fp32(L.handle, 4, None, _vp_array(s), 0, None) == INV
+        assert call(g, s, C=0) == INV
+        assert call(g, s, budget=-1) == INV
+        g2 = list(g); g2[5] = None
+        assert call(g2, s) == INV                     # null gradient of a non-empty parameter
+        g3 = list(g); g3[1] += 1
+        assert call(g3, s) == INV                     # odd address for bf16
+        s2 = list(s); s2[2] += 2
+        assert call(g, s2) == INV                     # fp32 shard not 4-byte aligned
+        s3 = list(s); s3[1] = s3[0] + 8
+        assert call(g, s3) == INV                     # shards overlap
+        s4 = list(s); s4[3] = g[2] + 4
+        assert call(g, s4) == INV                     # shard overlaps a gradient
+        assert lib.tide_last_hip_error() == 0
+
+
+def test_ag_rejects_bad_arguments_before_any_hip_call():
+    lib = tb.load_library()
+    with tide.Layout(TINY.shapes, TINY.R) as L:
+        stage = 1 << 32
+        params = [(1 << 33) + p * (1 << 20) for p in range(L.P)]
+        call = lambda st_, pp, mode=0, budget=0: lib.tide_ag_place(L.handle, st_, _vp_array(pp), mode, budget, None)
+        INV = tb.TIDE_ERR_INVALID
+        assert call(stage, params, mode=2) == INV
+        assert call(stage, params, budget=-1) == INV
+        assert call(None, params) == INV
+        assert call(stage + 1, params) == INV
+        pp = list(params); pp[0] = None
+        assert call(stage, pp) == INV
+        pp = list(params); pp[1] = stage + 10
+        assert call(stage, pp) == INV                 # parameter inside the stage
+        pp = list(params); pp[2] = pp[0] + 2
+        assert call(stage, pp) == INV                 # parameters overlap
+        assert lib.tide_ag_place(None, stage, _vp_array(params), 0, 0, None) == INV

@@ -1,0 +1,402 @@
+"""GPU parity of the HIP reduce-scatter and all-gather placement against the CPU oracle.
+
+Small and medium groups are compared element by element (bit-exact) with the oracle on the same
+seeded inputs; the full-size workloads are compared on sampled outputs that the oracle computes one
+by one, plus properties that hold at any size (bit-exact agreement with a plain torch
+fixed-order fp32 sum, padding zeros, write-once coverage, the AG->RS round trip).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import geometry as ogeo
+from oracle import rs as ors
+from all_gather_placement_amd import Layout, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError
+from workloads import ORDERED, TINY, normal_bf16_bits, normal_bf16_cuda, f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+POISON_F32 = 0x7FC0DEAD  # a NaN pattern no sum produces from these inputs
+POISON_BF16 = 0x7FC1
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def dev_bf16(bits: np.ndarray, pad_elems: int = 0):
+    """Upload uint16 bits as a contiguous bf16 cuda tensor; pad_elems shifts it off 16-B alignment."""
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    if pad_elems == 0:
+        return torch.from_numpy(flat.view(np.int16).copy()).cuda().view(torch.bfloat16).reshape(bits.shape)
+    buf = torch.empty(flat.size + pad_elems + 8, dtype=torch.int16, device="cuda")
+    view = buf[pad_elems: pad_elems + flat.size]
+    view.copy_(torch.from_numpy(flat.view(np.int16).copy()))
+    return view.view(torch.bfloat16).reshape(bits.shape)
+
+
+def host_bits_bf16(t) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_bits_f32(t) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+def poisoned_shards(R, S, pad_elems=0):
+    out = []
+    for r in range(R):
+        buf = torch.full((S + pad_elems + 4,), POISON_F32, dtype=torch.int32, device="cuda")
+        out.append(buf[pad_elems: pad_elems + S].view(torch.float32))
+    return out
+
+
+def run_rs(shapes, R, grads_bits, cu_budget=0, g_pad=None, s_pad=0, stream=None):
+    """Upload, run the HIP RS, return (R, S) uint32 bits."""
+    C = len(grads_bits)
+    g_pad = g_pad or (lambda c, p: 0)
+    grads = [[dev_bf16(grads_bits[c][p], g_pad(c, p)) for p in range(len(shapes))] for c in range(C)]
+    with Layout(shapes, R) as L:
+        shards = poisoned_shards(R, L.S, s_pad)
+        L.rs_bf16_to_fp32(grads, shards, cu_budget=cu_budget, stream=stream)
+        torch.cuda.synchronize()
+        return np.stack([host_bits_f32(s) for s in shards]) if L.S else np.zeros((R, 0), np.uint32)
+
+
+def assert_rs_equal(got_bits, want_f32):
+    want = np.asarray(want_f32, dtype=np.float32).view(np.uint32)
+    assert got_bits.shape == want.shape
+    bad = np.nonzero(got_bits != want)
+    if bad[0].size:
+        i = tuple(b[0] for b in bad)
+        raise AssertionError(f"{bad[0].size} mismatches; first at {i}: got {got_bits[i]:#010x} want {want[i]:#010x}")
+
+
+def run_ag(shapes, R, stage_bits, mode=TIDE_AG_KERNEL, cu_budget=0, st_pad=0, p_pad=None):
+    p_pad = p_pad or (lambda p: 0)
+    stage = dev_bf16(stage_bits, st_pad)
+    params = []
+    for p, s in enumerate(shapes):
+        n = int(np.prod(s, dtype=np.int64))
+        buf = torch.full((n + p_pad(p) + 8,), POISON_BF16, dtype=torch.int16, device="cuda")
+        params.append(buf[p_pad(p): p_pad(p) + n].view(torch.bfloat16).reshape(s))
+    with Layout(shapes, R) as L:
+        L.ag_place(stage, params, mode=mode, cu_budget=cu_budget)
+        torch.cuda.synchronize()
+    return [host_bits_bf16(q) for q in params]
+
+
+# ------------------------------------------------------------------------------------------------
+# Small groups: full element-by-element parity
+# ------------------------------------------------------------------------------------------------
+
+def test_tiny_rs_bit_exact(gpu_available):
+    say("tiny RS")
+    g = [[normal_bf16_bits(s, TINY.sigma, TINY.cfg_id, c, p) for p, s in enumerate(TINY.shapes)] for c in range(TINY.C)]
+    want = oracle.reduce_scatter(g, TINY.shapes, TINY.R)
+    for budget in (0, 1, 2, 5):
+        assert_rs_equal(run_rs(TINY.shapes, TINY.R, g, cu_budget=budget), want)
+
+
+@pytest.mark.parametrize("mode", [TIDE_AG_KERNEL, TIDE_AG_SDMA], ids=["kernel", "sdma"])
+def test_tiny_ag_bit_exact(gpu_available, mode):
+    say(f"tiny AG mode={mode}")
+    geo, S = ogeo.group_geometry(TINY.shapes, TINY.R)
+    stage = normal_bf16_bits((TINY.R * S,), 1.0, TINY.cfg_id, 1 << 20, 0)
+    # poison the stage padding: it must never reach a parameter
+    st2 = stage.reshape(TINY.R, S).copy()
+    for gg in geo:
+        for r in range(TINY.R):
+            v = ogeo.valid_rows(gg.rows, gg.m, r)
+            st2[r, gg.o + v * gg.L: gg.o + gg.e] = POISON_BF16
+    stage = st2.ravel()
+    want = oracle.all_gather_place(stage, TINY.shapes, TINY.R)
+    got = run_ag(TINY.shapes, TINY.R, stage, mode=mode)
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+
+
+GROUPS = [
+    # (shapes, R, C): ragged tails, rows < R, empty parameters, 1-D/3-D, runtime C > 8
+    ([(7, 5), (16, 3), (1, 9)], 4, 4),
+    ([(1000, 37), (4099,), (333, 65), (0, 4), (3, 2, 5)], 8, 8),
+    ([(5, 1), (2,), (9, 3, 3)], 9, 3),
+    ([(20000,), (129, 257)], 3, 1),
+    ([(64, 64)], 1, 2),
+    ([(77, 31), (3,)], 16, 10),
+    ([(40000, 3), (11, 4097)], 5, 5),
+    ([(2, 3)], 7, 12),
+]
+
+
+@pytest.mark.parametrize("case", range(len(GROUPS)))
+def test_groups_rs_bit_exact(gpu_available, case):
+    shapes, R, C = GROUPS[case]
+    say(f"group {case}: shapes={shapes} R={R} C={C}")
+    g = [[normal_bf16_bits(s, 1.0, 50 + case, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    want = oracle.reduce_scatter(g, shapes, R)
+    assert_rs_equal(run_rs(shapes, R, g), want)
+    assert_rs_equal(run_rs(shapes, R, g, cu_budget=3), want)
+
+
+@pytest.mark.parametrize("case", range(len(GROUPS)))
+@pytest.mark.parametrize("mode", [TIDE_AG_KERNEL, TIDE_AG_SDMA], ids=["kernel", "sdma"])
+def test_groups_ag_bit_exact(gpu_available, case, mode):
+    shapes, R, _ = GROUPS[case]
+    say(f"group {case} AG mode={mode}")
+    geo, S = ogeo.group_geometry(shapes, R)
+    stage = normal_bf16_bits((R * S,), 1.0, 60 + case, 0)
+    want = oracle.all_gather_place(stage, shapes, R)
+    got = run_ag(shapes, R, stage, mode=mode)
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("g_off", [0, 1, 3, 7])
+@pytest.mark.parametrize("s_off", [0, 1, 2])
+def test_rs_alignment_sweep(gpu_available, g_off, s_off):
+    """Base pointers shifted off 16-byte alignment: the element path must agree bit for bit."""
+    shapes, R, C = [(300, 17), (1025,), (8, 64)], 4, 6
+    say(f"alignment g_off={g_off} s_off={s_off}")
+    g = [[normal_bf16_bits(s, 1.0, 70, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    want = oracle.reduce_scatter(g, shapes, R)
+    # mixed offsets across contributors when g_off > 0
+    got = run_rs(shapes, R, g, g_pad=lambda c, p: (g_off * (c + 1)) % 8, s_pad=s_off)
+    assert_rs_equal(got, want)
+
+
+@pytest.mark.parametrize("st_off,p_off", [(0, 0), (1, 0), (0, 3), (5, 5), (2, 6)])
+def test_ag_alignment_sweep(gpu_available, st_off, p_off):
+    shapes, R = [(300, 17), (1025,), (8, 64)], 4
+    say(f"AG alignment st_off={st_off} p_off={p_off}")
+    geo, S = ogeo.group_geometry(shapes, R)
+    stage = normal_bf16_bits((R * S,), 1.0, 71, 0)
+    want = oracle.all_gather_place(stage, shapes, R)
+    for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA):
+        got = run_ag(shapes, R, stage, mode=mode, st_pad=st_off, p_pad=lambda p: (p_off * (p + 1)) % 8)
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b)
+
+
+def test_rs_special_values(gpu_available):
+    """-0.0, bf16 subnormals, +-inf, order-sensitive triples, integer sums."""
+    say("special values")
+    shapes, R = [(4, 8), (6,)], 2
+    vals = np.array([0x8000, 0x0000, 0x0001, 0x8001, 0x3F80, 0x3380, 0x7F80, 0xFF80, 0x7F00, 0x4B80],
+                    dtype=np.uint16)
+    rng = np.random.default_rng(5)
+    C = 5
+    g = [[vals[rng.integers(0, len(vals), size=s)] for s in shapes] for _ in range(C)]
+    # force the golden order case into element 0 and the all -0.0 case into element 1
+    for c, b in enumerate([0x3F80, 0x3380, 0x3380, 0x0000, 0x0000]):
+        g[c][0].reshape(-1)[0] = b if c < 3 else 0x0000
+    for c in range(C):
+        g[c][0].reshape(-1)[1] = 0x8000
+    want = oracle.reduce_scatter(g, shapes, R)
+    got = run_rs(shapes, R, g)
+    wb = want.view(np.uint32)
+    both_nan = np.isnan(want) & np.isnan(got.view(np.float32))
+    assert np.array_equal(got[~both_nan], wb[~both_nan])
+    assert got[0, 1] == 0x80000000
+
+
+def test_rs_inputs_unchanged_and_stream(gpu_available):
+    say("input immutability on a side stream")
+    shapes, R, C = [(513, 9), (77,)], 3, 4
+    g = [[normal_bf16_bits(s, 1.0, 72, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    grads = [[dev_bf16(g[c][p]) for p in range(len(shapes))] for c in range(C)]
+    before = [[host_bits_bf16(t).copy() for t in row] for row in grads]
+    side = torch.cuda.Stream()
+    with Layout(shapes, R) as L:
+        shards = poisoned_shards(R, L.S)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            L.rs_bf16_to_fp32(grads, shards)
+        side.synchronize()
+        got = np.stack([host_bits_f32(s) for s in shards])
+    assert_rs_equal(got, oracle.reduce_scatter(g, shapes, R))
+    for row_b, row in zip(before, grads):
+        for b, t in zip(row_b, row):
+            assert np.array_equal(b, host_bits_bf16(t))
+
+
+def test_identical_contributor_buffers(gpu_available):
+    """The same buffer passed as every contributor (inputs may alias): C * x exactly."""
+    say("aliased contributors")
+    shapes, R, C = [(100, 10)], 4, 8
+    x = normal_bf16_bits(shapes[0], 1.0, 73, 0)
+    t = dev_bf16(x)
+    with Layout(shapes, R) as L:
+        shards = poisoned_shards(R, L.S)
+        L.rs_bf16_to_fp32([[t]] * C, shards)
+        torch.cuda.synchronize()
+        got = np.stack([host_bits_f32(s) for s in shards])
+    assert_rs_equal(got, oracle.reduce_scatter([[x]] * C, shapes, R))
+
+
+def test_overlap_rejected(gpu_available):
+    shapes, R = [(64,)], 2
+    g = dev_bf16(normal_bf16_bits((64,), 1.0, 74, 0))
+    with Layout(shapes, R) as L:
+        buf = torch.empty(64, dtype=torch.float32, device="cuda")
+        with pytest.raises(TideError):
+            L.rs_bf16_to_fp32([[g]], [buf[:32], buf[16:48]])
+
+
+def test_ag_then_rs_round_trip(gpu_available):
+    say("AG -> RS(C=1) round trip")
+    shapes, R = [(7, 5), (16, 3), (1, 9), (1000, 33)], 4
+    geo, S = ogeo.group_geometry(shapes, R)
+    stage_bits = normal_bf16_bits((R * S,), 1.0, 75, 0)
+    stage = dev_bf16(stage_bits)
+    params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    with Layout(shapes, R) as L:
+        L.ag_place(stage, params)
+        shards = poisoned_shards(R, S)
+        L.rs_bf16_to_fp32([params], shards)
+        torch.cuda.synchronize()
+        got = np.stack([host_bits_f32(s) for s in shards])
+    W = ors.widen(stage_bits).reshape(R, S).view(np.uint32)
+    for gg in geo:
+        for r in range(R):
+            v = ogeo.valid_rows(gg.rows, gg.m, r)
+            a, b, e = gg.o, gg.o + v * gg.L, gg.o + gg.e
+            assert np.array_equal(got[r, a:b], W[r, a:b])
+            assert np.all(got[r, b:e] == 0)
+
+
+# ------------------------------------------------------------------------------------------------
+# Full-size workloads (the launch configuration the benchmark times: cu_budget = 0)
+# ------------------------------------------------------------------------------------------------
+
+FULL = [c for c in ORDERED if c.name != "tiny"]
+
+
+def _sample_positions(geo, S, R, n_random, rng):
+    """Random (r, k) plus the first and last element of every segment (and padding)."""
+    rs = list(rng.integers(0, R, n_random))
+    ks = list(rng.integers(0, S, n_random))
+    for g in geo:
+        if g.e == 0:
+            continue
+        for r in range(R):
+            rs += [r, r]
+            ks += [g.o, g.o + g.e - 1]
+    return np.array(rs, dtype=np.int64), np.array(ks, dtype=np.int64)
+
+
+def _locate_many(geo, R, rs, ks):
+    """Vectorised oracle geometry: (p, flat source index or -1 for padding) per sample."""
+    offs = np.array([g.o for g in geo], dtype=np.int64)
+    p = np.searchsorted(offs, ks, side="right") - 1
+    # skip empty parameters sharing an offset: searchsorted(right)-1 picks the last with o <= k
+    j = ks - offs[p]
+    m = np.array([g.m for g in geo], dtype=np.int64)[p]
+    L = np.array([g.L for g in geo], dtype=np.int64)[p]
+    rows = np.array([g.rows for g in geo], dtype=np.int64)[p]
+    v = np.clip(rows - rs * m, 0, m)
+    src = np.where(j < v * L, rs * m * L + j, -1)
+    return p, src
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
+def test_full_size_rs_and_ag(gpu_available, cfg):
+    say(f"full size {cfg.name}: generating inputs")
+    torch.cuda.empty_cache()
+    geo, S = ogeo.group_geometry(cfg.shapes, cfg.R)
+    grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
+             for c in range(cfg.C)]
+    with Layout(cfg.shapes, cfg.R) as L:
+        shards = poisoned_shards(cfg.R, S)
+        say(f"full size {cfg.name}: RS")
+        L.rs_bf16_to_fp32(grads, shards, cu_budget=0)
+        torch.cuda.synchronize()
+
+        # (1) sampled outputs against the oracle, computed one by one
+        rng = np.random.default_rng(cfg.cfg_id)
+        rs_, ks = _sample_positions(geo, S, cfg.R, 20000, rng)
+        p_idx, src = _locate_many(geo, cfg.R, rs_, ks)
+        got = np.empty(len(rs_), dtype=np.uint32)
+        for r in range(cfg.R):
+            sel = np.nonzero(rs_ == r)[0]
+            if sel.size:
+                got[sel] = host_bits_f32(shards[r][torch.from_numpy(ks[sel]).cuda()])
+        vals = np.zeros((cfg.C, len(rs_)), dtype=np.uint16)
+        for p in np.unique(p_idx):
+            sel = np.nonzero((p_idx == p) & (src >= 0))[0]
+            if sel.size == 0:
+                continue
+            idx = torch.from_numpy(src[sel]).cuda()
+            for c in range(cfg.C):
+                vals[c, sel] = host_bits_bf16(grads[c][p].reshape(-1)[idx])
+        want = ors.rs_sampled(vals).view(np.uint32)
+        want = np.where(src >= 0, want, 0).astype(np.uint32)
+        assert np.array_equal(got, want), f"{int((got != want).sum())} sampled mismatches"
+        say(f"full size {cfg.name}: sampled outputs OK ({len(rs_)})")
+
+        # (2) every element: plain torch fp32 sum in the same ascending order, same bits
+        for p, g in enumerate(geo):
+            if g.e == 0:
+                continue
+            acc = grads[0][p].reshape(-1).float()
+            for c in range(1, cfg.C):
+                acc = acc + grads[c][p].reshape(-1).float()
+            for r in range(cfg.R):
+                v = ogeo.valid_rows(g.rows, g.m, r)
+                seg = shards[r][g.o: g.o + g.e]
+                lo, hi = r * g.m * g.L, (r * g.m + v) * g.L
+                assert torch.equal(seg[: v * g.L].view(torch.int32), acc[lo:hi].view(torch.int32)), (r, p)
+                assert bool((seg[v * g.L:].view(torch.int32) == 0).all())
+            del acc
+        say(f"full size {cfg.name}: full comparison OK")
+        del grads
+
+        # (3) AG placement, both engines, bit-exact against torch slicing; then the round trip
+        stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
+        for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA):
+            params = [torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda") for s in cfg.shapes]
+            say(f"full size {cfg.name}: AG mode={mode}")
+            L.ag_place(stage, params, mode=mode)
+            torch.cuda.synchronize()
+            st2 = stage.view(cfg.R, S)
+            for p, g in enumerate(geo):
+                ref = st2[:, g.o: g.o + g.e].reshape(cfg.R * g.m, g.L)[: g.rows].reshape(-1)
+                assert torch.equal(params[p].reshape(-1).view(torch.int16), ref.view(torch.int16)), (mode, p)
+            # sampled against the oracle's own copy-out definition
+            for p in rng.choice(len(geo), size=min(4, len(geo)), replace=False):
+                g = geo[p]
+                k = rng.integers(0, g.rows * g.L, 256)
+                row, col = k // g.L, k % g.L
+                r_, i_ = row // g.m, row % g.m
+                sidx = r_ * S + g.o + i_ * g.L + col
+                sb = host_bits_bf16(stage[torch.from_numpy(sidx).cuda()])
+                pb = host_bits_bf16(params[p].reshape(-1)[torch.from_numpy(k).cuda()])
+                assert np.array_equal(sb, pb)
+            if mode == TIDE_AG_KERNEL:
+                L.rs_bf16_to_fp32([params], shards)
+                torch.cuda.synchronize()
+                for r in range(cfg.R):
+                    want_r = (stage[r * S:(r + 1) * S].view(torch.int16).to(torch.int32) << 16)
+                    assert torch.equal(shards[r].view(torch.int32), want_r), r
+                say(f"full size {cfg.name}: round trip OK")
+            del params
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def test_cu_budget_does_not_change_results(gpu_available):
+    say("cu_budget independence")
+    shapes, R, C = [(4096, 512), (2048,), (1500, 300)], 8, 8
+    grads = [[normal_bf16_cuda(s, 1e-3, 80, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    with Layout(shapes, R) as L:
+        ref = None
+        for budget in (0, 1, 7, 64, 256, 1024):
+            shards = poisoned_shards(R, L.S)
+            L.rs_bf16_to_fp32(grads, shards, cu_budget=budget)
+            torch.cuda.synchronize()
+            got = torch.stack([s.view(torch.int32) for s in shards])
+            if ref is None:
+                ref = got
+            else:
+                assert torch.equal(got, ref), budget
