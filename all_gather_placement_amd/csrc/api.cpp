@@ -40,10 +40,14 @@ tide_status hip_fail(int err) {
 
 // Stage `n` device pointers for a launch on `stream`; returns the slot that holds them.
 int acquire_ptrs(DeviceState* st, void* const* ptrs, size_t n, hipStream_t stream, PtrSlot** out) {
-  if (st->last >= 0) {
-    PtrSlot& s = st->slots[st->last];
-    if (s.n == n && s.stream == stream && std::memcmp(s.host, ptrs, n * sizeof(void*)) == 0) {
-      *out = &s;  // same table, same stream: stream order protects it
+  // A slot that already holds this exact table and was last used on this stream can be reused
+  // without a copy: stream order keeps its earlier readers ahead of the new launch.  Calls that
+  // alternate between tables (an RS and an AG on the same group) hit different slots.
+  for (int k = 0; k < kPtrSlots; ++k) {
+    PtrSlot& s = st->slots[k];
+    if (s.n == n && s.host != nullptr && s.stream == stream &&
+        std::memcmp(s.host, ptrs, n * sizeof(void*)) == 0) {
+      *out = &s;
       return hipSuccess;
     }
   }
@@ -80,7 +84,6 @@ int acquire_ptrs(DeviceState* st, void* const* ptrs, size_t n, hipStream_t strea
     s.n = 0;
     return e;
   }
-  st->last = idx;
   st->next = (idx + 1) % kPtrSlots;
   *out = &s;
   return hipSuccess;
@@ -104,7 +107,8 @@ struct Plan {
 
 Plan plan_for(int64_t count, int32_t cu_budget) {
   if (cu_budget <= 0) {
-    const int64_t g = std::min<int64_t>(count, int64_t(1) << 30);
+    const int64_t cap = kPersistentWorkgroups > 0 ? kPersistentWorkgroups : (int64_t(1) << 30);
+    const int64_t g = std::min<int64_t>(count, cap);
     const int items = int((count + g - 1) / g);
     return Plan{int(g), items, int64_t(g) * items};
   }

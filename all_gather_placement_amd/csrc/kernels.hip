@@ -37,17 +37,28 @@ __device__ __forceinline__ float widen1(unsigned short b) {
   return __uint_as_float(static_cast<unsigned int>(b) << 16);
 }
 
-// Streaming (non-temporal) 16-byte load: every input byte is read exactly once.
-__device__ __forceinline__ u32x4 load16_stream(const void* p) {
-  return __builtin_nontemporal_load((const TIDE_GLOBAL u32x4*)p);
+// Streaming (non-temporal) 16-byte accesses: every input byte is read once and every output byte
+// written once, so nothing is worth keeping in the caches.
+template <typename T>
+__device__ __forceinline__ T load_hbm(const T* p) {
+#if TIDE_LOAD_NT
+  return __builtin_nontemporal_load((const TIDE_GLOBAL T*)p);
+#else
+  return *(const TIDE_GLOBAL T*)p;
+#endif
 }
-__device__ __forceinline__ unsigned short load_u16(const unsigned short* p) {
-  return *(const TIDE_GLOBAL unsigned short*)p;
+template <typename T>
+__device__ __forceinline__ void store_hbm(T* p, T v) {
+#if TIDE_STORE_NT
+  __builtin_nontemporal_store(v, (TIDE_GLOBAL T*)p);
+#else
+  *(TIDE_GLOBAL T*)p = v;
+#endif
 }
-__device__ __forceinline__ void store16_stream(void* p, f32x4 v) {
-  __builtin_nontemporal_store(v, (TIDE_GLOBAL f32x4*)p);
-}
-__device__ __forceinline__ void store_f32(float* p, float v) { __builtin_nontemporal_store(v, (TIDE_GLOBAL float*)p); }
+__device__ __forceinline__ u32x4 load16_stream(const void* p) { return load_hbm(static_cast<const u32x4*>(p)); }
+__device__ __forceinline__ unsigned short load_u16(const unsigned short* p) { return *(const TIDE_GLOBAL unsigned short*)p; }
+__device__ __forceinline__ void store16_stream(void* p, f32x4 v) { store_hbm(static_cast<f32x4*>(p), v); }
+__device__ __forceinline__ void store_f32(float* p, float v) { store_hbm(p, v); }
 
 // acc[0..7] = widen(x); element order inside a bf16x8 vector: x.x low half is element 0.
 __device__ __forceinline__ void widen8(const u32x4 x, float acc[8]) {
@@ -85,26 +96,24 @@ __device__ __forceinline__ float sum1(const unsigned short* const* src, int C, i
   return acc;
 }
 
-// Two 8-output vectors (16 outputs) per call: all 2*C loads are issued before the first add.
-template <int CT>
-__device__ __forceinline__ void sum16(const unsigned short* const* src, int64_t i0, int64_t i1,
-                                      float* d0, float* d1, bool dst16) {
-  u32x4 x0[CT], x1[CT];
+// NV 8-output vectors per call, kThreads vectors apart: all NV*C loads are issued before the
+// first add, so each thread keeps NV*C 16-byte loads in flight.
+template <int CT, int NV>
+__device__ __forceinline__ void sum_vecs(const unsigned short* const* src, int64_t i0, float* dst, bool dst16) {
+  u32x4 x[NV][CT];
 #pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    x0[c] = load16_stream(src[c] + i0);
-    x1[c] = load16_stream(src[c] + i1);
-  }
-  float a0[8], a1[8];
-  widen8(x0[0], a0);
-  widen8(x1[0], a1);
+  for (int c = 0; c < CT; ++c)
 #pragma unroll
-  for (int c = 1; c < CT; ++c) {
-    add8(x0[c], a0);
-    add8(x1[c], a1);
+    for (int k = 0; k < NV; ++k) x[k][c] = load16_stream(src[c] + i0 + 8 * kThreads * k);
+  float a[NV][8];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    widen8(x[k][0], a[k]);
+#pragma unroll
+    for (int c = 1; c < CT; ++c) add8(x[k][c], a[k]);
   }
-  store8(d0, a0, dst16);
-  store8(d1, a1, dst16);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) store8(dst + i0 + 8 * kThreads * k, a[k], dst16);
 }
 
 template <int CT>
@@ -193,13 +202,11 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
         const int tail = (n - head) & 7;
         const bool dst16 = ((ch.dst + head) & 3) == 0;
         if (tid < head) store_f32(dst + tid, sum1<CT>(srcp, nc, tid));
+        constexpr int NV = TIDE_RS_VECS;
         int v = tid;
-        for (; v + kThreads < nb; v += 2 * kThreads) {
-          const int64_t i0 = head + 8 * static_cast<int64_t>(v);
-          const int64_t i1 = i0 + 8 * kThreads;
-          sum16<CT>(srcp, i0, i1, dst + i0, dst + i1, dst16);
-        }
-        if (v < nb) {
+        for (; v + (NV - 1) * kThreads < nb; v += NV * kThreads)
+          sum_vecs<CT, NV>(srcp, head + 8 * static_cast<int64_t>(v), dst, dst16);
+        for (; v < nb; v += kThreads) {
           const int64_t i0 = head + 8 * static_cast<int64_t>(v);
           sum8<CT>(srcp, nc, i0, dst + i0, dst16);
         }
@@ -230,34 +237,32 @@ __global__ __launch_bounds__(kThreads) void ag_kernel(const AgChunk* __restrict_
     const int64_t item = static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(j) * gridDim.x;
     if (item >= count) break;
     const AgChunk ch = chunks[first + item];
-    const TIDE_GLOBAL unsigned short* src = (const TIDE_GLOBAL unsigned short*)(stage + ch.src);
-    TIDE_GLOBAL unsigned short* dst = (TIDE_GLOBAL unsigned short*)(params[ch.p] + ch.dst);
+    const unsigned short* src = stage + ch.src;
+    unsigned short* dst = params[ch.p] + ch.dst;
     const int n = ch.n;
     if (VEC && ((ch.src - ch.dst) & 7) == 0) {
       const int head = min(n, static_cast<int>((-ch.src) & 7));
       const int nb = (n - head) >> 3;
       const int tail = (n - head) & 7;
-      if (tid < head) dst[tid] = src[tid];
-      const TIDE_GLOBAL u32x4* s = (const TIDE_GLOBAL u32x4*)(src + head);
-      TIDE_GLOBAL u32x4* d = (TIDE_GLOBAL u32x4*)(dst + head);
+      if (tid < head) store_hbm(dst + tid, load_hbm(src + tid));
+      const u32x4* s = reinterpret_cast<const u32x4*>(src + head);
+      u32x4* d = reinterpret_cast<u32x4*>(dst + head);
+      constexpr int NV = TIDE_AG_VECS;
       int v = tid;
-      for (; v + 3 * kThreads < nb; v += 4 * kThreads) {
-        const u32x4 a = __builtin_nontemporal_load(s + v);
-        const u32x4 b = __builtin_nontemporal_load(s + v + kThreads);
-        const u32x4 c = __builtin_nontemporal_load(s + v + 2 * kThreads);
-        const u32x4 e = __builtin_nontemporal_load(s + v + 3 * kThreads);
-        __builtin_nontemporal_store(a, d + v);
-        __builtin_nontemporal_store(b, d + v + kThreads);
-        __builtin_nontemporal_store(c, d + v + 2 * kThreads);
-        __builtin_nontemporal_store(e, d + v + 3 * kThreads);
+      for (; v + (NV - 1) * kThreads < nb; v += NV * kThreads) {
+        u32x4 x[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) x[k] = load_hbm(s + v + k * kThreads);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) store_hbm(d + v + k * kThreads, x[k]);
       }
-      for (; v < nb; v += kThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(s + v), d + v);
+      for (; v < nb; v += kThreads) store_hbm(d + v, load_hbm(s + v));
       if (tid < tail) {
         const int k = head + 8 * nb + tid;
-        dst[k] = src[k];
+        store_hbm(dst + k, load_hbm(src + k));
       }
     } else {
-      for (int i = tid; i < n; i += kThreads) dst[i] = src[i];
+      for (int i = tid; i < n; i += kThreads) store_hbm(dst + i, load_hbm(src + i));
     }
   }
 }

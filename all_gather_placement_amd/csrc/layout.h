@@ -40,7 +40,6 @@ struct DeviceState {
   AgChunk* ag = nullptr;
   PtrSlot slots[kPtrSlots];
   int next = 0;
-  int last = -1;
 };
 
 }  // namespace tide
