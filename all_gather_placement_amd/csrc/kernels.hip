@@ -1,21 +1,23 @@
 // gfx950 kernels of the layout-aware reduce-scatter and all-gather placement.
 //
 // Both kernels walk a host-built table of work items (tide_internal.h).  A work item lies inside
-// one (parameter, rank) segment, so a workgroup reads its item descriptor and the item's C source
-// pointers once, as wave-uniform scalar loads, and then streams contiguous memory: no per-element
-// index search, no atomics, no inter-workgroup communication.  Every output element has exactly
-// one writer.
+// one (parameter, rank) segment, so a workgroup reads its item descriptor and the item's source
+// pointers once, as wave-uniform scalar loads into SGPRs, and then streams contiguous memory: no
+// per-element index search, no atomics, no inter-workgroup communication.  Every output element
+// has exactly one writer, and every workgroup is short-lived (one work item, then exit).
 //
 // RS ([Endgame] Figure 6a, node-local fp32 sums; abstract, bf16 gradients reduced into fp32
-// shards): each thread takes 8 consecutive outputs at a time -- one 16-byte bf16x8 load from each
-// contributor, an exact widen to fp32, C-1 IEEE fp32 adds in ascending contributor order, and two
-// 16-byte non-temporal fp32 stores.  At C = 8 that is 20 bytes of HBM traffic per output and 7
-// adds: far below any ALU or matrix-core limit, so the kernel is HBM-bound and is shaped for
-// bytes in flight (two 8-output vectors per thread per step, non-temporal streaming accesses).
+// shards): outputs are handled in groups of 4.  For a group, a thread loads 8 bytes (4 bf16) from
+// each contributor, widens them exactly to fp32, adds them in ascending contributor order (C-1
+// IEEE binary32 adds per output) and writes 16 bytes.  Consecutive lanes take consecutive groups,
+// so each load instruction of a wave covers 512 contiguous bytes and each store instruction 1 KiB
+// of whole cache lines.  At C = 8 an output costs 20 bytes of HBM traffic and 7 adds: the kernel
+// is HBM-bound by two orders of magnitude, so it is shaped for bytes in flight and clean traffic,
+// not arithmetic (no matrix cores: nothing here is a contraction).
 //
 // AG ([Endgame] Figure 5b, one strided copy per parameter; Table 7, direct landing): a bit copy
 // of each rank's valid rows from the rank-major stage into the parameter's storage, 16 bytes per
-// thread per access when source and destination share their 16-byte phase.
+// lane per access when source and destination share their 16-byte phase.
 #include <hip/hip_runtime.h>
 
 #include "tide_internal.h"
@@ -23,22 +25,17 @@
 namespace tide {
 namespace {
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Every buffer the kernels touch is HBM; pointers that arrive through a table would otherwise be
-// generic (flat) pointers, so accesses go through global-address-space casts to get global_*
+// Every buffer the kernels touch is in HBM.  Pointers that arrive through a table would otherwise
+// be generic (flat) pointers; accesses go through global-address-space casts to get global_*
 // instructions instead of flat_* ones.
 #define TIDE_GLOBAL __attribute__((address_space(1)))
 
-__device__ __forceinline__ float widen_lo(unsigned int w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float widen_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float widen1(unsigned short b) {
-  return __uint_as_float(static_cast<unsigned int>(b) << 16);
-}
-
-// Streaming (non-temporal) 16-byte accesses: every input byte is read once and every output byte
-// written once, so nothing is worth keeping in the caches.
+// Streaming (non-temporal) accesses: every input byte is read once and every output byte written
+// once, so nothing is worth keeping in the caches.
 template <typename T>
 __device__ __forceinline__ T load_hbm(const T* p) {
 #if TIDE_LOAD_NT
@@ -55,172 +52,157 @@ __device__ __forceinline__ void store_hbm(T* p, T v) {
   *(TIDE_GLOBAL T*)p = v;
 #endif
 }
-__device__ __forceinline__ u32x4 load16_stream(const void* p) { return load_hbm(static_cast<const u32x4*>(p)); }
-__device__ __forceinline__ unsigned short load_u16(const unsigned short* p) { return *(const TIDE_GLOBAL unsigned short*)p; }
-__device__ __forceinline__ void store16_stream(void* p, f32x4 v) { store_hbm(static_cast<f32x4*>(p), v); }
-__device__ __forceinline__ void store_f32(float* p, float v) { store_hbm(p, v); }
 
-// acc[0..7] = widen(x); element order inside a bf16x8 vector: x.x low half is element 0.
-__device__ __forceinline__ void widen8(const u32x4 x, float acc[8]) {
-  acc[0] = widen_lo(x.x); acc[1] = widen_hi(x.x);
-  acc[2] = widen_lo(x.y); acc[3] = widen_hi(x.y);
-  acc[4] = widen_lo(x.z); acc[5] = widen_hi(x.z);
-  acc[6] = widen_lo(x.w); acc[7] = widen_hi(x.w);
+// bf16 -> fp32 is exact: the 16 bf16 bits become the upper half of the binary32.
+__device__ __forceinline__ float widen_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float widen_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float widen1(unsigned short b) { return __uint_as_float(static_cast<unsigned int>(b) << 16); }
+
+// acc[0..3] (+)= the 4 bf16 of x (element 0 in the low half of x.x).
+__device__ __forceinline__ void widen4(u32x2 x, float acc[4]) {
+  acc[0] = widen_lo(x.x); acc[1] = widen_hi(x.x); acc[2] = widen_lo(x.y); acc[3] = widen_hi(x.y);
 }
-
-__device__ __forceinline__ void add8(const u32x4 x, float acc[8]) {
-  acc[0] += widen_lo(x.x); acc[1] += widen_hi(x.x);
-  acc[2] += widen_lo(x.y); acc[3] += widen_hi(x.y);
-  acc[4] += widen_lo(x.z); acc[5] += widen_hi(x.z);
-  acc[6] += widen_lo(x.w); acc[7] += widen_hi(x.w);
+__device__ __forceinline__ void add4(u32x2 x, float acc[4]) {
+  acc[0] += widen_lo(x.x); acc[1] += widen_hi(x.x); acc[2] += widen_lo(x.y); acc[3] += widen_hi(x.y);
 }
-
-__device__ __forceinline__ void store8(float* dst, const float acc[8], bool dst16) {
+__device__ __forceinline__ void store4(float* d, const float a[4], bool dst16) {
   if (dst16) {
-    f32x4 a = {acc[0], acc[1], acc[2], acc[3]};
-    f32x4 b = {acc[4], acc[5], acc[6], acc[7]};
-    store16_stream(dst, a);
-    store16_stream(dst + 4, b);
+    store_hbm(reinterpret_cast<f32x4*>(d), f32x4{a[0], a[1], a[2], a[3]});
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) store_f32(dst + k, acc[k]);
+    for (int k = 0; k < 4; ++k) store_hbm(d + k, a[k]);
   }
 }
 
-// Fixed-order fp32 sum of one element over contributors (element path, head/tail, unaligned).
+// Work item taken by this workgroup.  Workgroups are dispatched round-robin over the XCDs
+// (workgroup b runs on XCD b mod kXcds).  With REMAP, when each workgroup takes one item, the items
+// are renumbered so that every XCD walks one contiguous range of the table, keeping its L2 and TLB
+// on one stream of pages; the map is a bijection on [0, count).
+template <bool REMAP>
+__device__ __forceinline__ int64_t item_of(int j, int64_t count) {
+  if (REMAP && gridDim.x == count) {
+    const int64_t b = blockIdx.x;
+    const int64_t x = b % kXcds, i = b / kXcds;
+    return x * (count / kXcds) + min<int64_t>(x, count % kXcds) + i;
+  }
+  return static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(j) * gridDim.x;
+}
+
+// One output element, fixed ascending contributor order (heads, tails, unaligned bases).
 template <int CT>
 __device__ __forceinline__ float sum1(const unsigned short* const* src, int C, int64_t i) {
   const int n = CT > 0 ? CT : C;
-  float acc = widen1(load_u16(src[0] + i));
-  for (int c = 1; c < n; ++c) acc += widen1(load_u16(src[c] + i));
+  float acc = widen1(load_hbm(src[0] + i));
+  for (int c = 1; c < n; ++c) acc += widen1(load_hbm(src[c] + i));
   return acc;
 }
 
-// NV 8-output vectors per call, kThreads vectors apart: all NV*C loads are issued before the
-// first add, so each thread keeps NV*C 16-byte loads in flight.
-template <int CT, int NV>
-__device__ __forceinline__ void sum_vecs(const unsigned short* const* src, int64_t i0, float* dst, bool dst16) {
-  u32x4 x[NV][CT];
+// Address = wave-uniform base (SGPRs) + 32-bit per-lane byte offset, which maps onto the
+// global_load/store "saddr + voffset" form and keeps 64-bit addresses out of VGPRs.
+template <typename T, typename B>
+__device__ __forceinline__ const T* at_bytes(const B* base, uint32_t byte_off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+template <typename T, typename B>
+__device__ __forceinline__ T* at_bytes(B* base, uint32_t byte_off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off);
+}
+
+// NQ groups of 4 outputs, kThreads groups apart, starting at element i0 of the item (i0 < 2^30,
+// item-relative).  All NQ*C loads are issued before the first add.
+template <int CT, int NQ>
+__device__ __forceinline__ void sum_groups(const unsigned short* const* src, uint32_t i0, float* dst, bool dst16) {
+  u32x2 x[NQ][CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
-    for (int k = 0; k < NV; ++k) x[k][c] = load16_stream(src[c] + i0 + 8 * kThreads * k);
-  float a[NV][8];
+    for (int k = 0; k < NQ; ++k) x[k][c] = load_hbm(at_bytes<u32x2>(src[c], 2u * (i0 + 4u * kThreads * k)));
 #pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    widen8(x[k][0], a[k]);
+  for (int k = 0; k < NQ; ++k) {
+    float a[4];
+    widen4(x[k][0], a);
 #pragma unroll
-    for (int c = 1; c < CT; ++c) add8(x[k][c], a[k]);
+    for (int c = 1; c < CT; ++c) add4(x[k][c], a);
+    store4(at_bytes<float>(dst, 4u * (i0 + 4u * kThreads * k)), a, dst16);
   }
-#pragma unroll
-  for (int k = 0; k < NV; ++k) store8(dst + i0 + 8 * kThreads * k, a[k], dst16);
 }
 
-template <int CT>
-__device__ __forceinline__ void sum8(const unsigned short* const* src, int C, int64_t i, float* d,
-                                     bool dst16) {
-  float a[8];
-  if constexpr (CT > 0) {
-    u32x4 x[CT];
-#pragma unroll
-    for (int c = 0; c < CT; ++c) x[c] = load16_stream(src[c] + i);
-    widen8(x[0], a);
-#pragma unroll
-    for (int c = 1; c < CT; ++c) add8(x[c], a);
-  } else {
-    widen8(load16_stream(src[0] + i), a);
-    for (int c = 1; c < C; ++c) add8(load16_stream(src[c] + i), a);
-  }
-  store8(d, a, dst16);
+// Runtime contributor count (C > 8): same mapping, contributors loaded one at a time.
+__device__ __forceinline__ void sum_group_rt(const unsigned short* const* gptr, int32_t P, int32_t p, int C,
+                                             int64_t e, float* d, bool dst16) {
+  float a[4];
+  widen4(load_hbm(reinterpret_cast<const u32x2*>(gptr[p] + e)), a);
+  for (int c = 1; c < C; ++c) add4(load_hbm(reinterpret_cast<const u32x2*>(gptr[static_cast<int64_t>(c) * P + p] + e)), a);
+  store4(d, a, dst16);
 }
 
-constexpr int kMaxStaticC = 8;
+// Element path for the runtime contributor count.
+__device__ __forceinline__ float sum1_rt(const unsigned short* const* gptr, int32_t P, int32_t p, int C, int64_t e) {
+  float acc = widen1(load_hbm(gptr[p] + e));
+  for (int c = 1; c < C; ++c) acc += widen1(load_hbm(gptr[static_cast<int64_t>(c) * P + p] + e));
+  return acc;
+}
 
-// RS kernel.  CT > 0: contributor count fixed at compile time; CT == 0: runtime C (any C >= 1).
+// RS kernel.  CT in 1..8: contributor count fixed at compile time; CT == 0: any C >= 1.
 // VEC: all gradient and shard base pointers are 16-byte aligned (checked on the host), so the
-// 16-byte phase of an element depends only on its offset.
+// alignment of an element depends only on its offset inside its buffer.
 template <int CT, bool VEC>
 __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict__ chunks, int64_t first,
                                                       int64_t count, int items_per_wg,
-                                                      void* const* __restrict__ ptrs, int32_t P,
-                                                      int32_t C) {
+                                                      void* const* __restrict__ ptrs, int32_t P, int32_t C) {
   const int tid = threadIdx.x;
   const unsigned short* const* __restrict__ gptr = reinterpret_cast<const unsigned short* const*>(ptrs);
   float* const* __restrict__ sptr = reinterpret_cast<float* const*>(ptrs + static_cast<int64_t>(C) * P);
   const int nc = CT > 0 ? CT : C;
 
   for (int j = 0; j < items_per_wg; ++j) {
-    const int64_t item = static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(j) * gridDim.x;
+    const int64_t item = item_of<TIDE_RS_XCD_REMAP != 0>(j, count);
     if (item >= count) break;
     const RsChunk ch = chunks[first + item];
-
-    // Source pointers of this item, one per contributor (wave-uniform).
-    const unsigned short* src[CT > 0 ? CT : kMaxStaticC];
-    const unsigned short* const* srcp;
-    if constexpr (CT > 0) {
-#pragma unroll
-      for (int c = 0; c < CT; ++c) src[c] = gptr[static_cast<int64_t>(c) * P + ch.p] + ch.src;
-      srcp = src;
-    } else {
-      srcp = nullptr;
-    }
     float* dst = sptr[ch.r] + ch.dst;
     const int n = ch.nvalid;
 
-    if constexpr (CT == 0) {
-      // Runtime C: per-element pointer lookups through the table (scalar loads, cached).
-      const int64_t base = ch.src;
-      const int head = VEC ? min(n, static_cast<int>((-base) & 7)) : n;
-      for (int i = tid; i < head; i += kThreads) {
-        const int64_t e = base + i;
-        float acc = widen1(load_u16(gptr[ch.p] + e));
-        for (int c = 1; c < nc; ++c) acc += widen1(load_u16(gptr[static_cast<int64_t>(c) * P + ch.p] + e));
-        store_f32(dst + i, acc);
-      }
-      if (VEC) {
-        const int nb = (n - head) >> 3;
-        const int tail = (n - head) & 7;
-        const bool dst16 = ((ch.dst + head) & 3) == 0;
-        for (int v = tid; v < nb; v += kThreads) {
-          const int64_t e = base + head + 8 * static_cast<int64_t>(v);
-          float a[8];
-          widen8(load16_stream(gptr[ch.p] + e), a);
-          for (int c = 1; c < nc; ++c) add8(load16_stream(gptr[static_cast<int64_t>(c) * P + ch.p] + e), a);
-          store8(dst + head + 8 * v, a, dst16);
+    if (VEC) {
+      // head: elements before the first 16-byte source boundary; then whole 4-output groups
+      // (2 per 8 elements); tail: fewer than 8 elements.
+      const int head = min(n, static_cast<int>((-ch.src) & 7));
+      const int nb = (n - head) >> 3;
+      const int ng = 2 * nb;
+      const int tail = (n - head) & 7;
+      const bool dst16 = ((ch.dst + head) & 3) == 0;
+      if constexpr (CT > 0) {
+        // Per-item source pointers (wave-uniform, SGPRs): contributor c's element ch.src of p.
+        const unsigned short* src[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) src[c] = gptr[static_cast<int64_t>(c) * P + ch.p] + ch.src;
+        if (tid < head) store_hbm(dst + tid, sum1<CT>(src, nc, tid));
+        constexpr int NQ = TIDE_RS_NQ;
+        int q = tid;
+        for (; q + (NQ - 1) * kThreads < ng; q += NQ * kThreads)
+          sum_groups<CT, NQ>(src, static_cast<uint32_t>(head + 4 * q), dst, dst16);
+        for (; q < ng; q += kThreads) sum_groups<CT, 1>(src, static_cast<uint32_t>(head + 4 * q), dst, dst16);
+        if (tid < tail) {
+          const int64_t k = head + 8 * static_cast<int64_t>(nb) + tid;
+          store_hbm(dst + k, sum1<CT>(src, nc, k));
+        }
+      } else {
+        for (int i = tid; i < head; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
+        for (int q = tid; q < ng; q += kThreads) {
+          const int64_t k = head + 4 * static_cast<int64_t>(q);
+          sum_group_rt(gptr, P, ch.p, nc, ch.src + k, dst + k, dst16);
         }
         for (int i = tid; i < tail; i += kThreads) {
           const int64_t k = head + 8 * static_cast<int64_t>(nb) + i;
-          float acc = widen1(load_u16(gptr[ch.p] + base + k));
-          for (int c = 1; c < nc; ++c) acc += widen1(load_u16(gptr[static_cast<int64_t>(c) * P + ch.p] + base + k));
-          store_f32(dst + k, acc);
+          store_hbm(dst + k, sum1_rt(gptr, P, ch.p, nc, ch.src + k));
         }
       }
     } else {
-      if (VEC) {
-        const int head = min(n, static_cast<int>((-ch.src) & 7));
-        const int nb = (n - head) >> 3;
-        const int tail = (n - head) & 7;
-        const bool dst16 = ((ch.dst + head) & 3) == 0;
-        if (tid < head) store_f32(dst + tid, sum1<CT>(srcp, nc, tid));
-        constexpr int NV = TIDE_RS_VECS;
-        int v = tid;
-        for (; v + (NV - 1) * kThreads < nb; v += NV * kThreads)
-          sum_vecs<CT, NV>(srcp, head + 8 * static_cast<int64_t>(v), dst, dst16);
-        for (; v < nb; v += kThreads) {
-          const int64_t i0 = head + 8 * static_cast<int64_t>(v);
-          sum8<CT>(srcp, nc, i0, dst + i0, dst16);
-        }
-        if (tid < tail) {
-          const int64_t k = head + 8 * static_cast<int64_t>(nb) + tid;
-          store_f32(dst + k, sum1<CT>(srcp, nc, k));
-        }
-      } else {
-        for (int i = tid; i < n; i += kThreads) store_f32(dst + i, sum1<CT>(srcp, nc, i));
-      }
+      // Element path: any 2-byte-aligned gradients and 4-byte-aligned shards.
+      for (int i = tid; i < n; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
     }
 
     // Padding rows of this rank's slice: +0.0.
-    for (int i = tid; i < ch.npad; i += kThreads) store_f32(dst + n + i, 0.0f);
+    for (int i = tid; i < ch.npad; i += kThreads) store_hbm(dst + n + i, 0.0f);
   }
 }
 
@@ -228,13 +210,13 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
 // aligned, so an item whose source and destination offsets agree mod 8 elements copies 16-byte
 // vectors after a short head.
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void ag_kernel(const AgChunk* __restrict__ chunks, int64_t first,
-                                                      int64_t count, int items_per_wg,
-                                                      const unsigned short* __restrict__ stage,
-                                                      unsigned short* const* __restrict__ params) {
+__global__ __launch_bounds__(kAgThreads) void ag_kernel(const AgChunk* __restrict__ chunks, int64_t first,
+                                                        int64_t count, int items_per_wg,
+                                                        const unsigned short* __restrict__ stage,
+                                                        unsigned short* const* __restrict__ params) {
   const int tid = threadIdx.x;
   for (int j = 0; j < items_per_wg; ++j) {
-    const int64_t item = static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(j) * gridDim.x;
+    const int64_t item = item_of<TIDE_AG_XCD_REMAP != 0>(j, count);
     if (item >= count) break;
     const AgChunk ch = chunks[first + item];
     const unsigned short* src = stage + ch.src;
@@ -249,20 +231,20 @@ __global__ __launch_bounds__(kThreads) void ag_kernel(const AgChunk* __restrict_
       u32x4* d = reinterpret_cast<u32x4*>(dst + head);
       constexpr int NV = TIDE_AG_VECS;
       int v = tid;
-      for (; v + (NV - 1) * kThreads < nb; v += NV * kThreads) {
+      for (; v + (NV - 1) * kAgThreads < nb; v += NV * kAgThreads) {
         u32x4 x[NV];
 #pragma unroll
-        for (int k = 0; k < NV; ++k) x[k] = load_hbm(s + v + k * kThreads);
+        for (int k = 0; k < NV; ++k) x[k] = load_hbm(at_bytes<u32x4>(s, 16u * (v + k * kAgThreads)));
 #pragma unroll
-        for (int k = 0; k < NV; ++k) store_hbm(d + v + k * kThreads, x[k]);
+        for (int k = 0; k < NV; ++k) store_hbm(at_bytes<u32x4>(d, 16u * (v + k * kAgThreads)), x[k]);
       }
-      for (; v < nb; v += kThreads) store_hbm(d + v, load_hbm(s + v));
+      for (; v < nb; v += kAgThreads) store_hbm(at_bytes<u32x4>(d, 16u * v), load_hbm(at_bytes<u32x4>(s, 16u * v)));
       if (tid < tail) {
         const int k = head + 8 * nb + tid;
         store_hbm(dst + k, load_hbm(src + k));
       }
     } else {
-      for (int i = tid; i < n; i += kThreads) store_hbm(dst + i, load_hbm(src + i));
+      for (int i = tid; i < n; i += kAgThreads) store_hbm(dst + i, load_hbm(src + i));
     }
   }
 }
@@ -271,11 +253,11 @@ template <int CT>
 hipError_t launch_rs_ct(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items,
                         void* const* ptrs, int32_t P, int32_t C, bool vec, hipStream_t s) {
   if (vec)
-    hipLaunchKernelGGL((rs_kernel<CT, true>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items,
-                       ptrs, P, C);
+    hipLaunchKernelGGL((rs_kernel<CT, true>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items, ptrs,
+                       P, C);
   else
-    hipLaunchKernelGGL((rs_kernel<CT, false>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items,
-                       ptrs, P, C);
+    hipLaunchKernelGGL((rs_kernel<CT, false>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items, ptrs,
+                       P, C);
   return hipGetLastError();
 }
 
@@ -304,10 +286,10 @@ int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int
   const unsigned short* st = static_cast<const unsigned short*>(stage);
   unsigned short* const* pp = reinterpret_cast<unsigned short* const*>(const_cast<void* const*>(dev_params));
   if (vec)
-    hipLaunchKernelGGL((ag_kernel<true>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items_per_wg,
+    hipLaunchKernelGGL((ag_kernel<true>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count, items_per_wg,
                        st, pp);
   else
-    hipLaunchKernelGGL((ag_kernel<false>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items_per_wg,
+    hipLaunchKernelGGL((ag_kernel<false>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count, items_per_wg,
                        st, pp);
   return hipGetLastError();
 }

@@ -11,6 +11,7 @@
 // source boundaries, so the kernels need no per-element lookup.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstring>
 #include <new>
 
@@ -42,7 +43,36 @@ void cut(int64_t src0, int64_t n, int64_t chunk, F&& emit) {
 
 thread_local int g_last_hip_error = 0;
 
+// Order in which workgroups take work items (before any XCD renumbering in the kernels):
+//   0: parameter-major (p, r, position): each contributor tensor is read front to back;
+//   1: rank-major (r, p, position): each shard is written front to back;
+//   2: interleaved: the k-th item of every segment before the (k+1)-th of any.
+template <typename Item, typename RankOf>
+void order_one(std::vector<Item>& v, int order, RankOf rank_of) {
+  if (order == 1) {
+    std::stable_sort(v.begin(), v.end(), [&](const Item& a, const Item& b) { return rank_of(a) < rank_of(b); });
+  } else if (order == 2) {
+    std::vector<int64_t> k(v.size());
+    for (size_t i = 0; i < v.size(); ++i) {
+      const bool same = i > 0 && v[i].p == v[i - 1].p && rank_of(v[i]) == rank_of(v[i - 1]);
+      k[i] = same ? k[i - 1] + 1 : 0;
+    }
+    std::vector<size_t> idx(v.size());
+    for (size_t i = 0; i < idx.size(); ++i) idx[i] = i;
+    std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return k[a] < k[b]; });
+    std::vector<Item> out(v.size());
+    for (size_t i = 0; i < idx.size(); ++i) out[i] = v[idx[i]];
+    v.swap(out);
+  }
+}
+
 }  // namespace
+
+void order_items(tide_layout* L) {
+  order_one(L->rs_chunks, TIDE_RS_ITEM_ORDER, [](const RsChunk& c) { return c.r; });
+  const int64_t S = L->S;
+  order_one(L->ag_chunks, TIDE_AG_ITEM_ORDER, [S](const AgChunk& c) { return S > 0 ? c.src / S : 0; });
+}
 
 void set_last_hip_error(int err) { g_last_hip_error = err; }
 
@@ -140,8 +170,7 @@ tide_status tide_layout_create(int32_t num_params, const int32_t* ndims, const i
     }
     L->S = o;
 
-    // Work items.  Order: parameter-major, then rank, then position, so consecutive workgroups
-    // stream consecutive addresses of each contributor's tensor.
+    // Work items, built parameter-major (p, r, position) and then put in kernel order.
     for (int32_t p = 0; p < num_params; ++p) {
       const ParamGeom& g = L->params[p];
       for (int32_t r = 0; r < num_ranks; ++r) {
@@ -161,6 +190,7 @@ tide_status tide_layout_create(int32_t num_params, const int32_t* ndims, const i
         });
       }
     }
+    tide::order_items(L);
   } catch (const std::bad_alloc&) {
     delete L;
     return TIDE_ERR_NOMEM;

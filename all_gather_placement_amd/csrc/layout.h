@@ -59,5 +59,7 @@ namespace tide {
 // Returns the device state for the current device, uploading the tables on first use.
 // Must be called with layout->mu held.  Returns a hipError_t.
 int device_state(const tide_layout* layout, DeviceState** out);
+// Reorders the work-item tables into the order workgroups take them.
+void order_items(tide_layout* layout);
 void set_last_hip_error(int err);
 }  // namespace tide

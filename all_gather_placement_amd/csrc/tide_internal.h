@@ -7,52 +7,77 @@
 
 namespace tide {
 
-// Threads per workgroup of every kernel (default: 4 wave64 waves, one per SIMD of a CDNA4 CU).
+// Kernel shape.  The defaults were chosen by measurement on MI355X (HBM GB/s over the Llama-3.1
+// 8B/70B, Qwen3-30B-A3B and Wan2.2 layer groups); each can be overridden at build time.
+//
+// RS: 256 threads (4 wave64 waves, one per SIMD of a CDNA4 CU) per workgroup; one work item is
+// 2048 outputs, i.e. exactly TIDE_RS_NQ = 2 four-output groups per thread, issued together.  A
+// workgroup moves 2048 * (2C + 4) bytes (40 KiB at C = 8) and exits.
+// AG: 128 threads per workgroup; one work item is 2048 bf16 elements (8 KiB moved), i.e. one or
+// two 16-byte vectors per thread.
+// Short-lived workgroups of this size streamed HBM faster than larger items (4K-64K elements),
+// more groups in flight per thread, or a persistent grid.
 #ifndef TIDE_THREADS
 #define TIDE_THREADS 256
 #endif
-constexpr int kThreads = TIDE_THREADS;
-
-// Work-item sizes, in elements.  One RS work item is 2048 outputs: with 256 threads each thread
-// sums exactly one 8-output vector (one 16-byte load per contributor, two 16-byte stores), and a
-// workgroup moves 2048 * (2C + 4) bytes (40 KiB at C = 8) and exits.  One AG work item is 4096
-// elements (16 KiB moved).  Measured on MI355X, such short-lived workgroups stream HBM faster than
-// larger items or a persistent grid.  Both sizes are multiples of 8, so every work item after a
-// segment's first starts on a 16-byte source boundary.
+#ifndef TIDE_AG_THREADS
+#define TIDE_AG_THREADS 128
+#endif
 #ifndef TIDE_RS_CHUNK
 #define TIDE_RS_CHUNK 2048
 #endif
 #ifndef TIDE_AG_CHUNK
-#define TIDE_AG_CHUNK 4096
+#define TIDE_AG_CHUNK 2048
 #endif
-constexpr int64_t kRsChunk = TIDE_RS_CHUNK;
-constexpr int64_t kAgChunk = TIDE_AG_CHUNK;
-static_assert(kRsChunk % 8 == 0 && kAgChunk % 8 == 0, "work items must be whole 16-byte vectors");
-
-// Work items a workgroup takes per launch when the caller bounds the resident workgroups.
-constexpr int kItemsPerBoundedWorkgroup = 4;
-
-// Unbounded launches (cu_budget 0): 0 = one workgroup per work item; N > 0 = at most N
-// workgroups, each walking items with a grid stride.
-#ifndef TIDE_PERSISTENT_WGS
-#define TIDE_PERSISTENT_WGS 0
-#endif
-constexpr int64_t kPersistentWorkgroups = TIDE_PERSISTENT_WGS;
-
-// Kernel shape: 8-output (RS) / 16-byte (AG) vectors each thread keeps in flight per step, and
-// whether HBM accesses carry the non-temporal (streaming) hint.
-#ifndef TIDE_RS_VECS
-#define TIDE_RS_VECS 1
+#ifndef TIDE_RS_NQ
+#define TIDE_RS_NQ 2
 #endif
 #ifndef TIDE_AG_VECS
 #define TIDE_AG_VECS 4
 #endif
+// Non-temporal (streaming) hints on HBM loads and stores.
 #ifndef TIDE_LOAD_NT
 #define TIDE_LOAD_NT 1
 #endif
 #ifndef TIDE_STORE_NT
 #define TIDE_STORE_NT 1
 #endif
+// Unbounded launches (cu_budget 0): 0 = one workgroup per work item; N > 0 = at most N
+// workgroups, each walking items with a grid stride.
+#ifndef TIDE_PERSISTENT_WGS
+#define TIDE_PERSISTENT_WGS 0
+#endif
+
+// Work-item order and XCD-aware renumbering (layout.cpp order_items, kernels.hip item_of).
+// Measured: the RS streams best rank-major (each shard written front to back) with each of the 8
+// XCDs of an MI355X walking one contiguous range of items; the AG copy best parameter-major with
+// plain round-robin dispatch.  Orders: 0 parameter-major, 1 rank-major, 2 interleaved.
+#ifndef TIDE_RS_ITEM_ORDER
+#define TIDE_RS_ITEM_ORDER 1
+#endif
+#ifndef TIDE_AG_ITEM_ORDER
+#define TIDE_AG_ITEM_ORDER 0
+#endif
+#ifndef TIDE_RS_XCD_REMAP
+#define TIDE_RS_XCD_REMAP 1
+#endif
+#ifndef TIDE_AG_XCD_REMAP
+#define TIDE_AG_XCD_REMAP 0
+#endif
+constexpr int64_t kXcds = 8;
+
+constexpr int kThreads = TIDE_THREADS;
+constexpr int kAgThreads = TIDE_AG_THREADS;
+constexpr int64_t kRsChunk = TIDE_RS_CHUNK;
+constexpr int64_t kAgChunk = TIDE_AG_CHUNK;
+constexpr int64_t kPersistentWorkgroups = TIDE_PERSISTENT_WGS;
+// Work items are whole 16-byte source vectors, so every item after a segment's first starts on a
+// 16-byte source boundary.
+static_assert(kRsChunk % 8 == 0 && kAgChunk % 8 == 0, "work items must be whole 16-byte vectors");
+static_assert(kRsChunk < (int64_t(1) << 31) && kAgChunk < (int64_t(1) << 31), "item sizes are int32");
+
+// Work items a workgroup takes per launch when the caller bounds the resident workgroups.
+constexpr int kItemsPerBoundedWorkgroup = 4;
 
 // One RS work item: nvalid summed elements of parameter p, starting at element `src` of the
 // parameter's storage, written to shard r at element `dst`; then npad zeros at dst + nvalid.

@@ -95,7 +95,7 @@ def test_layout_geometry_hypothesis(g):
     _check_geometry(shapes, R)
 
 
-def check_items_tile_exactly(shapes, R, rs_items, ag_items, rs_chunk=2048, ag_chunk=4096):
+def check_items_tile_exactly(shapes, R, rs_items, ag_items, rs_chunk=2048, ag_chunk=2048):
     """Every shard element written once, every parameter element placed once, all in bounds."""
     geo, S = ogeo.group_geometry(shapes, R)
     numel = [g.rows * g.L for g in geo]
