@@ -5,6 +5,7 @@ marshals arguments to it.  Importing the package does not load the library; the 
 and fails loudly if it has not been built (``python -m all_gather_placement_amd.build``).
 """
 from .tide import (  # noqa: F401
+    TIDE_AG_COPY2D,
     TIDE_AG_KERNEL,
     TIDE_AG_SDMA,
     Layout,

@@ -97,6 +97,22 @@ int release_ptrs(PtrSlot* s, hipStream_t stream) {
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Create the internal copy streams and their fork/join events on first use (layout mutex held).
+int ensure_dma(DeviceState* st) {
+  hipError_t e;
+  if (st->dma_fork == nullptr &&
+      (e = hipEventCreateWithFlags(&st->dma_fork, hipEventDisableTiming)) != hipSuccess)
+    return e;
+  for (int k = 0; k < kDmaStreams; ++k) {
+    if (st->dma[k] == nullptr && (e = hipStreamCreateWithFlags(&st->dma[k], hipStreamNonBlocking)) != hipSuccess)
+      return e;
+    if (st->dma_join[k] == nullptr &&
+        (e = hipEventCreateWithFlags(&st->dma_join[k], hipEventDisableTiming)) != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
+}
+
 // Launch plan for `count` work items: cu_budget 0 = one item per workgroup in one launch;
 // B > 0 = grids of at most B workgroups, each taking a few items and exiting.
 struct Plan {
@@ -189,7 +205,7 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
 tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params, int32_t mode,
                           int32_t cu_budget, void* stream) {
   if (layout == nullptr || params == nullptr || cu_budget < 0) return TIDE_ERR_INVALID;
-  if (mode != TIDE_AG_KERNEL && mode != TIDE_AG_SDMA) return TIDE_ERR_INVALID;
+  if (mode != TIDE_AG_KERNEL && mode != TIDE_AG_SDMA && mode != TIDE_AG_COPY2D) return TIDE_ERR_INVALID;
   const int32_t P = layout->P, R = layout->R;
   const int64_t S = layout->S;
   const int64_t stage_n = int64_t(R) * S;
@@ -212,11 +228,10 @@ tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* co
   if (tide::outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  if (mode == TIDE_AG_SDMA) {
+  if (mode == TIDE_AG_COPY2D) {
     // One 2-D copy per parameter covers the ranks whose slice is full (rows of the copy = ranks,
     // source pitch = one stage slot, destination pitch = one slice), plus one copy for the rank
-    // whose slice is partly padding.  Copies run on the DMA engines, not on compute units.
-    const hipMemcpyKind kind = hipMemcpyDeviceToDeviceNoCU;
+    // whose slice is partly padding.  The runtime chooses the engine.
     for (int32_t p = 0; p < P; ++p) {
       const tide::ParamGeom& g = layout->params[p];
       if (g.numel == 0) continue;
@@ -225,11 +240,12 @@ tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* co
       char* dst = static_cast<char*>(params[p]);
       hipError_t e = hipSuccess;
       if (full > 0)
-        e = hipMemcpy2DAsync(dst, size_t(2 * g.e), src, size_t(2 * S), size_t(2 * g.e), size_t(full), kind, hs);
+        e = hipMemcpy2DAsync(dst, size_t(2 * g.e), src, size_t(2 * S), size_t(2 * g.e), size_t(full),
+                             hipMemcpyDeviceToDevice, hs);
       if (e == hipSuccess && full < R) {
         const int64_t v = g.rows - full * g.m;
-        if (v > 0)
-          e = hipMemcpyAsync(dst + 2 * full * g.e, src + 2 * full * S, size_t(2 * v * g.L), kind, hs);
+        if (v > 0) e = hipMemcpyAsync(dst + 2 * full * g.e, src + 2 * full * S, size_t(2 * v * g.L),
+                                      hipMemcpyDeviceToDevice, hs);
       }
       if (e == hipErrorInvalidValue || e == hipErrorNotSupported) {
         tide::set_last_hip_error(e);
@@ -237,6 +253,49 @@ tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* co
       }
       if (e != hipSuccess) return tide::hip_fail(e);
     }
+    return TIDE_OK;
+  }
+
+  if (mode == TIDE_AG_SDMA) {
+    // DMA engines only: the runtime sends 1-D device-to-device copies of the "no compute unit"
+    // kind to the SDMA engines (2-D copies become shader kernels), so each (parameter, rank)
+    // segment -- contiguous on both sides -- is one copy.  Copies alternate over the internal
+    // copy streams, which fork from and join back into the caller's stream.
+    std::lock_guard<std::mutex> lock(layout->mu);
+    tide::DeviceState* st = nullptr;
+    int e = tide::device_state(layout, &st);
+    if (e != hipSuccess) return tide::hip_fail(e);
+    if ((e = tide::ensure_dma(st)) != hipSuccess) return tide::hip_fail(e);
+    if ((e = hipEventRecord(st->dma_fork, hs)) != hipSuccess) return tide::hip_fail(e);
+    for (int k = 0; k < tide::kDmaStreams; ++k)
+      if ((e = hipStreamWaitEvent(st->dma[k], st->dma_fork, 0)) != hipSuccess) return tide::hip_fail(e);
+    int64_t issued = 0;
+    for (int32_t p = 0; p < P && e == hipSuccess; ++p) {
+      const tide::ParamGeom& g = layout->params[p];
+      if (g.numel == 0) continue;
+      for (int32_t r = 0; r < R; ++r) {
+        const int64_t v = std::min<int64_t>(g.m, std::max<int64_t>(0, g.rows - int64_t(r) * g.m));
+        if (v == 0) break;
+        const char* src = static_cast<const char*>(stage) + 2 * (int64_t(r) * S + g.o);
+        char* dst = static_cast<char*>(params[p]) + 2 * int64_t(r) * g.e;
+        e = hipMemcpyAsync(dst, src, size_t(2 * v * g.L), hipMemcpyDeviceToDeviceNoCU,
+                           st->dma[issued % tide::kDmaStreams]);
+        if (e != hipSuccess) break;
+        ++issued;
+      }
+    }
+    // Join even after a failed copy, so the caller's stream never runs ahead of issued copies.
+    int ej = hipSuccess;
+    for (int k = 0; k < tide::kDmaStreams; ++k) {
+      if (ej == hipSuccess) ej = hipEventRecord(st->dma_join[k], st->dma[k]);
+      if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, st->dma_join[k], 0);
+    }
+    if (e == hipErrorInvalidValue || e == hipErrorNotSupported) {
+      tide::set_last_hip_error(e);
+      return TIDE_ERR_UNSUPPORTED;
+    }
+    if (e != hipSuccess) return tide::hip_fail(e);
+    if (ej != hipSuccess) return tide::hip_fail(ej);
     return TIDE_OK;
   }
 

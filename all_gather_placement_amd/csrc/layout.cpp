@@ -215,6 +215,14 @@ void tide_layout_destroy(tide_layout* layout) {
       if (s.dev) (void)hipFree(s.dev);
       if (s.host) (void)hipHostFree(s.host);
     }
+    for (int k = 0; k < tide::kDmaStreams; ++k) {
+      if (st.dma[k]) {
+        (void)hipStreamSynchronize(st.dma[k]);
+        (void)hipStreamDestroy(st.dma[k]);
+      }
+      if (st.dma_join[k]) (void)hipEventDestroy(st.dma_join[k]);
+    }
+    if (st.dma_fork) (void)hipEventDestroy(st.dma_fork);
     if (st.rs) (void)hipFree(st.rs);
     if (st.ag) (void)hipFree(st.ag);
   }

@@ -22,6 +22,7 @@ TIDE_ERR_HIP = 3
 TIDE_ERR_UNSUPPORTED = 4
 TIDE_AG_KERNEL = 0
 TIDE_AG_SDMA = 1
+TIDE_AG_COPY2D = 2
 
 _lib = None
 

@@ -39,11 +39,16 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_1_8b_layer")
     ap.add_argument("--cu-budget", type=int, default=0)
-    ap.add_argument("--ag-mode", choices=["kernel", "sdma"], default="kernel")
+    ap.add_argument("--ag-mode", choices=["kernel", "sdma", "copy2d"], default="kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain torch device copy of this many MiB per step (counter calibration)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--interference", action="store_true",
+                    help="instead of the step benchmark: slowdown of a concurrent one-wave bf16 GEMM per cu_budget")
+    ap.add_argument("--budgets", default="0,16,64,256,512,768,1024,1536,2048")
+    ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
+    ap.add_argument("--reps", type=int, default=15)
     return ap.parse_args()
 
 
@@ -127,6 +132,124 @@ def cpu_baseline(cfg, log, min_seconds: float = 10.0):
     }
 
 
+def interference(args, log):
+    """Slowdown of a concurrent one-wave bf16 GEMM while the RS runs at each CU budget.
+
+    The victim is a torch bf16 matmul (hipBLASLt) whose kernel is one wave on the device: at
+    4096^3 it runs 256 workgroups of 256x256 tiles, one per CU.  For each repetition the GEMM's
+    stream first runs a short spin kernel (so the RS is already resident when the GEMM starts), then
+    the GEMM between two events; the RS is enqueued on a second stream right after.  A repetition
+    counts when the RS started before the GEMM; `rs_outlasts_gemm` is the fraction of those where
+    it was still running when the GEMM finished (when it is not, the GEMM waited for the RS to
+    drain).  slowdown = median(GEMM with RS) / median(GEMM alone) - 1, the pages' statistic
+    (medians of launches).  The same is measured for the AG placement on each engine.
+    """
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import Layout
+    from oracle.geometry import group_geometry
+    from workloads import CONFIGS, normal_bf16_cuda
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    M, N, K = (int(x) for x in args.gemm.split(","))
+    a = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
+    grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
+             for c in range(cfg.C)]
+    _, S = group_geometry(cfg.shapes, cfg.R)
+    shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
+    rs_bytes = 2 * cfg.C * cfg.numel() + 4 * cfg.R * S
+    L = Layout(cfg.shapes, cfg.R)
+    L.prepare()
+    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    spin_cycles = 400_000  # ~0.2 ms at 2.4 GHz: the RS is resident before the GEMM starts
+
+    from all_gather_placement_amd import TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
+
+    stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
+    params = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in cfg.shapes]
+    ag_bytes = 4 * cfg.numel()
+
+    def comm(kind, budget):
+        if kind == "rs":
+            L.rs_bf16_to_fp32(grads, shards, cu_budget=budget, stream=sB)
+        else:
+            mode = {"ag_sdma": TIDE_AG_SDMA, "ag_copy2d": TIDE_AG_COPY2D}.get(kind, TIDE_AG_KERNEL)
+            for _ in range(1 if kind == "ag_sdma" else 4):  # long enough to cover the GEMM
+                L.ag_place(stage, params, mode=mode, cu_budget=budget, stream=sB)
+
+    def gemm_once(kind=None, budget=0):
+        torch.cuda.synchronize()
+        e0, e1, r0, r1 = ev(), ev(), ev(), ev()
+        with torch.cuda.stream(sA):
+            torch.cuda._sleep(spin_cycles)
+            e0.record(sA)
+            torch.matmul(a, b)
+            e1.record(sA)
+        if kind is not None:
+            r0.record(sB)
+            comm(kind, budget)
+            r1.record(sB)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1)
+        if kind is None:
+            return t, True, True
+        return t, r0.elapsed_time(e0) > 0, e1.elapsed_time(r1) > 0
+
+    def comm_alone(kind, budget):
+        ts = []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            r0, r1 = ev(), ev()
+            r0.record(sB)
+            comm(kind, budget)
+            r1.record(sB)
+            torch.cuda.synchronize()
+            ts.append(r0.elapsed_time(r1))
+        return statistics.median(ts)
+
+    for _ in range(3):
+        gemm_once()
+    alone_all = [gemm_once()[0] for _ in range(max(args.reps, 15))]
+    alone = statistics.median(alone_all)
+    log(f"victim GEMM {M}x{N}x{K} bf16 alone: {alone * 1e3:.1f} us (median of {len(alone_all)})")
+    rows = []
+    cases = [("rs", int(x)) for x in args.budgets.split(",")]
+    cases += [("ag_kernel", 0), ("ag_kernel", 768), ("ag_copy2d", 0), ("ag_sdma", 0)]
+    for kind, budget in cases:
+        t_alone = comm_alone(kind, budget)
+        conc, outlast = [], 0
+        for _ in range(args.reps):
+            t, started_first, outlasted = gemm_once(kind, budget)
+            if started_first:
+                conc.append(t)
+                outlast += int(outlasted)
+        nbytes = rs_bytes if kind == "rs" else (1 if kind == "ag_sdma" else 4) * ag_bytes
+        med = statistics.median(conc) if conc else None
+        row = {
+            "comm": kind, "cu_budget": budget,
+            "comm_ms": round(t_alone, 4),
+            "comm_gbps": round(nbytes / (t_alone * 1e-3) / 1e9, 1),
+            "gemm_alone_us": round(alone * 1e3, 2),
+            "gemm_concurrent_us": round(med * 1e3, 2) if med else None,
+            "gemm_concurrent_min_max_us": [round(min(conc) * 1e3, 2), round(max(conc) * 1e3, 2)] if conc else None,
+            "slowdown_pct": round((med / alone - 1) * 100, 2) if med else None,
+            "reps": len(conc),
+            "comm_outlasts_gemm": round(outlast / len(conc), 2) if conc else None,
+        }
+        log(json.dumps(row))
+        rows.append(row)
+    L.close()
+    out = {"experiment": "concurrent one-wave GEMM slowdown vs communication CU budget", "workload": cfg.name,
+           "gemm": [M, N, K], "gemm_alone_us_min_max": [round(min(alone_all) * 1e3, 2), round(max(alone_all) * 1e3, 2)],
+           "rows": rows}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -141,11 +264,15 @@ def main():
 
     import torch
 
-    from all_gather_placement_amd import Layout, TIDE_AG_KERNEL, TIDE_AG_SDMA
+    from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
     from oracle.geometry import group_geometry  # sizes only, for the byte formulas
     from workloads import CONFIGS, normal_bf16_cuda
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.interference:
+        torch.cuda.set_device(0)
+        interference(args, log)
+        return
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -165,7 +292,7 @@ def main():
     if args.calib_copy_mib:
         calib_src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         calib_dst = torch.empty_like(calib_src)
-    ag_mode = TIDE_AG_KERNEL if args.ag_mode == "kernel" else TIDE_AG_SDMA
+    ag_mode = {"kernel": TIDE_AG_KERNEL, "sdma": TIDE_AG_SDMA, "copy2d": TIDE_AG_COPY2D}[args.ag_mode]
 
     L = Layout(cfg.shapes, cfg.R)
     L.prepare()

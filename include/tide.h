@@ -55,8 +55,14 @@ typedef enum tide_status {
 
 /* Placement engines for tide_ag_place. */
 enum {
-  TIDE_AG_KERNEL = 0, /* hand-written copy kernel (bandwidth path; uses CUs) */
-  TIDE_AG_SDMA = 1    /* one 2-D DMA copy per parameter + one tail copy, no compute units */
+  TIDE_AG_KERNEL = 0, /* hand-written gfx950 copy kernel: the bandwidth path (uses CUs) */
+  TIDE_AG_SDMA = 1,   /* DMA (SDMA) engines only, no compute units: one 1-D copy per (parameter,
+                         rank) segment, spread over the library's internal copy streams.  On one
+                         MI355X the engines move roughly 0.06-0.2 TB/s locally, far below the
+                         kernel; this mode is for callers that must leave every CU to compute. */
+  TIDE_AG_COPY2D = 2  /* one runtime 2-D copy per parameter (row pitch = one stage slot) plus one
+                         copy for the rank whose slice is part padding; the HIP runtime picks the
+                         engine (on ROCm 7.2 a shader blit kernel, i.e. it uses CUs). */
 };
 
 /*
@@ -142,13 +148,15 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
  *   stage      device, R*S bf16 elements, rank-major: rank r's shard starts at element r*S.
  *   params     host [P]: params[p] is parameter p's contiguous bf16 device storage of rows_p * L_p
  *              elements (NULL allowed only for empty parameters).
- *   mode       TIDE_AG_KERNEL or TIDE_AG_SDMA.
- *   cu_budget  as for the RS (ignored by TIDE_AG_SDMA).
+ *   mode       TIDE_AG_KERNEL, TIDE_AG_SDMA or TIDE_AG_COPY2D.
+ *   cu_budget  as for the RS (used by TIDE_AG_KERNEL only).
  * Result: params[p][r*m_p*L_p + k] = stage[r*S + o_p + k] for every r and k < v*L_p, copied as
  * bits; stage padding is never read into a parameter; every parameter element is written once.
  * All pointers must be 2-byte aligned; 16-byte alignment selects the vector path.
+ * TIDE_AG_SDMA work is ordered after the caller's earlier work on `stream`, and later work on
+ * `stream` waits for it (event fork/join with the internal copy streams).
  * Errors: TIDE_ERR_INVALID (null/misaligned pointer, bad mode, a parameter overlapping the stage
- * or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a compute-unit-free copy),
+ * or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a copy kind), TIDE_ERR_NOMEM,
  * TIDE_ERR_HIP.
  */
 tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params,

@@ -261,7 +261,8 @@ def test_ag_rejects_bad_arguments_before_any_hip_call():
         params = [(1 << 33) + p * (1 << 20) for p in range(L.P)]
         call = lambda st_, pp, mode=0, budget=0: lib.tide_ag_place(L.handle, st_, _vp_array(pp), mode, budget, None)
         INV = tb.TIDE_ERR_INVALID
-        assert call(stage, params, mode=2) == INV
+        assert call(stage, params, mode=3) == INV
+        assert call(stage, params, mode=-1) == INV
         assert call(stage, params, budget=-1) == INV
         assert call(None, params) == INV
         assert call(stage + 1, params) == INV

@@ -12,7 +12,7 @@ import torch
 import oracle
 from oracle import geometry as ogeo
 from oracle import rs as ors
-from all_gather_placement_amd import Layout, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError
+from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError
 from workloads import ORDERED, TINY, normal_bf16_bits, normal_bf16_cuda, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -99,7 +99,7 @@ def test_tiny_rs_bit_exact(gpu_available):
         assert_rs_equal(run_rs(TINY.shapes, TINY.R, g, cu_budget=budget), want)
 
 
-@pytest.mark.parametrize("mode", [TIDE_AG_KERNEL, TIDE_AG_SDMA], ids=["kernel", "sdma"])
+@pytest.mark.parametrize("mode", [TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D], ids=["kernel", "sdma", "copy2d"])
 def test_tiny_ag_bit_exact(gpu_available, mode):
     say(f"tiny AG mode={mode}")
     geo, S = ogeo.group_geometry(TINY.shapes, TINY.R)
@@ -141,7 +141,7 @@ def test_groups_rs_bit_exact(gpu_available, case):
 
 
 @pytest.mark.parametrize("case", range(len(GROUPS)))
-@pytest.mark.parametrize("mode", [TIDE_AG_KERNEL, TIDE_AG_SDMA], ids=["kernel", "sdma"])
+@pytest.mark.parametrize("mode", [TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D], ids=["kernel", "sdma", "copy2d"])
 def test_groups_ag_bit_exact(gpu_available, case, mode):
     shapes, R, _ = GROUPS[case]
     say(f"group {case} AG mode={mode}")
@@ -173,7 +173,7 @@ def test_ag_alignment_sweep(gpu_available, st_off, p_off):
     geo, S = ogeo.group_geometry(shapes, R)
     stage = normal_bf16_bits((R * S,), 1.0, 71, 0)
     want = oracle.all_gather_place(stage, shapes, R)
-    for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA):
+    for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D):
         got = run_ag(shapes, R, stage, mode=mode, st_pad=st_off, p_pad=lambda p: (p_off * (p + 1)) % 8)
         for a, b in zip(got, want):
             assert np.array_equal(a, b)
@@ -244,15 +244,19 @@ def test_overlap_rejected(gpu_available):
             L.rs_bf16_to_fp32([[g]], [buf[:32], buf[16:48]])
 
 
-def test_ag_then_rs_round_trip(gpu_available):
-    say("AG -> RS(C=1) round trip")
-    shapes, R = [(7, 5), (16, 3), (1, 9), (1000, 33)], 4
+@pytest.mark.parametrize("mode", [TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D], ids=["kernel", "sdma", "copy2d"])
+def test_ag_then_rs_round_trip(gpu_available, mode):
+    """AG placement then RS of that single contributor on the same stream, no host sync between:
+    also checks that DMA-engine copies are ordered before the next kernel on the caller's stream."""
+    say(f"AG -> RS(C=1) round trip, mode={mode}")
+    shapes, R = [(7, 5), (16, 3), (1, 9), (1000, 33), (4096, 64)], 4
     geo, S = ogeo.group_geometry(shapes, R)
     stage_bits = normal_bf16_bits((R * S,), 1.0, 75, 0)
     stage = dev_bf16(stage_bits)
     params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+    torch.cuda.synchronize()
     with Layout(shapes, R) as L:
-        L.ag_place(stage, params)
+        L.ag_place(stage, params, mode=mode)
         shards = poisoned_shards(R, S)
         L.rs_bf16_to_fp32([params], shards)
         torch.cuda.synchronize()
@@ -354,7 +358,7 @@ def test_full_size_rs_and_ag(gpu_available, cfg):
 
         # (3) AG placement, both engines, bit-exact against torch slicing; then the round trip
         stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
-        for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA):
+        for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D):
             params = [torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda") for s in cfg.shapes]
             say(f"full size {cfg.name}: AG mode={mode}")
             L.ag_place(stage, params, mode=mode)
