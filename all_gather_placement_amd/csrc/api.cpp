@@ -114,22 +114,24 @@ int ensure_dma(DeviceState* st) {
 }
 
 // Launch plan for `count` work items: cu_budget 0 = one item per workgroup in one launch;
-// B > 0 = grids of at most B workgroups, each taking a few items and exiting.
+// B > 0 = grids of at most `max_wgs` workgroups, each taking `bounded_items` items and exiting
+// (bounded_items 0: one launch, workgroups walk every item).
 struct Plan {
   int grid;
   int items;
   int64_t per_launch;
 };
 
-Plan plan_for(int64_t count, int32_t cu_budget) {
+Plan plan_for(int64_t count, int32_t cu_budget, int64_t max_wgs, int bounded_items) {
   if (cu_budget <= 0) {
     const int64_t cap = kPersistentWorkgroups > 0 ? kPersistentWorkgroups : (int64_t(1) << 30);
     const int64_t g = std::min<int64_t>(count, cap);
     const int items = int((count + g - 1) / g);
     return Plan{int(g), items, int64_t(g) * items};
   }
-  const int grid = int(std::min<int64_t>(count, cu_budget));
-  return Plan{grid, kItemsPerBoundedWorkgroup, int64_t(grid) * kItemsPerBoundedWorkgroup};
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(count, max_wgs));
+  const int64_t items = bounded_items > 0 ? bounded_items : (count + grid - 1) / grid;
+  return Plan{int(grid), int(items), grid * items};
 }
 
 }  // namespace
@@ -187,7 +189,7 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
   tide::PtrSlot* slot = nullptr;
   if ((e = tide::acquire_ptrs(st, table.data(), table.size(), hs, &slot)) != hipSuccess) return tide::hip_fail(e);
 
-  const tide::Plan plan = tide::plan_for(count, cu_budget);
+  const tide::Plan plan = tide::plan_for(count, cu_budget, cu_budget, tide::kRsBoundedItems);
   for (int64_t first = 0; first < count; first += plan.per_launch) {
     const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
     const int grid = int(std::min<int64_t>(plan.grid, n));
@@ -307,7 +309,8 @@ tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* co
   if (e != hipSuccess) return tide::hip_fail(e);
   tide::PtrSlot* slot = nullptr;
   if ((e = tide::acquire_ptrs(st, params, size_t(P), hs, &slot)) != hipSuccess) return tide::hip_fail(e);
-  const tide::Plan plan = tide::plan_for(count, cu_budget);
+  const int64_t ag_wgs = int64_t(cu_budget) * tide::kThreads / tide::kAgThreads;
+  const tide::Plan plan = tide::plan_for(count, cu_budget, ag_wgs, tide::kAgBoundedItems);
   for (int64_t first = 0; first < count; first += plan.per_launch) {
     const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
     const int grid = int(std::min<int64_t>(plan.grid, n));

@@ -76,8 +76,23 @@ constexpr int64_t kPersistentWorkgroups = TIDE_PERSISTENT_WGS;
 static_assert(kRsChunk % 8 == 0 && kAgChunk % 8 == 0, "work items must be whole 16-byte vectors");
 static_assert(kRsChunk < (int64_t(1) << 31) && kAgChunk < (int64_t(1) << 31), "item sizes are int32");
 
-// Work items a workgroup takes per launch when the caller bounds the resident workgroups.
-constexpr int kItemsPerBoundedWorkgroup = 4;
+// Bounded launches (cu_budget B > 0): at most B RS workgroups (B * kThreads / kAgThreads AG
+// workgroups, the same number of threads) are resident; each takes this many work items and exits,
+// and the call issues as many launches as it needs.  0 = a single launch whose B workgroups walk
+// all items (resident for the whole call).
+// Measured on MI355X against a concurrent one-wave bf16 GEMM (hipBLASLt, one 256x256 tile per
+// CU): the GEMM's waves cannot share a SIMD with a resident RS wave, so a GEMM workgroup waits
+// until the RS workgroups on its CU exit.  Workgroups that live for the whole call (0) slowed the
+// GEMM ~7x even at B = 256; 64 items 0.5-2.5x; 16 items 4-27%; 4 items (a launch of B = 512 lasts
+// ~17 us) 4-8%.  Short-lived it is.
+#ifndef TIDE_RS_BOUNDED_ITEMS
+#define TIDE_RS_BOUNDED_ITEMS 4
+#endif
+#ifndef TIDE_AG_BOUNDED_ITEMS
+#define TIDE_AG_BOUNDED_ITEMS 16
+#endif
+constexpr int kRsBoundedItems = TIDE_RS_BOUNDED_ITEMS;
+constexpr int kAgBoundedItems = TIDE_AG_BOUNDED_ITEMS;
 
 // One RS work item: nvalid summed elements of parameter p, starting at element `src` of the
 // parameter's storage, written to shard r at element `dst`; then npad zeros at dst + nvalid.

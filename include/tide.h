@@ -126,8 +126,10 @@ tide_status tide_layout_copy_ag_items(const tide_layout* layout, int64_t first, 
  *              only for empty parameters).  Read in place, never written.
  *   shards     host [R]: shards[r] is rank r's flat fp32 device shard of S elements, 4-byte aligned.
  *   cu_budget  0: one launch, one short-lived workgroup per work item, as wide as the device runs.
- *              B > 0: at most B workgroups (256 threads each) resident at a time; each processes a
- *              few work items and exits, and the call issues as many launches as needed.
+ *              B > 0: at most B workgroups of 256 threads resident at a time; each processes a
+ *              bounded number of work items (4 by default, 160 KiB of traffic at C = 8) and
+ *              exits, and the call issues as many launches as needed, so a concurrent kernel's
+ *              workgroups find free CUs within one short launch.
  *   stream     hipStream_t as void*.
  * Result, for every r, p and element k of the slice: shards[r][o_p + k] =
  *   x_0 (+) x_1 (+) ... (+) x_{C-1}, x_c = grads[c*P+p][r*m_p*L_p + k] widened exactly to fp32,
@@ -149,7 +151,8 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
  *   params     host [P]: params[p] is parameter p's contiguous bf16 device storage of rows_p * L_p
  *              elements (NULL allowed only for empty parameters).
  *   mode       TIDE_AG_KERNEL, TIDE_AG_SDMA or TIDE_AG_COPY2D.
- *   cu_budget  as for the RS (used by TIDE_AG_KERNEL only).
+ *   cu_budget  as for the RS, counted in 256-thread slots (TIDE_AG_KERNEL only; its workgroups
+ *              are 128 threads, so B admits 2B of them).
  * Result: params[p][r*m_p*L_p + k] = stage[r*S + o_p + k] for every r and k < v*L_p, copied as
  * bits; stage padding is never read into a parameter; every parameter element is written once.
  * All pointers must be 2-byte aligned; 16-byte alignment selects the vector path.
