@@ -15,4 +15,6 @@ from .tide import (  # noqa: F401
     tide_ag_place,
     tide_layout_create,
     tide_rs_bf16_to_fp32,
+    tide_rs_slots_bf16_to_fp32,
+    tide_slot_pack,
 )

@@ -193,8 +193,8 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
   for (int64_t first = 0; first < count; first += plan.per_launch) {
     const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
     const int grid = int(std::min<int64_t>(plan.grid, n));
-    e = tide::launch_rs(st->rs, first, n, grid, plan.items, const_cast<const void* const*>(slot->dev), P, C, vec,
-                        hs);
+    e = tide::launch_rs(st->rs, first, n, grid, plan.items, const_cast<const void* const*>(slot->dev), P, C, S,
+                        /*flat=*/false, vec, hs);
     if (e != hipSuccess) {
       (void)tide::release_ptrs(slot, hs);
       return tide::hip_fail(e);
@@ -314,14 +314,114 @@ tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* co
   for (int64_t first = 0; first < count; first += plan.per_launch) {
     const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
     const int grid = int(std::min<int64_t>(plan.grid, n));
-    e = tide::launch_ag(st->ag, first, n, grid, plan.items, stage, const_cast<const void* const*>(slot->dev), vec,
-                        hs);
+    e = tide::launch_ag(st->ag, first, n, grid, plan.items, const_cast<void*>(stage),
+                        const_cast<const void* const*>(slot->dev), /*pack=*/false, vec, hs);
     if (e != hipSuccess) {
       (void)tide::release_ptrs(slot, hs);
       return tide::hip_fail(e);
     }
   }
   if ((e = tide::release_ptrs(slot, hs)) != hipSuccess) return tide::hip_fail(e);
+  return TIDE_OK;
+}
+
+tide_status tide_slot_pack(const tide_layout* layout, const void* const* grads, void* slot, int32_t cu_budget,
+                           void* stream) {
+  if (layout == nullptr || grads == nullptr || cu_budget < 0) return TIDE_ERR_INVALID;
+  const int32_t P = layout->P, R = layout->R;
+  const int64_t S = layout->S;
+  const int64_t slot_n = int64_t(R) * S;
+  if (slot_n > 0 && (slot == nullptr || !tide::aligned(slot, 2))) return TIDE_ERR_INVALID;
+  bool vec = slot_n == 0 || tide::aligned(slot, 16);
+  std::vector<Range> ins, outs;
+  if (slot_n > 0) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(slot);
+    outs.push_back(Range{lo, lo + uintptr_t(slot_n) * 2});
+  }
+  for (int32_t p = 0; p < P; ++p) {
+    const int64_t n = layout->params[p].numel;
+    if (n == 0) continue;
+    const void* g = grads[p];
+    if (g == nullptr || !tide::aligned(g, 2)) return TIDE_ERR_INVALID;
+    vec = vec && tide::aligned(g, 16);
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(g);
+    ins.push_back(Range{lo, lo + uintptr_t(n) * 2});
+  }
+  if (tide::outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
+  if (slot_n == 0) return TIDE_OK;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(layout->mu);
+  tide::DeviceState* st = nullptr;
+  int e = tide::device_state(layout, &st);
+  if (e != hipSuccess) return tide::hip_fail(e);
+  const int64_t count = int64_t(layout->ag_chunks.size());
+  if (count > 0) {
+    tide::PtrSlot* pslot = nullptr;
+    if ((e = tide::acquire_ptrs(st, const_cast<void* const*>(grads), size_t(P), hs, &pslot)) != hipSuccess)
+      return tide::hip_fail(e);
+    const int64_t ag_wgs = int64_t(cu_budget) * tide::kThreads / tide::kAgThreads;
+    const tide::Plan plan = tide::plan_for(count, cu_budget, ag_wgs, tide::kAgBoundedItems);
+    for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
+      const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
+      const int grid = int(std::min<int64_t>(plan.grid, n));
+      e = tide::launch_ag(st->ag, first, n, grid, plan.items, slot, const_cast<const void* const*>(pslot->dev),
+                          /*pack=*/true, vec, hs);
+    }
+    const int er = tide::release_ptrs(pslot, hs);
+    if (e != hipSuccess) return tide::hip_fail(e);
+    if (er != hipSuccess) return tide::hip_fail(er);
+  }
+  e = tide::launch_fill_zero(st->slot_pad, int64_t(layout->slot_pad_items.size()), slot, hs);
+  if (e != hipSuccess) return tide::hip_fail(e);
+  return TIDE_OK;
+}
+
+tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* slots,
+                                       float* const* shards, int32_t cu_budget, void* stream) {
+  if (layout == nullptr || slots == nullptr || shards == nullptr || C < 1 || cu_budget < 0)
+    return TIDE_ERR_INVALID;
+  const int32_t R = layout->R;
+  const int64_t S = layout->S;
+  if (C > (1 << 24)) return TIDE_ERR_INVALID;
+  if (S == 0) return TIDE_OK;
+  bool vec = true;
+  std::vector<Range> ins, outs;
+  for (int32_t c = 0; c < C; ++c) {
+    const void* g = slots[c];
+    if (g == nullptr || !tide::aligned(g, 2)) return TIDE_ERR_INVALID;
+    vec = vec && tide::aligned(g, 16);
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(g);
+    ins.push_back(Range{lo, lo + uintptr_t(int64_t(R) * S) * 2});
+  }
+  for (int32_t r = 0; r < R; ++r) {
+    const float* s = shards[r];
+    if (s == nullptr || !tide::aligned(s, 4)) return TIDE_ERR_INVALID;
+    vec = vec && tide::aligned(s, 16);
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(s);
+    outs.push_back(Range{lo, lo + uintptr_t(S) * 4});
+  }
+  if (tide::outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
+  const int64_t count = int64_t(layout->rs_chunks.size());
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(layout->mu);
+  tide::DeviceState* st = nullptr;
+  int e = tide::device_state(layout, &st);
+  if (e != hipSuccess) return tide::hip_fail(e);
+  std::vector<void*> table(size_t(C) + R);
+  for (int32_t c = 0; c < C; ++c) table[c] = const_cast<void*>(slots[c]);
+  for (int32_t r = 0; r < R; ++r) table[size_t(C) + r] = shards[r];
+  tide::PtrSlot* pslot = nullptr;
+  if ((e = tide::acquire_ptrs(st, table.data(), table.size(), hs, &pslot)) != hipSuccess) return tide::hip_fail(e);
+  const tide::Plan plan = tide::plan_for(count, cu_budget, cu_budget, tide::kRsBoundedItems);
+  for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
+    const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
+    const int grid = int(std::min<int64_t>(plan.grid, n));
+    e = tide::launch_rs(st->rs, first, n, grid, plan.items, const_cast<const void* const*>(pslot->dev), 1, C, S,
+                        /*flat=*/true, vec, hs);
+  }
+  const int er = tide::release_ptrs(pslot, hs);
+  if (e != hipSuccess) return tide::hip_fail(e);
+  if (er != hipSuccess) return tide::hip_fail(er);
   return TIDE_OK;
 }
 

@@ -144,12 +144,17 @@ __device__ __forceinline__ float sum1_rt(const unsigned short* const* gptr, int3
 }
 
 // RS kernel.  CT in 1..8: contributor count fixed at compile time; CT == 0: any C >= 1.
-// VEC: all gradient and shard base pointers are 16-byte aligned (checked on the host), so the
+// VEC: all source and shard base pointers are 16-byte aligned (checked on the host), so the
 // alignment of an element depends only on its offset inside its buffer.
-template <int CT, bool VEC>
+// FLAT = false: sources are the per-parameter gradients, pointer table [C*P grads][R shards],
+//   item source at gradient (c, p), element ch.src (in-place read).
+// FLAT = true: sources are C packed rank-major slots of R*S elements (Slot-Reuse), pointer table
+//   [C slots][R shards] (P = 1), item source at slot c, element ch.r * S + ch.dst.
+template <int CT, bool VEC, bool FLAT>
 __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict__ chunks, int64_t first,
                                                       int64_t count, int items_per_wg,
-                                                      void* const* __restrict__ ptrs, int32_t P, int32_t C) {
+                                                      void* const* __restrict__ ptrs, int32_t P, int32_t C,
+                                                      int64_t S) {
   const int tid = threadIdx.x;
   const unsigned short* const* __restrict__ gptr = reinterpret_cast<const unsigned short* const*>(ptrs);
   float* const* __restrict__ sptr = reinterpret_cast<float* const*>(ptrs + static_cast<int64_t>(C) * P);
@@ -158,7 +163,11 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
   for (int j = 0; j < items_per_wg; ++j) {
     const int64_t item = item_of<TIDE_RS_XCD_REMAP != 0>(j, count);
     if (item >= count) break;
-    const RsChunk ch = chunks[first + item];
+    RsChunk ch = chunks[first + item];
+    if (FLAT) {
+      ch.src = static_cast<int64_t>(ch.r) * S + ch.dst;
+      ch.p = 0;
+    }
     float* dst = sptr[ch.r] + ch.dst;
     const int n = ch.nvalid;
 
@@ -209,21 +218,24 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
 // AG kernel: bit copy of n bf16 elements per item.  VEC: stage and parameter bases are 16-byte
 // aligned, so an item whose source and destination offsets agree mod 8 elements copies 16-byte
 // vectors after a short head.
-template <bool VEC>
+// PACK = false: placement, stage -> parameters.  PACK = true: the inverse (Slot-Reuse packing),
+// parameters -> stage slot, over the same items.
+template <bool VEC, bool PACK>
 __global__ __launch_bounds__(kAgThreads) void ag_kernel(const AgChunk* __restrict__ chunks, int64_t first,
                                                         int64_t count, int items_per_wg,
-                                                        const unsigned short* __restrict__ stage,
+                                                        unsigned short* __restrict__ stage,
                                                         unsigned short* const* __restrict__ params) {
   const int tid = threadIdx.x;
   for (int j = 0; j < items_per_wg; ++j) {
     const int64_t item = item_of<TIDE_AG_XCD_REMAP != 0>(j, count);
     if (item >= count) break;
     const AgChunk ch = chunks[first + item];
-    const unsigned short* src = stage + ch.src;
-    unsigned short* dst = params[ch.p] + ch.dst;
+    const unsigned short* src = PACK ? params[ch.p] + ch.dst : stage + ch.src;
+    unsigned short* dst = PACK ? stage + ch.src : params[ch.p] + ch.dst;
+    const int64_t src_off = PACK ? ch.dst : ch.src;
     const int n = ch.n;
     if (VEC && ((ch.src - ch.dst) & 7) == 0) {
-      const int head = min(n, static_cast<int>((-ch.src) & 7));
+      const int head = min(n, static_cast<int>((-src_off) & 7));
       const int nb = (n - head) >> 3;
       const int tail = (n - head) & 7;
       if (tid < head) store_hbm(dst + tid, load_hbm(src + tid));
@@ -249,48 +261,81 @@ __global__ __launch_bounds__(kAgThreads) void ag_kernel(const AgChunk* __restric
   }
 }
 
-template <int CT>
+// Zero-fill kernel for the padding of a packed slot: items (src = slot element offset, n).
+__global__ __launch_bounds__(kAgThreads) void fill_zero_kernel(const AgChunk* __restrict__ items, int64_t count,
+                                                                unsigned short* __restrict__ slot) {
+  const int64_t item = blockIdx.x;
+  if (item >= count) return;
+  const AgChunk ch = items[item];
+  for (int i = threadIdx.x; i < ch.n; i += kAgThreads) store_hbm(slot + ch.src + i, static_cast<unsigned short>(0));
+}
+
+template <int CT, bool FLAT>
 hipError_t launch_rs_ct(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items,
-                        void* const* ptrs, int32_t P, int32_t C, bool vec, hipStream_t s) {
+                        void* const* ptrs, int32_t P, int32_t C, int64_t S, bool vec, hipStream_t s) {
   if (vec)
-    hipLaunchKernelGGL((rs_kernel<CT, true>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items, ptrs,
-                       P, C);
+    hipLaunchKernelGGL((rs_kernel<CT, true, FLAT>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items,
+                       ptrs, P, C, S);
   else
-    hipLaunchKernelGGL((rs_kernel<CT, false>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items, ptrs,
-                       P, C);
+    hipLaunchKernelGGL((rs_kernel<CT, false, FLAT>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items,
+                       ptrs, P, C, S);
   return hipGetLastError();
+}
+
+template <bool FLAT>
+hipError_t launch_rs_c(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items, void* const* ptrs,
+                       int32_t P, int32_t C, int64_t S, bool vec, hipStream_t s) {
+  switch (C) {
+    case 1: return launch_rs_ct<1, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    case 2: return launch_rs_ct<2, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    case 3: return launch_rs_ct<3, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    case 4: return launch_rs_ct<4, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    case 5: return launch_rs_ct<5, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    case 6: return launch_rs_ct<6, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    case 7: return launch_rs_ct<7, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    case 8: return launch_rs_ct<8, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    default: return launch_rs_ct<0, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+  }
 }
 
 }  // namespace
 
 int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,
-              const void* const* dev_ptrs, int32_t P, int32_t C, bool vec, void* hip_stream) {
+              const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, void* hip_stream) {
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   void* const* ptrs = const_cast<void* const*>(dev_ptrs);
-  switch (C) {
-    case 1: return launch_rs_ct<1>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-    case 2: return launch_rs_ct<2>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-    case 3: return launch_rs_ct<3>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-    case 4: return launch_rs_ct<4>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-    case 5: return launch_rs_ct<5>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-    case 6: return launch_rs_ct<6>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-    case 7: return launch_rs_ct<7>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-    case 8: return launch_rs_ct<8>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-    default: return launch_rs_ct<0>(chunks, first, count, grid, items_per_wg, ptrs, P, C, vec, s);
-  }
+  if (flat) return launch_rs_c<true>(chunks, first, count, grid, items_per_wg, ptrs, 1, C, S, vec, s);
+  return launch_rs_c<false>(chunks, first, count, grid, items_per_wg, ptrs, P, C, S, vec, s);
 }
 
-int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,
-              const void* stage, const void* const* dev_params, bool vec, void* hip_stream) {
+int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, void* stage,
+              const void* const* dev_params, bool pack, bool vec, void* hip_stream) {
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const unsigned short* st = static_cast<const unsigned short*>(stage);
+  unsigned short* st = static_cast<unsigned short*>(stage);
   unsigned short* const* pp = reinterpret_cast<unsigned short* const*>(const_cast<void* const*>(dev_params));
-  if (vec)
-    hipLaunchKernelGGL((ag_kernel<true>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count, items_per_wg,
-                       st, pp);
-  else
-    hipLaunchKernelGGL((ag_kernel<false>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count, items_per_wg,
-                       st, pp);
+  if (pack) {
+    if (vec)
+      hipLaunchKernelGGL((ag_kernel<true, true>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count,
+                         items_per_wg, st, pp);
+    else
+      hipLaunchKernelGGL((ag_kernel<false, true>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count,
+                         items_per_wg, st, pp);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((ag_kernel<true, false>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count,
+                         items_per_wg, st, pp);
+    else
+      hipLaunchKernelGGL((ag_kernel<false, false>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count,
+                         items_per_wg, st, pp);
+  }
+  return hipGetLastError();
+}
+
+int launch_fill_zero(const AgChunk* items, int64_t count, void* slot, void* hip_stream) {
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(count)), dim3(kAgThreads), 0, s, items, count,
+                     static_cast<unsigned short*>(slot));
   return hipGetLastError();
 }
 

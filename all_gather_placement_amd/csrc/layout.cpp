@@ -43,6 +43,21 @@ void cut(int64_t src0, int64_t n, int64_t chunk, F&& emit) {
 
 thread_local int g_last_hip_error = 0;
 
+// Copy a host table to new device memory (nothing for an empty table).
+template <typename T>
+hipError_t upload(const std::vector<T>& v, T** out) {
+  *out = nullptr;
+  if (v.empty()) return hipSuccess;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(out), v.size() * sizeof(T));
+  if (e != hipSuccess) return e;
+  e = hipMemcpy(*out, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(*out);
+    *out = nullptr;
+  }
+  return e;
+}
+
 // Order in which workgroups take work items (before any XCD renumbering in the kernels):
 //   0: parameter-major (p, r, position): each contributor tensor is read front to back;
 //   1: rank-major (r, p, position): each shard is written front to back;
@@ -86,25 +101,14 @@ int device_state(const tide_layout* layout, DeviceState** out) {
     return hipSuccess;
   }
   DeviceState st;
-  const size_t rs_bytes = layout->rs_chunks.size() * sizeof(RsChunk);
-  const size_t ag_bytes = layout->ag_chunks.size() * sizeof(AgChunk);
-  if (rs_bytes) {
-    if ((e = hipMalloc(reinterpret_cast<void**>(&st.rs), rs_bytes)) != hipSuccess) return e;
-    if ((e = hipMemcpy(st.rs, layout->rs_chunks.data(), rs_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
-      (void)hipFree(st.rs);
-      return e;
-    }
-  }
-  if (ag_bytes) {
-    if ((e = hipMalloc(reinterpret_cast<void**>(&st.ag), ag_bytes)) != hipSuccess) {
-      if (st.rs) (void)hipFree(st.rs);
-      return e;
-    }
-    if ((e = hipMemcpy(st.ag, layout->ag_chunks.data(), ag_bytes, hipMemcpyHostToDevice)) != hipSuccess) {
-      if (st.rs) (void)hipFree(st.rs);
-      (void)hipFree(st.ag);
-      return e;
-    }
+  e = upload(layout->rs_chunks, &st.rs);
+  if (e == hipSuccess) e = upload(layout->ag_chunks, &st.ag);
+  if (e == hipSuccess) e = upload(layout->slot_pad_items, &st.slot_pad);
+  if (e != hipSuccess) {
+    if (st.rs) (void)hipFree(st.rs);
+    if (st.ag) (void)hipFree(st.ag);
+    if (st.slot_pad) (void)hipFree(st.slot_pad);
+    return e;
   }
   auto res = layout->devices.emplace(dev, st);
   *out = &res.first->second;
@@ -188,6 +192,10 @@ tide_status tide_layout_create(int32_t num_params, const int32_t* ndims, const i
         tide::cut(stage0, nvalid, tide::kAgChunk, [&](int64_t pos, int64_t len) {
           L->ag_chunks.push_back(AgChunk{stage0 + pos, src0 + pos, p, int32_t(len), 0});
         });
+        for (int64_t pos = 0; pos < npad; pos += tide::kAgChunk) {
+          const int64_t len = (npad - pos) < tide::kAgChunk ? (npad - pos) : tide::kAgChunk;
+          L->slot_pad_items.push_back(AgChunk{stage0 + nvalid + pos, 0, p, int32_t(len), 0});
+        }
       }
     }
     tide::order_items(L);
@@ -225,6 +233,7 @@ void tide_layout_destroy(tide_layout* layout) {
     if (st.dma_fork) (void)hipEventDestroy(st.dma_fork);
     if (st.rs) (void)hipFree(st.rs);
     if (st.ag) (void)hipFree(st.ag);
+    if (st.slot_pad) (void)hipFree(st.slot_pad);
   }
   if (have_dev && !layout->devices.empty()) (void)hipSetDevice(cur);
   delete layout;
@@ -296,6 +305,22 @@ tide_status tide_layout_copy_ag_items(const tide_layout* layout, int64_t first, 
     const AgChunk& c = layout->ag_chunks[first + i];
     int64_t* o = out + 4 * i;
     o[0] = c.p; o[1] = c.src; o[2] = c.dst; o[3] = c.n;
+  }
+  return TIDE_OK;
+}
+
+int64_t tide_layout_num_slot_pad_items(const tide_layout* layout) {
+  return layout ? int64_t(layout->slot_pad_items.size()) : -1;
+}
+
+tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t first, int64_t n, int64_t* out) {
+  if (layout == nullptr || out == nullptr || first < 0 || n < 0 ||
+      first + n > int64_t(layout->slot_pad_items.size()))
+    return TIDE_ERR_INVALID;
+  for (int64_t i = 0; i < n; ++i) {
+    const AgChunk& c = layout->slot_pad_items[first + i];
+    out[2 * i] = c.src;
+    out[2 * i + 1] = c.n;
   }
   return TIDE_OK;
 }

@@ -42,6 +42,7 @@ constexpr int kDmaStreams = 2;
 struct DeviceState {
   RsChunk* rs = nullptr;
   AgChunk* ag = nullptr;
+  AgChunk* slot_pad = nullptr;
   PtrSlot slots[kPtrSlots];
   int next = 0;
   hipStream_t dma[kDmaStreams] = {};
@@ -58,6 +59,8 @@ struct tide_layout {
   std::vector<tide::ParamGeom> params;
   std::vector<tide::RsChunk> rs_chunks;
   std::vector<tide::AgChunk> ag_chunks;
+  // Padding ranges of a packed rank-major slot (src = slot element offset, n), for Slot-Reuse.
+  std::vector<tide::AgChunk> slot_pad_items;
   mutable std::mutex mu;
   mutable std::map<int, tide::DeviceState> devices;
 };

@@ -117,9 +117,14 @@ struct AgChunk {
 static_assert(sizeof(AgChunk) == 32, "AgChunk is two 16-byte scalar loads");
 
 // Kernel launchers (kernels.hip).  `hip_stream` is a hipStream_t.  They return a hipError_t.
+// launch_rs: flat = false reads per-parameter gradients (table [C*P grads][R shards]); flat = true
+// reads C packed slots of R*S elements (table [C slots][R shards]).
+// launch_ag: pack = false places stage -> parameters; pack = true packs parameters -> stage slot.
+// launch_fill_zero: zeros the slot ranges of `items` (src = slot element offset, n).
 int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,
-              const void* const* dev_ptrs, int32_t P, int32_t C, bool vec, void* hip_stream);
-int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,
-              const void* stage, const void* const* dev_params, bool vec, void* hip_stream);
+              const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, void* hip_stream);
+int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, void* stage,
+              const void* const* dev_params, bool pack, bool vec, void* hip_stream);
+int launch_fill_zero(const AgChunk* items, int64_t count, void* slot, void* hip_stream);
 
 }  // namespace tide

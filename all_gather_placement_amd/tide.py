@@ -66,6 +66,10 @@ def load_library(path: str | None = None):
         "tide_ag_place": (i32, [vp, vp, ctypes.POINTER(vp), i32, i32, vp]),
         "tide_layout_copy_rs_items": (i32, [vp, i64, i64, P_i64]),
         "tide_layout_copy_ag_items": (i32, [vp, i64, i64, P_i64]),
+        "tide_slot_pack": (i32, [vp, ctypes.POINTER(vp), vp, i32, vp]),
+        "tide_rs_slots_bf16_to_fp32": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]),
+        "tide_layout_num_slot_pad_items": (i64, [vp]),
+        "tide_layout_copy_slot_pad_items": (i32, [vp, i64, i64, P_i64]),
         "tide_status_str": (ctypes.c_char_p, [i32]),
         "tide_last_hip_error": (i32, []),
     }
@@ -140,6 +144,25 @@ def tide_ag_place(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_bud
            "tide_ag_place")
 
 
+def tide_slot_pack(layout: int, grads, slot, cu_budget: int = 0, stream=None):
+    """grads: P bf16 tensors of one contributor (or addresses); slot: R*S bf16 tensor (or address)."""
+    lib = load_library()
+    g_list = [_ptr(g) for g in grads]
+    g_arr = (ctypes.c_void_p * max(len(g_list), 1))(*g_list)
+    _check(lib.tide_slot_pack(layout, g_arr, _ptr(slot), int(cu_budget), _stream_handle(stream)), "tide_slot_pack")
+
+
+def tide_rs_slots_bf16_to_fp32(layout: int, slots, shards, cu_budget: int = 0, stream=None):
+    """slots: C packed R*S bf16 tensors (or addresses); shards: R fp32 tensors (or addresses)."""
+    lib = load_library()
+    sl = [_ptr(x) for x in slots]
+    sl_arr = (ctypes.c_void_p * max(len(sl), 1))(*sl)
+    sh = [_ptr(x) for x in shards]
+    sh_arr = (ctypes.c_void_p * max(len(sh), 1))(*sh)
+    _check(lib.tide_rs_slots_bf16_to_fp32(layout, len(sl), sl_arr, sh_arr, int(cu_budget), _stream_handle(stream)),
+           "tide_rs_slots_bf16_to_fp32")
+
+
 class Layout:
     """Owning wrapper of a tide_layout handle for one parameter group over R ranks."""
 
@@ -210,6 +233,17 @@ class Layout:
                "tide_layout_copy_ag_items")
         return out[:n]
 
+    def slot_pad_items(self):
+        """Padding ranges of a packed slot as an (n, 2) int64 array: slot offset, count."""
+        import numpy as np
+
+        n = self._lib.tide_layout_num_slot_pad_items(self.handle)
+        out = np.zeros((max(n, 1), 2), dtype=np.int64)
+        _check(self._lib.tide_layout_copy_slot_pad_items(self.handle, 0, n,
+                                                         out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+               "tide_layout_copy_slot_pad_items")
+        return out[:n]
+
     def prepare(self):
         _check(self._lib.tide_layout_prepare(self.handle), "tide_layout_prepare")
 
@@ -221,6 +255,16 @@ class Layout:
     def ag_place(self, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0, stream=None):
         _check_shapes_ag(self, stage, params)
         tide_ag_place(self.handle, stage, params, mode, cu_budget, stream)
+
+    def slot_pack(self, grads, slot, cu_budget: int = 0, stream=None):
+        _check_shapes_ag(self, slot, grads)
+        tide_slot_pack(self.handle, grads, slot, cu_budget, stream)
+
+    def rs_slots_bf16_to_fp32(self, slots, shards, cu_budget: int = 0, stream=None):
+        _check_shapes_rs(self, [], shards)
+        for sl in slots:
+            _check_stage(self, sl)
+        tide_rs_slots_bf16_to_fp32(self.handle, slots, shards, cu_budget, stream)
 
 
 def _is_tensor(x) -> bool:
@@ -246,14 +290,20 @@ def _check_shapes_rs(L: Layout, grads, shards):
                 raise ValueError(f"shard must be a contiguous cuda fp32 tensor of {L.S} elements")
 
 
+def _check_stage(L: Layout, stage):
+    import torch
+
+    if _is_tensor(stage):
+        if stage.dtype != torch.bfloat16 or not stage.is_cuda or not stage.is_contiguous() or stage.numel() != L.R * L.S:
+            raise ValueError(f"stage/slot must be a contiguous cuda bf16 tensor of R*S = {L.R * L.S} elements")
+
+
 def _check_shapes_ag(L: Layout, stage, params):
     import torch
 
     if len(params) != L.P:
         raise ValueError(f"expected {L.P} parameters, got {len(params)}")
-    if _is_tensor(stage):
-        if stage.dtype != torch.bfloat16 or not stage.is_cuda or not stage.is_contiguous() or stage.numel() != L.R * L.S:
-            raise ValueError(f"stage must be a contiguous cuda bf16 tensor of R*S = {L.R * L.S} elements")
+    _check_stage(L, stage)
     for q, shape in zip(params, L.shapes):
         if _is_tensor(q):
             if q.dtype != torch.bfloat16 or not q.is_cuda or not q.is_contiguous() or tuple(q.shape) != shape:

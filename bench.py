@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--budgets", default="0,16,64,256,512,768,1024,1536,2048")
     ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
     ap.add_argument("--reps", type=int, default=15)
+    ap.add_argument("--slot-reuse", action="store_true",
+                    help="instead of the step benchmark: Slot-Reuse (pack into slots + RS from slots) vs in-place RS")
     return ap.parse_args()
 
 
@@ -250,6 +252,71 @@ def interference(args, log):
     print(json.dumps(out), flush=True)
 
 
+def slot_reuse(args, log):
+    """Slot-Reuse against In-Place on one workload: times, GB/s and the bytes live during the RS.
+
+    Slot-Reuse packs each contributor's gradients into a vacated all-gather slot (R*S bf16, the
+    stage layout) and reduces from the slots; the per-parameter gradients can be released after
+    their pack.  In-Place reads the gradients where they are.  Bytes: pack = 2*numel read +
+    2*R*S written per contributor; RS from slots = 2*C*R*S read + 4*R*S written.
+    """
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import Layout
+    from oracle.geometry import group_geometry
+    from workloads import CONFIGS, normal_bf16_cuda
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    _, S = group_geometry(cfg.shapes, cfg.R)
+    numel = cfg.numel()
+    grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
+             for c in range(cfg.C)]
+    slots = [torch.empty(cfg.R * S, dtype=torch.bfloat16, device=dev) for _ in range(cfg.C)]
+    shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
+    L = Layout(cfg.shapes, cfg.R)
+    L.prepare()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.median(ts)
+
+    t_inplace = timed(lambda: L.rs_bf16_to_fp32(grads, shards, cu_budget=args.cu_budget), args.steps)
+    t_pack = timed(lambda: [L.slot_pack(grads[c], slots[c], cu_budget=args.cu_budget) for c in range(cfg.C)], args.steps)
+    t_rs_slots = timed(lambda: L.rs_slots_bf16_to_fp32(slots, shards, cu_budget=args.cu_budget), args.steps)
+    L.close()
+    rs_bytes = 2 * cfg.C * numel + 4 * cfg.R * S
+    pack_bytes = cfg.C * (2 * numel + 2 * cfg.R * S)
+    rs_slot_bytes = 2 * cfg.C * cfg.R * S + 4 * cfg.R * S
+    out = {
+        "experiment": "Slot-Reuse vs In-Place reduce-scatter", "workload": cfg.name, "R": cfg.R, "C": cfg.C,
+        "cu_budget": args.cu_budget,
+        "in_place_rs_ms": round(t_inplace, 4), "in_place_rs_gbps": round(rs_bytes / t_inplace / 1e6, 1),
+        "pack_all_contributors_ms": round(t_pack, 4), "pack_gbps": round(pack_bytes / t_pack / 1e6, 1),
+        "rs_from_slots_ms": round(t_rs_slots, 4), "rs_from_slots_gbps": round(rs_slot_bytes / t_rs_slots / 1e6, 1),
+        "slot_reuse_total_ms": round(t_pack + t_rs_slots, 4),
+        "bytes_live_during_rs_in_place": 2 * cfg.C * numel + 4 * cfg.R * S,
+        "bytes_live_during_rs_slot_reuse": 2 * cfg.C * cfg.R * S + 4 * cfg.R * S,
+        "note": "Slot-Reuse's slots are vacated all-gather buffers (already allocated); the gradients can be "
+                "released once packed, so their 2*C*numel bytes are not live during its RS.",
+    }
+    log(json.dumps(out))
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -272,6 +339,10 @@ def main():
     if args.interference:
         torch.cuda.set_device(0)
         interference(args, log)
+        return
+    if args.slot_reuse:
+        torch.cuda.set_device(0)
+        slot_reuse(args, log)
         return
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")

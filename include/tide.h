@@ -115,6 +115,10 @@ tide_status tide_layout_segment(const tide_layout* layout, int32_t p, int32_t r,
  * int64 each (p, stage_offset, param_offset, n).  Errors: TIDE_ERR_INVALID (null, range). */
 tide_status tide_layout_copy_rs_items(const tide_layout* layout, int64_t first, int64_t n, int64_t* out);
 tide_status tide_layout_copy_ag_items(const tide_layout* layout, int64_t first, int64_t n, int64_t* out);
+/* Padding ranges of a packed slot (tide_slot_pack zero-fills them): 2 int64 each (slot element
+ * offset, count).  tide_layout_num_slot_pad_items gives their number (-1 for NULL). */
+int64_t tide_layout_num_slot_pad_items(const tide_layout* layout);
+tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t first, int64_t n, int64_t* out);
 
 /*
  * Reduce-scatter, bf16 in, fp32 out ([Endgame] abstract: per-parameter bf16 gradients reduced
@@ -164,6 +168,34 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
  */
 tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params,
                           int32_t mode, int32_t cu_budget, void* stream);
+
+/*
+ * Slot-Reuse, step 1: pack one contributor's per-parameter bf16 gradients into a vacated rank-major
+ * all-gather slot ([Endgame] abstract: Slot-Reuse stages gradients in vacated all-gather slots;
+ * Figure 7: gradients are copied into a vacated slot whose reuse waits for the reduce-scatter's read).
+ *   grads      host [P]: grads[p] is parameter p's contiguous bf16 gradient (rows_p * L_p elements,
+ *              2-byte aligned; NULL allowed only for empty parameters).  Read, never written.
+ *   slot       device, R*S bf16 elements in the stage layout (rank r's shard at element r*S).
+ *   cu_budget  as for tide_ag_place.
+ * Result: slot[r*S + o_p + k] = grads[p][r*m_p*L_p + k] for k < v*L_p (bit copy), and +0 (bits 0)
+ * in every padding element; every slot element is written once.  The exact inverse of
+ * tide_ag_place.  Errors: as tide_ag_place (the slot must not overlap any gradient).
+ */
+tide_status tide_slot_pack(const tide_layout* layout, const void* const* grads, void* slot, int32_t cu_budget,
+                           void* stream);
+
+/*
+ * Slot-Reuse, step 2: reduce-scatter from C packed slots ([Endgame] Figure 7).
+ *   slots      host [C]: slots[c] is contributor c's packed slot, R*S bf16 elements, 2-byte aligned
+ *              (slots may alias each other; they are read, never written).
+ *   shards, cu_budget, stream: as tide_rs_bf16_to_fp32.
+ * Result: shards[r][k] = x_0 (+) ... (+) x_{C-1} with x_c = slots[c][r*S + k] widened, for every
+ * valid element, and +0.0 for every padding element whatever the slots hold there.  Identical to
+ * tide_rs_bf16_to_fp32 on the gradients the slots were packed from.
+ * Errors: as tide_rs_bf16_to_fp32.
+ */
+tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* slots,
+                                       float* const* shards, int32_t cu_budget, void* stream);
 
 /* Static, NUL-terminated name of a status code ("TIDE_OK", ...; "unknown" otherwise). */
 const char* tide_status_str(int32_t status);

@@ -18,6 +18,8 @@ but lost every math symbol, so the definitions here are the plainest reading of 
                in-place path reaches the same values while skipping the pack (abstract; Table 1
                "RS input preparation: In-Place Read"; Figure 1 "writes each piece once, at its
                final address");
+* Slot-Reuse staging -- gradients packed into a vacated all-gather slot, then reduced from the
+               slots (abstract; Figure 7); see oracle/slot.py;
 * all-gather placement -- FSDP2's copy-out of the rank-major all-gather output into
                per-parameter storage (Table 7 caption: split_with_sizes_copy), which TIDE-AG
                replaces by landing shards directly (abstract; Figure 5b).
@@ -40,3 +42,4 @@ from .geometry import ParamGeom, group_geometry, valid_rows  # noqa: F401
 from .rs import widen, pack_contributor, reduce_scatter, rs_sampled  # noqa: F401
 from .ag import all_gather_place  # noqa: F401
 from .brute import brute_reduce_scatter, brute_all_gather_place  # noqa: F401
+from .slot import pack_slot, rs_from_slots  # noqa: F401

@@ -145,17 +145,32 @@ def check_items_tile_exactly(shapes, R, rs_items, ag_items, rs_chunk=2048, ag_ch
         assert sum(numel) == 0
 
 
+def check_slot_items_tile(shapes, R, ag_items, pad_items):
+    """A packed slot: AG items (valid parts) and padding items cover [0, R*S) exactly once."""
+    geo, S = ogeo.group_geometry(shapes, R)
+    cover = np.zeros(R * S, dtype=np.int32)
+    for src, n in zip(ag_items[:, 1], ag_items[:, 3]):
+        cover[src: src + n] += 1
+    for off, n in pad_items:
+        assert 0 <= off and off + n <= R * S
+        cover[off: off + n] += 1
+    assert np.all(cover == 1)
+
+
 @settings(max_examples=60, deadline=None)
 @given(groups())
 def test_work_items_tile_hypothesis(g):
     shapes, R = g
     with tide.Layout(shapes, R) as L:
         check_items_tile_exactly(shapes, R, L.rs_items(), L.ag_items())
+        check_slot_items_tile(shapes, R, L.ag_items(), L.slot_pad_items())
 
 
 def test_work_items_tile_tiny():
     with tide.Layout(TINY.shapes, TINY.R) as L:
         check_items_tile_exactly(TINY.shapes, TINY.R, L.rs_items(), L.ag_items())
+        check_slot_items_tile(TINY.shapes, TINY.R, L.ag_items(), L.slot_pad_items())
+        assert int(L.slot_pad_items()[:, 1].sum()) == 32
 
 
 @pytest.mark.parametrize("cfg", [c for c in ORDERED if c.name != "tiny"], ids=lambda c: c.name)
@@ -273,3 +288,33 @@ def test_ag_rejects_bad_arguments_before_any_hip_call():
         pp = list(params); pp[2] = pp[0] + 2
         assert call(stage, pp) == INV                 # parameters overlap
         assert lib.tide_ag_place(None, stage, _vp_array(params), 0, 0, None) == INV
+
+
+def test_slot_entry_points_reject_bad_arguments_before_any_hip_call():
+    lib = tb.load_library()
+    INV = tb.TIDE_ERR_INVALID
+    with tide.Layout(TINY.shapes, TINY.R) as L:
+        slot = 1 << 32
+        grads = [(1 << 33) + p * (1 << 20) for p in range(L.P)]
+        pack = lambda gg, sl, budget=0: lib.tide_slot_pack(L.handle, _vp_array(gg), sl, budget, None)
+        assert lib.tide_slot_pack(None, _vp_array(grads), slot, 0, None) == INV
+        assert lib.tide_slot_pack(L.handle, None, slot, 0, None) == INV
+        assert pack(grads, None) == INV
+        assert pack(grads, slot + 1) == INV
+        assert pack(grads, slot, budget=-1) == INV
+        gg = list(grads); gg[1] = slot + 64
+        assert pack(gg, slot) == INV                  # gradient inside the slot
+        gg = list(grads); gg[0] = None
+        assert pack(gg, slot) == INV
+        slots = [(1 << 34) + c * (1 << 20) for c in range(4)]
+        shards = [(1 << 35) + r * (1 << 20) for r in range(L.R)]
+        rs = lambda sl, sh, C=4, budget=0: lib.tide_rs_slots_bf16_to_fp32(L.handle, C, _vp_array(sl), _vp_array(sh), budget, None)
+        assert rs(slots, shards, C=0) == INV
+        assert rs(slots, shards, budget=-1) == INV
+        ss = list(slots); ss[2] = None
+        assert rs(ss, shards) == INV
+        sh = list(shards); sh[0] = slots[1] + 8
+        assert rs(slots, sh) == INV                   # shard overlaps a slot
+        sh = list(shards); sh[1] += 2
+        assert rs(slots, sh) == INV                   # misaligned fp32 shard
+        assert lib.tide_last_hip_error() == 0

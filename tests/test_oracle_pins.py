@@ -449,3 +449,40 @@ def test_mutants_are_caught():
     geo, S = ogeo.group_geometry(TINY.shapes, TINY.R)
     stage = normal_bf16_bits((TINY.R * S,), 1.0, 0, 80)
     assert not check_ag_against_torch_chunks(_ag_transposed, TINY.shapes, TINY.R, stage)
+
+
+# ---------------------------------------------------------------------------------------------
+# Slot-Reuse staging (pack into a vacated all-gather slot, then reduce from the slots)
+# ---------------------------------------------------------------------------------------------
+
+@settings(max_examples=40, deadline=None)
+@given(tiny_groups())
+def test_slot_pack_is_inverse_of_ag_and_rs_from_slots_equals_in_place(group):
+    R, C, shapes, seed = group
+    g = _rand_grads(C, shapes, seed)
+    geo, S = ogeo.group_geometry(shapes, R)
+    slots = [oracle.pack_slot(g[c], shapes, R) for c in range(C)]
+    for c in range(C):
+        # placing a packed slot gives the gradients back, bit for bit
+        back = oracle.all_gather_place(slots[c], shapes, R)
+        for a, b in zip(back, g[c]):
+            assert np.array_equal(a, b)
+        # the bf16 slot widened is the stock fp32 pack
+        assert np.array_equal(ors.widen(slots[c]).reshape(R, S).view(np.uint32),
+                              ors.pack_contributor(g[c], shapes, R).view(np.uint32))
+    Y = oracle.rs_from_slots(slots, shapes, R)
+    assert np.array_equal(Y.view(np.uint32), oracle.reduce_scatter(g, shapes, R).view(np.uint32))
+    assert np.array_equal(Y.view(np.uint32), oracle.brute_reduce_scatter(g, shapes, R).view(np.uint32))
+
+
+def test_rs_from_slots_ignores_slot_padding():
+    geo, S = ogeo.group_geometry(TINY.shapes, TINY.R)
+    g = _tiny_grads()
+    slots = [oracle.pack_slot(g[c], TINY.shapes, TINY.R).reshape(TINY.R, S) for c in range(TINY.C)]
+    for s in slots:  # garbage in the padding of every slot
+        for gg in geo:
+            for r in range(TINY.R):
+                v = ogeo.valid_rows(gg.rows, gg.m, r)
+                s[r, gg.o + v * gg.L: gg.o + gg.e] = 0x7FC1
+    Y = oracle.rs_from_slots([s.ravel() for s in slots], TINY.shapes, TINY.R)
+    assert np.array_equal(Y.view(np.uint32), oracle.reduce_scatter(g, TINY.shapes, TINY.R).view(np.uint32))
