@@ -256,6 +256,36 @@ class Layout:
         _check_shapes_ag(self, stage, params)
         tide_ag_place(self.handle, stage, params, mode, cu_budget, stream)
 
+    # pre-marshalled calls (validate once, launch many times) ----------------------------------
+    def bind_rs(self, grads, shards, cu_budget: int = 0) -> BoundCall:
+        _check_shapes_rs(self, grads, shards)
+        flat = [_ptr(g) for row in grads for g in row]
+        g_arr = (ctypes.c_void_p * max(len(flat), 1))(*flat)
+        s_arr = (ctypes.c_void_p * max(len(shards), 1))(*[_ptr(x) for x in shards])
+        return BoundCall(self._lib.tide_rs_bf16_to_fp32, "tide_rs_bf16_to_fp32",
+                         (self.handle, len(grads), g_arr, s_arr, int(cu_budget)), (grads, shards, self))
+
+    def bind_ag(self, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0) -> BoundCall:
+        _check_shapes_ag(self, stage, params)
+        p_arr = (ctypes.c_void_p * max(len(params), 1))(*[_ptr(x) for x in params])
+        return BoundCall(self._lib.tide_ag_place, "tide_ag_place",
+                         (self.handle, _ptr(stage), p_arr, int(mode), int(cu_budget)), (stage, params, self))
+
+    def bind_slot_pack(self, grads, slot, cu_budget: int = 0) -> BoundCall:
+        _check_shapes_ag(self, slot, grads)
+        g_arr = (ctypes.c_void_p * max(len(grads), 1))(*[_ptr(x) for x in grads])
+        return BoundCall(self._lib.tide_slot_pack, "tide_slot_pack",
+                         (self.handle, g_arr, _ptr(slot), int(cu_budget)), (grads, slot, self))
+
+    def bind_rs_slots(self, slots, shards, cu_budget: int = 0) -> BoundCall:
+        _check_shapes_rs(self, [], shards)
+        for sl in slots:
+            _check_stage(self, sl)
+        sl_arr = (ctypes.c_void_p * max(len(slots), 1))(*[_ptr(x) for x in slots])
+        sh_arr = (ctypes.c_void_p * max(len(shards), 1))(*[_ptr(x) for x in shards])
+        return BoundCall(self._lib.tide_rs_slots_bf16_to_fp32, "tide_rs_slots_bf16_to_fp32",
+                         (self.handle, len(slots), sl_arr, sh_arr, int(cu_budget)), (slots, shards, self))
+
     def slot_pack(self, grads, slot, cu_budget: int = 0, stream=None):
         _check_shapes_ag(self, slot, grads)
         tide_slot_pack(self.handle, grads, slot, cu_budget, stream)
@@ -265,6 +295,20 @@ class Layout:
         for sl in slots:
             _check_stage(self, sl)
         tide_rs_slots_bf16_to_fp32(self.handle, slots, shards, cu_budget, stream)
+
+
+class BoundCall:
+    """A validated, pre-marshalled call: the argument arrays are built once, each launch() is one
+    ctypes call.  Keeps references to the tensors so their memory outlives the binding."""
+
+    def __init__(self, fn, where: str, args, keep):
+        self._fn = fn
+        self._where = where
+        self._args = args
+        self._keep = keep
+
+    def launch(self, stream=None):
+        _check(self._fn(*self._args, _stream_handle(stream)), self._where)
 
 
 def _is_tensor(x) -> bool:
