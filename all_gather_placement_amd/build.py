@@ -18,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtide.so")
 SOURCES = ["layout.cpp", "api.cpp", "kernels.hip"]
+PROBE_LIB = os.path.join(PKG, "libtide_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 
@@ -36,13 +38,15 @@ def compile_flags(extra=()) -> list:
     ]
 
 
-def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    objdir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, extra=(), out: str = LIB, sources=SOURCES, probe: bool = True) -> str:
+    """Compile every source and link the shared library (and the probe library); returns its path."""
+    if probe and out == LIB:
+        build(verbose=verbose, extra=extra, out=PROBE_LIB, sources=PROBE_SOURCES, probe=False)
+    objdir = os.path.join(PKG, "_build", os.path.splitext(os.path.basename(out))[0])
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [cc, *compile_flags(extra), *lang, "-c", os.path.join(CSRC, src), "-o", obj]

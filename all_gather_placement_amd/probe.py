@@ -1,0 +1,65 @@
+"""ctypes binding of libtide_probe.so (include/tide_probe.h): occupancy and interference probes.
+
+Measurement instruments only (GEMM-shaped and small spin workgroups that record where and when
+they ran); the reduce-scatter and placement path never uses them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+TIDE_PROBE_GEMM_SHAPED = 0
+TIDE_PROBE_SMALL = 1
+RECORD_BYTES = 32
+_lib = None
+
+
+def load_probe_library():
+    global _lib
+    if _lib is None:
+        path = os.path.join(_PKG, "libtide_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m all_gather_placement_amd.build`")
+        lib = ctypes.CDLL(path)
+        lib.tide_probe_launch.restype = ctypes.c_int32
+        lib.tide_probe_launch.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        lib.tide_probe_wall_clock_khz.restype = ctypes.c_int64
+        lib.tide_probe_wall_clock_khz.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def probe_launch(num_wgs: int, shape: int, spin_ticks: int, records=None, stream=None):
+    """records: a torch uint8/int64 cuda tensor of at least num_wgs * 32 bytes, or None."""
+    lib = load_probe_library()
+    if records is not None and records.numel() * records.element_size() < num_wgs * RECORD_BYTES:
+        raise ValueError("records buffer too small")
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream()
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    rc = lib.tide_probe_launch(int(num_wgs), int(shape), int(spin_ticks),
+                               None if records is None else records.data_ptr(), handle)
+    if rc != 0:
+        raise RuntimeError(f"tide_probe_launch failed: {rc}")
+
+
+def wall_clock_khz() -> int:
+    return int(load_probe_library().tide_probe_wall_clock_khz())
+
+
+def decode(records_host):
+    """numpy (n, 4) uint64 view of the records -> dict of arrays: start, end, xcc, se, sh, cu, cu_key."""
+    import numpy as np
+
+    r = np.asarray(records_host).reshape(-1, 4)
+    hw = (r[:, 2] & 0xFFFFFFFF).astype(np.int64)
+    xcc = ((r[:, 2] >> 32) & 0xF).astype(np.int64)
+    cu = (hw >> 8) & 0xF
+    sh = (hw >> 12) & 0x1
+    se = (hw >> 13) & 0x3
+    return {"start": r[:, 0].astype(np.int64), "end": r[:, 1].astype(np.int64), "xcc": xcc, "se": se, "sh": sh,
+            "cu": cu, "cu_key": ((xcc * 4 + se) * 2 + sh) * 16 + cu}

@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--budgets", default="0,16,64,256,512,768,1024,1536,2048")
     ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
     ap.add_argument("--reps", type=int, default=15)
+    ap.add_argument("--probes", action="store_true",
+                    help="instead of the step benchmark: occupancy probe, spin-kernel curve and more victims")
     ap.add_argument("--slot-reuse", action="store_true",
                     help="instead of the step benchmark: Slot-Reuse (pack into slots + RS from slots) vs in-place RS")
     return ap.parse_args()
@@ -323,6 +325,137 @@ def slot_reuse(args, log):
     print(json.dumps(out), flush=True)
 
 
+def probes(args, log):
+    """Interference instruments: the pages' SM-id probe, spin-kernel curve and extra victims.
+
+    (1) Occupancy probe (Table 5 analogue): 256 GEMM-shaped probe workgroups (256 threads, 64 KiB
+        LDS, 256 VGPRs per wave: the one-wave GEMM's footprint, one per CU) spin ~100 us and record
+        their CU and start/end; launched while the RS runs at a given cu_budget.  A probe workgroup
+        that starts more than 5 us after the first one was displaced into a second wave.
+    (2) Spin-kernel curve (Figure 4 lines): k small workgroups resident for ~2 ms, the one-wave GEMM
+        launched meanwhile; GEMM slowdown against k.
+    (3) Victims of Table 4's other columns: a ~28-wave GEMM and a memory-bound elementwise add,
+        with the RS unbounded and at the training budget.
+    """
+    import statistics
+
+    import numpy as np
+    import torch
+
+    from all_gather_placement_amd import Layout
+    from all_gather_placement_amd import probe as pr
+    from oracle.geometry import group_geometry
+    from workloads import CONFIGS, normal_bf16_cuda
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    khz = pr.wall_clock_khz()
+    tpu = khz / 1000.0  # wall-clock ticks per microsecond
+    grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
+             for c in range(cfg.C)]
+    _, S = group_geometry(cfg.shapes, cfg.R)
+    shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
+    L = Layout(cfg.shapes, cfg.R)
+    L.prepare()
+    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+    spin_cycles = 400_000
+    rs_calls = {}
+
+    def rs_call(b):
+        if b not in rs_calls:
+            rs_calls[b] = L.bind_rs(grads, shards, cu_budget=b)
+        return rs_calls[b]
+
+    # (1) occupancy probe
+    recs = torch.zeros(256 * 4, dtype=torch.int64, device=dev)
+    probe_ticks = int(100 * tpu)
+
+    def probe_once(budget):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(sA):
+            torch.cuda._sleep(spin_cycles)
+            pr.probe_launch(256, pr.TIDE_PROBE_GEMM_SHAPED, probe_ticks, recs, sA)
+        if budget is not None:
+            rs_call(budget).launch(sB)
+        torch.cuda.synchronize()
+        d = pr.decode(recs.cpu().numpy().view(np.uint64))
+        t0 = d["start"].min()
+        displaced = int((d["start"] > t0 + 5 * tpu).sum())
+        span_us = (d["end"].max() - t0) / tpu
+        return displaced, span_us, len(np.unique(d["cu_key"])), d
+
+    for _ in range(2):
+        probe_once(None)
+    table5 = []
+    for budget in [None, 0, 16, 64, 256, 512, 768, 1024, 2048]:
+        res = [probe_once(budget) for _ in range(args.reps)]
+        disp = [r[0] for r in res]
+        row = {"cu_budget": budget, "displaced_median": statistics.median(disp), "displaced_max": max(disp),
+               "reps_with_displacement_pct": round(100 * sum(1 for x in disp if x) / len(disp), 1),
+               "probe_span_us_median": round(statistics.median(r[1] for r in res), 1),
+               "distinct_cus": statistics.median(r[2] for r in res)}
+        log("probe " + json.dumps(row))
+        table5.append(row)
+    d_alone = probe_once(None)[3]
+    per_xcc = np.bincount(d_alone["xcc"], minlength=8).tolist()
+
+    # (2) spin-kernel curve against the one-wave GEMM
+    a = torch.randn(4096, 4096, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(4096, 4096, dtype=torch.bfloat16, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def victim_once(victim, comm):
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(sA):
+            torch.cuda._sleep(spin_cycles)
+            e0.record(sA)
+            victim()
+            e1.record(sA)
+        if comm is not None:
+            comm()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    gemm1 = lambda: torch.matmul(a, b)
+    for _ in range(3):
+        victim_once(gemm1, None)
+    alone = statistics.median(victim_once(gemm1, None) for _ in range(args.reps))
+    spin = []
+    for k in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048]:
+        t = statistics.median(victim_once(gemm1, lambda: pr.probe_launch(k, pr.TIDE_PROBE_SMALL, int(2000 * tpu),
+                                                                           None, sB)) for _ in range(args.reps))
+        row = {"spin_wgs": k, "gemm_us": round(t * 1e3, 2), "slowdown_pct": round((t / alone - 1) * 100, 2)}
+        log("spin " + json.dumps(row))
+        spin.append(row)
+
+    # (3) more victims
+    big_a = torch.randn(21504, 2048, dtype=torch.bfloat16, device=dev)
+    big_b = torch.randn(2048, 21504, dtype=torch.bfloat16, device=dev)
+    ea = torch.randn(256 << 20, dtype=torch.bfloat16, device=dev)
+    eb = torch.randn(256 << 20, dtype=torch.bfloat16, device=dev)
+    ec = torch.empty_like(ea)
+    victims = {"gemm_one_wave_4096^3": gemm1,
+               "gemm_28_wave_21504x21504x2048": lambda: torch.matmul(big_a, big_b),
+               "elementwise_add_256M_bf16": lambda: torch.add(ea, eb, out=ec)}
+    table4 = []
+    for name, fn in victims.items():
+        for _ in range(2):
+            victim_once(fn, None)
+        t_alone = statistics.median(victim_once(fn, None) for _ in range(args.reps))
+        row = {"victim": name, "alone_us": round(t_alone * 1e3, 1)}
+        for budget in (0, 512):
+            t = statistics.median(victim_once(fn, lambda: rs_call(budget).launch(sB)) for _ in range(args.reps))
+            row[f"slowdown_pct_rs_budget_{budget}"] = round((t / t_alone - 1) * 100, 2)
+        log("victim " + json.dumps(row))
+        table4.append(row)
+    L.close()
+    out = {"experiment": "interference instruments", "workload": cfg.name, "wall_clock_khz": khz,
+           "probe_cus_per_xcc_alone": per_xcc, "occupancy_probe": table5, "spin_curve": spin,
+           "gemm_one_wave_alone_us": round(alone * 1e3, 2), "victims": table4}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -349,6 +482,10 @@ def main():
     if args.slot_reuse:
         torch.cuda.set_device(0)
         slot_reuse(args, log)
+        return
+    if args.probes:
+        torch.cuda.set_device(0)
+        probes(args, log)
         return
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")

@@ -1,0 +1,60 @@
+/*
+ * tide_probe.h -- occupancy and interference instruments for MI355X (gfx950), a separate library
+ * (libtide_probe.so) used by the measurements, not by the reduce-scatter or placement path.
+ *
+ * They reproduce, on MI355X, the two instruments of "The Endgame of FSDP Communication:
+ * Layout-Aware Collectives on Copy Engines, RDMA, and NVSwitch" ([Endgame]) that explain why
+ * communication workgroups slow a concurrent GEMM:
+ *   - Table 5's probe: workgroups shaped like a one-wave GEMM's, one per compute unit, each
+ *     recording where it ran (XCC, shader engine, shader array, CU) and when it started and ended;
+ *     probe workgroups that start after the first wave were displaced by resident workgroups;
+ *   - Figure 4's spin kernels: k small workgroups that stay resident for a fixed time.
+ * All waits are bounded by a deadline on the constant-rate wall clock and by an iteration cap, so
+ * every wave exits.  Records are written with vector stores.
+ */
+#ifndef TIDE_PROBE_H
+#define TIDE_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One record per probe workgroup (32 bytes): wall-clock start and end (ticks of the device wall
+ * clock, see tide_probe_wall_clock_khz), the raw HW_ID register (CU_ID bits 11:8, SH_ID bit 12,
+ * SE_ID bits 14:13) and the XCC_ID register (bits 3:0) of the workgroup's first wave. */
+typedef struct tide_probe_record {
+  uint64_t start;
+  uint64_t end;
+  uint32_t hw_id;
+  uint32_t xcc_id;
+  uint64_t reserved;
+} tide_probe_record;
+
+/* Shapes of probe workgroup. */
+enum {
+  TIDE_PROBE_GEMM_SHAPED = 0, /* 256 threads, 64 KiB LDS, 256 VGPRs per wave: the footprint of the
+                                 one-wave bf16 GEMM victim (one 256x256 tile per CU) */
+  TIDE_PROBE_SMALL = 1        /* 256 threads, no LDS, few VGPRs: the footprint of a communication
+                                 workgroup (spin kernel) */
+};
+
+/*
+ * Launch `num_wgs` probe workgroups of `shape` on `stream` (a hipStream_t as void*).  Each
+ * workgroup records its start time, spins until `spin_ticks` wall-clock ticks have passed since
+ * its own start (at most 2^26 polls), records its end and location into records[blockIdx].
+ *   records  device array of num_wgs tide_probe_record, or NULL (no records written).
+ * Returns 0 or a hipError_t value; -1 for bad arguments (num_wgs < 1, bad shape, spin_ticks < 0).
+ */
+int32_t tide_probe_launch(int32_t num_wgs, int32_t shape, int64_t spin_ticks, tide_probe_record* records,
+                          void* stream);
+
+/* Device wall-clock rate in kHz (hipDeviceAttributeWallClockRate of the current device), or -1. */
+int64_t tide_probe_wall_clock_khz(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIDE_PROBE_H */

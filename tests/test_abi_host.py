@@ -318,3 +318,18 @@ def test_slot_entry_points_reject_bad_arguments_before_any_hip_call():
         sh = list(shards); sh[1] += 2
         assert rs(slots, sh) == INV                   # misaligned fp32 shard
         assert lib.tide_last_hip_error() == 0
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    from all_gather_placement_amd import probe as pr
+
+    lib = pr.load_probe_library()
+    text = open(os.path.join(ROOT, "include", "tide_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(tide_probe_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["tide_probe_launch", "tide_probe_wall_clock_khz"]
+    for n in names:
+        assert hasattr(lib, n)
+    assert lib.tide_probe_launch(0, 0, 10, None, None) == -1
+    assert lib.tide_probe_launch(4, 7, 10, None, None) == -1
+    assert lib.tide_probe_launch(4, 0, -1, None, None) == -1
