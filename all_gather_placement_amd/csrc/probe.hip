@@ -31,13 +31,15 @@ __device__ __forceinline__ void record(tide_probe_record* records, unsigned long
   }
 }
 
-// GEMM-shaped: 64 KiB of LDS and 256 VGPRs per wave (the clobber of v255 makes the register
-// allocation cover v0..v255), so the workgroup needs the same CU resources as the victim GEMM's.
+// GEMM-shaped: 64 KiB of LDS and the whole unified register file of a SIMD per wave -- 256
+// architectural VGPRs and 256 accumulation registers (the clobbers of v255 and a255 make the
+// allocation cover both), as a matrix-core GEMM holding its accumulators in AGPRs does -- so the
+// workgroup needs the same CU resources as the victim GEMM's: one wave per SIMD, nothing beside it.
 __global__ __launch_bounds__(kProbeThreads) void probe_gemm_shaped(tide_probe_record* records,
                                                                    unsigned long long ticks) {
   __shared__ unsigned int lds[16384];
   const unsigned long long t0 = static_cast<unsigned long long>(wall_clock64());
-  asm volatile("" ::: "v255");
+  asm volatile("" ::: "v255", "a255");
   lds[threadIdx.x * 64] = threadIdx.x;
   __syncthreads();
   spin_until(t0, ticks);

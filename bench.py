@@ -366,32 +366,40 @@ def probes(args, log):
             rs_calls[b] = L.bind_rs(grads, shards, cu_budget=b)
         return rs_calls[b]
 
-    # (1) occupancy probe
+    # (1) occupancy probe.  A one-wave marker workgroup (one wave, 8 VGPRs: it fits beside
+    # anything but a full SIMD) runs on the probe's stream just before it and records when the
+    # stream reached the probe; start delay = first probe start - marker end.
     recs = torch.zeros(256 * 4, dtype=torch.int64, device=dev)
+    marker = torch.zeros(4, dtype=torch.int64, device=dev)
     probe_ticks = int(100 * tpu)
 
     def probe_once(budget):
         torch.cuda.synchronize()
         with torch.cuda.stream(sA):
             torch.cuda._sleep(spin_cycles)
+            pr.probe_launch(1, pr.TIDE_PROBE_SMALL, 0, marker, sA)
             pr.probe_launch(256, pr.TIDE_PROBE_GEMM_SHAPED, probe_ticks, recs, sA)
         if budget is not None:
             rs_call(budget).launch(sB)
         torch.cuda.synchronize()
         d = pr.decode(recs.cpu().numpy().view(np.uint64))
+        m = pr.decode(marker.cpu().numpy().view(np.uint64))
         t0 = d["start"].min()
         displaced = int((d["start"] > t0 + 5 * tpu).sum())
         span_us = (d["end"].max() - t0) / tpu
-        return displaced, span_us, len(np.unique(d["cu_key"])), d
+        delay_us = (t0 - m["end"][0]) / tpu
+        return displaced, span_us, len(np.unique(d["cu_key"])), d, delay_us
 
     for _ in range(2):
         probe_once(None)
     table5 = []
     for budget in [None, 0, 16, 64, 256, 512, 768, 1024, 2048]:
-        res = [probe_once(budget) for _ in range(args.reps)]
+        res = [probe_once(budget) for _ in range(max(args.reps, 15))]
         disp = [r[0] for r in res]
         row = {"cu_budget": budget, "displaced_median": statistics.median(disp), "displaced_max": max(disp),
                "reps_with_displacement_pct": round(100 * sum(1 for x in disp if x) / len(disp), 1),
+               "start_delay_us_median": round(statistics.median(r[4] for r in res), 1),
+               "start_delay_us_max": round(max(r[4] for r in res), 1),
                "probe_span_us_median": round(statistics.median(r[1] for r in res), 1),
                "distinct_cus": statistics.median(r[2] for r in res)}
         log("probe " + json.dumps(row))

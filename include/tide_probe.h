@@ -34,8 +34,9 @@ typedef struct tide_probe_record {
 
 /* Shapes of probe workgroup. */
 enum {
-  TIDE_PROBE_GEMM_SHAPED = 0, /* 256 threads, 64 KiB LDS, 256 VGPRs per wave: the footprint of the
-                                 one-wave bf16 GEMM victim (one 256x256 tile per CU) */
+  TIDE_PROBE_GEMM_SHAPED = 0, /* 256 threads, 64 KiB LDS, 256 VGPRs + 256 AGPRs per wave (a whole
+                                 SIMD register file): the footprint of a matrix-core GEMM workgroup
+                                 such as the one-wave bf16 victim (one 256x256 tile per CU) */
   TIDE_PROBE_SMALL = 1        /* 256 threads, no LDS, few VGPRs: the footprint of a communication
                                  workgroup (spin kernel) */
 };
