@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--reps", type=int, default=15)
     ap.add_argument("--probes", action="store_true",
                     help="instead of the step benchmark: occupancy probe, spin-kernel curve and more victims")
+    ap.add_argument("--engines", action="store_true",
+                    help="instead of the step benchmark: AG placement on CUs vs copy engines, served GB/s and victim slowdown")
     ap.add_argument("--slot-reuse", action="store_true",
                     help="instead of the step benchmark: Slot-Reuse (pack into slots + RS from slots) vs in-place RS")
     return ap.parse_args()
@@ -464,6 +466,90 @@ def probes(args, log):
     print(json.dumps(out), flush=True)
 
 
+def engines(args, log):
+    """CU-initiated vs copy-engine placement (analogue of [Endgame] Table 3 on one GPU).
+
+    The same placement bytes (the workload's AG, repeated so it covers the victim) are moved by the
+    placement kernel (compute units), by the DMA engines (1-D no-compute-unit copies) and by the
+    runtime's 2-D copy; for each, the traffic it serves alone and the slowdown of two victims: the
+    one-wave bf16 GEMM (compute-bound) and a 256M-element bf16 add (HBM-bound).  Peer pull/push
+    directions of the pages' table need a second GPU and are not measured.
+    """
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
+    from oracle.geometry import group_geometry
+    from workloads import CONFIGS, normal_bf16_cuda
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    _, S = group_geometry(cfg.shapes, cfg.R)
+    stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
+    params = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in cfg.shapes]
+    ag_bytes = 4 * cfg.numel()
+    L = Layout(cfg.shapes, cfg.R)
+    L.prepare()
+    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    a = torch.randn(4096, 4096, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(4096, 4096, dtype=torch.bfloat16, device=dev)
+    ea = torch.randn(256 << 20, dtype=torch.bfloat16, device=dev)
+    eb = torch.randn(256 << 20, dtype=torch.bfloat16, device=dev)
+    ec = torch.empty_like(ea)
+    victims = {"gemm_one_wave_4096^3": lambda: torch.matmul(a, b),
+               "elementwise_add_256M_bf16": lambda: torch.add(ea, eb, out=ec)}
+    engines_ = {"cu_kernel": (TIDE_AG_KERNEL, 0), "cu_kernel_budget_512": (TIDE_AG_KERNEL, 512),
+                "copy_engine_sdma": (TIDE_AG_SDMA, 0), "runtime_copy2d": (TIDE_AG_COPY2D, 0)}
+    calls = {k: L.bind_ag(stage, params, mode=m, cu_budget=bud) for k, (m, bud) in engines_.items()}
+
+    def alone_ms(call, reps):
+        for _ in range(2):  # first calls on a stream stage the pointer table
+            call.launch(sB)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(sB)
+        for _ in range(reps):
+            call.launch(sB)
+        e1.record(sB)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def victim_once(fn, comm):
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(sA):
+            torch.cuda._sleep(400_000)
+            e0.record(sA)
+            fn()
+            e1.record(sA)
+        if comm is not None:
+            comm()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    rows = []
+    for name, call in calls.items():
+        t1 = alone_ms(call, 3)
+        reps = max(1, int(2.0 / t1) + 1)  # cover >= 2 ms
+        row = {"engine": name, "served_gbps_alone": round(ag_bytes / (t1 * 1e-3) / 1e9, 1), "placements": reps}
+        for vname, fn in victims.items():
+            for _ in range(2):
+                victim_once(fn, None)
+            t_alone = statistics.median(victim_once(fn, None) for _ in range(args.reps))
+
+            def comm():
+                for _ in range(reps):
+                    call.launch(sB)
+            t_conc = statistics.median(victim_once(fn, comm) for _ in range(args.reps))
+            row[f"{vname}_slowdown_pct"] = round((t_conc / t_alone - 1) * 100, 2)
+        log("engine " + json.dumps(row))
+        rows.append(row)
+    L.close()
+    print(json.dumps({"experiment": "placement engines vs victims", "workload": cfg.name, "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -494,6 +580,10 @@ def main():
     if args.probes:
         torch.cuda.set_device(0)
         probes(args, log)
+        return
+    if args.engines:
+        torch.cuda.set_device(0)
+        engines(args, log)
         return
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
