@@ -184,6 +184,32 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
         const unsigned short* src[CT];
 #pragma unroll
         for (int c = 0; c < CT; ++c) src[c] = gptr[static_cast<int64_t>(c) * P + ch.p] + ch.src;
+#if TIDE_RS_WIDE
+        // Full aligned item: one 16-byte load per contributor per lane (1 KiB contiguous per wave
+        // instruction), 8 sums per lane, then the fp32 results are redistributed through LDS so that
+        // each 16-byte store instruction of a wave covers 1 KiB of whole lines.
+        if (n == kThreads * 8 && head == 0 && dst16) {
+          __shared__ f32x4 xfer[2 * kThreads];
+          u32x4 x[CT];
+#pragma unroll
+          for (int c = 0; c < CT; ++c) x[c] = load_hbm(at_bytes<u32x4>(src[c], 16u * tid));
+          float a[8];
+          a[0] = widen_lo(x[0].x); a[1] = widen_hi(x[0].x); a[2] = widen_lo(x[0].y); a[3] = widen_hi(x[0].y);
+          a[4] = widen_lo(x[0].z); a[5] = widen_hi(x[0].z); a[6] = widen_lo(x[0].w); a[7] = widen_hi(x[0].w);
+#pragma unroll
+          for (int c = 1; c < CT; ++c) {
+            a[0] += widen_lo(x[c].x); a[1] += widen_hi(x[c].x); a[2] += widen_lo(x[c].y); a[3] += widen_hi(x[c].y);
+            a[4] += widen_lo(x[c].z); a[5] += widen_hi(x[c].z); a[6] += widen_lo(x[c].w); a[7] += widen_hi(x[c].w);
+          }
+          __syncthreads();  // the previous item's readers are done with xfer
+          xfer[2 * tid] = f32x4{a[0], a[1], a[2], a[3]};
+          xfer[2 * tid + 1] = f32x4{a[4], a[5], a[6], a[7]};
+          __syncthreads();
+          store_hbm(at_bytes<f32x4>(dst, 16u * tid), xfer[tid]);
+          store_hbm(at_bytes<f32x4>(dst, 16u * (tid + kThreads)), xfer[tid + kThreads]);
+          continue;  // no tail, no padding in a full item
+        }
+#endif
         if (tid < head) store_hbm(dst + tid, sum1<CT>(src, nc, tid));
         constexpr int NQ = TIDE_RS_NQ;
         int q = tid;
