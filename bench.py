@@ -699,7 +699,7 @@ def main():
         "rs_host_us_per_call": {"bound": round(host_bound, 1), "validate_and_marshal": round(host_unbound, 1)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "rs_kernel<8, true>",
+            "kernel": "rs_kernel<8, true, false>",
             "achieved": round(rs_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
