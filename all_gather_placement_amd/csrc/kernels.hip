@@ -191,8 +191,17 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
         if (n == kThreads * 8 && head == 0 && dst16) {
           __shared__ f32x4 xfer[2 * kThreads];
           u32x4 x[CT];
+#if TIDE_RS_LOAD_AUX >= 0
+#pragma unroll
+          for (int c = 0; c < CT; ++c) {
+            const __amdgpu_buffer_rsrc_t rsrc =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(src[c]), 0, 16 * kThreads, 0x00020000);
+            x[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * tid, 0, TIDE_RS_LOAD_AUX));
+          }
+#else
 #pragma unroll
           for (int c = 0; c < CT; ++c) x[c] = load_hbm(at_bytes<u32x4>(src[c], 16u * tid));
+#endif
           float a[8];
           a[0] = widen_lo(x[0].x); a[1] = widen_hi(x[0].x); a[2] = widen_lo(x[0].y); a[3] = widen_hi(x[0].y);
           a[4] = widen_lo(x[0].z); a[5] = widen_hi(x[0].z); a[6] = widen_lo(x[0].w); a[7] = widen_hi(x[0].w);
@@ -205,8 +214,18 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
           xfer[2 * tid] = f32x4{a[0], a[1], a[2], a[3]};
           xfer[2 * tid + 1] = f32x4{a[4], a[5], a[6], a[7]};
           __syncthreads();
+#if TIDE_RS_STORE_AUX >= 0
+          {
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, 32 * kThreads, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid]), rsrc, 16 * tid, 0,
+                                                   TIDE_RS_STORE_AUX);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid + kThreads]), rsrc,
+                                                   16 * (tid + kThreads), 0, TIDE_RS_STORE_AUX);
+          }
+#else
           store_hbm(at_bytes<f32x4>(dst, 16u * tid), xfer[tid]);
           store_hbm(at_bytes<f32x4>(dst, 16u * (tid + kThreads)), xfer[tid + kThreads]);
+#endif
           continue;  // no tail, no padding in a full item
         }
 #endif

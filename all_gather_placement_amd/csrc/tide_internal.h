@@ -38,6 +38,16 @@ namespace tide {
 #ifndef TIDE_RS_WIDE
 #define TIDE_RS_WIDE 1
 #endif
+// Cache policy of the wide path's HBM accesses: -1 = global loads/stores with the non-temporal
+// hint; >= 0 = raw buffer loads/stores with this cache-policy field (gfx950: bit 0 sc0, bit 1 nt,
+// bit 4 sc1), each bounded in hardware by its work item's byte range.  Measured: without nt -5%;
+// loads nt (2) and stores nt + sc1 (18) +0.6-1.6% over global non-temporal accesses.
+#ifndef TIDE_RS_LOAD_AUX
+#define TIDE_RS_LOAD_AUX 2
+#endif
+#ifndef TIDE_RS_STORE_AUX
+#define TIDE_RS_STORE_AUX 18
+#endif
 #ifndef TIDE_AG_VECS
 #define TIDE_AG_VECS 4
 #endif
