@@ -286,8 +286,16 @@ __global__ __launch_bounds__(kAgThreads) void ag_kernel(const AgChunk* __restric
       if (tid < head) store_hbm(dst + tid, load_hbm(src + tid));
       const u32x4* s = reinterpret_cast<const u32x4*>(src + head);
       u32x4* d = reinterpret_cast<u32x4*>(dst + head);
-      constexpr int NV = TIDE_AG_VECS;
       int v = tid;
+#if TIDE_AG_BUF_AUX >= 0
+      // Raw buffer accesses bounded to the item's vectors, cache policy TIDE_AG_BUF_AUX.
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(s), 0, 16 * nb, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(d, 0, 16 * nb, 0x00020000);
+      for (; v < nb; v += kAgThreads)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(rs, 16 * v, 0, TIDE_AG_BUF_AUX),
+                                               rd, 16 * v, 0, TIDE_AG_BUF_AUX | TIDE_AG_STORE_EXTRA);
+#else
+      constexpr int NV = TIDE_AG_VECS;
       for (; v + (NV - 1) * kAgThreads < nb; v += NV * kAgThreads) {
         u32x4 x[NV];
 #pragma unroll
@@ -296,6 +304,7 @@ __global__ __launch_bounds__(kAgThreads) void ag_kernel(const AgChunk* __restric
         for (int k = 0; k < NV; ++k) store_hbm(at_bytes<u32x4>(d, 16u * (v + k * kAgThreads)), x[k]);
       }
       for (; v < nb; v += kAgThreads) store_hbm(at_bytes<u32x4>(d, 16u * v), load_hbm(at_bytes<u32x4>(s, 16u * v)));
+#endif
       if (tid < tail) {
         const int k = head + 8 * nb + tid;
         store_hbm(dst + k, load_hbm(src + k));

@@ -48,6 +48,14 @@ namespace tide {
 #ifndef TIDE_RS_STORE_AUX
 #define TIDE_RS_STORE_AUX 18
 #endif
+// AG vector path: -1 = global non-temporal accesses; >= 0 = raw buffer accesses with this
+// cache-policy field (stores add TIDE_AG_STORE_EXTRA).  Measured: no better than -1 for the copy.
+#ifndef TIDE_AG_BUF_AUX
+#define TIDE_AG_BUF_AUX -1
+#endif
+#ifndef TIDE_AG_STORE_EXTRA
+#define TIDE_AG_STORE_EXTRA 0
+#endif
 #ifndef TIDE_AG_VECS
 #define TIDE_AG_VECS 4
 #endif
