@@ -1,0 +1,127 @@
+// Host-only exercise of libtide's layout and validation code under AddressSanitizer and UBSan.
+// Built with g++ (no device code): the kernel launchers are stubs that abort, and every call made
+// here returns before any HIP call (layouts never reach a device; invalid arguments are rejected
+// first).  Exit status 0 = all checks passed.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <vector>
+
+#include "../../all_gather_placement_amd/csrc/tide_internal.h"
+#include "tide.h"
+
+namespace tide {
+int launch_rs(const RsChunk*, int64_t, int64_t, int, int, const void* const*, int32_t, int32_t, int64_t, bool, bool,
+              void*) {
+  std::fprintf(stderr, "launch_rs reached in a host-only check\n");
+  std::abort();
+}
+int launch_ag(const AgChunk*, int64_t, int64_t, int, int, void*, const void* const*, bool, bool, void*) {
+  std::fprintf(stderr, "launch_ag reached in a host-only check\n");
+  std::abort();
+}
+int launch_fill_zero(const AgChunk*, int64_t, void*, void*) {
+  std::fprintf(stderr, "launch_fill_zero reached in a host-only check\n");
+  std::abort();
+}
+}  // namespace tide
+
+static int failures = 0;
+#define CHECK(cond)                                                       \
+  do {                                                                    \
+    if (!(cond)) {                                                        \
+      std::fprintf(stderr, "CHECK failed at line %d: %s\n", __LINE__, #cond); \
+      ++failures;                                                         \
+    }                                                                     \
+  } while (0)
+
+int main() {
+  std::mt19937_64 rng(12345);
+  int64_t groups = 0;
+  for (int it = 0; it < 400; ++it) {
+    const int32_t R = 1 + int32_t(rng() % 70);
+    const int32_t P = 1 + int32_t(rng() % 7);
+    std::vector<int32_t> nd(P);
+    std::vector<int64_t> dims;
+    std::vector<int64_t> rows(P), len(P);
+    for (int32_t p = 0; p < P; ++p) {
+      nd[p] = 1 + int32_t(rng() % 4);
+      rows[p] = int64_t(rng() % 3000);
+      len[p] = 1;
+      dims.push_back(rows[p]);
+      for (int k = 1; k < nd[p]; ++k) {
+        const int64_t d = int64_t(rng() % 9);
+        dims.push_back(d);
+        len[p] *= d;
+      }
+    }
+    tide_layout* L = nullptr;
+    CHECK(tide_layout_create(P, nd.data(), dims.data(), R, &L) == TIDE_OK);
+    if (!L) continue;
+    ++groups;
+    // geometry against the closed forms; every output element covered exactly once
+    int64_t S = 0;
+    for (int32_t p = 0; p < P; ++p) {
+      int64_t r0, l0, m0, o0;
+      CHECK(tide_layout_param(L, p, &r0, &l0, &m0, &o0) == TIDE_OK);
+      CHECK(r0 == rows[p] && l0 == len[p] && m0 == (rows[p] + R - 1) / R && o0 == S);
+      S += m0 * l0;
+    }
+    CHECK(tide_layout_shard_numel(L) == S);
+    const int64_t nrs = tide_layout_num_rs_chunks(L), nag = tide_layout_num_ag_chunks(L);
+    const int64_t npad = tide_layout_num_slot_pad_items(L);
+    std::vector<int64_t> rs(6 * (nrs + 1)), ag(4 * (nag + 1)), pad(2 * (npad + 1));
+    CHECK(tide_layout_copy_rs_items(L, 0, nrs, rs.data()) == TIDE_OK);
+    CHECK(tide_layout_copy_ag_items(L, 0, nag, ag.data()) == TIDE_OK);
+    CHECK(tide_layout_copy_slot_pad_items(L, 0, npad, pad.data()) == TIDE_OK);
+    CHECK(tide_layout_copy_rs_items(L, nrs, 1, rs.data()) == TIDE_ERR_INVALID);
+    std::vector<uint8_t> cover(size_t(R) * size_t(S), 0), slot(size_t(R) * size_t(S), 0);
+    for (int64_t i = 0; i < nrs; ++i) {
+      const int64_t* c = &rs[6 * i];
+      for (int64_t k = 0; k < c[4] + c[5]; ++k) ++cover[size_t(c[1]) * S + c[3] + k];
+    }
+    for (int64_t i = 0; i < nag; ++i)
+      for (int64_t k = 0; k < ag[4 * i + 3]; ++k) ++slot[ag[4 * i + 1] + k];
+    for (int64_t i = 0; i < npad; ++i)
+      for (int64_t k = 0; k < pad[2 * i + 1]; ++k) ++slot[pad[2 * i] + k];
+    for (size_t i = 0; i < cover.size(); ++i) {
+      CHECK(cover[i] == 1);
+      CHECK(slot[i] == 1);
+      if (failures > 20) return 1;
+    }
+    tide_layout_destroy(L);
+  }
+  // invalid arguments, each rejected before any HIP call
+  int32_t nd1[1] = {2};
+  int64_t d1[2] = {4, 4};
+  tide_layout* L = nullptr;
+  CHECK(tide_layout_create(0, nd1, d1, 4, &L) == TIDE_ERR_INVALID);
+  CHECK(tide_layout_create(1, nd1, d1, 0, &L) == TIDE_ERR_INVALID);
+  int64_t huge[2] = {int64_t(1) << 40, int64_t(1) << 40};
+  CHECK(tide_layout_create(1, nd1, huge, 4, &L) == TIDE_ERR_INVALID);
+  CHECK(tide_layout_create(1, nd1, d1, 4, &L) == TIDE_OK);
+  const uintptr_t base = uintptr_t(1) << 40;
+  const void* g[1] = {reinterpret_cast<void*>(base)};
+  float* sh[4];
+  for (int r = 0; r < 4; ++r) sh[r] = reinterpret_cast<float*>(base + (uintptr_t(1) << 20) * (r + 1));
+  CHECK(tide_rs_bf16_to_fp32(L, 0, g, sh, 0, nullptr) == TIDE_ERR_INVALID);
+  sh[2] = sh[1];
+  CHECK(tide_rs_bf16_to_fp32(L, 1, g, sh, 0, nullptr) == TIDE_ERR_INVALID);  // shards overlap
+  sh[2] = reinterpret_cast<float*>(base + 8);
+  CHECK(tide_rs_bf16_to_fp32(L, 1, g, sh, 0, nullptr) == TIDE_ERR_INVALID);  // shard inside a gradient
+  void* pp[1] = {reinterpret_cast<void*>(base + 2)};
+  CHECK(tide_ag_place(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, 0, nullptr) == TIDE_ERR_INVALID);
+  CHECK(tide_ag_place(L, reinterpret_cast<void*>(base), pp, 7, 0, nullptr) == TIDE_ERR_INVALID);
+  CHECK(tide_slot_pack(L, const_cast<const void* const*>(pp), reinterpret_cast<void*>(base), 0, nullptr) ==
+        TIDE_ERR_INVALID);
+  const void* sl[2] = {reinterpret_cast<void*>(base), reinterpret_cast<void*>(base + 1)};
+  float* sh2[4];
+  for (int r = 0; r < 4; ++r) sh2[r] = reinterpret_cast<float*>(base + (uintptr_t(1) << 20) * (r + 1));
+  CHECK(tide_rs_slots_bf16_to_fp32(L, 2, sl, sh2, 0, nullptr) == TIDE_ERR_INVALID);  // odd slot address
+  CHECK(tide_last_hip_error() == 0);
+  tide_layout_destroy(L);
+  tide_layout_destroy(nullptr);
+  std::printf("host checks: %lld groups, %d failures\n", static_cast<long long>(groups), failures);
+  return failures == 0 ? 0 : 1;
+}
