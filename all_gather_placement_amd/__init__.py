@@ -12,9 +12,16 @@ from .tide import (  # noqa: F401
     TideError,
     library_path,
     load_library,
+    BoundCall,
     tide_ag_place,
+    tide_ag_prepare,
+    tide_call_destroy,
+    tide_call_launch,
     tide_layout_create,
     tide_rs_bf16_to_fp32,
+    tide_rs_prepare,
     tide_rs_slots_bf16_to_fp32,
+    tide_rs_slots_prepare,
     tide_slot_pack,
+    tide_slot_pack_prepare,
 )

@@ -1,9 +1,15 @@
-// Entry points of the reduce-scatter and all-gather placement: argument checks, the per-call
-// device pointer table, and dispatch to the gfx950 kernels or to the DMA engines.
+// Entry points of the reduce-scatter, the all-gather placement and Slot-Reuse: argument checks,
+// device pointer tables, and dispatch to the gfx950 kernels or to the DMA engines.
+//
+// Every entry point first turns its arguments into a validated Request (the host table of device
+// pointers the kernels read, plus launch parameters).  Immediate calls stage that table through
+// the layout's ring of pointer-table slots; prepared calls (tide_*_prepare) give it a device
+// buffer of its own, so tide_call_launch only enqueues kernels.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstring>
+#include <new>
 #include <utility>
 #include <vector>
 
@@ -24,10 +30,9 @@ bool outputs_overlap(std::vector<Range> outs, const std::vector<Range>& ins) {
   for (size_t i = 1; i < outs.size(); ++i)
     if (outs[i].lo < outs[i - 1].hi) return true;
   for (const Range& in : ins) {
-    // first output whose end is beyond in.lo
+    // first output whose end is beyond in.lo (outs are sorted and disjoint, so their ends are too)
     auto it = std::upper_bound(outs.begin(), outs.end(), in.lo,
                                [](uintptr_t v, const Range& r) { return v < r.hi; });
-    // outs are sorted and disjoint, so their `hi` values are sorted too
     if (it != outs.end() && it->lo < in.hi) return true;
   }
   return false;
@@ -38,6 +43,129 @@ tide_status hip_fail(int err) {
   return err == hipErrorOutOfMemory ? TIDE_ERR_NOMEM : TIDE_ERR_HIP;
 }
 
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + uintptr_t(bytes)};
+}
+
+// ---------------------------------------------------------------------------------------------
+// Validated requests
+// ---------------------------------------------------------------------------------------------
+
+enum Kind { kRs = 0, kAg = 1, kPack = 2, kRsSlots = 3 };
+
+struct Request {
+  Kind kind = kRs;
+  int32_t C = 0;          // contributors (RS kinds)
+  int32_t mode = TIDE_AG_KERNEL;
+  int32_t cu_budget = 0;
+  bool vec = true;        // every base pointer 16-byte aligned
+  void* stage = nullptr;  // AG stage / packed slot
+  // Device pointers the kernels read, host copy:
+  //   kRs [C*P gradients][R shards]; kAg, kPack [P parameters/gradients]; kRsSlots [C slots][R shards]
+  std::vector<void*> table;
+};
+
+tide_status validate_rs(const tide_layout* L, int32_t C, const void* const* grads, float* const* shards,
+                        int32_t cu_budget, Request* q) {
+  if (L == nullptr || grads == nullptr || shards == nullptr || C < 1 || cu_budget < 0) return TIDE_ERR_INVALID;
+  const int32_t P = L->P, R = L->R;
+  const int64_t S = L->S;
+  if (int64_t(C) * P > (int64_t(1) << 24)) return TIDE_ERR_INVALID;
+  q->kind = kRs;
+  q->C = C;
+  q->cu_budget = cu_budget;
+  q->vec = true;
+  std::vector<Range> ins, outs;
+  ins.reserve(size_t(C) * P);
+  for (int32_t c = 0; c < C; ++c) {
+    for (int32_t p = 0; p < P; ++p) {
+      const void* g = grads[size_t(c) * P + p];
+      const int64_t n = L->params[p].numel;
+      if (n == 0) continue;
+      if (g == nullptr || !aligned(g, 2)) return TIDE_ERR_INVALID;
+      q->vec = q->vec && aligned(g, 16);
+      ins.push_back(range_of(g, n * 2));
+    }
+  }
+  for (int32_t r = 0; r < R; ++r) {
+    if (S == 0) continue;
+    if (shards[r] == nullptr || !aligned(shards[r], 4)) return TIDE_ERR_INVALID;
+    q->vec = q->vec && aligned(shards[r], 16);
+    outs.push_back(range_of(shards[r], S * 4));
+  }
+  if (outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
+  q->table.assign(size_t(C) * P + R, nullptr);
+  for (size_t i = 0; i < size_t(C) * P; ++i) q->table[i] = const_cast<void*>(grads[i]);
+  for (int32_t r = 0; r < R; ++r) q->table[size_t(C) * P + r] = shards[r];
+  return TIDE_OK;
+}
+
+tide_status validate_rs_slots(const tide_layout* L, int32_t C, const void* const* slots, float* const* shards,
+                              int32_t cu_budget, Request* q) {
+  if (L == nullptr || slots == nullptr || shards == nullptr || C < 1 || cu_budget < 0) return TIDE_ERR_INVALID;
+  if (C > (1 << 24)) return TIDE_ERR_INVALID;
+  const int32_t R = L->R;
+  const int64_t S = L->S;
+  q->kind = kRsSlots;
+  q->C = C;
+  q->cu_budget = cu_budget;
+  q->vec = true;
+  std::vector<Range> ins, outs;
+  if (S > 0) {
+    for (int32_t c = 0; c < C; ++c) {
+      if (slots[c] == nullptr || !aligned(slots[c], 2)) return TIDE_ERR_INVALID;
+      q->vec = q->vec && aligned(slots[c], 16);
+      ins.push_back(range_of(slots[c], int64_t(R) * S * 2));
+    }
+    for (int32_t r = 0; r < R; ++r) {
+      if (shards[r] == nullptr || !aligned(shards[r], 4)) return TIDE_ERR_INVALID;
+      q->vec = q->vec && aligned(shards[r], 16);
+      outs.push_back(range_of(shards[r], S * 4));
+    }
+  }
+  if (outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
+  q->table.assign(size_t(C) + R, nullptr);
+  for (int32_t c = 0; c < C; ++c) q->table[c] = const_cast<void*>(slots[c]);
+  for (int32_t r = 0; r < R; ++r) q->table[size_t(C) + r] = shards[r];
+  return TIDE_OK;
+}
+
+// AG placement (pack = false: stage -> params) and Slot-Reuse packing (pack = true: params ->
+// slot) share one layout of arguments: a stage/slot of R*S bf16 and P per-parameter tensors.
+tide_status validate_ag(const tide_layout* L, const void* stage, void* const* params, int32_t mode,
+                        int32_t cu_budget, bool pack, Request* q) {
+  if (L == nullptr || params == nullptr || cu_budget < 0) return TIDE_ERR_INVALID;
+  if (!pack && mode != TIDE_AG_KERNEL && mode != TIDE_AG_SDMA && mode != TIDE_AG_COPY2D) return TIDE_ERR_INVALID;
+  const int32_t P = L->P, R = L->R;
+  const int64_t stage_n = int64_t(R) * L->S;
+  if (stage_n > 0 && (stage == nullptr || !aligned(stage, 2))) return TIDE_ERR_INVALID;
+  q->kind = pack ? kPack : kAg;
+  q->mode = pack ? TIDE_AG_KERNEL : mode;
+  q->cu_budget = cu_budget;
+  q->vec = stage_n == 0 || aligned(stage, 16);
+  q->stage = const_cast<void*>(stage);
+  std::vector<Range> stage_r, tensors;
+  if (stage_n > 0) stage_r.push_back(range_of(stage, stage_n * 2));
+  for (int32_t p = 0; p < P; ++p) {
+    const int64_t n = L->params[p].numel;
+    if (n == 0) continue;
+    if (params[p] == nullptr || !aligned(params[p], 2)) return TIDE_ERR_INVALID;
+    q->vec = q->vec && aligned(params[p], 16);
+    tensors.push_back(range_of(params[p], n * 2));
+  }
+  // placement writes the parameters (outputs) from the stage; packing writes the slot
+  if (pack ? outputs_overlap(stage_r, tensors) : outputs_overlap(tensors, stage_r)) return TIDE_ERR_INVALID;
+  q->table.assign(params, params + P);
+  return TIDE_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Pointer-table ring (immediate calls)
+// ---------------------------------------------------------------------------------------------
+
 // Stage `n` device pointers for a launch on `stream`; returns the slot that holds them.
 int acquire_ptrs(DeviceState* st, void* const* ptrs, size_t n, hipStream_t stream, PtrSlot** out) {
   // A slot that already holds this exact table and was last used on this stream can be reused
@@ -45,8 +173,7 @@ int acquire_ptrs(DeviceState* st, void* const* ptrs, size_t n, hipStream_t strea
   // alternate between tables (an RS and an AG on the same group) hit different slots.
   for (int k = 0; k < kPtrSlots; ++k) {
     PtrSlot& s = st->slots[k];
-    if (s.n == n && s.host != nullptr && s.stream == stream &&
-        std::memcmp(s.host, ptrs, n * sizeof(void*)) == 0) {
+    if (s.n == n && s.host != nullptr && s.stream == stream && std::memcmp(s.host, ptrs, n * sizeof(void*)) == 0) {
       *out = &s;
       return hipSuccess;
     }
@@ -67,7 +194,7 @@ int acquire_ptrs(DeviceState* st, void* const* ptrs, size_t n, hipStream_t strea
     s.dev = nullptr;
     s.host = nullptr;
     s.cap = 0;
-    size_t cap = std::max<size_t>(n, 256);
+    const size_t cap = std::max<size_t>(n, 256);
     if ((e = hipMalloc(reinterpret_cast<void**>(&s.dev), cap * sizeof(void*))) != hipSuccess) return e;
     if ((e = hipHostMalloc(reinterpret_cast<void**>(&s.host), cap * sizeof(void*), hipHostMallocDefault)) !=
         hipSuccess) {
@@ -95,13 +222,10 @@ int release_ptrs(PtrSlot* s, hipStream_t stream) {
   return e;
 }
 
-inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
 // Create the internal copy streams and their fork/join events on first use (layout mutex held).
 int ensure_dma(DeviceState* st) {
   hipError_t e;
-  if (st->dma_fork == nullptr &&
-      (e = hipEventCreateWithFlags(&st->dma_fork, hipEventDisableTiming)) != hipSuccess)
+  if (st->dma_fork == nullptr && (e = hipEventCreateWithFlags(&st->dma_fork, hipEventDisableTiming)) != hipSuccess)
     return e;
   for (int k = 0; k < kDmaStreams; ++k) {
     if (st->dma[k] == nullptr && (e = hipStreamCreateWithFlags(&st->dma[k], hipStreamNonBlocking)) != hipSuccess)
@@ -112,6 +236,10 @@ int ensure_dma(DeviceState* st) {
   }
   return hipSuccess;
 }
+
+// ---------------------------------------------------------------------------------------------
+// Enqueueing validated work
+// ---------------------------------------------------------------------------------------------
 
 // Launch plan for `count` work items: cu_budget 0 = one item per workgroup in one launch;
 // B > 0 = grids of at most `max_wgs` workgroups, each taking `bounded_items` items and exiting
@@ -134,295 +262,261 @@ Plan plan_for(int64_t count, int32_t cu_budget, int64_t max_wgs, int bounded_ite
   return Plan{int(grid), int(items), grid * items};
 }
 
+// Kernels of a table-driven request (RS, RS from slots, AG kernel, slot pack), reading the device
+// pointer table `dev_table`.  Only kernel launches: nothing is allocated, copied or recorded.
+int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& q, void* const* dev_table,
+                    hipStream_t hs) {
+  const void* const* tbl = const_cast<const void* const*>(dev_table);
+  int e = hipSuccess;
+  if (q.kind == kRs || q.kind == kRsSlots) {
+    const int64_t count = int64_t(L->rs_chunks.size());
+    const bool flat = q.kind == kRsSlots;
+    const Plan plan = plan_for(count, q.cu_budget, q.cu_budget, kRsBoundedItems);
+    for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
+      const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
+      e = launch_rs(st->rs, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, tbl, flat ? 1 : L->P, q.C,
+                    L->S, flat, q.vec, hs);
+    }
+    return e;
+  }
+  const int64_t count = int64_t(L->ag_chunks.size());
+  const int64_t ag_wgs = int64_t(q.cu_budget) * kThreads / kAgThreads;
+  const Plan plan = plan_for(count, q.cu_budget, ag_wgs, kAgBoundedItems);
+  for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
+    const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
+    e = launch_ag(st->ag, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, q.stage, tbl,
+                  q.kind == kPack, q.vec, hs);
+  }
+  if (e == hipSuccess && q.kind == kPack)
+    e = launch_fill_zero(st->slot_pad, int64_t(L->slot_pad_items.size()), q.stage, hs);
+  return e;
+}
+
+bool needs_kernels(const tide_layout* L, const Request& q) {
+  if (q.kind == kRs || q.kind == kRsSlots) return !L->rs_chunks.empty();
+  if (q.kind == kPack) return int64_t(L->R) * L->S > 0;
+  return !L->ag_chunks.empty();
+}
+
+// One 2-D copy per parameter covers the ranks whose slice is full (rows of the copy = ranks,
+// source pitch = one stage slot, destination pitch = one slice), plus one copy for the rank whose
+// slice is partly padding.  The runtime chooses the engine.
+tide_status enqueue_ag_copy2d(const tide_layout* L, const Request& q, hipStream_t hs) {
+  const int64_t S = L->S;
+  for (int32_t p = 0; p < L->P; ++p) {
+    const ParamGeom& g = L->params[p];
+    if (g.numel == 0) continue;
+    const int64_t full = g.rows / g.m;  // ranks with v == m_p
+    const char* src = static_cast<const char*>(q.stage) + 2 * g.o;
+    char* dst = static_cast<char*>(q.table[p]);
+    hipError_t e = hipSuccess;
+    if (full > 0)
+      e = hipMemcpy2DAsync(dst, size_t(2 * g.e), src, size_t(2 * S), size_t(2 * g.e), size_t(full),
+                           hipMemcpyDeviceToDevice, hs);
+    if (e == hipSuccess && full < L->R) {
+      const int64_t v = g.rows - full * g.m;
+      if (v > 0)
+        e = hipMemcpyAsync(dst + 2 * full * g.e, src + 2 * full * S, size_t(2 * v * g.L), hipMemcpyDeviceToDevice, hs);
+    }
+    if (e == hipErrorInvalidValue || e == hipErrorNotSupported) {
+      set_last_hip_error(e);
+      return TIDE_ERR_UNSUPPORTED;
+    }
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return TIDE_OK;
+}
+
+// DMA engines only: the runtime sends 1-D device-to-device copies of the "no compute unit" kind
+// to the SDMA engines (2-D copies become shader kernels), so each (parameter, rank) segment --
+// contiguous on both sides -- is one copy.  Copies alternate over the internal copy streams, which
+// fork from and join back into the caller's stream.  Layout mutex held.
+tide_status enqueue_ag_sdma(const tide_layout* L, DeviceState* st, const Request& q, hipStream_t hs) {
+  int e = ensure_dma(st);
+  if (e != hipSuccess) return hip_fail(e);
+  if ((e = hipEventRecord(st->dma_fork, hs)) != hipSuccess) return hip_fail(e);
+  for (int k = 0; k < kDmaStreams; ++k)
+    if ((e = hipStreamWaitEvent(st->dma[k], st->dma_fork, 0)) != hipSuccess) return hip_fail(e);
+  const int64_t S = L->S;
+  int64_t issued = 0;
+  for (int32_t p = 0; p < L->P && e == hipSuccess; ++p) {
+    const ParamGeom& g = L->params[p];
+    if (g.numel == 0) continue;
+    for (int32_t r = 0; r < L->R; ++r) {
+      const int64_t v = std::min<int64_t>(g.m, std::max<int64_t>(0, g.rows - int64_t(r) * g.m));
+      if (v == 0) break;
+      const char* src = static_cast<const char*>(q.stage) + 2 * (int64_t(r) * S + g.o);
+      char* dst = static_cast<char*>(q.table[p]) + 2 * int64_t(r) * g.e;
+      e = hipMemcpyAsync(dst, src, size_t(2 * v * g.L), hipMemcpyDeviceToDeviceNoCU, st->dma[issued % kDmaStreams]);
+      if (e != hipSuccess) break;
+      ++issued;
+    }
+  }
+  // Join even after a failed copy, so the caller's stream never runs ahead of issued copies.
+  int ej = hipSuccess;
+  for (int k = 0; k < kDmaStreams; ++k) {
+    if (ej == hipSuccess) ej = hipEventRecord(st->dma_join[k], st->dma[k]);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, st->dma_join[k], 0);
+  }
+  if (e == hipErrorInvalidValue || e == hipErrorNotSupported) {
+    set_last_hip_error(e);
+    return TIDE_ERR_UNSUPPORTED;
+  }
+  if (e != hipSuccess) return hip_fail(e);
+  if (ej != hipSuccess) return hip_fail(ej);
+  return TIDE_OK;
+}
+
+// Immediate execution of a validated request.
+tide_status run_now(const tide_layout* L, const Request& q, void* stream) {
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (q.kind == kAg && q.mode == TIDE_AG_COPY2D) return enqueue_ag_copy2d(L, q, hs);
+  if (!(q.kind == kAg && q.mode == TIDE_AG_SDMA) && !needs_kernels(L, q)) return TIDE_OK;
+  std::lock_guard<std::mutex> lock(L->mu);
+  DeviceState* st = nullptr;
+  int e = device_state(L, &st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (q.kind == kAg && q.mode == TIDE_AG_SDMA) return enqueue_ag_sdma(L, st, q, hs);
+  PtrSlot* slot = nullptr;
+  if ((e = acquire_ptrs(st, q.table.data(), q.table.size(), hs, &slot)) != hipSuccess) return hip_fail(e);
+  e = enqueue_kernels(L, st, q, slot->dev, hs);
+  const int er = release_ptrs(slot, hs);
+  if (e != hipSuccess) return hip_fail(e);
+  if (er != hipSuccess) return hip_fail(er);
+  return TIDE_OK;
+}
+
 }  // namespace
 }  // namespace tide
 
-using tide::Range;
+// A prepared call: a validated request with a device pointer table of its own.
+struct tide_call {
+  const tide_layout* layout = nullptr;
+  tide::Request q;
+  int device = -1;
+  void** dev_table = nullptr;
+  tide::DeviceState* st = nullptr;  // node of layout->devices; std::map nodes do not move
+};
+
+namespace {
+
+tide_status prepare(const tide_layout* L, tide::Request&& q, tide_call** out) {
+  if (out == nullptr) return TIDE_ERR_INVALID;
+  tide_call* call = new (std::nothrow) tide_call();
+  if (call == nullptr) return TIDE_ERR_NOMEM;
+  call->layout = L;
+  call->q = std::move(q);
+  int e = hipGetDevice(&call->device);
+  if (e == hipSuccess) {
+    std::lock_guard<std::mutex> lock(L->mu);
+    e = tide::device_state(L, &call->st);
+  }
+  // The DMA placement modes address parameters from the host table; only kernels read a device one.
+  const bool kernels = !(call->q.kind == tide::kAg && call->q.mode != TIDE_AG_KERNEL);
+  if (e == hipSuccess && kernels && !call->q.table.empty()) {
+    const size_t bytes = call->q.table.size() * sizeof(void*);
+    e = hipMalloc(reinterpret_cast<void**>(&call->dev_table), bytes);
+    if (e == hipSuccess) e = hipMemcpy(call->dev_table, call->q.table.data(), bytes, hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    if (call->dev_table) (void)hipFree(call->dev_table);
+    delete call;
+    return tide::hip_fail(e);
+  }
+  *out = call;
+  return TIDE_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
 tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* grads,
                                  float* const* shards, int32_t cu_budget, void* stream) {
-  if (layout == nullptr || grads == nullptr || shards == nullptr || C < 1 || cu_budget < 0)
-    return TIDE_ERR_INVALID;
-  const int32_t P = layout->P, R = layout->R;
-  const int64_t S = layout->S;
-  if (int64_t(C) * P > (int64_t(1) << 24)) return TIDE_ERR_INVALID;
-
-  bool vec = true;
-  std::vector<Range> ins, outs;
-  ins.reserve(size_t(C) * P);
-  outs.reserve(R);
-  for (int32_t c = 0; c < C; ++c) {
-    for (int32_t p = 0; p < P; ++p) {
-      const void* g = grads[size_t(c) * P + p];
-      const int64_t n = layout->params[p].numel;
-      if (n == 0) continue;
-      if (g == nullptr || !tide::aligned(g, 2)) return TIDE_ERR_INVALID;
-      vec = vec && tide::aligned(g, 16);
-      const uintptr_t lo = reinterpret_cast<uintptr_t>(g);
-      ins.push_back(Range{lo, lo + uintptr_t(n) * 2});
-    }
-  }
-  for (int32_t r = 0; r < R; ++r) {
-    const float* s = shards[r];
-    if (S == 0) continue;
-    if (s == nullptr || !tide::aligned(s, 4)) return TIDE_ERR_INVALID;
-    vec = vec && tide::aligned(s, 16);
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(s);
-    outs.push_back(Range{lo, lo + uintptr_t(S) * 4});
-  }
-  if (tide::outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
-  const int64_t count = int64_t(layout->rs_chunks.size());
-  if (count == 0) return TIDE_OK;
-
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  std::lock_guard<std::mutex> lock(layout->mu);
-  tide::DeviceState* st = nullptr;
-  int e = tide::device_state(layout, &st);
-  if (e != hipSuccess) return tide::hip_fail(e);
-
-  // Pointer table: C*P gradient pointers, then R shard pointers.
-  std::vector<void*> table(size_t(C) * P + R);
-  for (size_t i = 0; i < size_t(C) * P; ++i) table[i] = const_cast<void*>(grads[i]);
-  for (int32_t r = 0; r < R; ++r) table[size_t(C) * P + r] = shards[r];
-  tide::PtrSlot* slot = nullptr;
-  if ((e = tide::acquire_ptrs(st, table.data(), table.size(), hs, &slot)) != hipSuccess) return tide::hip_fail(e);
-
-  const tide::Plan plan = tide::plan_for(count, cu_budget, cu_budget, tide::kRsBoundedItems);
-  for (int64_t first = 0; first < count; first += plan.per_launch) {
-    const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
-    const int grid = int(std::min<int64_t>(plan.grid, n));
-    e = tide::launch_rs(st->rs, first, n, grid, plan.items, const_cast<const void* const*>(slot->dev), P, C, S,
-                        /*flat=*/false, vec, hs);
-    if (e != hipSuccess) {
-      (void)tide::release_ptrs(slot, hs);
-      return tide::hip_fail(e);
-    }
-  }
-  if ((e = tide::release_ptrs(slot, hs)) != hipSuccess) return tide::hip_fail(e);
-  return TIDE_OK;
+  tide::Request q;
+  const tide_status s = tide::validate_rs(layout, C, grads, shards, cu_budget, &q);
+  return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
 }
 
 tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params, int32_t mode,
                           int32_t cu_budget, void* stream) {
-  if (layout == nullptr || params == nullptr || cu_budget < 0) return TIDE_ERR_INVALID;
-  if (mode != TIDE_AG_KERNEL && mode != TIDE_AG_SDMA && mode != TIDE_AG_COPY2D) return TIDE_ERR_INVALID;
-  const int32_t P = layout->P, R = layout->R;
-  const int64_t S = layout->S;
-  const int64_t stage_n = int64_t(R) * S;
-  if (stage_n > 0 && (stage == nullptr || !tide::aligned(stage, 2))) return TIDE_ERR_INVALID;
-  bool vec = stage_n == 0 || tide::aligned(stage, 16);
-  std::vector<Range> ins, outs;
-  if (stage_n > 0) {
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(stage);
-    ins.push_back(Range{lo, lo + uintptr_t(stage_n) * 2});
-  }
-  for (int32_t p = 0; p < P; ++p) {
-    const int64_t n = layout->params[p].numel;
-    if (n == 0) continue;
-    const void* q = params[p];
-    if (q == nullptr || !tide::aligned(q, 2)) return TIDE_ERR_INVALID;
-    vec = vec && tide::aligned(q, 16);
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(q);
-    outs.push_back(Range{lo, lo + uintptr_t(n) * 2});
-  }
-  if (tide::outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-
-  if (mode == TIDE_AG_COPY2D) {
-    // One 2-D copy per parameter covers the ranks whose slice is full (rows of the copy = ranks,
-    // source pitch = one stage slot, destination pitch = one slice), plus one copy for the rank
-    // whose slice is partly padding.  The runtime chooses the engine.
-    for (int32_t p = 0; p < P; ++p) {
-      const tide::ParamGeom& g = layout->params[p];
-      if (g.numel == 0) continue;
-      const int64_t full = g.rows / g.m;  // ranks with v == m_p
-      const char* src = static_cast<const char*>(stage) + 2 * g.o;
-      char* dst = static_cast<char*>(params[p]);
-      hipError_t e = hipSuccess;
-      if (full > 0)
-        e = hipMemcpy2DAsync(dst, size_t(2 * g.e), src, size_t(2 * S), size_t(2 * g.e), size_t(full),
-                             hipMemcpyDeviceToDevice, hs);
-      if (e == hipSuccess && full < R) {
-        const int64_t v = g.rows - full * g.m;
-        if (v > 0) e = hipMemcpyAsync(dst + 2 * full * g.e, src + 2 * full * S, size_t(2 * v * g.L),
-                                      hipMemcpyDeviceToDevice, hs);
-      }
-      if (e == hipErrorInvalidValue || e == hipErrorNotSupported) {
-        tide::set_last_hip_error(e);
-        return TIDE_ERR_UNSUPPORTED;
-      }
-      if (e != hipSuccess) return tide::hip_fail(e);
-    }
-    return TIDE_OK;
-  }
-
-  if (mode == TIDE_AG_SDMA) {
-    // DMA engines only: the runtime sends 1-D device-to-device copies of the "no compute unit"
-    // kind to the SDMA engines (2-D copies become shader kernels), so each (parameter, rank)
-    // segment -- contiguous on both sides -- is one copy.  Copies alternate over the internal
-    // copy streams, which fork from and join back into the caller's stream.
-    std::lock_guard<std::mutex> lock(layout->mu);
-    tide::DeviceState* st = nullptr;
-    int e = tide::device_state(layout, &st);
-    if (e != hipSuccess) return tide::hip_fail(e);
-    if ((e = tide::ensure_dma(st)) != hipSuccess) return tide::hip_fail(e);
-    if ((e = hipEventRecord(st->dma_fork, hs)) != hipSuccess) return tide::hip_fail(e);
-    for (int k = 0; k < tide::kDmaStreams; ++k)
-      if ((e = hipStreamWaitEvent(st->dma[k], st->dma_fork, 0)) != hipSuccess) return tide::hip_fail(e);
-    int64_t issued = 0;
-    for (int32_t p = 0; p < P && e == hipSuccess; ++p) {
-      const tide::ParamGeom& g = layout->params[p];
-      if (g.numel == 0) continue;
-      for (int32_t r = 0; r < R; ++r) {
-        const int64_t v = std::min<int64_t>(g.m, std::max<int64_t>(0, g.rows - int64_t(r) * g.m));
-        if (v == 0) break;
-        const char* src = static_cast<const char*>(stage) + 2 * (int64_t(r) * S + g.o);
-        char* dst = static_cast<char*>(params[p]) + 2 * int64_t(r) * g.e;
-        e = hipMemcpyAsync(dst, src, size_t(2 * v * g.L), hipMemcpyDeviceToDeviceNoCU,
-                           st->dma[issued % tide::kDmaStreams]);
-        if (e != hipSuccess) break;
-        ++issued;
-      }
-    }
-    // Join even after a failed copy, so the caller's stream never runs ahead of issued copies.
-    int ej = hipSuccess;
-    for (int k = 0; k < tide::kDmaStreams; ++k) {
-      if (ej == hipSuccess) ej = hipEventRecord(st->dma_join[k], st->dma[k]);
-      if (ej == hipSuccess) ej = hipStreamWaitEvent(hs, st->dma_join[k], 0);
-    }
-    if (e == hipErrorInvalidValue || e == hipErrorNotSupported) {
-      tide::set_last_hip_error(e);
-      return TIDE_ERR_UNSUPPORTED;
-    }
-    if (e != hipSuccess) return tide::hip_fail(e);
-    if (ej != hipSuccess) return tide::hip_fail(ej);
-    return TIDE_OK;
-  }
-
-  const int64_t count = int64_t(layout->ag_chunks.size());
-  if (count == 0) return TIDE_OK;
-  std::lock_guard<std::mutex> lock(layout->mu);
-  tide::DeviceState* st = nullptr;
-  int e = tide::device_state(layout, &st);
-  if (e != hipSuccess) return tide::hip_fail(e);
-  tide::PtrSlot* slot = nullptr;
-  if ((e = tide::acquire_ptrs(st, params, size_t(P), hs, &slot)) != hipSuccess) return tide::hip_fail(e);
-  const int64_t ag_wgs = int64_t(cu_budget) * tide::kThreads / tide::kAgThreads;
-  const tide::Plan plan = tide::plan_for(count, cu_budget, ag_wgs, tide::kAgBoundedItems);
-  for (int64_t first = 0; first < count; first += plan.per_launch) {
-    const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
-    const int grid = int(std::min<int64_t>(plan.grid, n));
-    e = tide::launch_ag(st->ag, first, n, grid, plan.items, const_cast<void*>(stage),
-                        const_cast<const void* const*>(slot->dev), /*pack=*/false, vec, hs);
-    if (e != hipSuccess) {
-      (void)tide::release_ptrs(slot, hs);
-      return tide::hip_fail(e);
-    }
-  }
-  if ((e = tide::release_ptrs(slot, hs)) != hipSuccess) return tide::hip_fail(e);
-  return TIDE_OK;
+  tide::Request q;
+  const tide_status s = tide::validate_ag(layout, stage, params, mode, cu_budget, /*pack=*/false, &q);
+  return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
 }
 
 tide_status tide_slot_pack(const tide_layout* layout, const void* const* grads, void* slot, int32_t cu_budget,
                            void* stream) {
-  if (layout == nullptr || grads == nullptr || cu_budget < 0) return TIDE_ERR_INVALID;
-  const int32_t P = layout->P, R = layout->R;
-  const int64_t S = layout->S;
-  const int64_t slot_n = int64_t(R) * S;
-  if (slot_n > 0 && (slot == nullptr || !tide::aligned(slot, 2))) return TIDE_ERR_INVALID;
-  bool vec = slot_n == 0 || tide::aligned(slot, 16);
-  std::vector<Range> ins, outs;
-  if (slot_n > 0) {
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(slot);
-    outs.push_back(Range{lo, lo + uintptr_t(slot_n) * 2});
-  }
-  for (int32_t p = 0; p < P; ++p) {
-    const int64_t n = layout->params[p].numel;
-    if (n == 0) continue;
-    const void* g = grads[p];
-    if (g == nullptr || !tide::aligned(g, 2)) return TIDE_ERR_INVALID;
-    vec = vec && tide::aligned(g, 16);
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(g);
-    ins.push_back(Range{lo, lo + uintptr_t(n) * 2});
-  }
-  if (tide::outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
-  if (slot_n == 0) return TIDE_OK;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  std::lock_guard<std::mutex> lock(layout->mu);
-  tide::DeviceState* st = nullptr;
-  int e = tide::device_state(layout, &st);
-  if (e != hipSuccess) return tide::hip_fail(e);
-  const int64_t count = int64_t(layout->ag_chunks.size());
-  if (count > 0) {
-    tide::PtrSlot* pslot = nullptr;
-    if ((e = tide::acquire_ptrs(st, const_cast<void* const*>(grads), size_t(P), hs, &pslot)) != hipSuccess)
-      return tide::hip_fail(e);
-    const int64_t ag_wgs = int64_t(cu_budget) * tide::kThreads / tide::kAgThreads;
-    const tide::Plan plan = tide::plan_for(count, cu_budget, ag_wgs, tide::kAgBoundedItems);
-    for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
-      const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
-      const int grid = int(std::min<int64_t>(plan.grid, n));
-      e = tide::launch_ag(st->ag, first, n, grid, plan.items, slot, const_cast<const void* const*>(pslot->dev),
-                          /*pack=*/true, vec, hs);
-    }
-    const int er = tide::release_ptrs(pslot, hs);
-    if (e != hipSuccess) return tide::hip_fail(e);
-    if (er != hipSuccess) return tide::hip_fail(er);
-  }
-  e = tide::launch_fill_zero(st->slot_pad, int64_t(layout->slot_pad_items.size()), slot, hs);
-  if (e != hipSuccess) return tide::hip_fail(e);
-  return TIDE_OK;
+  tide::Request q;
+  const tide_status s = tide::validate_ag(layout, slot, const_cast<void* const*>(grads), TIDE_AG_KERNEL, cu_budget,
+                                          /*pack=*/true, &q);
+  return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
 }
 
 tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* slots,
                                        float* const* shards, int32_t cu_budget, void* stream) {
-  if (layout == nullptr || slots == nullptr || shards == nullptr || C < 1 || cu_budget < 0)
-    return TIDE_ERR_INVALID;
-  const int32_t R = layout->R;
-  const int64_t S = layout->S;
-  if (C > (1 << 24)) return TIDE_ERR_INVALID;
-  if (S == 0) return TIDE_OK;
-  bool vec = true;
-  std::vector<Range> ins, outs;
-  for (int32_t c = 0; c < C; ++c) {
-    const void* g = slots[c];
-    if (g == nullptr || !tide::aligned(g, 2)) return TIDE_ERR_INVALID;
-    vec = vec && tide::aligned(g, 16);
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(g);
-    ins.push_back(Range{lo, lo + uintptr_t(int64_t(R) * S) * 2});
-  }
-  for (int32_t r = 0; r < R; ++r) {
-    const float* s = shards[r];
-    if (s == nullptr || !tide::aligned(s, 4)) return TIDE_ERR_INVALID;
-    vec = vec && tide::aligned(s, 16);
-    const uintptr_t lo = reinterpret_cast<uintptr_t>(s);
-    outs.push_back(Range{lo, lo + uintptr_t(S) * 4});
-  }
-  if (tide::outputs_overlap(outs, ins)) return TIDE_ERR_INVALID;
-  const int64_t count = int64_t(layout->rs_chunks.size());
+  tide::Request q;
+  const tide_status s = tide::validate_rs_slots(layout, C, slots, shards, cu_budget, &q);
+  return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
+}
+
+tide_status tide_rs_prepare(const tide_layout* layout, int32_t C, const void* const* grads, float* const* shards,
+                            int32_t cu_budget, tide_call** out) {
+  tide::Request q;
+  const tide_status s = tide::validate_rs(layout, C, grads, shards, cu_budget, &q);
+  return s != TIDE_OK ? s : prepare(layout, std::move(q), out);
+}
+
+tide_status tide_ag_prepare(const tide_layout* layout, const void* stage, void* const* params, int32_t mode,
+                            int32_t cu_budget, tide_call** out) {
+  tide::Request q;
+  const tide_status s = tide::validate_ag(layout, stage, params, mode, cu_budget, /*pack=*/false, &q);
+  return s != TIDE_OK ? s : prepare(layout, std::move(q), out);
+}
+
+tide_status tide_slot_pack_prepare(const tide_layout* layout, const void* const* grads, void* slot,
+                                   int32_t cu_budget, tide_call** out) {
+  tide::Request q;
+  const tide_status s = tide::validate_ag(layout, slot, const_cast<void* const*>(grads), TIDE_AG_KERNEL, cu_budget,
+                                          /*pack=*/true, &q);
+  return s != TIDE_OK ? s : prepare(layout, std::move(q), out);
+}
+
+tide_status tide_rs_slots_prepare(const tide_layout* layout, int32_t C, const void* const* slots,
+                                  float* const* shards, int32_t cu_budget, tide_call** out) {
+  tide::Request q;
+  const tide_status s = tide::validate_rs_slots(layout, C, slots, shards, cu_budget, &q);
+  return s != TIDE_OK ? s : prepare(layout, std::move(q), out);
+}
+
+tide_status tide_call_launch(const tide_call* call, void* stream) {
+  if (call == nullptr) return TIDE_ERR_INVALID;
+  int dev = -1;
+  int e = hipGetDevice(&dev);
+  if (e != hipSuccess) return tide::hip_fail(e);
+  if (dev != call->device) return TIDE_ERR_INVALID;
+  const tide::Request& q = call->q;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  std::lock_guard<std::mutex> lock(layout->mu);
-  tide::DeviceState* st = nullptr;
-  int e = tide::device_state(layout, &st);
-  if (e != hipSuccess) return tide::hip_fail(e);
-  std::vector<void*> table(size_t(C) + R);
-  for (int32_t c = 0; c < C; ++c) table[c] = const_cast<void*>(slots[c]);
-  for (int32_t r = 0; r < R; ++r) table[size_t(C) + r] = shards[r];
-  tide::PtrSlot* pslot = nullptr;
-  if ((e = tide::acquire_ptrs(st, table.data(), table.size(), hs, &pslot)) != hipSuccess) return tide::hip_fail(e);
-  const tide::Plan plan = tide::plan_for(count, cu_budget, cu_budget, tide::kRsBoundedItems);
-  for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
-    const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
-    const int grid = int(std::min<int64_t>(plan.grid, n));
-    e = tide::launch_rs(st->rs, first, n, grid, plan.items, const_cast<const void* const*>(pslot->dev), 1, C, S,
-                        /*flat=*/true, vec, hs);
+  if (q.kind == tide::kAg && q.mode == TIDE_AG_COPY2D) return tide::enqueue_ag_copy2d(call->layout, q, hs);
+  if (q.kind == tide::kAg && q.mode == TIDE_AG_SDMA) {
+    std::lock_guard<std::mutex> lock(call->layout->mu);
+    return tide::enqueue_ag_sdma(call->layout, call->st, q, hs);
   }
-  const int er = tide::release_ptrs(pslot, hs);
-  if (e != hipSuccess) return tide::hip_fail(e);
-  if (er != hipSuccess) return tide::hip_fail(er);
-  return TIDE_OK;
+  if (!tide::needs_kernels(call->layout, q)) return TIDE_OK;
+  e = tide::enqueue_kernels(call->layout, call->st, q, call->dev_table, hs);
+  return e == hipSuccess ? TIDE_OK : tide::hip_fail(e);
+}
+
+void tide_call_destroy(tide_call* call) {
+  if (call == nullptr) return;
+  if (call->dev_table) {
+    int cur = 0;
+    const bool have = hipGetDevice(&cur) == hipSuccess;
+    if (have && cur != call->device) (void)hipSetDevice(call->device);
+    (void)hipFree(call->dev_table);
+    if (have && cur != call->device) (void)hipSetDevice(cur);
+  }
+  delete call;
 }
 
 }  // extern "C"

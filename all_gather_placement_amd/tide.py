@@ -70,6 +70,12 @@ def load_library(path: str | None = None):
         "tide_rs_slots_bf16_to_fp32": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]),
         "tide_layout_num_slot_pad_items": (i64, [vp]),
         "tide_layout_copy_slot_pad_items": (i32, [vp, i64, i64, P_i64]),
+        "tide_rs_prepare": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]),
+        "tide_ag_prepare": (i32, [vp, vp, ctypes.POINTER(vp), i32, i32, ctypes.POINTER(vp)]),
+        "tide_slot_pack_prepare": (i32, [vp, ctypes.POINTER(vp), vp, i32, ctypes.POINTER(vp)]),
+        "tide_rs_slots_prepare": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]),
+        "tide_call_launch": (i32, [vp, vp]),
+        "tide_call_destroy": (None, [vp]),
         "tide_status_str": (ctypes.c_char_p, [i32]),
         "tide_last_hip_error": (i32, []),
     }
@@ -161,6 +167,52 @@ def tide_rs_slots_bf16_to_fp32(layout: int, slots, shards, cu_budget: int = 0, s
     sh_arr = (ctypes.c_void_p * max(len(sh), 1))(*sh)
     _check(lib.tide_rs_slots_bf16_to_fp32(layout, len(sl), sl_arr, sh_arr, int(cu_budget), _stream_handle(stream)),
            "tide_rs_slots_bf16_to_fp32")
+
+
+def _ptr_array(xs):
+    xs = [_ptr(x) for x in xs]
+    return (ctypes.c_void_p * max(len(xs), 1))(*xs)
+
+
+def tide_rs_prepare(layout: int, grads, shards, cu_budget: int = 0) -> int:
+    """Prepared RS call (see tide_call_launch); returns the raw tide_call handle."""
+    lib = load_library()
+    out = ctypes.c_void_p()
+    _check(lib.tide_rs_prepare(layout, len(grads), _ptr_array([g for row in grads for g in row]),
+                               _ptr_array(shards), int(cu_budget), ctypes.byref(out)), "tide_rs_prepare")
+    return out.value
+
+
+def tide_ag_prepare(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0) -> int:
+    lib = load_library()
+    out = ctypes.c_void_p()
+    _check(lib.tide_ag_prepare(layout, _ptr(stage), _ptr_array(params), int(mode), int(cu_budget), ctypes.byref(out)),
+           "tide_ag_prepare")
+    return out.value
+
+
+def tide_slot_pack_prepare(layout: int, grads, slot, cu_budget: int = 0) -> int:
+    lib = load_library()
+    out = ctypes.c_void_p()
+    _check(lib.tide_slot_pack_prepare(layout, _ptr_array(grads), _ptr(slot), int(cu_budget), ctypes.byref(out)),
+           "tide_slot_pack_prepare")
+    return out.value
+
+
+def tide_rs_slots_prepare(layout: int, slots, shards, cu_budget: int = 0) -> int:
+    lib = load_library()
+    out = ctypes.c_void_p()
+    _check(lib.tide_rs_slots_prepare(layout, len(slots), _ptr_array(slots), _ptr_array(shards), int(cu_budget),
+                                     ctypes.byref(out)), "tide_rs_slots_prepare")
+    return out.value
+
+
+def tide_call_launch(call: int, stream=None):
+    _check(load_library().tide_call_launch(call, _stream_handle(stream)), "tide_call_launch")
+
+
+def tide_call_destroy(call: int):
+    load_library().tide_call_destroy(call)
 
 
 class Layout:
@@ -256,35 +308,24 @@ class Layout:
         _check_shapes_ag(self, stage, params)
         tide_ag_place(self.handle, stage, params, mode, cu_budget, stream)
 
-    # pre-marshalled calls (validate once, launch many times) ----------------------------------
+    # prepared calls (validate once, launch many times; graph-capturable kernel paths) ---------
     def bind_rs(self, grads, shards, cu_budget: int = 0) -> BoundCall:
         _check_shapes_rs(self, grads, shards)
-        flat = [_ptr(g) for row in grads for g in row]
-        g_arr = (ctypes.c_void_p * max(len(flat), 1))(*flat)
-        s_arr = (ctypes.c_void_p * max(len(shards), 1))(*[_ptr(x) for x in shards])
-        return BoundCall(self._lib.tide_rs_bf16_to_fp32, "tide_rs_bf16_to_fp32",
-                         (self.handle, len(grads), g_arr, s_arr, int(cu_budget)), (grads, shards, self))
+        return BoundCall(tide_rs_prepare(self.handle, grads, shards, cu_budget), (grads, shards, self))
 
     def bind_ag(self, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0) -> BoundCall:
         _check_shapes_ag(self, stage, params)
-        p_arr = (ctypes.c_void_p * max(len(params), 1))(*[_ptr(x) for x in params])
-        return BoundCall(self._lib.tide_ag_place, "tide_ag_place",
-                         (self.handle, _ptr(stage), p_arr, int(mode), int(cu_budget)), (stage, params, self))
+        return BoundCall(tide_ag_prepare(self.handle, stage, params, mode, cu_budget), (stage, params, self))
 
     def bind_slot_pack(self, grads, slot, cu_budget: int = 0) -> BoundCall:
         _check_shapes_ag(self, slot, grads)
-        g_arr = (ctypes.c_void_p * max(len(grads), 1))(*[_ptr(x) for x in grads])
-        return BoundCall(self._lib.tide_slot_pack, "tide_slot_pack",
-                         (self.handle, g_arr, _ptr(slot), int(cu_budget)), (grads, slot, self))
+        return BoundCall(tide_slot_pack_prepare(self.handle, grads, slot, cu_budget), (grads, slot, self))
 
     def bind_rs_slots(self, slots, shards, cu_budget: int = 0) -> BoundCall:
         _check_shapes_rs(self, [], shards)
         for sl in slots:
             _check_stage(self, sl)
-        sl_arr = (ctypes.c_void_p * max(len(slots), 1))(*[_ptr(x) for x in slots])
-        sh_arr = (ctypes.c_void_p * max(len(shards), 1))(*[_ptr(x) for x in shards])
-        return BoundCall(self._lib.tide_rs_slots_bf16_to_fp32, "tide_rs_slots_bf16_to_fp32",
-                         (self.handle, len(slots), sl_arr, sh_arr, int(cu_budget)), (slots, shards, self))
+        return BoundCall(tide_rs_slots_prepare(self.handle, slots, shards, cu_budget), (slots, shards, self))
 
     def slot_pack(self, grads, slot, cu_budget: int = 0, stream=None):
         _check_shapes_ag(self, slot, grads)
@@ -298,17 +339,29 @@ class Layout:
 
 
 class BoundCall:
-    """A validated, pre-marshalled call: the argument arrays are built once, each launch() is one
-    ctypes call.  Keeps references to the tensors so their memory outlives the binding."""
+    """Owner of a prepared call (tide_call): checked and uploaded once, each launch() is one ctypes
+    call that only enqueues work.  Keeps references to the tensors and the layout so that their
+    memory outlives the call."""
 
-    def __init__(self, fn, where: str, args, keep):
-        self._fn = fn
-        self._where = where
-        self._args = args
+    def __init__(self, handle: int, keep):
+        self._lib = load_library()
+        self.handle = handle
         self._keep = keep
 
     def launch(self, stream=None):
-        _check(self._fn(*self._args, _stream_handle(stream)), self._where)
+        _check(self._lib.tide_call_launch(self.handle, _stream_handle(stream)), "tide_call_launch")
+
+    def close(self):
+        """Free the call.  Streams that launched it must have been synchronised."""
+        if getattr(self, "handle", None):
+            self._lib.tide_call_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _is_tensor(x) -> bool:

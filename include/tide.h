@@ -197,6 +197,48 @@ tide_status tide_slot_pack(const tide_layout* layout, const void* const* grads, 
 tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* slots,
                                        float* const* shards, int32_t cu_budget, void* stream);
 
+/*
+ * Prepared calls.  A training step issues the same collectives on the same buffers every step
+ * (FSDP2 keeps its gradient, shard and stage buffers for the whole run), so the argument checks
+ * and the device table of buffer addresses can be done once.  tide_*_prepare takes exactly the
+ * arguments of the immediate call of the same name (minus the stream), applies the same checks,
+ * and uploads a device table of the buffer addresses that the call owns; tide_call_launch then
+ * enqueues the work on a stream with the result the immediate call would have given.
+ *   - For the kernel paths (RS, RS from slots, slot packing, TIDE_AG_KERNEL placement),
+ *     tide_call_launch only launches kernels: no allocation, no copy, no event, no check beyond
+ *     the current device.  Such launches may be captured into a HIP graph and the graph replayed;
+ *     each replay recomputes the result from the buffers' current contents.
+ *   - TIDE_AG_COPY2D and TIDE_AG_SDMA calls enqueue runtime copies as the immediate call does
+ *     (TIDE_AG_SDMA through the layout's internal copy streams).
+ *   - The buffers named at prepare time must stay allocated while the call may launch; their
+ *     contents may change freely between launches.  The layout must outlive its calls.
+ *   - A call may be launched from several threads and streams at once (it is immutable); launches
+ *     whose outputs overlap race, as immediate calls do.
+ *   - The call belongs to the device that was current at prepare time; tide_call_launch returns
+ *     TIDE_ERR_INVALID on any other device.
+ * Errors of tide_*_prepare: those of the immediate call, plus TIDE_ERR_INVALID for a NULL `out`;
+ * `*out` is set only on TIDE_OK.  Errors of tide_call_launch: TIDE_ERR_INVALID (NULL call, wrong
+ * device), TIDE_ERR_UNSUPPORTED, TIDE_ERR_HIP.
+ */
+typedef struct tide_call tide_call;
+
+tide_status tide_rs_prepare(const tide_layout* layout, int32_t C, const void* const* grads, float* const* shards,
+                            int32_t cu_budget, tide_call** out);
+tide_status tide_ag_prepare(const tide_layout* layout, const void* stage, void* const* params, int32_t mode,
+                            int32_t cu_budget, tide_call** out);
+tide_status tide_slot_pack_prepare(const tide_layout* layout, const void* const* grads, void* slot,
+                                   int32_t cu_budget, tide_call** out);
+tide_status tide_rs_slots_prepare(const tide_layout* layout, int32_t C, const void* const* slots,
+                                  float* const* shards, int32_t cu_budget, tide_call** out);
+
+/* Enqueue a prepared call on `stream` (hipStream_t as void*). */
+tide_status tide_call_launch(const tide_call* call, void* stream);
+
+/* Free a prepared call (its device table, on the call's device).  Every stream that launched it
+ * must have been synchronised, and no graph holding its launches may be replayed afterwards.
+ * NULL is ignored. */
+void tide_call_destroy(tide_call* call);
+
 /* Static, NUL-terminated name of a status code ("TIDE_OK", ...; "unknown" otherwise). */
 const char* tide_status_str(int32_t status);
 

@@ -119,6 +119,19 @@ int main() {
   float* sh2[4];
   for (int r = 0; r < 4; ++r) sh2[r] = reinterpret_cast<float*>(base + (uintptr_t(1) << 20) * (r + 1));
   CHECK(tide_rs_slots_bf16_to_fp32(L, 2, sl, sh2, 0, nullptr) == TIDE_ERR_INVALID);  // odd slot address
+  // prepared calls apply the same checks, and leave *out untouched
+  tide_call* call = nullptr;
+  CHECK(tide_rs_prepare(L, 1, g, sh, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_rs_prepare(L, 0, g, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_rs_prepare(L, 1, g, sh2, -1, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, 0, &call) == TIDE_ERR_INVALID);
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, 7, 0, &call) == TIDE_ERR_INVALID);
+  CHECK(tide_slot_pack_prepare(L, const_cast<const void* const*>(pp), reinterpret_cast<void*>(base), 0, &call) ==
+        TIDE_ERR_INVALID);
+  CHECK(tide_rs_slots_prepare(L, 2, sl, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_rs_prepare(L, 1, g, sh2, 0, nullptr) == TIDE_ERR_INVALID);  // no output handle
+  CHECK(tide_call_launch(nullptr, nullptr) == TIDE_ERR_INVALID);
+  tide_call_destroy(nullptr);
   CHECK(tide_last_hip_error() == 0);
   tide_layout_destroy(L);
   tide_layout_destroy(nullptr);

@@ -1,0 +1,291 @@
+"""GPU parity of prepared calls (tide_*_prepare + tide_call_launch) and of their HIP-graph replays.
+
+A prepared call is checked once and owns a device table of its buffers' addresses; launching it
+must give bit for bit what the immediate call gives, and what the oracle gives, on whatever the
+buffers hold at launch time.  The kernel paths are captured into a HIP graph on a side stream and
+the graph is replayed several times, with new inputs written by eager work and host
+synchronisations between the replays; every replay is checked against the oracle and against the
+immediate calls.
+"""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import geometry as ogeo
+from oracle import rs as ors
+from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError
+from workloads import CONFIGS, normal_bf16_bits, normal_bf16_cuda
+from tests.test_gpu_parity import (GROUPS, POISON_BF16, POISON_F32, assert_rs_equal, dev_bf16, host_bits_bf16,
+                                   host_bits_f32, poisoned_shards, say, _locate_many, _sample_positions)
+
+pytestmark = pytest.mark.gpu
+
+MODES = [(TIDE_AG_KERNEL, "kernel"), (TIDE_AG_SDMA, "sdma"), (TIDE_AG_COPY2D, "copy2d")]
+
+
+def poison_(tensors, pattern, dtype):
+    for t in tensors:
+        t.view(dtype).fill_(pattern)
+
+
+def poisoned_params(shapes):
+    return [torch.full(s, POISON_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16) for s in shapes]
+
+
+def poisoned_slot(R, S):
+    return torch.full((R * S,), POISON_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def shards_bits(shards):
+    return np.stack([host_bits_f32(s) for s in shards])
+
+
+@pytest.mark.parametrize("case", range(len(GROUPS)))
+def test_prepared_calls_bit_exact(gpu_available, case):
+    shapes, R, C = GROUPS[case]
+    say(f"prepared calls, group {case}: shapes={shapes} R={R} C={C}")
+    geo, S = ogeo.group_geometry(shapes, R)
+    g = [[normal_bf16_bits(s, 1.0, 110 + case, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    stage_bits = normal_bf16_bits((R * S,), 1.0, 120 + case, 0)
+    want_rs = oracle.reduce_scatter(g, shapes, R)
+    want_ag = oracle.all_gather_place(stage_bits, shapes, R)
+    want_pack = oracle.pack_slot(g[0], shapes, R)
+    grads = [[dev_bf16(x) for x in row] for row in g]
+    stage = dev_bf16(stage_bits)
+    with Layout(shapes, R) as L:
+        for budget in (0, 3):
+            shards = poisoned_shards(R, S)
+            call = L.bind_rs(grads, shards, cu_budget=budget)
+            for _ in range(2):  # a launch rewrites every element: the second must change nothing
+                call.launch()
+                torch.cuda.synchronize()
+                assert_rs_equal(shards_bits(shards), want_rs)
+            call.close()
+        for mode, name in MODES:
+            params = poisoned_params(shapes)
+            call = L.bind_ag(stage, params, mode=mode)
+            call.launch()
+            torch.cuda.synchronize()
+            for a, b in zip([host_bits_bf16(q) for q in params], want_ag):
+                assert np.array_equal(a, b), name
+        slots = [poisoned_slot(R, S) for _ in range(C)]
+        packs = [L.bind_slot_pack(grads[c], slots[c], cu_budget=3) for c in range(C)]
+        for p in packs:
+            p.launch()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits_bf16(slots[0]), want_pack)
+        shards = poisoned_shards(R, S)
+        L.bind_rs_slots(slots, shards).launch()
+        torch.cuda.synchronize()
+        assert_rs_equal(shards_bits(shards), want_rs)
+
+
+def test_prepared_call_reads_current_contents(gpu_available):
+    """The call holds addresses, not values: new gradient values give the new sum."""
+    shapes, R, C = GROUPS[1]
+    say("prepared call after the inputs changed")
+    geo, S = ogeo.group_geometry(shapes, R)
+    with Layout(shapes, R) as L:
+        grads = [[torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes] for _ in range(C)]
+        shards = poisoned_shards(R, S)
+        call = L.bind_rs(grads, shards)
+        for it in range(3):
+            g = [[normal_bf16_bits(s, 1.0, 130, it, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+            for c in range(C):
+                for p in range(len(shapes)):
+                    grads[c][p].copy_(dev_bf16(g[c][p]))
+            call.launch()
+            torch.cuda.synchronize()
+            assert_rs_equal(shards_bits(shards), oracle.reduce_scatter(g, shapes, R))
+
+
+def test_prepare_rejects_what_the_immediate_call_rejects(gpu_available):
+    shapes, R = [(64, 8), (33,)], 4
+    say("prepare argument checks")
+    geo, S = ogeo.group_geometry(shapes, R)
+    with Layout(shapes, R) as L:
+        grads = [[torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]]
+        shards = poisoned_shards(R, S)
+        bad = list(shards)
+        bad[1] = bad[0]  # two ranks writing one shard
+        with pytest.raises(TideError, match="INVALID"):
+            L.bind_rs(grads, bad)
+        with pytest.raises(TideError, match="INVALID"):
+            L.bind_rs(grads, shards, cu_budget=-1)
+        stage = torch.zeros(R * S, dtype=torch.bfloat16, device="cuda")
+        params = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+        with pytest.raises(TideError, match="INVALID"):
+            L.bind_ag(stage, [params[0], params[0].view(-1)[: shapes[1][0]]])  # parameters overlap
+        with pytest.raises(TideError, match="INVALID"):
+            L.bind_ag(stage, params, mode=9)
+
+
+def _capture(calls, stream):
+    for c in calls:  # one eager launch first, so nothing is loaded for the first time under capture
+        c.launch(stream)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c.launch(stream)
+    return g
+
+
+@pytest.mark.parametrize("budget", [0, 3])
+def test_graph_replay_kernel_paths(gpu_available, budget):
+    """RS, AG placement (kernel), Slot-Reuse pack + RS from slots, captured once, replayed 4 times."""
+    shapes, R, C = GROUPS[1]
+    say(f"graph capture and replay, budget={budget}")
+    geo, S = ogeo.group_geometry(shapes, R)
+    with Layout(shapes, R) as L:
+        grads = [[torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes] for _ in range(C)]
+        stage = torch.empty(R * S, dtype=torch.bfloat16, device="cuda")
+        shards = poisoned_shards(R, S)
+        shards2 = poisoned_shards(R, S)
+        params = poisoned_params(shapes)
+        slots = [poisoned_slot(R, S) for _ in range(C)]
+        calls = [L.bind_rs(grads, shards, cu_budget=budget), L.bind_ag(stage, params, cu_budget=budget)]
+        calls += [L.bind_slot_pack(grads[c], slots[c], cu_budget=budget) for c in range(C)]
+        calls.append(L.bind_rs_slots(slots, shards2, cu_budget=budget))
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        graph = _capture(calls, side)
+        torch.cuda.synchronize()
+        for it in range(4):
+            g = [[normal_bf16_bits(s, 1.0, 140, it, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+            st = normal_bf16_bits((R * S,), 1.0, 141, it)
+            for c in range(C):
+                for p in range(len(shapes)):
+                    grads[c][p].copy_(dev_bf16(g[c][p]))
+            stage.copy_(dev_bf16(st))
+            poison_(shards + shards2, POISON_F32, torch.int32)
+            poison_(params + slots, POISON_BF16, torch.int16)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            want = oracle.reduce_scatter(g, shapes, R)
+            assert_rs_equal(shards_bits(shards), want)
+            assert_rs_equal(shards_bits(shards2), want)
+            for a, b in zip([host_bits_bf16(q) for q in params], oracle.all_gather_place(st, shapes, R)):
+                assert np.array_equal(a, b), f"replay {it}"
+            for c in range(C):
+                assert np.array_equal(host_bits_bf16(slots[c]), oracle.pack_slot(g[c], shapes, R)), f"replay {it}"
+            # eager immediate calls on the same inputs agree with the replay
+            eager = poisoned_shards(R, S)
+            L.rs_bf16_to_fp32(grads, eager, cu_budget=budget)
+            torch.cuda.synchronize()
+            assert np.array_equal(shards_bits(eager), shards_bits(shards))
+        del graph
+        torch.cuda.synchronize()
+        for c in calls:
+            c.close()
+
+
+def test_graph_replay_full_size_step(gpu_available):
+    """The Llama-3.1-8B layer group's step (RS from 8 contributors + AG placement) as a graph: each
+    replay must equal the immediate calls bit for bit; inputs change between replays."""
+    cfg = CONFIGS["llama3_1_8b_layer"]
+    say(f"graph replay full size {cfg.name}")
+    torch.cuda.empty_cache()
+    geo, S = ogeo.group_geometry(cfg.shapes, cfg.R)
+    with Layout(cfg.shapes, cfg.R) as L:
+        grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
+                 for c in range(cfg.C)]
+        stage = normal_bf16_cuda((cfg.R * S,), 1.0, cfg.cfg_id, 1 << 20)
+        shards = [torch.empty(S, dtype=torch.float32, device="cuda") for _ in range(cfg.R)]
+        params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in cfg.shapes]
+        rs = L.bind_rs(grads, shards, cu_budget=512)
+        ag = L.bind_ag(stage, params, cu_budget=512)
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        graph = _capture([rs, ag], side)
+        torch.cuda.synchronize()
+        ref_shards = [torch.empty_like(x) for x in shards]
+        ref_params = [torch.empty_like(x) for x in params]
+        for it in range(3):
+            if it:
+                for c in range(cfg.C):  # new gradients: scale every contributor's first parameter
+                    grads[c][0].mul_(-0.5 if (c + it) % 2 else 2.0)
+                stage.neg_()
+            poison_(shards, POISON_F32, torch.int32)
+            poison_(params, POISON_BF16, torch.int16)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            L.rs_bf16_to_fp32(grads, ref_shards, cu_budget=0)
+            L.ag_place(stage, ref_params)
+            torch.cuda.synchronize()
+            for a, b in zip(shards, ref_shards):
+                assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"replay {it}"
+            for a, b in zip(params, ref_params):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {it}"
+        # sampled outputs of the last replay against the oracle, computed one by one
+        rng = np.random.default_rng(cfg.cfg_id + 7)
+        rs_, ks = _sample_positions(geo, S, cfg.R, 4000, rng)
+        p_idx, src = _locate_many(geo, cfg.R, rs_, ks)
+        got = np.empty(len(rs_), dtype=np.uint32)
+        for r in range(cfg.R):
+            sel = np.nonzero(rs_ == r)[0]
+            if sel.size:
+                got[sel] = host_bits_f32(shards[r][torch.from_numpy(ks[sel]).cuda()])
+        vals = np.zeros((cfg.C, len(rs_)), dtype=np.uint16)
+        for p in np.unique(p_idx):
+            sel = np.nonzero((p_idx == p) & (src >= 0))[0]
+            if sel.size:
+                idx = torch.from_numpy(src[sel]).cuda()
+                for c in range(cfg.C):
+                    vals[c, sel] = host_bits_bf16(grads[c][p].reshape(-1)[idx])
+        want = np.where(src >= 0, ors.rs_sampled(vals).view(np.uint32), 0).astype(np.uint32)
+        assert np.array_equal(got, want), f"{int((got != want).sum())} sampled mismatches"
+        del graph
+        torch.cuda.synchronize()
+        rs.close()
+        ag.close()
+
+
+def test_prepared_calls_from_threads(gpu_available):
+    """One layout, four host threads, each with its own stream, buffers and prepared calls."""
+    shapes, R, C = GROUPS[6]
+    say("prepared calls from 4 threads")
+    geo, S = ogeo.group_geometry(shapes, R)
+    nthreads, iters = 4, 5
+    errors = []
+    with Layout(shapes, R) as L:
+        work = []
+        for t in range(nthreads):
+            g = [[normal_bf16_bits(s, 1.0, 150, t, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+            st = normal_bf16_bits((R * S,), 1.0, 151, t)
+            work.append(dict(g=g, st=st, grads=[[dev_bf16(x) for x in row] for row in g], stage=dev_bf16(st),
+                             shards=poisoned_shards(R, S), params=poisoned_params(shapes),
+                             stream=torch.cuda.Stream()))
+        torch.cuda.synchronize()
+
+        def run(w):
+            try:
+                with torch.cuda.stream(w["stream"]):
+                    rs = L.bind_rs(w["grads"], w["shards"], cu_budget=7)
+                    ag = L.bind_ag(w["stage"], w["params"])
+                    for _ in range(iters):
+                        rs.launch(w["stream"])
+                        ag.launch(w["stream"])
+                        L.rs_bf16_to_fp32(w["grads"], w["shards"], stream=w["stream"])
+                    w["stream"].synchronize()
+                    rs.close()
+                    ag.close()
+            except Exception as e:  # reported by the main thread
+                errors.append(e)
+
+        threads = [threading.Thread(target=run, args=(w,)) for w in work]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        torch.cuda.synchronize()
+        assert not errors, errors
+        for w in work:
+            assert_rs_equal(shards_bits(w["shards"]), oracle.reduce_scatter(w["g"], shapes, R))
+            for a, b in zip([host_bits_bf16(q) for q in w["params"]], oracle.all_gather_place(w["st"], shapes, R)):
+                assert np.array_equal(a, b)
