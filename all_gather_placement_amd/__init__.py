@@ -19,6 +19,7 @@ from .tide import (  # noqa: F401
     tide_call_launch,
     tide_layout_create,
     tide_rs_bf16_to_fp32,
+    tide_rs_launch_shape,
     tide_rs_prepare,
     tide_rs_slots_bf16_to_fp32,
     tide_rs_slots_prepare,

@@ -271,16 +271,19 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
   if (q.kind == kRs || q.kind == kRsSlots) {
     const int64_t count = int64_t(L->rs_chunks.size());
     const bool flat = q.kind == kRsSlots;
-    const Plan plan = plan_for(count, q.cu_budget, q.cu_budget, kRsBoundedItems);
+    const int64_t rs_wgs = int64_t(q.cu_budget) * kBudgetThreads / kThreads;
+    const Plan plan = plan_for(count, q.cu_budget, rs_wgs, kRsBoundedItems);
+    // Unbounded launches cap the RS workgroups per CU; bounded ones are capped by the budget.
+    const int lds = q.cu_budget == 0 ? st->rs_dyn_lds : 0;
     for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
       const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
       e = launch_rs(st->rs, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, tbl, flat ? 1 : L->P, q.C,
-                    L->S, flat, q.vec, hs);
+                    L->S, flat, q.vec, lds, hs);
     }
     return e;
   }
   const int64_t count = int64_t(L->ag_chunks.size());
-  const int64_t ag_wgs = int64_t(q.cu_budget) * kThreads / kAgThreads;
+  const int64_t ag_wgs = int64_t(q.cu_budget) * kBudgetThreads / kAgThreads;
   const Plan plan = plan_for(count, q.cu_budget, ag_wgs, kAgBoundedItems);
   for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
     const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
@@ -505,6 +508,18 @@ tide_status tide_call_launch(const tide_call* call, void* stream) {
   if (!tide::needs_kernels(call->layout, q)) return TIDE_OK;
   e = tide::enqueue_kernels(call->layout, call->st, q, call->dev_table, hs);
   return e == hipSuccess ? TIDE_OK : tide::hip_fail(e);
+}
+
+tide_status tide_rs_launch_shape(int32_t* threads, int32_t* item_outputs, int32_t* lds_bytes) {
+  if (threads == nullptr || item_outputs == nullptr || lds_bytes == nullptr) return TIDE_ERR_INVALID;
+  int dev = 0, dyn = 0, total = 0;
+  int e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = tide::rs_occupancy_lds(dev, &dyn, &total);
+  if (e != hipSuccess) return tide::hip_fail(e);
+  *threads = tide::kThreads;
+  *item_outputs = int32_t(tide::kRsChunk);
+  *lds_bytes = total;
+  return TIDE_OK;
 }
 
 void tide_call_destroy(tide_call* call) {

@@ -7,13 +7,15 @@
 // has exactly one writer, and every workgroup is short-lived (one work item, then exit).
 //
 // RS ([Endgame] Figure 6a, node-local fp32 sums; abstract, bf16 gradients reduced into fp32
-// shards): outputs are handled in groups of 4.  For a group, a thread loads 8 bytes (4 bf16) from
-// each contributor, widens them exactly to fp32, adds them in ascending contributor order (C-1
-// IEEE binary32 adds per output) and writes 16 bytes.  Consecutive lanes take consecutive groups,
-// so each load instruction of a wave covers 512 contiguous bytes and each store instruction 1 KiB
-// of whole cache lines.  At C = 8 an output costs 20 bytes of HBM traffic and 7 adds: the kernel
-// is HBM-bound by two orders of magnitude, so it is shaped for bytes in flight and clean traffic,
-// not arithmetic (no matrix cores: nothing here is a contraction).
+// shards): every output is the sum of its C contributors' bf16 inputs, each widened exactly to
+// fp32 and added in ascending contributor order (C-1 IEEE binary32 adds).  On a full, aligned work
+// item a lane loads one 16-byte vector (8 bf16) per contributor, so each wave load instruction
+// covers 1 KiB of one contributor; the 8 fp32 sums per lane are exchanged through LDS so that each
+// wave store instruction covers 1 KiB of whole cache lines.  Partial items (segment heads and
+// tails) take 4-output lane groups (8-byte loads, 16-byte stores).  At C = 8 an output costs
+// 20 bytes of HBM traffic and 7 adds: the kernel is HBM-bound by two orders of magnitude, so it
+// is shaped for bytes in flight and clean traffic, not arithmetic (no matrix cores: nothing here
+// is a contraction).
 //
 // AG ([Endgame] Figure 5b, one strided copy per parameter; Table 7, direct landing): a bit copy
 // of each rank's valid rows from the rank-major stage into the parameter's storage, 16 bytes per
@@ -326,40 +328,63 @@ __global__ __launch_bounds__(kAgThreads) void fill_zero_kernel(const AgChunk* __
 
 template <int CT, bool FLAT>
 hipError_t launch_rs_ct(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items,
-                        void* const* ptrs, int32_t P, int32_t C, int64_t S, bool vec, hipStream_t s) {
+                        void* const* ptrs, int32_t P, int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
   if (vec)
-    hipLaunchKernelGGL((rs_kernel<CT, true, FLAT>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items,
+    hipLaunchKernelGGL((rs_kernel<CT, true, FLAT>), dim3(grid), dim3(kThreads), lds, s, chunks, first, count, items,
                        ptrs, P, C, S);
   else
-    hipLaunchKernelGGL((rs_kernel<CT, false, FLAT>), dim3(grid), dim3(kThreads), 0, s, chunks, first, count, items,
+    hipLaunchKernelGGL((rs_kernel<CT, false, FLAT>), dim3(grid), dim3(kThreads), lds, s, chunks, first, count, items,
                        ptrs, P, C, S);
   return hipGetLastError();
 }
 
 template <bool FLAT>
 hipError_t launch_rs_c(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items, void* const* ptrs,
-                       int32_t P, int32_t C, int64_t S, bool vec, hipStream_t s) {
+                       int32_t P, int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
   switch (C) {
-    case 1: return launch_rs_ct<1, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
-    case 2: return launch_rs_ct<2, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
-    case 3: return launch_rs_ct<3, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
-    case 4: return launch_rs_ct<4, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
-    case 5: return launch_rs_ct<5, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
-    case 6: return launch_rs_ct<6, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
-    case 7: return launch_rs_ct<7, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
-    case 8: return launch_rs_ct<8, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
-    default: return launch_rs_ct<0, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, s);
+    case 1: return launch_rs_ct<1, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 2: return launch_rs_ct<2, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 3: return launch_rs_ct<3, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 4: return launch_rs_ct<4, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 5: return launch_rs_ct<5, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 6: return launch_rs_ct<6, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 7: return launch_rs_ct<7, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 8: return launch_rs_ct<8, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    default: return launch_rs_ct<0, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
   }
 }
 
 }  // namespace
 
 int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,
-              const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, void* hip_stream) {
+              const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, int dyn_lds,
+              void* hip_stream) {
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   void* const* ptrs = const_cast<void* const*>(dev_ptrs);
-  if (flat) return launch_rs_c<true>(chunks, first, count, grid, items_per_wg, ptrs, 1, C, S, vec, s);
-  return launch_rs_c<false>(chunks, first, count, grid, items_per_wg, ptrs, P, C, S, vec, s);
+  if (flat) return launch_rs_c<true>(chunks, first, count, grid, items_per_wg, ptrs, 1, C, S, vec, dyn_lds, s);
+  return launch_rs_c<false>(chunks, first, count, grid, items_per_wg, ptrs, P, C, S, vec, dyn_lds, s);
+}
+
+int rs_occupancy_lds(int device, int* dyn_lds, int* total_lds) {
+  *dyn_lds = 0;
+  hipFuncAttributes attr;
+  hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&rs_kernel<8, true, false>));
+  if (e != hipSuccess) return e;
+  *total_lds = static_cast<int>(attr.sharedSizeBytes);
+  if (kRsWgsPerCu <= 0) return hipSuccess;
+  int lds_per_cu = 0;
+  e = hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device);
+  if (e != hipSuccess) return e;
+  // The full-item path's exchange buffer is the kernel's only static LDS.  Each workgroup's total
+  // is rounded down to 512 bytes, so kRsWgsPerCu of them fit in a CU (and, for counts up to 16,
+  // one more does not).
+  const int per_wg = (lds_per_cu / kRsWgsPerCu) / 512 * 512;
+  const int dyn = per_wg - static_cast<int>(attr.sharedSizeBytes);
+  if (dyn > 0) {
+    *dyn_lds = dyn;
+    *total_lds = per_wg;
+  }
+  return hipSuccess;
 }
 
 int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, void* stage,

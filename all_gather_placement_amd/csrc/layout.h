@@ -48,6 +48,7 @@ struct DeviceState {
   hipStream_t dma[kDmaStreams] = {};
   hipEvent_t dma_fork = nullptr;
   hipEvent_t dma_join[kDmaStreams] = {};
+  int rs_dyn_lds = 0;  // dynamic LDS of unbounded RS launches (occupancy cap, rs_occupancy_lds)
 };
 
 }  // namespace tide

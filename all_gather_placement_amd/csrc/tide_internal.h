@@ -10,24 +10,32 @@ namespace tide {
 // Kernel shape.  The defaults were chosen by measurement on MI355X (HBM GB/s over the Llama-3.1
 // 8B/70B, Qwen3-30B-A3B and Wan2.2 layer groups); each can be overridden at build time.
 //
-// RS: 256 threads (4 wave64 waves, one per SIMD of a CDNA4 CU) per workgroup; one work item is
-// 2048 outputs, i.e. exactly TIDE_RS_NQ = 2 four-output groups per thread, issued together.  A
-// workgroup moves 2048 * (2C + 4) bytes (40 KiB at C = 8) and exits.
+// RS: 128 threads (2 wave64 waves) per workgroup; one work item is 1024 outputs, i.e. 8 per
+// thread: one 16-byte load per contributor per lane on full items.  A workgroup moves
+// 1024 * (2C + 4) bytes (20 KiB at C = 8) and exits.
 // AG: 128 threads per workgroup; one work item is 2048 bf16 elements (8 KiB moved), i.e. one or
 // two 16-byte vectors per thread.
 // Short-lived workgroups of this size streamed HBM faster than larger items (4K-64K elements),
 // more groups in flight per thread, or a persistent grid.
 #ifndef TIDE_THREADS
-#define TIDE_THREADS 256
+#define TIDE_THREADS 128
 #endif
 #ifndef TIDE_AG_THREADS
 #define TIDE_AG_THREADS 128
 #endif
 #ifndef TIDE_RS_CHUNK
-#define TIDE_RS_CHUNK 2048
+#define TIDE_RS_CHUNK 1024
 #endif
 #ifndef TIDE_AG_CHUNK
 #define TIDE_AG_CHUNK 2048
+#endif
+// RS occupancy cap of unbounded launches (cu_budget 0): at most this many RS workgroups per CU,
+// enforced by the local-memory size each launch requests (the CU's LDS divided by this count).
+// Fewer loads in flight stream HBM better than a full CU: with 128-thread workgroups, 6 per CU
+// (12 waves, ~96 KiB of loads in flight per CU at C = 8) beat 4, 5, 7, 8 and the uncapped 16 by
+// 2-5% on all four layer groups; 0 = no cap.
+#ifndef TIDE_RS_WGS_PER_CU
+#define TIDE_RS_WGS_PER_CU 6
 #endif
 #ifndef TIDE_RS_NQ
 #define TIDE_RS_NQ 2
@@ -92,6 +100,11 @@ constexpr int64_t kXcds = 8;
 
 constexpr int kThreads = TIDE_THREADS;
 constexpr int kAgThreads = TIDE_AG_THREADS;
+// Unit of cu_budget: B admits B * kBudgetThreads threads of resident communication workgroups.
+constexpr int kBudgetThreads = 256;
+constexpr int kRsWgsPerCu = TIDE_RS_WGS_PER_CU;
+static_assert(kBudgetThreads % kThreads == 0 && kBudgetThreads % TIDE_AG_THREADS == 0,
+              "a budget slot holds whole workgroups");
 constexpr int64_t kRsChunk = TIDE_RS_CHUNK;
 constexpr int64_t kAgChunk = TIDE_AG_CHUNK;
 constexpr int64_t kPersistentWorkgroups = TIDE_PERSISTENT_WGS;
@@ -100,15 +113,14 @@ constexpr int64_t kPersistentWorkgroups = TIDE_PERSISTENT_WGS;
 static_assert(kRsChunk % 8 == 0 && kAgChunk % 8 == 0, "work items must be whole 16-byte vectors");
 static_assert(kRsChunk < (int64_t(1) << 31) && kAgChunk < (int64_t(1) << 31), "item sizes are int32");
 
-// Bounded launches (cu_budget B > 0): at most B RS workgroups (B * kThreads / kAgThreads AG
-// workgroups, the same number of threads) are resident; each takes this many work items and exits,
-// and the call issues as many launches as it needs.  0 = a single launch whose B workgroups walk
-// all items (resident for the whole call).
+// Bounded launches (cu_budget B > 0): at most B * kBudgetThreads threads of RS (or AG) workgroups
+// are resident; each workgroup takes this many work items and exits, and the call issues as many
+// launches as it needs.  0 = a single launch whose workgroups walk all items (resident for the
+// whole call).
 // Measured on MI355X against a concurrent one-wave bf16 GEMM (hipBLASLt, one 256x256 tile per
 // CU): the GEMM's waves cannot share a SIMD with a resident RS wave, so a GEMM workgroup waits
 // until the RS workgroups on its CU exit.  Workgroups that live for the whole call (0) slowed the
-// GEMM ~7x even at B = 256; 64 items 0.5-2.5x; 16 items 4-27%; 4 items (a launch of B = 512 lasts
-// ~17 us) 4-8%.  Short-lived it is.
+// GEMM ~7x even at B = 256; 64 items 0.5-2.5x; 16 items 4-27%; 4 items 4-8%.  Short-lived it is.
 #ifndef TIDE_RS_BOUNDED_ITEMS
 #define TIDE_RS_BOUNDED_ITEMS 4
 #endif
@@ -145,8 +157,14 @@ static_assert(sizeof(AgChunk) == 32, "AgChunk is two 16-byte scalar loads");
 // reads C packed slots of R*S elements (table [C slots][R shards]).
 // launch_ag: pack = false places stage -> parameters; pack = true packs parameters -> stage slot.
 // launch_fill_zero: zeros the slot ranges of `items` (src = slot element offset, n).
+// `dyn_lds` is the dynamic local memory each RS workgroup requests (occupancy cap; 0 = none).
+// rs_occupancy_lds: the dyn_lds that admits at most kRsWgsPerCu RS workgroups per CU of `device`
+// (0 when the cap is off or the device reports no usable LDS size), and the total (static +
+// dynamic) LDS each such workgroup holds.
 int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,
-              const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, void* hip_stream);
+              const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, int dyn_lds,
+              void* hip_stream);
+int rs_occupancy_lds(int device, int* dyn_lds, int* total_lds);
 int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, void* stage,
               const void* const* dev_params, bool pack, bool vec, void* hip_stream);
 int launch_fill_zero(const AgChunk* items, int64_t count, void* slot, void* hip_stream);

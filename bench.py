@@ -9,6 +9,8 @@ in-place reduce-scatter (C bf16 contributors -> R fp32 shards) followed by the a
   value       effective HBM GB/s of the step: algorithmic bytes of RS and AG / step time;
   roofline    the RS kernel (the dominant one): algorithmic bytes per launch / its mean duration,
               measured with HIP events on the launch stream, against the 8 TB/s HBM peak;
+  calibration a runtime device-to-device copy moving the RS's bytes, timed in the same run (the
+              rate a plain stream reaches on this device), and the RS's ratio to it;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload (same byte formula).
 
 Algorithmic bytes: RS = 2*C*numel (bf16 reads) + 4*R*S (fp32 writes, padding included);
@@ -564,7 +566,7 @@ def main():
 
     import torch
 
-    from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
+    from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, tide_rs_launch_shape
     from oracle.geometry import group_geometry  # sizes only, for the byte formulas
     from workloads import CONFIGS, normal_bf16_cuda
 
@@ -665,6 +667,24 @@ def main():
     host_unbound = host_us(lambda: L.rs_bf16_to_fp32(grads, shards, cu_budget=args.cu_budget, stream=stream))
     torch.cuda.synchronize()
 
+    # Same-run calibration: a runtime device-to-device copy moving the RS's bytes (half read, half
+    # written), the practical ceiling a plain stream reaches on this device; median of 10.
+    cal_src = torch.empty(rs_bytes // 2, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_ms = []
+    for i in range(13):
+        a, b = ev(), ev()
+        a.record(stream)
+        cal_dst.copy_(cal_src)
+        b.record(stream)
+        b.synchronize()
+        if i >= 3:
+            cal_ms.append(a.elapsed_time(b))
+    cal_med = sorted(cal_ms)[len(cal_ms) // 2]
+    cal_gbps = 2 * cal_src.numel() / (cal_med * 1e-3) / 1e9
+    del cal_src, cal_dst
+    log(f"device-to-device copy of the same bytes: {cal_gbps:.0f} GB/s (median {cal_med:.4f} ms)")
+
     value = (rs_bytes + ag_bytes) / (ms_per_step * 1e-3) / 1e9
     rs_gbps = rs_bytes / (rs_mean * 1e-3) / 1e9
     ag_gbps = ag_bytes / (ag_mean * 1e-3) / 1e9
@@ -697,6 +717,9 @@ def main():
         "ag_frac_of_peak": round(ag_gbps / HBM_PEAK_GBPS, 4),
         "ag_ms_mean": round(ag_mean, 5),
         "rs_host_us_per_call": {"bound": round(host_bound, 1), "validate_and_marshal": round(host_unbound, 1)},
+        "rs_launch_shape": tide_rs_launch_shape(),
+        "calibration": {"d2d_copy_gbps": round(cal_gbps, 2), "bytes_moved": 2 * (rs_bytes // 2),
+                        "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
         "roofline": {
             "bound": "hbm",
             "kernel": "rs_kernel<8, true, false>",

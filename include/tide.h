@@ -129,11 +129,13 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              row-major bf16 device tensor of rows_p * L_p elements, 2-byte aligned (NULL allowed
  *              only for empty parameters).  Read in place, never written.
  *   shards     host [R]: shards[r] is rank r's flat fp32 device shard of S elements, 4-byte aligned.
- *   cu_budget  0: one launch, one short-lived workgroup per work item, as wide as the device runs.
- *              B > 0: at most B workgroups of 256 threads resident at a time; each processes a
- *              bounded number of work items (4 by default, 160 KiB of traffic at C = 8) and
- *              exits, and the call issues as many launches as needed, so a concurrent kernel's
- *              workgroups find free CUs within one short launch.
+ *   cu_budget  0: one launch, one short-lived workgroup per work item, with at most 6 of them
+ *              resident per CU (each requests a sixth of the CU's local memory: fewer loads in
+ *              flight stream HBM better than a full CU).
+ *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of
+ *              128 threads); each processes a bounded number of work items (4 by default, 80 KiB
+ *              of traffic at C = 8) and exits, and the call issues as many launches as needed, so
+ *              a concurrent kernel's workgroups find free CUs within one short launch.
  *   stream     hipStream_t as void*.
  * Result, for every r, p and element k of the slice: shards[r][o_p + k] =
  *   x_0 (+) x_1 (+) ... (+) x_{C-1}, x_c = grads[c*P+p][r*m_p*L_p + k] widened exactly to fp32,
@@ -238,6 +240,12 @@ tide_status tide_call_launch(const tide_call* call, void* stream);
  * must have been synchronised, and no graph holding its launches may be replayed afterwards.
  * NULL is ignored. */
 void tide_call_destroy(tide_call* call);
+
+/* Launch shape of unbounded (cu_budget 0) RS calls on the current device: threads per workgroup,
+ * outputs per full work item, and the local memory (static + dynamic, bytes) each workgroup
+ * requests -- a CU holds as many RS workgroups as fit in its local memory, so this sets the
+ * occupancy cap.  Errors: TIDE_ERR_INVALID (a NULL pointer), TIDE_ERR_HIP. */
+tide_status tide_rs_launch_shape(int32_t* threads, int32_t* item_outputs, int32_t* lds_bytes);
 
 /* Static, NUL-terminated name of a status code ("TIDE_OK", ...; "unknown" otherwise). */
 const char* tide_status_str(int32_t status);

@@ -95,8 +95,20 @@ def test_layout_geometry_hypothesis(g):
     _check_geometry(shapes, R)
 
 
-def check_items_tile_exactly(shapes, R, rs_items, ag_items, rs_chunk=2048, ag_chunk=2048):
-    """Every shard element written once, every parameter element placed once, all in bounds."""
+def library_item_sizes():
+    """(RS, AG) work-item lengths of the built library, read from a layout of one 2^20-element
+    parameter on one rank: every item of an aligned segment is full."""
+    with tide.Layout([(1 << 20,)], 1) as L:
+        n_rs, n_ag = L.num_rs_chunks, L.num_ag_chunks
+    assert (1 << 20) % n_rs == 0 and (1 << 20) % n_ag == 0
+    return (1 << 20) // n_rs, (1 << 20) // n_ag
+
+
+def check_items_tile_exactly(shapes, R, rs_items, ag_items, rs_chunk=None, ag_chunk=None):
+    """Every shard element written once, every parameter element placed once, all in bounds;
+    inside a segment every item but the first and the last is a full one."""
+    if rs_chunk is None:
+        rs_chunk, ag_chunk = library_item_sizes()
     geo, S = ogeo.group_geometry(shapes, R)
     numel = [g.rows * g.L for g in geo]
     # --- RS: bounds
@@ -120,6 +132,9 @@ def check_items_tile_exactly(shapes, R, rs_items, ag_items, rs_chunk=2048, ag_ch
             assert np.all(src[sel] - r[sel] * g.m * g.L == dst[sel] - g.o)
             assert int(nv[sel].sum()) == v * g.L
             assert int(npad[(p == q) & (r == rr)].sum()) == (g.m - v) * g.L
+            inner = np.sort(src[sel])[1:-1]
+            assert np.all(nv[sel][np.argsort(src[sel])][1:-1] == rs_chunk), "interior items are full"
+            assert np.all((inner - (rr * g.m * g.L) // 8 * 8) % rs_chunk == 0)
     # interior item boundaries on 16-byte (8-element) source boundaries
     starts_inside = nz & (src % 8 != 0)
     for i in np.nonzero(starts_inside)[0]:

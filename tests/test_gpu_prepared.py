@@ -16,7 +16,8 @@ import torch
 import oracle
 from oracle import geometry as ogeo
 from oracle import rs as ors
-from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError
+from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError,
+                                      tide_rs_launch_shape)
 from workloads import CONFIGS, normal_bf16_bits, normal_bf16_cuda
 from tests.test_gpu_parity import (GROUPS, POISON_BF16, POISON_F32, assert_rs_equal, dev_bf16, host_bits_bf16,
                                    host_bits_f32, poisoned_shards, say, _locate_many, _sample_positions)
@@ -289,3 +290,13 @@ def test_prepared_calls_from_threads(gpu_available):
             assert_rs_equal(shards_bits(w["shards"]), oracle.reduce_scatter(w["g"], shapes, R))
             for a, b in zip([host_bits_bf16(q) for q in w["params"]], oracle.all_gather_place(w["st"], shapes, R)):
                 assert np.array_equal(a, b)
+
+
+def test_rs_launch_shape_caps_occupancy(gpu_available):
+    """Unbounded RS launches request a sixth of a gfx950 CU's 160 KiB of local memory per
+    128-thread workgroup, so at most 6 are resident per CU."""
+    shape = tide_rs_launch_shape()
+    say(f"RS launch shape {shape}")
+    assert shape["threads"] == 128 and shape["item_outputs"] == 1024
+    lds_per_cu = 160 * 1024
+    assert shape["lds_bytes"] * 6 <= lds_per_cu < shape["lds_bytes"] * 7
