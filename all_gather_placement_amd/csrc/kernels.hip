@@ -145,6 +145,57 @@ __device__ __forceinline__ float sum1_rt(const unsigned short* const* gptr, int3
   return acc;
 }
 
+// Full work item: kThreads * 8 valid outputs, 16-byte-aligned source and destination offsets
+// (so every lane takes whole 16-byte vectors), no padding.  Most items of a layer group are full.
+__device__ __forceinline__ bool full_item(const RsChunk& ch) {
+  return ch.nvalid == kThreads * 8 && ch.npad == 0 && (ch.src & 7) == 0 && (ch.dst & 3) == 0;
+}
+
+// Full item, step 1: one 16-byte load per contributor per lane, so each wave load instruction
+// covers 1 KiB of one contributor.  Raw buffer loads are bounded in hardware to the item's bytes.
+template <int CT>
+__device__ __forceinline__ void full_item_load(const unsigned short* const* src, int tid, u32x4 x[CT]) {
+#if TIDE_RS_LOAD_AUX >= 0
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(src[c]), 0, 16 * kThreads, 0x00020000);
+    x[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * tid, 0, TIDE_RS_LOAD_AUX));
+  }
+#else
+#pragma unroll
+  for (int c = 0; c < CT; ++c) x[c] = load_hbm(at_bytes<u32x4>(src[c], 16u * tid));
+#endif
+}
+
+// Full item, step 2: 8 sums per lane in ascending contributor order, then the fp32 results are
+// exchanged through LDS so that each 16-byte store instruction of a wave covers 1 KiB of whole
+// cache lines.  All threads of the workgroup call it (it synchronises the workgroup).
+template <int CT>
+__device__ __forceinline__ void full_item_finish(const u32x4 x[CT], float* dst, f32x4* xfer, int tid) {
+  float a[8];
+  a[0] = widen_lo(x[0].x); a[1] = widen_hi(x[0].x); a[2] = widen_lo(x[0].y); a[3] = widen_hi(x[0].y);
+  a[4] = widen_lo(x[0].z); a[5] = widen_hi(x[0].z); a[6] = widen_lo(x[0].w); a[7] = widen_hi(x[0].w);
+#pragma unroll
+  for (int c = 1; c < CT; ++c) {
+    a[0] += widen_lo(x[c].x); a[1] += widen_hi(x[c].x); a[2] += widen_lo(x[c].y); a[3] += widen_hi(x[c].y);
+    a[4] += widen_lo(x[c].z); a[5] += widen_hi(x[c].z); a[6] += widen_lo(x[c].w); a[7] += widen_hi(x[c].w);
+  }
+  __syncthreads();  // the previous item's readers are done with xfer
+  xfer[2 * tid] = f32x4{a[0], a[1], a[2], a[3]};
+  xfer[2 * tid + 1] = f32x4{a[4], a[5], a[6], a[7]};
+  __syncthreads();
+#if TIDE_RS_STORE_AUX >= 0
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, 32 * kThreads, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid]), rsrc, 16 * tid, 0, TIDE_RS_STORE_AUX);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid + kThreads]), rsrc, 16 * (tid + kThreads),
+                                         0, TIDE_RS_STORE_AUX);
+#else
+  store_hbm(at_bytes<f32x4>(dst, 16u * tid), xfer[tid]);
+  store_hbm(at_bytes<f32x4>(dst, 16u * (tid + kThreads)), xfer[tid + kThreads]);
+#endif
+}
+
 // RS kernel.  CT in 1..8: contributor count fixed at compile time; CT == 0: any C >= 1.
 // VEC: all source and shard base pointers are 16-byte aligned (checked on the host), so the
 // alignment of an element depends only on its offset inside its buffer.
@@ -161,6 +212,10 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
   const unsigned short* const* __restrict__ gptr = reinterpret_cast<const unsigned short* const*>(ptrs);
   float* const* __restrict__ sptr = reinterpret_cast<float* const*>(ptrs + static_cast<int64_t>(C) * P);
   const int nc = CT > 0 ? CT : C;
+
+#if TIDE_RS_WIDE
+  __shared__ f32x4 xfer[2 * kThreads];
+#endif
 
   for (int j = 0; j < items_per_wg; ++j) {
     const int64_t item = item_of<TIDE_RS_XCD_REMAP != 0>(j, count);
@@ -187,47 +242,10 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
 #pragma unroll
         for (int c = 0; c < CT; ++c) src[c] = gptr[static_cast<int64_t>(c) * P + ch.p] + ch.src;
 #if TIDE_RS_WIDE
-        // Full aligned item: one 16-byte load per contributor per lane (1 KiB contiguous per wave
-        // instruction), 8 sums per lane, then the fp32 results are redistributed through LDS so that
-        // each 16-byte store instruction of a wave covers 1 KiB of whole lines.
-        if (n == kThreads * 8 && head == 0 && dst16) {
-          __shared__ f32x4 xfer[2 * kThreads];
+        if (full_item(ch)) {
           u32x4 x[CT];
-#if TIDE_RS_LOAD_AUX >= 0
-#pragma unroll
-          for (int c = 0; c < CT; ++c) {
-            const __amdgpu_buffer_rsrc_t rsrc =
-                __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(src[c]), 0, 16 * kThreads, 0x00020000);
-            x[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * tid, 0, TIDE_RS_LOAD_AUX));
-          }
-#else
-#pragma unroll
-          for (int c = 0; c < CT; ++c) x[c] = load_hbm(at_bytes<u32x4>(src[c], 16u * tid));
-#endif
-          float a[8];
-          a[0] = widen_lo(x[0].x); a[1] = widen_hi(x[0].x); a[2] = widen_lo(x[0].y); a[3] = widen_hi(x[0].y);
-          a[4] = widen_lo(x[0].z); a[5] = widen_hi(x[0].z); a[6] = widen_lo(x[0].w); a[7] = widen_hi(x[0].w);
-#pragma unroll
-          for (int c = 1; c < CT; ++c) {
-            a[0] += widen_lo(x[c].x); a[1] += widen_hi(x[c].x); a[2] += widen_lo(x[c].y); a[3] += widen_hi(x[c].y);
-            a[4] += widen_lo(x[c].z); a[5] += widen_hi(x[c].z); a[6] += widen_lo(x[c].w); a[7] += widen_hi(x[c].w);
-          }
-          __syncthreads();  // the previous item's readers are done with xfer
-          xfer[2 * tid] = f32x4{a[0], a[1], a[2], a[3]};
-          xfer[2 * tid + 1] = f32x4{a[4], a[5], a[6], a[7]};
-          __syncthreads();
-#if TIDE_RS_STORE_AUX >= 0
-          {
-            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, 32 * kThreads, 0x00020000);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid]), rsrc, 16 * tid, 0,
-                                                   TIDE_RS_STORE_AUX);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid + kThreads]), rsrc,
-                                                   16 * (tid + kThreads), 0, TIDE_RS_STORE_AUX);
-          }
-#else
-          store_hbm(at_bytes<f32x4>(dst, 16u * tid), xfer[tid]);
-          store_hbm(at_bytes<f32x4>(dst, 16u * (tid + kThreads)), xfer[tid + kThreads]);
-#endif
+          full_item_load<CT>(src, tid, x);
+          full_item_finish<CT>(x, dst, xfer, tid);
           continue;  // no tail, no padding in a full item
         }
 #endif
