@@ -285,9 +285,11 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
   const int64_t count = int64_t(L->ag_chunks.size());
   const int64_t ag_wgs = int64_t(q.cu_budget) * kBudgetThreads / kAgThreads;
   const Plan plan = plan_for(count, q.cu_budget, ag_wgs, kAgBoundedItems);
+  // Few workgroups per CU (small budgets): each loads two items at a time.
+  const int batch = q.cu_budget > 0 && ag_wgs <= int64_t(kAgBatchMaxWgsPerCu) * std::max(st->cus, 1) ? 2 : 1;
   for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
     const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
-    e = launch_ag(st->ag, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, q.stage, tbl,
+    e = launch_ag(st->ag, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, batch, q.stage, tbl,
                   q.kind == kPack, q.vec, hs);
   }
   if (e == hipSuccess && q.kind == kPack)

@@ -285,13 +285,48 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
 // vectors after a short head.
 // PACK = false: placement, stage -> parameters.  PACK = true: the inverse (Slot-Reuse packing),
 // parameters -> stage slot, over the same items.
+//
+// Bounded launches with few workgroups per CU leave a copy with one vector in flight per lane
+// latency-bound: with batch = 2, two full items (whole 16-byte vectors, kAgChunk elements) are
+// loaded together before either is stored.  batch = 1 copies one item at a time.
 template <bool VEC, bool PACK>
 __global__ __launch_bounds__(kAgThreads) void ag_kernel(const AgChunk* __restrict__ chunks, int64_t first,
-                                                        int64_t count, int items_per_wg,
+                                                        int64_t count, int items_per_wg, int batch,
                                                         unsigned short* __restrict__ stage,
                                                         unsigned short* const* __restrict__ params) {
   const int tid = threadIdx.x;
   for (int j = 0; j < items_per_wg; ++j) {
+    if (VEC && batch == 2 && j + 2 <= items_per_wg) {
+      constexpr int G = 2;
+      constexpr int NV = kAgChunk / 8 / kAgThreads;  // vectors per lane of a full item
+      const u32x4* bs[G];
+      u32x4* bd[G];
+      bool full = true;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t it = item_of<TIDE_AG_XCD_REMAP != 0>(j + g, count);
+        full = full && it < count;
+        if (full) {
+          const AgChunk c = chunks[first + it];
+          full = c.n == kAgChunk && (c.src & 7) == 0 && (c.dst & 7) == 0;
+          bs[g] = reinterpret_cast<const u32x4*>(PACK ? params[c.p] + c.dst : stage + c.src);
+          bd[g] = reinterpret_cast<u32x4*>(PACK ? stage + c.src : params[c.p] + c.dst);
+        }
+      }
+      if (full) {
+        u32x4 x[G][NV];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int k = 0; k < NV; ++k) x[g][k] = load_hbm(at_bytes<u32x4>(bs[g], 16u * (tid + k * kAgThreads)));
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int k = 0; k < NV; ++k) store_hbm(at_bytes<u32x4>(bd[g], 16u * (tid + k * kAgThreads)), x[g][k]);
+        j += G - 1;
+        continue;
+      }
+    }
     const int64_t item = item_of<TIDE_AG_XCD_REMAP != 0>(j, count);
     if (item >= count) break;
     const AgChunk ch = chunks[first + item];
@@ -405,25 +440,25 @@ int rs_occupancy_lds(int device, int* dyn_lds, int* total_lds) {
   return hipSuccess;
 }
 
-int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, void* stage,
-              const void* const* dev_params, bool pack, bool vec, void* hip_stream) {
+int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, int batch,
+              void* stage, const void* const* dev_params, bool pack, bool vec, void* hip_stream) {
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   unsigned short* st = static_cast<unsigned short*>(stage);
   unsigned short* const* pp = reinterpret_cast<unsigned short* const*>(const_cast<void* const*>(dev_params));
   if (pack) {
     if (vec)
       hipLaunchKernelGGL((ag_kernel<true, true>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count,
-                         items_per_wg, st, pp);
+                         items_per_wg, batch, st, pp);
     else
       hipLaunchKernelGGL((ag_kernel<false, true>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count,
-                         items_per_wg, st, pp);
+                         items_per_wg, batch, st, pp);
   } else {
     if (vec)
       hipLaunchKernelGGL((ag_kernel<true, false>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count,
-                         items_per_wg, st, pp);
+                         items_per_wg, batch, st, pp);
     else
       hipLaunchKernelGGL((ag_kernel<false, false>), dim3(grid), dim3(kAgThreads), 0, s, chunks, first, count,
-                         items_per_wg, st, pp);
+                         items_per_wg, batch, st, pp);
   }
   return hipGetLastError();
 }

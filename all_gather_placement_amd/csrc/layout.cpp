@@ -103,6 +103,7 @@ int device_state(const tide_layout* layout, DeviceState** out) {
   DeviceState st;
   int total_lds = 0;
   e = static_cast<hipError_t>(rs_occupancy_lds(dev, &st.rs_dyn_lds, &total_lds));
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&st.cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   e = upload(layout->rs_chunks, &st.rs);
   if (e == hipSuccess) e = upload(layout->ag_chunks, &st.ag);

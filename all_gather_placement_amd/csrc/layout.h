@@ -49,6 +49,7 @@ struct DeviceState {
   hipEvent_t dma_fork = nullptr;
   hipEvent_t dma_join[kDmaStreams] = {};
   int rs_dyn_lds = 0;  // dynamic LDS of unbounded RS launches (occupancy cap, rs_occupancy_lds)
+  int cus = 0;         // compute units of the device
 };
 
 }  // namespace tide

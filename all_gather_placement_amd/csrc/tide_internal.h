@@ -67,6 +67,14 @@ namespace tide {
 #ifndef TIDE_AG_VECS
 #define TIDE_AG_VECS 4
 #endif
+// AG, bounded launches: with at most this many AG workgroups per CU, a workgroup loads two full
+// items before storing them (more bytes in flight where few waves are resident).  Measured on the
+// Llama-3.1-8B and Qwen3 groups: budget 256 2.4-2.7 -> 4.1-4.9 TB/s, 512 4.2-4.5 -> 5.4-5.5 TB/s;
+// at 6 or more workgroups per CU pairing was 3-10% slower, and batches of 4 or 8 slower still.
+#ifndef TIDE_AG_BATCH_MAX_WGS_PER_CU
+#define TIDE_AG_BATCH_MAX_WGS_PER_CU 4
+#endif
+constexpr int kAgBatchMaxWgsPerCu = TIDE_AG_BATCH_MAX_WGS_PER_CU;
 // Non-temporal (streaming) hints on HBM loads and stores.
 #ifndef TIDE_LOAD_NT
 #define TIDE_LOAD_NT 1
@@ -112,6 +120,7 @@ constexpr int64_t kPersistentWorkgroups = TIDE_PERSISTENT_WGS;
 // 16-byte source boundary.
 static_assert(kRsChunk % 8 == 0 && kAgChunk % 8 == 0, "work items must be whole 16-byte vectors");
 static_assert(kRsChunk < (int64_t(1) << 31) && kAgChunk < (int64_t(1) << 31), "item sizes are int32");
+static_assert(kAgChunk % (8 * TIDE_AG_THREADS) == 0, "a full AG item is whole vectors for every lane");
 
 // Bounded launches (cu_budget B > 0): at most B * kBudgetThreads threads of RS (or AG) workgroups
 // are resident; each workgroup takes this many work items and exits, and the call issues as many
@@ -157,7 +166,8 @@ static_assert(sizeof(AgChunk) == 32, "AgChunk is two 16-byte scalar loads");
 // reads C packed slots of R*S elements (table [C slots][R shards]).
 // launch_ag: pack = false places stage -> parameters; pack = true packs parameters -> stage slot.
 // launch_fill_zero: zeros the slot ranges of `items` (src = slot element offset, n).
-// `dyn_lds` is the dynamic local memory each RS workgroup requests (occupancy cap; 0 = none).
+// `dyn_lds` is the dynamic local memory each RS workgroup requests (occupancy cap; 0 = none);
+// `batch` (1 or 2) is the number of full AG items a workgroup loads before storing.
 // rs_occupancy_lds: the dyn_lds that admits at most kRsWgsPerCu RS workgroups per CU of `device`
 // (0 when the cap is off or the device reports no usable LDS size), and the total (static +
 // dynamic) LDS each such workgroup holds.
@@ -165,8 +175,8 @@ int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int
               const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, int dyn_lds,
               void* hip_stream);
 int rs_occupancy_lds(int device, int* dyn_lds, int* total_lds);
-int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, void* stage,
-              const void* const* dev_params, bool pack, bool vec, void* hip_stream);
+int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, int batch,
+              void* stage, const void* const* dev_params, bool pack, bool vec, void* hip_stream);
 int launch_fill_zero(const AgChunk* items, int64_t count, void* slot, void* hip_stream);
 
 }  // namespace tide

@@ -232,7 +232,7 @@ def interference(args, log):
     log(f"victim GEMM {M}x{N}x{K} bf16 alone: {alone * 1e3:.1f} us (median of {len(alone_all)})")
     rows = []
     cases = [("rs", int(x)) for x in args.budgets.split(",")]
-    cases += [("ag_kernel", 0), ("ag_kernel", 768), ("ag_copy2d", 0), ("ag_sdma", 0)]
+    cases += [("ag_kernel", 0), ("ag_kernel", 512), ("ag_kernel", 768), ("ag_copy2d", 0), ("ag_sdma", 0)]
     for kind, budget in cases:
         t_alone = comm_alone(kind, budget)
         conc, outlast = [], 0

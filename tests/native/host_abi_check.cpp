@@ -21,7 +21,7 @@ int rs_occupancy_lds(int, int*, int*) {
   std::fprintf(stderr, "rs_occupancy_lds reached in a host-only check\n");
   std::abort();
 }
-int launch_ag(const AgChunk*, int64_t, int64_t, int, int, void*, const void* const*, bool, bool, void*) {
+int launch_ag(const AgChunk*, int64_t, int64_t, int, int, int, void*, const void* const*, bool, bool, void*) {
   std::fprintf(stderr, "launch_ag reached in a host-only check\n");
   std::abort();
 }

@@ -148,9 +148,10 @@ def test_groups_ag_bit_exact(gpu_available, case, mode):
     geo, S = ogeo.group_geometry(shapes, R)
     stage = normal_bf16_bits((R * S,), 1.0, 60 + case, 0)
     want = oracle.all_gather_place(stage, shapes, R)
-    got = run_ag(shapes, R, stage, mode=mode)
-    for a, b in zip(got, want):
-        assert np.array_equal(a, b)
+    for budget in ((0, 1, 3, 1024) if mode == TIDE_AG_KERNEL else (0,)):
+        got = run_ag(shapes, R, stage, mode=mode, cu_budget=budget)
+        for a, b in zip(got, want):
+            assert np.array_equal(a, b), budget
 
 
 @pytest.mark.parametrize("g_off", [0, 1, 3, 7])
@@ -404,3 +405,21 @@ def test_cu_budget_does_not_change_results(gpu_available):
                 ref = got
             else:
                 assert torch.equal(got, ref), budget
+        # the placement too: small budgets load two items per workgroup at a time, large ones one
+        stage = normal_bf16_cuda((R * L.S,), 1.0, 81, 0)
+        pref = None
+        for budget in (0, 1, 7, 64, 256, 512, 513, 1024):
+            params = [torch.full(s, POISON_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+                      for s in shapes]
+            L.ag_place(stage, params, cu_budget=budget)
+            torch.cuda.synchronize()
+            got = [q.view(torch.int16).clone() for q in params]
+            if pref is None:
+                pref = got
+                geo, S = ogeo.group_geometry(shapes, R)
+                st2 = stage.view(R, S)
+                for p, g in enumerate(geo):
+                    want = st2[:, g.o: g.o + g.e].reshape(R * g.m, g.L)[: g.rows].reshape(-1)
+                    assert torch.equal(got[p].reshape(-1), want.view(torch.int16)), p
+            else:
+                assert all(torch.equal(a, b) for a, b in zip(got, pref)), budget
