@@ -133,8 +133,11 @@ static_assert(kAgChunk % (8 * TIDE_AG_THREADS) == 0, "a full AG item is whole ve
 #ifndef TIDE_RS_BOUNDED_ITEMS
 #define TIDE_RS_BOUNDED_ITEMS 4
 #endif
+// AG: 8 items (64 KiB of traffic per workgroup, like the RS's 80 KiB).  Measured on the Llama-3.1-70B group
+// at budget 512 against the one-wave GEMM: 16 items 5.55 TB/s, GEMM +10.9%; 8 items 4.94 TB/s, +3.7%;
+// 4 items 4.06 TB/s, +5.5%.
 #ifndef TIDE_AG_BOUNDED_ITEMS
-#define TIDE_AG_BOUNDED_ITEMS 16
+#define TIDE_AG_BOUNDED_ITEMS 8
 #endif
 constexpr int kRsBoundedItems = TIDE_RS_BOUNDED_ITEMS;
 constexpr int kAgBoundedItems = TIDE_AG_BOUNDED_ITEMS;
