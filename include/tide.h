@@ -33,6 +33,9 @@
  *     code behind the calling thread's most recent TIDE_ERR_HIP.
  *   - A layout is immutable after creation and may be used from several streams and threads at
  *     once.  The library owns it; the caller owns every buffer and stream.
+ *   - Environment: TIDE_RS_WGS_PER_CU (an integer 0..64, read when a layout first meets a device)
+ *     overrides the per-CU cap of unbounded RS workgroups (default 6; 0 = no cap).  It changes
+ *     speed only, never results.
  */
 #ifndef TIDE_H
 #define TIDE_H

@@ -300,3 +300,26 @@ def test_rs_launch_shape_caps_occupancy(gpu_available):
     assert shape["threads"] == 128 and shape["item_outputs"] == 1024
     lds_per_cu = 160 * 1024
     assert shape["lds_bytes"] * 6 <= lds_per_cu < shape["lds_bytes"] * 7
+
+
+def test_rs_occupancy_override_changes_speed_only(gpu_available, monkeypatch):
+    """TIDE_RS_WGS_PER_CU overrides the cap for layouts that first meet the device afterwards;
+    the shards stay bit for bit the same."""
+    shapes, R, C = GROUPS[1]
+    geo, S = ogeo.group_geometry(shapes, R)
+    g = [[normal_bf16_bits(s, 1.0, 160, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    grads = [[dev_bf16(x) for x in row] for row in g]
+    want = oracle.reduce_scatter(g, shapes, R)
+    for value, lds in (("3", (160 * 1024 // 3) // 512 * 512), ("0", 4096), ("junk", None), ("65", None)):
+        monkeypatch.setenv("TIDE_RS_WGS_PER_CU", value)
+        say(f"TIDE_RS_WGS_PER_CU={value}")
+        shape = tide_rs_launch_shape()
+        if lds is None:  # ignored: the built-in cap
+            assert shape["lds_bytes"] * 6 <= 160 * 1024 < shape["lds_bytes"] * 7
+        else:
+            assert shape["lds_bytes"] == lds
+        with Layout(shapes, R) as L:
+            shards = poisoned_shards(R, S)
+            L.rs_bf16_to_fp32(grads, shards)
+            torch.cuda.synchronize()
+            assert_rs_equal(shards_bits(shards), want)
