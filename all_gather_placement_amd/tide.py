@@ -32,7 +32,7 @@ class TideError(RuntimeError):
         self.status = status
         self.hip_error = hip_error
         name = _lib.tide_status_str(status).decode() if _lib is not None else str(status)
-        extra = f" (hipError {hip_error})" if status == TIDE_ERR_HIP else ""
+        extra = f" (hipError {hip_error})" if hip_error else ""
         super().__init__(f"{where}: {name}{extra}")
 
 
@@ -91,7 +91,8 @@ def load_library(path: str | None = None):
 
 def _check(status: int, where: str):
     if status != TIDE_OK:
-        raise TideError(status, where, _lib.tide_last_hip_error() if status == TIDE_ERR_HIP else 0)
+        hip = _lib.tide_last_hip_error() if status in (TIDE_ERR_HIP, TIDE_ERR_UNSUPPORTED) else 0
+        raise TideError(status, where, hip)
 
 
 def _ptr(x) -> int | None:

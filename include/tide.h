@@ -28,9 +28,12 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  RS and AG calls are
  *     stream-ordered and asynchronous: they return after enqueueing, results are valid once the
  *     stream reaches that point.  Inputs are never written.
- *   - Errors are returned as tide_status; nothing is printed and nothing is thrown.  On an error
- *     other than TIDE_ERR_HIP no work has been enqueued.  tide_last_hip_error() gives the HIP error
- *     code behind the calling thread's most recent TIDE_ERR_HIP.
+ *   - Errors are returned as tide_status; nothing is printed and nothing is thrown.  On
+ *     TIDE_ERR_INVALID or TIDE_ERR_NOMEM no work has been enqueued; on TIDE_ERR_HIP or
+ *     TIDE_ERR_UNSUPPORTED part of the work may have been (the stream then holds an incomplete
+ *     result, and TIDE_AG_SDMA still joins its copy streams back into `stream`).
+ *     tide_last_hip_error() gives the HIP error code behind the calling thread's most recent
+ *     TIDE_ERR_HIP or TIDE_ERR_UNSUPPORTED.
  *   - A layout is immutable after creation and may be used from several streams and threads at
  *     once.  The library owns it; the caller owns every buffer and stream.
  *   - Environment: TIDE_RS_WGS_PER_CU (an integer 0..64, read when a layout first meets a device)
@@ -253,7 +256,8 @@ tide_status tide_rs_launch_shape(int32_t* threads, int32_t* item_outputs, int32_
 /* Static, NUL-terminated name of a status code ("TIDE_OK", ...; "unknown" otherwise). */
 const char* tide_status_str(int32_t status);
 
-/* HIP error code (hipError_t value) behind the calling thread's last TIDE_ERR_HIP, 0 if none. */
+/* HIP error code (hipError_t value) behind the calling thread's last TIDE_ERR_HIP or
+ * TIDE_ERR_UNSUPPORTED (also set for TIDE_ERR_NOMEM from a device allocation), 0 if none. */
 int32_t tide_last_hip_error(void);
 
 #ifdef __cplusplus
