@@ -1,6 +1,7 @@
 """Benchmark of the layout-aware bf16->fp32 reduce-scatter + all-gather placement on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cu-budget B] [--ag-mode kernel|sdma]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cu-budget B] [--ag-mode kernel|sdma|copy2d]
+                    [--graph]
 
 One step = one pass of the whole hot path over one parameter group already resident in HBM: the
 in-place reduce-scatter (C bf16 contributors -> R fp32 shards) followed by the all-gather placement
@@ -46,6 +47,8 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain torch device copy of this many MiB per step (counter calibration)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture the step (prepared RS + AG calls) in a HIP graph and time its replays")
     ap.add_argument("--interference", action="store_true",
                     help="instead of the step benchmark: slowdown of a concurrent one-wave bf16 GEMM per cu_budget")
     ap.add_argument("--budgets", default="0,16,64,256,512,768,1024,1536,2048")
@@ -667,6 +670,36 @@ def main():
     host_unbound = host_us(lambda: L.rs_bf16_to_fp32(grads, shards, cu_budget=args.cu_budget, stream=stream))
     torch.cuda.synchronize()
 
+    graph_info = None
+    if args.graph and args.ag_mode != "kernel":
+        log("--graph: only the kernel placement is captured; skipped for --ag-mode " + args.ag_mode)
+    elif args.graph:
+        # The same two prepared calls captured once on a side stream; K replays timed between events.
+        side = torch.cuda.Stream()
+        rs_call.launch(side)
+        ag_call.launch(side)
+        side.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            rs_call.launch(side)
+            ag_call.launch(side)
+        with torch.cuda.stream(side):
+            for _ in range(args.warmup):
+                graph.replay()
+            g0, g1 = ev(), ev()
+            side.synchronize()
+            g0.record(side)
+            for _ in range(K):
+                graph.replay()
+            g1.record(side)
+        g1.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+        graph_info = {"ms_per_step": round(graph_ms, 5),
+                      "value": round((rs_bytes + ag_bytes) / (graph_ms * 1e-3) / 1e9, 2)}
+        log(f"graph replay: {graph_ms:.4f} ms per step ({graph_info['value']:.0f} GB/s)")
+        del graph
+        torch.cuda.synchronize()
+
     # Same-run calibration: a runtime device-to-device copy moving the RS's bytes (half read, half
     # written), the practical ceiling a plain stream reaches on this device; median of 10.
     cal_src = torch.empty(rs_bytes // 2, dtype=torch.uint8, device=dev)
@@ -718,6 +751,7 @@ def main():
         "ag_ms_mean": round(ag_mean, 5),
         "rs_host_us_per_call": {"bound": round(host_bound, 1), "validate_and_marshal": round(host_unbound, 1)},
         "rs_launch_shape": tide_rs_launch_shape(),
+        "graph_replay": graph_info,
         "calibration": {"d2d_copy_gbps": round(cal_gbps, 2), "bytes_moved": 2 * (rs_bytes // 2),
                         "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
         "roofline": {
