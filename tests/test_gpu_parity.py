@@ -162,9 +162,10 @@ def test_rs_alignment_sweep(gpu_available, g_off, s_off):
     say(f"alignment g_off={g_off} s_off={s_off}")
     g = [[normal_bf16_bits(s, 1.0, 70, c, p) for p, s in enumerate(shapes)] for c in range(C)]
     want = oracle.reduce_scatter(g, shapes, R)
-    # mixed offsets across contributors when g_off > 0
-    got = run_rs(shapes, R, g, g_pad=lambda c, p: (g_off * (c + 1)) % 8, s_pad=s_off)
-    assert_rs_equal(got, want)
+    # mixed offsets across contributors when g_off > 0; one launch, and short bounded launches
+    for budget in (0, 2):
+        got = run_rs(shapes, R, g, cu_budget=budget, g_pad=lambda c, p: (g_off * (c + 1)) % 8, s_pad=s_off)
+        assert_rs_equal(got, want)
 
 
 @pytest.mark.parametrize("st_off,p_off", [(0, 0), (1, 0), (0, 3), (5, 5), (2, 6)])
@@ -174,10 +175,11 @@ def test_ag_alignment_sweep(gpu_available, st_off, p_off):
     geo, S = ogeo.group_geometry(shapes, R)
     stage = normal_bf16_bits((R * S,), 1.0, 71, 0)
     want = oracle.all_gather_place(stage, shapes, R)
-    for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D):
-        got = run_ag(shapes, R, stage, mode=mode, st_pad=st_off, p_pad=lambda p: (p_off * (p + 1)) % 8)
+    for mode, budget in ((TIDE_AG_KERNEL, 0), (TIDE_AG_KERNEL, 2), (TIDE_AG_SDMA, 0), (TIDE_AG_COPY2D, 0)):
+        got = run_ag(shapes, R, stage, mode=mode, cu_budget=budget, st_pad=st_off,
+                     p_pad=lambda p: (p_off * (p + 1)) % 8)
         for a, b in zip(got, want):
-            assert np.array_equal(a, b)
+            assert np.array_equal(a, b), (mode, budget)
 
 
 def test_rs_special_values(gpu_available):

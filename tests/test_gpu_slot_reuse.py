@@ -45,10 +45,11 @@ def test_slot_pack_alignment(gpu_available, g_off, s_off):
     g = [normal_bf16_bits(s, 1.0, 91, 0, p) for p, s in enumerate(shapes)]
     geo, S = ogeo.group_geometry(shapes, R)
     with Layout(shapes, R) as L:
-        slot = poisoned_slot(R, S, s_off)
-        L.slot_pack([dev_bf16(x, (g_off * (p + 1)) % 8) for p, x in enumerate(g)], slot)
-        torch.cuda.synchronize()
-        assert np.array_equal(host_bits_bf16(slot), oracle.pack_slot(g, shapes, R))
+        for budget in (0, 3):
+            slot = poisoned_slot(R, S, s_off)
+            L.slot_pack([dev_bf16(x, (g_off * (p + 1)) % 8) for p, x in enumerate(g)], slot, cu_budget=budget)
+            torch.cuda.synchronize()
+            assert np.array_equal(host_bits_bf16(slot), oracle.pack_slot(g, shapes, R)), budget
 
 
 @pytest.mark.parametrize("case", range(len(GROUPS)))
