@@ -64,5 +64,13 @@ def build(verbose: bool = False, extra=(), out: str = LIB, sources=SOURCES, prob
     return out
 
 
+def ensure_built(verbose: bool = False) -> str:
+    """Build the libraries only if they are not there yet (tests, smoke and benchmark entry points);
+    returns the path of libtide.so."""
+    if not (os.path.exists(LIB) and os.path.exists(PROBE_LIB)):
+        build(verbose=verbose)
+    return LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

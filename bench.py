@@ -573,6 +573,9 @@ def main():
     from oracle.geometry import group_geometry  # sizes only, for the byte formulas
     from workloads import CONFIGS, normal_bf16_cuda
 
+    from all_gather_placement_amd.build import ensure_built
+
+    ensure_built()  # load what is built; build only when nothing is
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.interference:
         torch.cuda.set_device(0)

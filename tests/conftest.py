@@ -11,6 +11,10 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs a real MI355X (gfx950) and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workloads (seconds to minutes)")
+    # Load what is built; build only when nothing is (hipcc cross-compiles without a GPU).
+    from all_gather_placement_amd.build import ensure_built
+
+    ensure_built()
 
 
 def golden_path(name: str) -> str:
