@@ -1,0 +1,75 @@
+"""Randomised GPU parity: many small seeded groups, each checked bit for bit against the oracle.
+
+Every group draws R, C, the parameter shapes (1-3 dimensions, rows 0-3000, so empty parameters,
+rows < R and ragged tails all occur), a CU budget and per-buffer base offsets (0-7 elements, so both
+the vector and the element paths run), then runs the reduce-scatter, the placement and the
+Slot-Reuse packing through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import geometry as ogeo
+from all_gather_placement_amd import Layout
+from tests.test_gpu_parity import POISON_BF16, assert_rs_equal, dev_bf16, host_bits_bf16, host_bits_f32, poisoned_shards, say
+
+pytestmark = pytest.mark.gpu
+
+N_GROUPS = 40
+
+
+def _random_group(rng):
+    R = int(rng.integers(1, 18))
+    C = int(rng.integers(1, 13))
+    shapes = []
+    for _ in range(int(rng.integers(1, 6))):
+        nd = int(rng.integers(1, 4))
+        rows = int(rng.choice([0, int(rng.integers(1, R + 1)), int(rng.integers(1, 3001))]))
+        rest = [int(rng.integers(1, 40)) for _ in range(nd - 1)]
+        while rows * int(np.prod(rest, dtype=np.int64)) > 200_000:
+            rows //= 2
+        shapes.append(tuple([rows] + rest))
+    budget = int(rng.choice([0, 0, 1, 2, 5, 64]))
+    return shapes, R, C, budget
+
+
+def _random_inputs(rng, shapes, R, C, S):
+    """Random bf16 bit patterns with the exponent's top bit cleared: every finite value below 2 in
+    magnitude, subnormals and signed zeros included (no inf or NaN, so results compare bit for bit)."""
+    bits = lambda size: np.asarray(rng.integers(0, 1 << 16, size=size), dtype=np.uint16) & np.uint16(0xBFFF)
+    return [[bits(s) for s in shapes] for _ in range(C)], bits(R * S)
+
+
+@pytest.mark.parametrize("case", range(N_GROUPS))
+def test_random_group_bit_exact(gpu_available, case):
+    rng = np.random.default_rng(1000 + case)
+    shapes, R, C, budget = _random_group(rng)
+    offset = (lambda: int(rng.integers(0, 8))) if case % 3 == 0 else (lambda: 0)
+    say(f"random group {case}: shapes={shapes} R={R} C={C} budget={budget} offsets={'on' if case % 3 == 0 else 'off'}")
+    geo, S = ogeo.group_geometry(shapes, R)
+    g, stage_bits = _random_inputs(rng, shapes, R, C, S)
+    want = oracle.reduce_scatter(g, shapes, R)
+    want_ag = oracle.all_gather_place(stage_bits, shapes, R)
+    with Layout(shapes, R) as L:
+        grads = [[dev_bf16(x, offset()) for x in row] for row in g]
+        shards = poisoned_shards(R, S, offset())
+        L.rs_bf16_to_fp32(grads, shards, cu_budget=budget)
+        stage = dev_bf16(stage_bits, offset())
+        params = []
+        for s in shapes:
+            n = int(np.prod(s, dtype=np.int64))
+            o = offset()
+            buf = torch.full((n + o + 8,), POISON_BF16, dtype=torch.int16, device="cuda")
+            params.append(buf[o: o + n].view(torch.bfloat16).reshape(s))
+        L.ag_place(stage, params, cu_budget=budget)
+        o = offset()
+        slot_buf = torch.full((R * S + o + 8,), POISON_BF16, dtype=torch.int16, device="cuda")
+        slot = slot_buf[o: o + R * S].view(torch.bfloat16)
+        L.slot_pack(grads[0], slot, cu_budget=budget)
+        torch.cuda.synchronize()
+        got = np.stack([host_bits_f32(x) for x in shards]) if S else np.zeros((R, 0), np.uint32)
+        assert_rs_equal(got, want)
+        for q, w in zip(params, want_ag):
+            assert np.array_equal(host_bits_bf16(q), w)
+        assert np.array_equal(host_bits_bf16(slot), oracle.pack_slot(g[0], shapes, R))
