@@ -150,8 +150,9 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *   independently of cu_budget; fp32 denormals are kept.
  * 16-byte-aligned grads and shards take the vector path; any other legal alignment takes a
  * slower element path with identical results.
- * Errors: TIDE_ERR_INVALID (null layout/arrays, C < 1, cu_budget < 0, null or misaligned pointer,
- * any shard overlapping another shard or any gradient), TIDE_ERR_NOMEM, TIDE_ERR_HIP.
+ * Errors: TIDE_ERR_INVALID (null layout/arrays, C < 1, C*P > 2^24, cu_budget < 0, null or
+ * misaligned pointer, any shard overlapping another shard or any gradient), TIDE_ERR_NOMEM,
+ * TIDE_ERR_HIP.
  */
 tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* grads,
                                  float* const* shards, int32_t cu_budget, void* stream);
@@ -164,7 +165,9 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
  *              elements (NULL allowed only for empty parameters).
  *   mode       TIDE_AG_KERNEL, TIDE_AG_SDMA or TIDE_AG_COPY2D.
  *   cu_budget  as for the RS, counted in 256-thread slots (TIDE_AG_KERNEL only; its workgroups
- *              are 128 threads, so B admits 2B of them).
+ *              are 128 threads, so B admits 2B of them, each copying 8 work items -- 64 KiB of
+ *              traffic -- before it exits; with at most 4 of them per CU, two items are loaded
+ *              before either is stored).  0: one workgroup per work item, no cap.
  * Result: params[p][r*m_p*L_p + k] = stage[r*S + o_p + k] for every r and k < v*L_p, copied as
  * bits; stage padding is never read into a parameter; every parameter element is written once.
  * All pointers must be 2-byte aligned; 16-byte alignment selects the vector path.
