@@ -59,6 +59,8 @@ def parse():
                     help="instead of the step benchmark: occupancy probe, spin-kernel curve and more victims")
     ap.add_argument("--engines", action="store_true",
                     help="instead of the step benchmark: AG placement on CUs vs copy engines, served GB/s and victim slowdown")
+    ap.add_argument("--copy-sizes", action="store_true",
+                    help="placement of one flat parameter of 1-256 MiB over R = 1 and 8 ranks on each engine")
     ap.add_argument("--slot-reuse", action="store_true",
                     help="instead of the step benchmark: Slot-Reuse (pack into slots + RS from slots) vs in-place RS")
     return ap.parse_args()
@@ -556,6 +558,48 @@ def engines(args, log):
     print(json.dumps({"experiment": "placement engines vs victims", "workload": cfg.name, "rows": rows}), flush=True)
 
 
+def copy_sizes(args, log):
+    """Per-copy cost of the placement engines: one flat bf16 parameter of 1, 8, 64 and 256 MiB placed
+    from a stage over R = 1 (one copy) and R = 8 (eight copies), on the DMA engines, the runtime 2-D
+    copy and the kernel; median of 7 HIP-event timings each."""
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
+
+    def med(call, n=7):
+        call.launch()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call.launch()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.median(ts)
+
+    rows = []
+    for mib in (1, 8, 64, 256):
+        for R in (1, 8):
+            n = mib << 19
+            with Layout([(n,)], R) as L:
+                stage = torch.randn(R * L.S, device="cuda").to(torch.bfloat16)
+                param = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+                row = {"param_mib": mib, "R": R, "copies": R}
+                for mode, name in ((TIDE_AG_SDMA, "sdma"), (TIDE_AG_COPY2D, "copy2d"), (TIDE_AG_KERNEL, "kernel")):
+                    call = L.bind_ag(stage, [param], mode=mode)
+                    t = med(call)
+                    call.close()
+                    row[f"{name}_ms"] = round(t, 4)
+                    row[f"{name}_gbps_copied"] = round(mib * 2**20 / (t * 1e-3) / 1e9, 1)
+                log(json.dumps(row))
+                rows.append(row)
+    print(json.dumps({"experiment": "placement engines vs copy size", "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -593,6 +637,10 @@ def main():
     if args.engines:
         torch.cuda.set_device(0)
         engines(args, log)
+        return
+    if args.copy_sizes:
+        torch.cuda.set_device(0)
+        copy_sizes(args, log)
         return
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")

@@ -62,10 +62,12 @@ typedef enum tide_status {
 /* Placement engines for tide_ag_place. */
 enum {
   TIDE_AG_KERNEL = 0, /* hand-written gfx950 copy kernel: the bandwidth path (uses CUs) */
-  TIDE_AG_SDMA = 1,   /* DMA (SDMA) engines only, no compute units: one 1-D copy per (parameter,
-                         rank) segment, spread over the library's internal copy streams.  On one
-                         MI355X the engines move roughly 0.06-0.2 TB/s locally, far below the
-                         kernel; this mode is for callers that must leave every CU to compute. */
+  TIDE_AG_SDMA = 1,   /* DMA (SDMA) engines: one 1-D no-compute-unit copy per (parameter, rank)
+                         segment, spread over the library's internal copy streams (the runtime runs
+                         only the tiniest segments as a small copy kernel).  On one MI355X a call
+                         costs ~65 us before any byte moves and large copies stream 1.1-1.6 TB/s:
+                         0.9-2 TB/s of traffic for large segments, 0.03-0.1 TB/s for thousands of
+                         small ones.  For callers that must leave the CUs to compute. */
   TIDE_AG_COPY2D = 2  /* one runtime 2-D copy per parameter (row pitch = one stage slot) plus one
                          copy for the rank whose slice is part padding; the HIP runtime picks the
                          engine (on ROCm 7.2 a shader blit kernel, i.e. it uses CUs). */
