@@ -93,7 +93,10 @@ void tide_layout_destroy(tide_layout* layout);
 
 /* Upload the layout's device tables to the current device (idempotent).  After this, RS and AG
  * calls on that device allocate nothing except when a call passes more pointers than any earlier
- * one.  Errors: TIDE_ERR_INVALID (null), TIDE_ERR_NOMEM, TIDE_ERR_HIP. */
+ * one.  An immediate call stages its table of buffer addresses in one of 8 slots per device; when
+ * all 8 hold tables of calls still in flight, it waits on the host for the oldest to finish
+ * (prepared calls own their tables and never wait).  Errors: TIDE_ERR_INVALID (null),
+ * TIDE_ERR_NOMEM, TIDE_ERR_HIP. */
 tide_status tide_layout_prepare(const tide_layout* layout);
 
 /* Geometry queries (host only).  Return -1 for a NULL layout. */
