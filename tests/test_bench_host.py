@@ -1,0 +1,32 @@
+"""Host-side contract of bench.py (no GPU): the multi-GPU refusal and where `traffic` comes from."""
+import os
+import re
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_only_from_counters_taken_on_this_kernel_source(tmp_path, monkeypatch):
+    text = open(os.path.join(ROOT, "profiles", "rs_kernel_llama3_1_8b_layer_pmc.md")).read()
+    recorded = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text).group(1)
+    hbm = float(re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text).group(1))
+    # the committed summary is read when its hash matches the kernel source...
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: recorded)
+    assert bench.read_traffic("llama3_1_8b_layer") == hbm
+    # ...and ignored (null) for any other source
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.read_traffic("llama3_1_8b_layer") is None
+    assert bench.read_traffic("no_such_workload") is None
+    # the counters moved every algorithmic byte about once (reads + writes within 1% of 20 B per output)
+    algorithmic = int(re.search(r"algorithmic_bytes_per_launch:\s*([0-9]+)", text).group(1))
+    assert abs(hbm / algorithmic - 1.0) < 0.01
