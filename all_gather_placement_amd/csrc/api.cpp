@@ -273,8 +273,8 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
     const bool flat = q.kind == kRsSlots;
     const int64_t rs_wgs = int64_t(q.cu_budget) * kBudgetThreads / kThreads;
     const Plan plan = plan_for(count, q.cu_budget, rs_wgs, kRsBoundedItems);
-    // Unbounded launches cap the RS workgroups per CU; bounded ones are capped by the budget.
-    const int lds = q.cu_budget == 0 ? st->rs_dyn_lds : 0;
+    // Unbounded launches cap the RS workgroups per CU (by C); bounded ones are capped by the budget.
+    const int lds = q.cu_budget == 0 ? rs_launch_lds(*st, q.C) : 0;
     for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
       const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
       e = launch_rs(st->rs, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, tbl, flat ? 1 : L->P, q.C,
@@ -512,15 +512,17 @@ tide_status tide_call_launch(const tide_call* call, void* stream) {
   return e == hipSuccess ? TIDE_OK : tide::hip_fail(e);
 }
 
-tide_status tide_rs_launch_shape(int32_t* threads, int32_t* item_outputs, int32_t* lds_bytes) {
-  if (threads == nullptr || item_outputs == nullptr || lds_bytes == nullptr) return TIDE_ERR_INVALID;
-  int dev = 0, dyn = 0, total = 0;
+tide_status tide_rs_launch_shape(int32_t C, int32_t* threads, int32_t* item_outputs, int32_t* lds_bytes) {
+  if (C < 1 || threads == nullptr || item_outputs == nullptr || lds_bytes == nullptr) return TIDE_ERR_INVALID;
+  tide::DeviceState st;
+  int dev = 0;
   int e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = tide::rs_occupancy_lds(dev, &dyn, &total);
+  if (e == hipSuccess) e = tide::rs_lds_info(dev, &st.lds_per_cu, &st.rs_static_lds_ct, &st.rs_static_lds_rt);
   if (e != hipSuccess) return tide::hip_fail(e);
+  st.rs_env_cap = tide::rs_env_wgs_per_cu();
   *threads = tide::kThreads;
   *item_outputs = int32_t(tide::kRsChunk);
-  *lds_bytes = total;
+  *lds_bytes = (C <= 8 ? st.rs_static_lds_ct : st.rs_static_lds_rt) + tide::rs_launch_lds(st, C);
   return TIDE_OK;
 }
 

@@ -22,8 +22,6 @@
 // lane per access when source and destination share their 16-byte phase.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-
 #include "tide_internal.h"
 
 namespace tide {
@@ -420,33 +418,16 @@ int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int
   return launch_rs_c<false>(chunks, first, count, grid, items_per_wg, ptrs, P, C, S, vec, dyn_lds, s);
 }
 
-int rs_occupancy_lds(int device, int* dyn_lds, int* total_lds) {
-  *dyn_lds = 0;
+int rs_lds_info(int device, int* lds_per_cu, int* static_lds_ct, int* static_lds_rt) {
+  hipError_t e = hipDeviceGetAttribute(lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device);
+  if (e != hipSuccess) return e;
   hipFuncAttributes attr;
-  hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&rs_kernel<8, true, false>));
-  if (e != hipSuccess) return e;
-  *total_lds = static_cast<int>(attr.sharedSizeBytes);
-  // TIDE_RS_WGS_PER_CU in the environment (0..64; 0 = no cap) overrides the built-in cap, for
-  // measurements; anything else is ignored.
-  int wgs_per_cu = kRsWgsPerCu;
-  if (const char* env = std::getenv("TIDE_RS_WGS_PER_CU")) {
-    char* end = nullptr;
-    const long v = std::strtol(env, &end, 10);
-    if (end != env && *end == '\0' && v >= 0 && v <= 64) wgs_per_cu = static_cast<int>(v);
-  }
-  if (wgs_per_cu <= 0) return hipSuccess;
-  int lds_per_cu = 0;
-  e = hipDeviceGetAttribute(&lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device);
-  if (e != hipSuccess) return e;
-  // The full-item path's exchange buffer is the kernel's only static LDS.  Each workgroup's total
-  // is rounded down to 512 bytes, so kRsWgsPerCu of them fit in a CU (and, for counts up to 16,
-  // one more does not).
-  const int per_wg = (lds_per_cu / wgs_per_cu) / 512 * 512;
-  const int dyn = per_wg - static_cast<int>(attr.sharedSizeBytes);
-  if (dyn > 0) {
-    *dyn_lds = dyn;
-    *total_lds = per_wg;
-  }
+  if ((e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&rs_kernel<8, true, false>))) != hipSuccess)
+    return e;
+  *static_lds_ct = static_cast<int>(attr.sharedSizeBytes);
+  if ((e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&rs_kernel<0, true, false>))) != hipSuccess)
+    return e;
+  *static_lds_rt = static_cast<int>(attr.sharedSizeBytes);
   return hipSuccess;
 }
 

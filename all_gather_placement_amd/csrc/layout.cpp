@@ -12,6 +12,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -91,6 +92,14 @@ void order_items(tide_layout* L) {
 
 void set_last_hip_error(int err) { g_last_hip_error = err; }
 
+int rs_env_wgs_per_cu() {
+  const char* env = std::getenv("TIDE_RS_WGS_PER_CU");
+  if (env == nullptr) return -1;
+  char* end = nullptr;
+  const long v = std::strtol(env, &end, 10);
+  return (end != env && *end == '\0' && v >= 0 && v <= 64) ? static_cast<int>(v) : -1;
+}
+
 int device_state(const tide_layout* layout, DeviceState** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -101,9 +110,9 @@ int device_state(const tide_layout* layout, DeviceState** out) {
     return hipSuccess;
   }
   DeviceState st;
-  int total_lds = 0;
-  e = static_cast<hipError_t>(rs_occupancy_lds(dev, &st.rs_dyn_lds, &total_lds));
+  e = static_cast<hipError_t>(rs_lds_info(dev, &st.lds_per_cu, &st.rs_static_lds_ct, &st.rs_static_lds_rt));
   if (e == hipSuccess) e = hipDeviceGetAttribute(&st.cus, hipDeviceAttributeMultiprocessorCount, dev);
+  st.rs_env_cap = rs_env_wgs_per_cu();
   if (e != hipSuccess) return e;
   e = upload(layout->rs_chunks, &st.rs);
   if (e == hipSuccess) e = upload(layout->ag_chunks, &st.ag);

@@ -29,14 +29,15 @@ namespace tide {
 #ifndef TIDE_AG_CHUNK
 #define TIDE_AG_CHUNK 2048
 #endif
-// RS occupancy cap of unbounded launches (cu_budget 0): at most this many RS workgroups per CU,
-// enforced by the local-memory size each launch requests (the CU's LDS divided by this count).
-// Fewer loads in flight stream HBM better than a full CU: with 128-thread workgroups, 6 per CU
-// (12 waves, ~96 KiB of loads in flight per CU at C = 8) beat 4, 5, 7, 8 and the uncapped 16 by
-// 2-5% on all four layer groups; 0 = no cap.
-#ifndef TIDE_RS_WGS_PER_CU
-#define TIDE_RS_WGS_PER_CU 6
-#endif
+// RS occupancy cap of unbounded launches (cu_budget 0): at most rs_wgs_per_cu(C) RS workgroups per
+// CU, enforced by the local-memory size each launch requests (the CU's LDS divided by that count).
+// Fewer requests in flight stream HBM better than a full CU, and a workgroup's traffic grows with
+// C (2C + 4 bytes per output), so the best count falls as C grows.  Measured with 128-thread
+// workgroups on the Llama-3.1-8B group: C = 8: 6 per CU beat 3, 4, 5, 7, 8 and no cap by 1-5%;
+// C = 4: 8 beat 6, 12 and 16 (+2.4% over 6); C = 2 and 1: 12 beat 8, 16 and no cap (C = 1: 4.1
+// TB/s at 6 -> 6.4 TB/s).  C > 8 takes the runtime-C path, which loads one contributor at a time
+// and streams best uncapped (3.5 -> 5.5 TB/s at C = 12).
+constexpr int rs_wgs_per_cu(int C) { return C <= 2 ? 12 : C <= 4 ? 8 : C <= 8 ? 6 : 0; }
 #ifndef TIDE_RS_NQ
 #define TIDE_RS_NQ 2
 #endif
@@ -110,7 +111,6 @@ constexpr int kThreads = TIDE_THREADS;
 constexpr int kAgThreads = TIDE_AG_THREADS;
 // Unit of cu_budget: B admits B * kBudgetThreads threads of resident communication workgroups.
 constexpr int kBudgetThreads = 256;
-constexpr int kRsWgsPerCu = TIDE_RS_WGS_PER_CU;
 static_assert(kBudgetThreads % kThreads == 0 && kBudgetThreads % TIDE_AG_THREADS == 0,
               "a budget slot holds whole workgroups");
 constexpr int64_t kRsChunk = TIDE_RS_CHUNK;
@@ -171,13 +171,21 @@ static_assert(sizeof(AgChunk) == 32, "AgChunk is two 16-byte scalar loads");
 // launch_fill_zero: zeros the slot ranges of `items` (src = slot element offset, n).
 // `dyn_lds` is the dynamic local memory each RS workgroup requests (occupancy cap; 0 = none);
 // `batch` (1 or 2) is the number of full AG items a workgroup loads before storing.
-// rs_occupancy_lds: the dyn_lds that admits at most kRsWgsPerCu RS workgroups per CU of `device`
-// (0 when the cap is off or the device reports no usable LDS size), and the total (static +
-// dynamic) LDS each such workgroup holds.
+// rs_lds_info: the local memory per CU of `device` and the static local memory of the RS kernel
+// for C <= 8 (compile-time contributor count) and for C > 8 (runtime count).
+// rs_dynamic_lds: the dynamic local memory that admits at most `wgs_per_cu` RS workgroups per CU
+// (0 = no cap, or when it cannot be met).
 int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,
               const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, int dyn_lds,
               void* hip_stream);
-int rs_occupancy_lds(int device, int* dyn_lds, int* total_lds);
+int rs_lds_info(int device, int* lds_per_cu, int* static_lds_ct, int* static_lds_rt);
+inline int rs_dynamic_lds(int lds_per_cu, int static_lds, int wgs_per_cu) {
+  if (wgs_per_cu <= 0 || lds_per_cu <= 0) return 0;
+  // rounded down to 512 bytes per workgroup, so wgs_per_cu of them fit in a CU (and, for counts up
+  // to 16, one more does not)
+  const int dyn = (lds_per_cu / wgs_per_cu) / 512 * 512 - static_lds;
+  return dyn > 0 ? dyn : 0;
+}
 int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, int batch,
               void* stage, const void* const* dev_params, bool pack, bool vec, void* hip_stream);
 int launch_fill_zero(const AgChunk* items, int64_t count, void* slot, void* hip_stream);

@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default="llama3_1_8b_layer")
     ap.add_argument("--cu-budget", type=int, default=0)
     ap.add_argument("--ag-mode", choices=["kernel", "sdma", "copy2d"], default="kernel")
+    ap.add_argument("--contributors", type=int, default=0,
+                    help="override the workload's contributor count C (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain torch device copy of this many MiB per step (counter calibration)")
@@ -643,6 +645,10 @@ def main():
         copy_sizes(args, log)
         return
     cfg = CONFIGS[args.workload]
+    if args.contributors:
+        import dataclasses
+
+        cfg = dataclasses.replace(cfg, C=args.contributors)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"workload {cfg.name}: P={cfg.P} R={cfg.R} C={cfg.C}")
@@ -773,7 +779,8 @@ def main():
     value = (rs_bytes + ag_bytes) / (ms_per_step * 1e-3) / 1e9
     rs_gbps = rs_bytes / (rs_mean * 1e-3) / 1e9
     ag_gbps = ag_bytes / (ag_mean * 1e-3) / 1e9
-    traffic = read_traffic(cfg.name) if args.cu_budget == 0 else None
+    # counters were taken for the workload's own contributor count and the unbounded launch
+    traffic = read_traffic(cfg.name) if args.cu_budget == 0 and not args.contributors else None
 
     out = {
         "metric": METRIC,
@@ -802,13 +809,13 @@ def main():
         "ag_frac_of_peak": round(ag_gbps / HBM_PEAK_GBPS, 4),
         "ag_ms_mean": round(ag_mean, 5),
         "rs_host_us_per_call": {"bound": round(host_bound, 1), "validate_and_marshal": round(host_unbound, 1)},
-        "rs_launch_shape": tide_rs_launch_shape(),
+        "rs_launch_shape": tide_rs_launch_shape(cfg.C),
         "graph_replay": graph_info,
         "calibration": {"d2d_copy_gbps": round(cal_gbps, 2), "bytes_moved": 2 * (rs_bytes // 2),
                         "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "rs_kernel<8, true, false>",
+            "kernel": f"rs_kernel<{cfg.C if cfg.C <= 8 else 0}, true, false>",
             "achieved": round(rs_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -37,7 +37,7 @@
  *   - A layout is immutable after creation and may be used from several streams and threads at
  *     once.  The library owns it; the caller owns every buffer and stream.
  *   - Environment: TIDE_RS_WGS_PER_CU (an integer 0..64, read when a layout first meets a device)
- *     overrides the per-CU cap of unbounded RS workgroups (default 6; 0 = no cap).  It changes
+ *     replaces the per-CU cap of unbounded RS workgroups for every C (0 = no cap).  It changes
  *     speed only, never results.
  */
 #ifndef TIDE_H
@@ -140,9 +140,10 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              row-major bf16 device tensor of rows_p * L_p elements, 2-byte aligned (NULL allowed
  *              only for empty parameters).  Read in place, never written.
  *   shards     host [R]: shards[r] is rank r's flat fp32 device shard of S elements, 4-byte aligned.
- *   cu_budget  0: one launch, one short-lived workgroup per work item, with at most 6 of them
- *              resident per CU (each requests a sixth of the CU's local memory: fewer loads in
- *              flight stream HBM better than a full CU).
+ *   cu_budget  0: one launch, one short-lived workgroup per work item, with at most N of them
+ *              resident per CU: N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 8, no cap above
+ *              (each requests 1/N of the CU's local memory; fewer requests in flight stream HBM
+ *              better than a full CU, and a workgroup's traffic grows with C).
  *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of
  *              128 threads); each processes a bounded number of work items (4 by default, 80 KiB
  *              of traffic at C = 8) and exits, and the call issues as many launches as needed, so
@@ -255,11 +256,12 @@ tide_status tide_call_launch(const tide_call* call, void* stream);
  * NULL is ignored. */
 void tide_call_destroy(tide_call* call);
 
-/* Launch shape of unbounded (cu_budget 0) RS calls on the current device: threads per workgroup,
- * outputs per full work item, and the local memory (static + dynamic, bytes) each workgroup
- * requests -- a CU holds as many RS workgroups as fit in its local memory, so this sets the
- * occupancy cap.  Errors: TIDE_ERR_INVALID (a NULL pointer), TIDE_ERR_HIP. */
-tide_status tide_rs_launch_shape(int32_t* threads, int32_t* item_outputs, int32_t* lds_bytes);
+/* Launch shape of unbounded (cu_budget 0) RS calls with C contributors on the current device:
+ * threads per workgroup, outputs per full work item, and the local memory (static + dynamic,
+ * bytes) each workgroup requests -- a CU holds as many RS workgroups as fit in its local memory,
+ * so this sets the occupancy cap.  Errors: TIDE_ERR_INVALID (C < 1 or a NULL pointer),
+ * TIDE_ERR_HIP. */
+tide_status tide_rs_launch_shape(int32_t C, int32_t* threads, int32_t* item_outputs, int32_t* lds_bytes);
 
 /* Static, NUL-terminated name of a status code ("TIDE_OK", ...; "unknown" otherwise). */
 const char* tide_status_str(int32_t status);

@@ -17,8 +17,8 @@ int launch_rs(const RsChunk*, int64_t, int64_t, int, int, const void* const*, in
   std::fprintf(stderr, "launch_rs reached in a host-only check\n");
   std::abort();
 }
-int rs_occupancy_lds(int, int*, int*) {
-  std::fprintf(stderr, "rs_occupancy_lds reached in a host-only check\n");
+int rs_lds_info(int, int*, int*, int*) {
+  std::fprintf(stderr, "rs_lds_info reached in a host-only check\n");
   std::abort();
 }
 int launch_ag(const AgChunk*, int64_t, int64_t, int, int, int, void*, const void* const*, bool, bool, void*) {
@@ -135,7 +135,9 @@ int main() {
   CHECK(tide_rs_slots_prepare(L, 2, sl, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
   CHECK(tide_rs_prepare(L, 1, g, sh2, 0, nullptr) == TIDE_ERR_INVALID);  // no output handle
   CHECK(tide_call_launch(nullptr, nullptr) == TIDE_ERR_INVALID);
-  CHECK(tide_rs_launch_shape(nullptr, nullptr, nullptr) == TIDE_ERR_INVALID);
+  CHECK(tide_rs_launch_shape(8, nullptr, nullptr, nullptr) == TIDE_ERR_INVALID);
+  int32_t th = 0, it = 0, lds = 0;
+  CHECK(tide_rs_launch_shape(0, &th, &it, &lds) == TIDE_ERR_INVALID);
   tide_call_destroy(nullptr);
   CHECK(tide_last_hip_error() == 0);
   tide_layout_destroy(L);

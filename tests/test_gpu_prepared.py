@@ -293,13 +293,17 @@ def test_prepared_calls_from_threads(gpu_available):
 
 
 def test_rs_launch_shape_caps_occupancy(gpu_available):
-    """Unbounded RS launches request a sixth of a gfx950 CU's 160 KiB of local memory per
-    128-thread workgroup, so at most 6 are resident per CU."""
-    shape = tide_rs_launch_shape()
-    say(f"RS launch shape {shape}")
-    assert shape["threads"] == 128 and shape["item_outputs"] == 1024
+    """Unbounded RS launches request 1/N of a gfx950 CU's 160 KiB of local memory per 128-thread
+    workgroup, N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 8; no cap above 8 contributors."""
     lds_per_cu = 160 * 1024
-    assert shape["lds_bytes"] * 6 <= lds_per_cu < shape["lds_bytes"] * 7
+    for C, n in ((1, 12), (2, 12), (3, 8), (4, 8), (5, 6), (8, 6), (9, 0), (12, 0)):
+        shape = tide_rs_launch_shape(C)
+        say(f"RS launch shape C={C}: {shape}")
+        assert shape["threads"] == 128 and shape["item_outputs"] == 1024
+        if n:
+            assert shape["lds_bytes"] * n <= lds_per_cu < shape["lds_bytes"] * (n + 1), (C, shape)
+        else:
+            assert shape["lds_bytes"] * 16 <= lds_per_cu, (C, shape)  # only the kernel's own
 
 
 def test_rs_occupancy_override_changes_speed_only(gpu_available, monkeypatch):
@@ -313,7 +317,7 @@ def test_rs_occupancy_override_changes_speed_only(gpu_available, monkeypatch):
     for value, lds in (("3", (160 * 1024 // 3) // 512 * 512), ("0", 4096), ("junk", None), ("65", None)):
         monkeypatch.setenv("TIDE_RS_WGS_PER_CU", value)
         say(f"TIDE_RS_WGS_PER_CU={value}")
-        shape = tide_rs_launch_shape()
+        shape = tide_rs_launch_shape(C)
         if lds is None:  # ignored: the built-in cap
             assert shape["lds_bytes"] * 6 <= 160 * 1024 < shape["lds_bytes"] * 7
         else:
