@@ -522,7 +522,7 @@ tide_status tide_rs_launch_shape(int32_t C, int32_t* threads, int32_t* item_outp
   st.rs_env_cap = tide::rs_env_wgs_per_cu();
   *threads = tide::kThreads;
   *item_outputs = int32_t(tide::kRsChunk);
-  *lds_bytes = (C <= 8 ? st.rs_static_lds_ct : st.rs_static_lds_rt) + tide::rs_launch_lds(st, C);
+  *lds_bytes = (C <= tide::kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt) + tide::rs_launch_lds(st, C);
   return TIDE_OK;
 }
 

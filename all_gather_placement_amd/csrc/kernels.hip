@@ -129,7 +129,7 @@ __device__ __forceinline__ void sum_groups(const unsigned short* const* src, uin
   }
 }
 
-// Runtime contributor count (C > 8): same mapping, contributors loaded one at a time.
+// Runtime contributor count (C > kRsMaxCt): same mapping, contributors loaded one at a time.
 __device__ __forceinline__ void sum_group_rt(const unsigned short* const* gptr, int32_t P, int32_t p, int C,
                                              int64_t e, float* d, bool dst16) {
   float a[4];
@@ -196,7 +196,7 @@ __device__ __forceinline__ void full_item_finish(const u32x4 x[CT], float* dst, 
 #endif
 }
 
-// RS kernel.  CT in 1..8: contributor count fixed at compile time; CT == 0: any C >= 1.
+// RS kernel.  CT in 1..kRsMaxCt: contributor count fixed at compile time; CT == 0: any C >= 1.
 // VEC: all source and shard base pointers are 16-byte aligned (checked on the host), so the
 // alignment of an element depends only on its offset inside its buffer.
 // FLAT = false: sources are the per-parameter gradients, pointer table [C*P grads][R shards],
@@ -403,6 +403,14 @@ hipError_t launch_rs_c(const RsChunk* chunks, int64_t first, int64_t count, int 
     case 6: return launch_rs_ct<6, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
     case 7: return launch_rs_ct<7, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
     case 8: return launch_rs_ct<8, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 9: return launch_rs_ct<9, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 10: return launch_rs_ct<10, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 11: return launch_rs_ct<11, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 12: return launch_rs_ct<12, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 13: return launch_rs_ct<13, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 14: return launch_rs_ct<14, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 15: return launch_rs_ct<15, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
+    case 16: return launch_rs_ct<16, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
     default: return launch_rs_ct<0, FLAT>(chunks, first, count, grid, items, ptrs, P, C, S, vec, lds, s);
   }
 }

@@ -50,8 +50,8 @@ struct DeviceState {
   hipEvent_t dma_join[kDmaStreams] = {};
   int cus = 0;              // compute units of the device
   int lds_per_cu = 0;       // local memory per CU (bytes)
-  int rs_static_lds_ct = 0; // static local memory of the RS kernel, C <= 8
-  int rs_static_lds_rt = 0; // static local memory of the RS kernel, C > 8
+  int rs_static_lds_ct = 0; // static local memory of the RS kernel, C <= kRsMaxCt
+  int rs_static_lds_rt = 0; // static local memory of the RS kernel, C > kRsMaxCt
   int rs_env_cap = -1;      // TIDE_RS_WGS_PER_CU when set (0..64), else -1
 };
 
@@ -61,7 +61,7 @@ int rs_env_wgs_per_cu();
 // Dynamic local memory of an unbounded RS launch with C contributors on this device.
 inline int rs_launch_lds(const DeviceState& st, int C) {
   const int wgs = st.rs_env_cap >= 0 ? st.rs_env_cap : rs_wgs_per_cu(C);
-  return rs_dynamic_lds(st.lds_per_cu, C <= 8 ? st.rs_static_lds_ct : st.rs_static_lds_rt, wgs);
+  return rs_dynamic_lds(st.lds_per_cu, C <= kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt, wgs);
 }
 
 }  // namespace tide

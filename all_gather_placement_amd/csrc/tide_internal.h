@@ -35,9 +35,12 @@ namespace tide {
 // C (2C + 4 bytes per output), so the best count falls as C grows.  Measured with 128-thread
 // workgroups on the Llama-3.1-8B group: C = 8: 6 per CU beat 3, 4, 5, 7, 8 and no cap by 1-5%;
 // C = 4: 8 beat 6, 12 and 16 (+2.4% over 6); C = 2 and 1: 12 beat 8, 16 and no cap (C = 1: 4.1
-// TB/s at 6 -> 6.4 TB/s).  C > 8 takes the runtime-C path, which loads one contributor at a time
-// and streams best uncapped (3.5 -> 5.5 TB/s at C = 12).
-constexpr int rs_wgs_per_cu(int C) { return C <= 2 ? 12 : C <= 4 ? 8 : C <= 8 ? 6 : 0; }
+// TB/s at 6 -> 6.4 TB/s); C = 12: 6 beat 3, 4, 5 and no cap (5.93 TB/s); C = 16: 4 and 5 beat 2,
+// 3 and no cap (5.82 TB/s).  Contributor counts up to kRsMaxCt are compiled in (full-item path);
+// above, the runtime-C path loads one contributor at a time and streams best uncapped (at C = 12,
+// before 9..16 were compiled in: 3.5 TB/s capped at 6, 5.5 TB/s uncapped).
+constexpr int kRsMaxCt = 16;
+constexpr int rs_wgs_per_cu(int C) { return C <= 2 ? 12 : C <= 4 ? 8 : C <= 12 ? 6 : C <= kRsMaxCt ? 4 : 0; }
 #ifndef TIDE_RS_NQ
 #define TIDE_RS_NQ 2
 #endif
@@ -172,7 +175,7 @@ static_assert(sizeof(AgChunk) == 32, "AgChunk is two 16-byte scalar loads");
 // `dyn_lds` is the dynamic local memory each RS workgroup requests (occupancy cap; 0 = none);
 // `batch` (1 or 2) is the number of full AG items a workgroup loads before storing.
 // rs_lds_info: the local memory per CU of `device` and the static local memory of the RS kernel
-// for C <= 8 (compile-time contributor count) and for C > 8 (runtime count).
+// for C <= kRsMaxCt (compile-time contributor count) and above (runtime count).
 // rs_dynamic_lds: the dynamic local memory that admits at most `wgs_per_cu` RS workgroups per CU
 // (0 = no cap, or when it cannot be met).
 int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,

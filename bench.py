@@ -815,7 +815,7 @@ def main():
                         "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
         "roofline": {
             "bound": "hbm",
-            "kernel": f"rs_kernel<{cfg.C if cfg.C <= 8 else 0}, true, false>",
+            "kernel": f"rs_kernel<{cfg.C if cfg.C <= 16 else 0}, true, false>",
             "achieved": round(rs_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

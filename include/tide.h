@@ -141,9 +141,10 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              only for empty parameters).  Read in place, never written.
  *   shards     host [R]: shards[r] is rank r's flat fp32 device shard of S elements, 4-byte aligned.
  *   cu_budget  0: one launch, one short-lived workgroup per work item, with at most N of them
- *              resident per CU: N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 8, no cap above
- *              (each requests 1/N of the CU's local memory; fewer requests in flight stream HBM
- *              better than a full CU, and a workgroup's traffic grows with C).
+ *              resident per CU: N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 12, 4 for C <= 16,
+ *              no cap above (each requests 1/N of the CU's local memory; fewer requests in flight
+ *              stream HBM better than a full CU, and a workgroup's traffic grows with C).
+ *              C <= 16 runs a kernel compiled for that C; larger C a slower runtime-C kernel.
  *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of
  *              128 threads); each processes a bounded number of work items (4 by default, 80 KiB
  *              of traffic at C = 8) and exits, and the call issues as many launches as needed, so

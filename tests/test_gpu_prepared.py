@@ -294,9 +294,10 @@ def test_prepared_calls_from_threads(gpu_available):
 
 def test_rs_launch_shape_caps_occupancy(gpu_available):
     """Unbounded RS launches request 1/N of a gfx950 CU's 160 KiB of local memory per 128-thread
-    workgroup, N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 8; no cap above 8 contributors."""
+    workgroup, N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 12, 4 for C <= 16; no cap above 16."""
     lds_per_cu = 160 * 1024
-    for C, n in ((1, 12), (2, 12), (3, 8), (4, 8), (5, 6), (8, 6), (9, 0), (12, 0)):
+    for C, n in ((1, 12), (2, 12), (3, 8), (4, 8), (5, 6), (8, 6), (9, 6), (12, 6), (13, 4), (16, 4), (17, 0),
+                 (40, 0)):
         shape = tide_rs_launch_shape(C)
         say(f"RS launch shape C={C}: {shape}")
         assert shape["threads"] == 128 and shape["item_outputs"] == 1024
