@@ -53,7 +53,7 @@ def parse():
                     help="also capture the step (prepared RS + AG calls) in a HIP graph and time its replays")
     ap.add_argument("--interference", action="store_true",
                     help="instead of the step benchmark: slowdown of a concurrent one-wave bf16 GEMM per cu_budget")
-    ap.add_argument("--budgets", default="0,16,64,256,512,768,1024,1536,2048")
+    ap.add_argument("--budgets", default="0,8,16,32,64,128,256,512,768,1024,1536,2048")
     ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
     ap.add_argument("--reps", type=int, default=31,
                     help="repetitions per row of the interference measurements (medians)")
