@@ -70,7 +70,8 @@ struct Request {
 
 tide_status validate_rs(const tide_layout* L, int32_t C, const void* const* grads, float* const* shards,
                         int32_t cu_budget, Request* q) {
-  if (L == nullptr || grads == nullptr || shards == nullptr || C < 1 || cu_budget < 0) return TIDE_ERR_INVALID;
+  if (L == nullptr || grads == nullptr || shards == nullptr || C < 1 || cu_budget < -TIDE_RS_MAX_WGS_PER_CU)
+    return TIDE_ERR_INVALID;
   const int32_t P = L->P, R = L->R;
   const int64_t S = L->S;
   if (int64_t(C) * P > (int64_t(1) << 24)) return TIDE_ERR_INVALID;
@@ -105,7 +106,8 @@ tide_status validate_rs(const tide_layout* L, int32_t C, const void* const* grad
 
 tide_status validate_rs_slots(const tide_layout* L, int32_t C, const void* const* slots, float* const* shards,
                               int32_t cu_budget, Request* q) {
-  if (L == nullptr || slots == nullptr || shards == nullptr || C < 1 || cu_budget < 0) return TIDE_ERR_INVALID;
+  if (L == nullptr || slots == nullptr || shards == nullptr || C < 1 || cu_budget < -TIDE_RS_MAX_WGS_PER_CU)
+    return TIDE_ERR_INVALID;
   if (C > (1 << 24)) return TIDE_ERR_INVALID;
   const int32_t R = L->R;
   const int64_t S = L->S;
@@ -241,7 +243,7 @@ int ensure_dma(DeviceState* st) {
 // Enqueueing validated work
 // ---------------------------------------------------------------------------------------------
 
-// Launch plan for `count` work items: cu_budget 0 = one item per workgroup in one launch;
+// Launch plan for `count` work items: cu_budget <= 0 = one item per workgroup in one launch;
 // B > 0 = grids of at most `max_wgs` workgroups, each taking `bounded_items` items and exiting
 // (bounded_items 0: one launch, workgroups walk every item).
 struct Plan {
@@ -273,8 +275,9 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
     const bool flat = q.kind == kRsSlots;
     const int64_t rs_wgs = int64_t(q.cu_budget) * kBudgetThreads / kThreads;
     const Plan plan = plan_for(count, q.cu_budget, rs_wgs, kRsBoundedItems);
-    // Unbounded launches cap the RS workgroups per CU (by C); bounded ones are capped by the budget.
-    const int lds = q.cu_budget == 0 ? rs_launch_lds(*st, q.C) : 0;
+    // Unbounded launches cap the RS workgroups per CU (by C, or -cu_budget); bounded ones are
+    // capped by the budget.
+    const int lds = rs_launch_lds(*st, q.C, q.cu_budget);
     for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
       const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
       e = launch_rs(st->rs, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, tbl, flat ? 1 : L->P, q.C,
@@ -512,17 +515,19 @@ tide_status tide_call_launch(const tide_call* call, void* stream) {
   return e == hipSuccess ? TIDE_OK : tide::hip_fail(e);
 }
 
-tide_status tide_rs_launch_shape(int32_t C, int32_t* threads, int32_t* item_outputs, int32_t* lds_bytes) {
-  if (C < 1 || threads == nullptr || item_outputs == nullptr || lds_bytes == nullptr) return TIDE_ERR_INVALID;
+tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads, int32_t* item_outputs,
+                                 int32_t* lds_bytes) {
+  if (C < 1 || cu_budget < -TIDE_RS_MAX_WGS_PER_CU || threads == nullptr || item_outputs == nullptr ||
+      lds_bytes == nullptr)
+    return TIDE_ERR_INVALID;
   tide::DeviceState st;
   int dev = 0;
   int e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = tide::rs_lds_info(dev, &st.lds_per_cu, &st.rs_static_lds_ct, &st.rs_static_lds_rt);
+  if (e == hipSuccess) e = tide::rs_device_info(dev, &st);
   if (e != hipSuccess) return tide::hip_fail(e);
-  st.rs_env_cap = tide::rs_env_wgs_per_cu();
   *threads = tide::kThreads;
   *item_outputs = int32_t(tide::kRsChunk);
-  *lds_bytes = (C <= tide::kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt) + tide::rs_launch_lds(st, C);
+  *lds_bytes = (C <= tide::kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt) + tide::rs_launch_lds(st, C, cu_budget);
   return TIDE_OK;
 }
 

@@ -12,7 +12,6 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
-#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -92,12 +91,12 @@ void order_items(tide_layout* L) {
 
 void set_last_hip_error(int err) { g_last_hip_error = err; }
 
-int rs_env_wgs_per_cu() {
-  const char* env = std::getenv("TIDE_RS_WGS_PER_CU");
-  if (env == nullptr) return -1;
-  char* end = nullptr;
-  const long v = std::strtol(env, &end, 10);
-  return (end != env && *end == '\0' && v >= 0 && v <= 64) ? static_cast<int>(v) : -1;
+int rs_device_info(int device, DeviceState* st) {
+  hipError_t e = static_cast<hipError_t>(
+      rs_lds_info(device, &st->lds_per_cu, &st->rs_static_lds_ct, &st->rs_static_lds_rt));
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&st->lds_per_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&st->cus, hipDeviceAttributeMultiprocessorCount, device);
+  return e;
 }
 
 int device_state(const tide_layout* layout, DeviceState** out) {
@@ -110,9 +109,7 @@ int device_state(const tide_layout* layout, DeviceState** out) {
     return hipSuccess;
   }
   DeviceState st;
-  e = static_cast<hipError_t>(rs_lds_info(dev, &st.lds_per_cu, &st.rs_static_lds_ct, &st.rs_static_lds_rt));
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&st.cus, hipDeviceAttributeMultiprocessorCount, dev);
-  st.rs_env_cap = rs_env_wgs_per_cu();
+  e = static_cast<hipError_t>(rs_device_info(dev, &st));
   if (e != hipSuccess) return e;
   e = upload(layout->rs_chunks, &st.rs);
   if (e == hipSuccess) e = upload(layout->ag_chunks, &st.ag);

@@ -50,19 +50,27 @@ struct DeviceState {
   hipEvent_t dma_join[kDmaStreams] = {};
   int cus = 0;              // compute units of the device
   int lds_per_cu = 0;       // local memory per CU (bytes)
+  int lds_per_wg = 0;       // largest local memory one workgroup may request (bytes)
   int rs_static_lds_ct = 0; // static local memory of the RS kernel, C <= kRsMaxCt
   int rs_static_lds_rt = 0; // static local memory of the RS kernel, C > kRsMaxCt
-  int rs_env_cap = -1;      // TIDE_RS_WGS_PER_CU when set (0..64), else -1
 };
 
-// TIDE_RS_WGS_PER_CU from the environment (0..64; 0 = no cap), or -1 when unset or malformed.
-int rs_env_wgs_per_cu();
-
-// Dynamic local memory of an unbounded RS launch with C contributors on this device.
-inline int rs_launch_lds(const DeviceState& st, int C) {
-  const int wgs = st.rs_env_cap >= 0 ? st.rs_env_cap : rs_wgs_per_cu(C);
-  return rs_dynamic_lds(st.lds_per_cu, C <= kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt, wgs);
+// Dynamic local memory of an RS launch with C contributors at `cu_budget` on this device: 0 caps
+// the RS workgroups per CU at rs_wgs_per_cu(C), -N at N; bounded launches (> 0) add none.  Needs
+// lds_per_cu, lds_per_wg and the static sizes filled in (rs_device_info).
+inline int rs_launch_lds(const DeviceState& st, int C, int cu_budget) {
+  if (cu_budget > 0) return 0;
+  const int wgs = cu_budget < 0 ? -cu_budget : rs_wgs_per_cu(C);
+  const int static_lds = C <= kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt;
+  const int dyn = rs_dynamic_lds(st.lds_per_cu, static_lds, wgs);
+  // caps below what one workgroup's local memory can express become the smallest that it can
+  const int room = st.lds_per_wg - static_lds;
+  return dyn < room ? dyn : (room > 0 ? room : 0);
 }
+
+// Fills cus, lds_per_cu, lds_per_wg and the RS kernel's static local memory for `device`.
+// Returns a hipError_t.
+int rs_device_info(int device, DeviceState* st);
 
 }  // namespace tide
 

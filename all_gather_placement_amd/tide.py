@@ -76,7 +76,7 @@ def load_library(path: str | None = None):
         "tide_rs_slots_prepare": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]),
         "tide_call_launch": (i32, [vp, vp]),
         "tide_call_destroy": (None, [vp]),
-        "tide_rs_launch_shape": (i32, [i32, P_i32, P_i32, P_i32]),
+        "tide_rs_launch_shape": (i32, [i32, i32, P_i32, P_i32, P_i32]),
         "tide_status_str": (ctypes.c_char_p, [i32]),
         "tide_last_hip_error": (i32, []),
     }
@@ -217,11 +217,12 @@ def tide_call_destroy(call: int):
     load_library().tide_call_destroy(call)
 
 
-def tide_rs_launch_shape(C: int = 8) -> dict:
-    """Unbounded RS launch shape for C contributors on the current device: threads, item_outputs,
+def tide_rs_launch_shape(C: int = 8, cu_budget: int = 0) -> dict:
+    """RS launch shape for C contributors at cu_budget on the current device: threads, item_outputs,
     lds_bytes."""
     v = [ctypes.c_int32() for _ in range(3)]
-    _check(load_library().tide_rs_launch_shape(int(C), *[ctypes.byref(x) for x in v]), "tide_rs_launch_shape")
+    _check(load_library().tide_rs_launch_shape(int(C), int(cu_budget), *[ctypes.byref(x) for x in v]),
+           "tide_rs_launch_shape")
     return dict(zip(("threads", "item_outputs", "lds_bytes"), (x.value for x in v)))
 
 

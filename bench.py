@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_1_8b_layer")
     ap.add_argument("--cu-budget", type=int, default=0)
+    ap.add_argument("--rs-wgs-per-cu", type=int, default=0,
+                    help="unbounded RS with at most N workgroups per CU (RS cu_budget -N; 0 = the library's cap by C)")
     ap.add_argument("--ag-mode", choices=["kernel", "sdma", "copy2d"], default="kernel")
     ap.add_argument("--contributors", type=int, default=0,
                     help="override the workload's contributor count C (default: the workload's own)")
@@ -607,7 +609,11 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the node-local level on one GPU only; runs on more than one GPU "
-              "(--gpus > 1) are not part of this build.", file=sys.stderr, flush=True)
+              "(--gpus > 1) are not supported.", file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.rs_wgs_per_cu and (args.cu_budget or not 0 < args.rs_wgs_per_cu <= 64):
+        print("--rs-wgs-per-cu takes 1..64 and applies to the unbounded RS only (--cu-budget 0)",
+              file=sys.stderr, flush=True)
         sys.exit(2)
 
     def log(msg):
@@ -673,7 +679,8 @@ def main():
     L.prepare()
     stream = torch.cuda.current_stream()
     # Arguments are validated and marshalled once; each call below is one C-ABI call.
-    rs_call = L.bind_rs(grads, shards, cu_budget=args.cu_budget)
+    rs_budget = -args.rs_wgs_per_cu if args.rs_wgs_per_cu else args.cu_budget
+    rs_call = L.bind_rs(grads, shards, cu_budget=rs_budget)
     ag_call = L.bind_ag(stage, params, mode=ag_mode, cu_budget=args.cu_budget)
 
     def step(ev_rs=None, ev_ag=None):
@@ -725,7 +732,7 @@ def main():
             fn()
         return (time.perf_counter() - t) / n * 1e6
     host_bound = host_us(lambda: rs_call.launch(stream))
-    host_unbound = host_us(lambda: L.rs_bf16_to_fp32(grads, shards, cu_budget=args.cu_budget, stream=stream))
+    host_unbound = host_us(lambda: L.rs_bf16_to_fp32(grads, shards, cu_budget=rs_budget, stream=stream))
     torch.cuda.synchronize()
 
     graph_info = None
@@ -780,7 +787,7 @@ def main():
     rs_gbps = rs_bytes / (rs_mean * 1e-3) / 1e9
     ag_gbps = ag_bytes / (ag_mean * 1e-3) / 1e9
     # counters were taken for the workload's own contributor count and the unbounded launch
-    traffic = read_traffic(cfg.name) if args.cu_budget == 0 and not args.contributors else None
+    traffic = read_traffic(cfg.name) if rs_budget == 0 and not args.contributors else None
 
     out = {
         "metric": METRIC,
@@ -798,7 +805,7 @@ def main():
         "config": {
             "workload": f"{cfg.name} RS+AG step (R={cfg.R}, C={cfg.C}, P={cfg.P})",
             "R": cfg.R, "C": cfg.C, "P": cfg.P, "numel": numel, "S": S,
-            "cu_budget": args.cu_budget, "ag_mode": args.ag_mode,
+            "cu_budget": args.cu_budget, "rs_cu_budget": rs_budget, "ag_mode": args.ag_mode,
             "rs_bytes": rs_bytes, "ag_bytes": ag_bytes, "parallelism": "none (1 GPU, node-local level)",
         },
         "rs_gbps": round(rs_gbps, 2),
@@ -809,7 +816,7 @@ def main():
         "ag_frac_of_peak": round(ag_gbps / HBM_PEAK_GBPS, 4),
         "ag_ms_mean": round(ag_mean, 5),
         "rs_host_us_per_call": {"bound": round(host_bound, 1), "validate_and_marshal": round(host_unbound, 1)},
-        "rs_launch_shape": tide_rs_launch_shape(cfg.C),
+        "rs_launch_shape": tide_rs_launch_shape(cfg.C, rs_budget),
         "graph_replay": graph_info,
         "calibration": {"d2d_copy_gbps": round(cal_gbps, 2), "bytes_moved": 2 * (rs_bytes // 2),
                         "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
@@ -823,6 +830,9 @@ def main():
             "traffic": traffic,
         },
         "kernel_source_sha256_16": kernel_source_hash(),
+        "software": {"torch": torch.__version__, "hip": torch.version.hip},
+        "device": {"name": torch.cuda.get_device_name(dev),
+                   "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
     }
     L.close()
     del grads, shards, stage, params

@@ -36,9 +36,7 @@
  *     TIDE_ERR_HIP or TIDE_ERR_UNSUPPORTED.
  *   - A layout is immutable after creation and may be used from several streams and threads at
  *     once.  The library owns it; the caller owns every buffer and stream.
- *   - Environment: TIDE_RS_WGS_PER_CU (an integer 0..64, read when a layout first meets a device)
- *     replaces the per-CU cap of unbounded RS workgroups for every C (0 = no cap).  It changes
- *     speed only, never results.
+ *   - The library reads no environment variables: every choice (mode, cu_budget) is an argument.
  */
 #ifndef TIDE_H
 #define TIDE_H
@@ -50,6 +48,9 @@ extern "C" {
 #endif
 
 typedef struct tide_layout tide_layout;
+
+/* Largest per-CU cap an RS call may ask for with a negative cu_budget. */
+#define TIDE_RS_MAX_WGS_PER_CU 64
 
 typedef enum tide_status {
   TIDE_OK = 0,
@@ -145,10 +146,13 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              no cap above (each requests 1/N of the CU's local memory; fewer requests in flight
  *              stream HBM better than a full CU, and a workgroup's traffic grows with C).
  *              C <= 16 runs a kernel compiled for that C; larger C a slower runtime-C kernel.
+ *              -N (1 <= N <= TIDE_RS_MAX_WGS_PER_CU): as 0, with at most N per CU for any C (an N
+ *              at or above the hardware's own limit leaves that limit).
  *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of
  *              128 threads); each processes a bounded number of work items (4 by default, 80 KiB
  *              of traffic at C = 8) and exits, and the call issues as many launches as needed, so
  *              a concurrent kernel's workgroups find free CUs within one short launch.
+ *              The budget changes speed and residency only, never results.
  *   stream     hipStream_t as void*.
  * Result, for every r, p and element k of the slice: shards[r][o_p + k] =
  *   x_0 (+) x_1 (+) ... (+) x_{C-1}, x_c = grads[c*P+p][r*m_p*L_p + k] widened exactly to fp32,
@@ -157,7 +161,8 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *   independently of cu_budget; fp32 denormals are kept.
  * 16-byte-aligned grads and shards take the vector path; any other legal alignment takes a
  * slower element path with identical results.
- * Errors: TIDE_ERR_INVALID (null layout/arrays, C < 1, C*P > 2^24, cu_budget < 0, null or
+ * Errors: TIDE_ERR_INVALID (null layout/arrays, C < 1, C*P > 2^24,
+ * cu_budget < -TIDE_RS_MAX_WGS_PER_CU, null or
  * misaligned pointer, any shard overlapping another shard or any gradient), TIDE_ERR_NOMEM,
  * TIDE_ERR_HIP.
  */
@@ -171,7 +176,7 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
  *   params     host [P]: params[p] is parameter p's contiguous bf16 device storage of rows_p * L_p
  *              elements (NULL allowed only for empty parameters).
  *   mode       TIDE_AG_KERNEL, TIDE_AG_SDMA or TIDE_AG_COPY2D.
- *   cu_budget  as for the RS, counted in 256-thread slots (TIDE_AG_KERNEL only; its workgroups
+ *   cu_budget  >= 0, as for the RS, counted in 256-thread slots (TIDE_AG_KERNEL only; its workgroups
  *              are 128 threads, so B admits 2B of them, each copying 8 work items -- 64 KiB of
  *              traffic -- before it exits; with at most 4 of them per CU, two items are loaded
  *              before either is stored).  0: one workgroup per work item, no cap.
@@ -180,8 +185,8 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
  * All pointers must be 2-byte aligned; 16-byte alignment selects the vector path.
  * TIDE_AG_SDMA work is ordered after the caller's earlier work on `stream`, and later work on
  * `stream` waits for it (event fork/join with the internal copy streams).
- * Errors: TIDE_ERR_INVALID (null/misaligned pointer, bad mode, a parameter overlapping the stage
- * or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a copy kind), TIDE_ERR_NOMEM,
+ * Errors: TIDE_ERR_INVALID (null/misaligned pointer, bad mode, cu_budget < 0, a parameter
+ * overlapping the stage or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a copy kind), TIDE_ERR_NOMEM,
  * TIDE_ERR_HIP.
  */
 tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params,
@@ -257,12 +262,13 @@ tide_status tide_call_launch(const tide_call* call, void* stream);
  * NULL is ignored. */
 void tide_call_destroy(tide_call* call);
 
-/* Launch shape of unbounded (cu_budget 0) RS calls with C contributors on the current device:
- * threads per workgroup, outputs per full work item, and the local memory (static + dynamic,
- * bytes) each workgroup requests -- a CU holds as many RS workgroups as fit in its local memory,
- * so this sets the occupancy cap.  Errors: TIDE_ERR_INVALID (C < 1 or a NULL pointer),
- * TIDE_ERR_HIP. */
-tide_status tide_rs_launch_shape(int32_t C, int32_t* threads, int32_t* item_outputs, int32_t* lds_bytes);
+/* Launch shape of RS calls with C contributors at `cu_budget` on the current device: threads per
+ * workgroup, outputs per full work item, and the local memory (static + dynamic, bytes) each
+ * workgroup requests -- a CU holds as many RS workgroups as fit in its local memory, so for
+ * cu_budget <= 0 this sets the per-CU cap.  Errors: TIDE_ERR_INVALID (C < 1,
+ * cu_budget < -TIDE_RS_MAX_WGS_PER_CU or a NULL pointer), TIDE_ERR_HIP. */
+tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads, int32_t* item_outputs,
+                                 int32_t* lds_bytes);
 
 /* Static, NUL-terminated name of a status code ("TIDE_OK", ...; "unknown" otherwise). */
 const char* tide_status_str(int32_t status);

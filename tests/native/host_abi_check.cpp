@@ -127,7 +127,8 @@ int main() {
   tide_call* call = nullptr;
   CHECK(tide_rs_prepare(L, 1, g, sh, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
   CHECK(tide_rs_prepare(L, 0, g, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
-  CHECK(tide_rs_prepare(L, 1, g, sh2, -1, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_rs_prepare(L, 1, g, sh2, -TIDE_RS_MAX_WGS_PER_CU - 1, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, -1, &call) == TIDE_ERR_INVALID);
   CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, 0, &call) == TIDE_ERR_INVALID);
   CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, 7, 0, &call) == TIDE_ERR_INVALID);
   CHECK(tide_slot_pack_prepare(L, const_cast<const void* const*>(pp), reinterpret_cast<void*>(base), 0, &call) ==
@@ -135,9 +136,10 @@ int main() {
   CHECK(tide_rs_slots_prepare(L, 2, sl, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
   CHECK(tide_rs_prepare(L, 1, g, sh2, 0, nullptr) == TIDE_ERR_INVALID);  // no output handle
   CHECK(tide_call_launch(nullptr, nullptr) == TIDE_ERR_INVALID);
-  CHECK(tide_rs_launch_shape(8, nullptr, nullptr, nullptr) == TIDE_ERR_INVALID);
+  CHECK(tide_rs_launch_shape(8, 0, nullptr, nullptr, nullptr) == TIDE_ERR_INVALID);
   int32_t th = 0, it = 0, lds = 0;
-  CHECK(tide_rs_launch_shape(0, &th, &it, &lds) == TIDE_ERR_INVALID);
+  CHECK(tide_rs_launch_shape(0, 0, &th, &it, &lds) == TIDE_ERR_INVALID);
+  CHECK(tide_rs_launch_shape(8, -TIDE_RS_MAX_WGS_PER_CU - 1, &th, &it, &lds) == TIDE_ERR_INVALID);
   tide_call_destroy(nullptr);
   CHECK(tide_last_hip_error() == 0);
   tide_layout_destroy(L);

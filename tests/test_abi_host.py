@@ -270,7 +270,7 @@ def test_rs_rejects_bad_arguments_before_any_hip_call():
         assert lib.tide_rs_bf16_to_fp32(None, 4, _vp_array(g), _vp_array(s), 0, None) == INV
         assert lib.tide_rs_bf16_to_fp32(L.handle, 4, None, _vp_array(s), 0, None) == INV
         assert call(g, s, C=0) == INV
-        assert call(g, s, budget=-1) == INV
+        assert call(g, s, budget=-65) == INV           # beyond TIDE_RS_MAX_WGS_PER_CU
         g2 = list(g); g2[5] = None
         assert call(g2, s) == INV                     # null gradient of a non-empty parameter
         g3 = list(g); g3[1] += 1
@@ -325,7 +325,7 @@ def test_slot_entry_points_reject_bad_arguments_before_any_hip_call():
         shards = [(1 << 35) + r * (1 << 20) for r in range(L.R)]
         rs = lambda sl, sh, C=4, budget=0: lib.tide_rs_slots_bf16_to_fp32(L.handle, C, _vp_array(sl), _vp_array(sh), budget, None)
         assert rs(slots, shards, C=0) == INV
-        assert rs(slots, shards, budget=-1) == INV
+        assert rs(slots, shards, budget=-65) == INV
         ss = list(slots); ss[2] = None
         assert rs(ss, shards) == INV
         sh = list(shards); sh[0] = slots[1] + 8

@@ -115,7 +115,7 @@ def test_prepare_rejects_what_the_immediate_call_rejects(gpu_available):
         with pytest.raises(TideError, match="INVALID"):
             L.bind_rs(grads, bad)
         with pytest.raises(TideError, match="INVALID"):
-            L.bind_rs(grads, shards, cu_budget=-1)
+            L.bind_rs(grads, shards, cu_budget=-65)
         stage = torch.zeros(R * S, dtype=torch.bfloat16, device="cuda")
         params = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
         with pytest.raises(TideError, match="INVALID"):
@@ -307,24 +307,32 @@ def test_rs_launch_shape_caps_occupancy(gpu_available):
             assert shape["lds_bytes"] * 16 <= lds_per_cu, (C, shape)  # only the kernel's own
 
 
-def test_rs_occupancy_override_changes_speed_only(gpu_available, monkeypatch):
-    """TIDE_RS_WGS_PER_CU overrides the cap for layouts that first meet the device afterwards;
-    the shards stay bit for bit the same."""
-    shapes, R, C = GROUPS[1]
-    geo, S = ogeo.group_geometry(shapes, R)
-    g = [[normal_bf16_bits(s, 1.0, 160, c, p) for p, s in enumerate(shapes)] for c in range(C)]
-    grads = [[dev_bf16(x) for x in row] for row in g]
-    want = oracle.reduce_scatter(g, shapes, R)
-    for value, lds in (("3", (160 * 1024 // 3) // 512 * 512), ("0", 4096), ("junk", None), ("65", None)):
-        monkeypatch.setenv("TIDE_RS_WGS_PER_CU", value)
-        say(f"TIDE_RS_WGS_PER_CU={value}")
-        shape = tide_rs_launch_shape(C)
-        if lds is None:  # ignored: the built-in cap
-            assert shape["lds_bytes"] * 6 <= 160 * 1024 < shape["lds_bytes"] * 7
-        else:
-            assert shape["lds_bytes"] == lds
-        with Layout(shapes, R) as L:
-            shards = poisoned_shards(R, S)
-            L.rs_bf16_to_fp32(grads, shards)
-            torch.cuda.synchronize()
-            assert_rs_equal(shards_bits(shards), want)
+def test_rs_negative_budget_sets_the_cap_and_changes_speed_only(gpu_available):
+    """cu_budget = -N: one unbounded launch with at most N RS workgroups per CU, for any C (compiled-C
+    and runtime-C kernels); the shards stay bit for bit those of the oracle, immediate and prepared."""
+    for shapes, R, C in (GROUPS[1], ([(300, 70), (17,), (2048, 3)], 4, 18)):
+        geo, S = ogeo.group_geometry(shapes, R)
+        g = [[normal_bf16_bits(s, 1.0, 160, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+        grads = [[dev_bf16(x) for x in row] for row in g]
+        want = oracle.reduce_scatter(g, shapes, R)
+        static = tide_rs_launch_shape(C, 5)["lds_bytes"]  # bounded launches add none: the kernel's own
+        for n in (1, 3, 6, 16, 64):
+            shape = tide_rs_launch_shape(C, -n)
+            say(f"RS C={C} cu_budget={-n}: {shape}")
+            want_lds = max(static, (160 * 1024 // n) // 512 * 512)
+            if n == 1:  # may exceed one workgroup's limit: then the smallest cap it can express
+                assert static < shape["lds_bytes"] <= want_lds, shape
+            else:
+                assert shape["lds_bytes"] == want_lds, (n, shape)
+            with Layout(shapes, R) as L:
+                shards = poisoned_shards(R, S)
+                L.rs_bf16_to_fp32(grads, shards, cu_budget=-n)
+                torch.cuda.synchronize()
+                assert_rs_equal(shards_bits(shards), want)
+                shards = poisoned_shards(R, S)
+                call = L.bind_rs(grads, shards, cu_budget=-n)
+                call.launch()
+                torch.cuda.synchronize()
+                call.close()
+                assert_rs_equal(shards_bits(shards), want)
+        assert static < 160 * 1024 // 16
