@@ -53,9 +53,33 @@ __global__ __launch_bounds__(kProbeThreads) void probe_small(tide_probe_record* 
   record(records, t0);
 }
 
+// One wave that sleeps for `ticks` of the constant-rate wall clock and reads the shader cycle
+// counter (s_memtime, which counts shader clocks) at both ends: cycles / wall time = the mean shader
+// clock of the CU it ran on over that interval.
+__global__ __launch_bounds__(64) void probe_clock(uint64_t* out, unsigned long long ticks) {
+  const unsigned long long w0 = static_cast<unsigned long long>(wall_clock64());
+  const unsigned long long c0 = static_cast<unsigned long long>(clock64());
+  spin_until(w0, ticks);
+  const unsigned long long c1 = static_cast<unsigned long long>(clock64());
+  const unsigned long long w1 = static_cast<unsigned long long>(wall_clock64());
+  if (threadIdx.x == 0) {
+    out[0] = w0;
+    out[1] = w1;
+    out[2] = c0;
+    out[3] = c1;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t tide_probe_clock(int64_t spin_ticks, uint64_t* out, void* stream) {
+  if (spin_ticks < 0 || out == nullptr) return -1;
+  hipLaunchKernelGGL(probe_clock, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), out,
+                     static_cast<unsigned long long>(spin_ticks));
+  return static_cast<int32_t>(hipGetLastError());
+}
 
 int32_t tide_probe_launch(int32_t num_wgs, int32_t shape, int64_t spin_ticks, tide_probe_record* records,
                           void* stream) {

@@ -25,6 +25,8 @@ def load_probe_library():
         lib.tide_probe_launch.restype = ctypes.c_int32
         lib.tide_probe_launch.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p]
+        lib.tide_probe_clock.restype = ctypes.c_int32
+        lib.tide_probe_clock.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         lib.tide_probe_wall_clock_khz.restype = ctypes.c_int64
         lib.tide_probe_wall_clock_khz.argtypes = []
         _lib = lib
@@ -45,6 +47,27 @@ def probe_launch(num_wgs: int, shape: int, spin_ticks: int, records=None, stream
                                None if records is None else records.data_ptr(), handle)
     if rc != 0:
         raise RuntimeError(f"tide_probe_launch failed: {rc}")
+
+
+def clock_probe(spin_ticks: int, out, stream=None):
+    """Launch the shader clock probe; out: a torch int64 cuda tensor of at least 4 elements."""
+    lib = load_probe_library()
+    if out.numel() * out.element_size() < 32 or not out.is_cuda:
+        raise ValueError("out must be a cuda tensor of at least 32 bytes")
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream()
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    rc = lib.tide_probe_clock(int(spin_ticks), out.data_ptr(), handle)
+    if rc != 0:
+        raise RuntimeError(f"tide_probe_clock failed: {rc}")
+
+
+def clock_mhz(out_host, wall_khz: int) -> float:
+    """Mean shader clock (MHz) from the probe's four values (a host sequence of 4 integers)."""
+    w0, w1, c0, c1 = (int(x) & 0xFFFFFFFFFFFFFFFF for x in list(out_host)[:4])
+    return (c1 - c0) / max(w1 - w0, 1) * wall_khz / 1e3
 
 
 def wall_clock_khz() -> int:

@@ -783,6 +783,31 @@ def main():
     del cal_src, cal_dst
     log(f"device-to-device copy of the same bytes: {cal_gbps:.0f} GB/s (median {cal_med:.4f} ms)")
 
+    # Shader clock (clocks are not fixed on these devices, so they are recorded): one sleeping probe
+    # wave on a side stream reads the shader cycle counter against the wall clock for 2 ms, once with
+    # the device idle and once while RS calls run back to back beside it (outside the timed region).
+    clock_info = None
+    try:
+        from all_gather_placement_amd import probe as pr
+
+        khz = pr.wall_clock_khz()
+        ticks = 2 * khz  # 2 ms
+        out = torch.zeros(4, dtype=torch.int64, device=dev)
+        side = torch.cuda.Stream(device=dev)
+        pr.clock_probe(ticks, out, side)
+        side.synchronize()
+        idle = pr.clock_mhz(out.cpu().tolist(), khz)
+        torch.cuda.synchronize()
+        pr.clock_probe(ticks, out, side)
+        for _ in range(int(2.5 / max(rs_mean, 1e-3)) + 2):  # > 2.5 ms of RS, covering the probe
+            rs_call.launch(stream)
+        torch.cuda.synchronize()
+        clock_info = {"idle_mhz": round(idle, 1), "during_rs_mhz": round(pr.clock_mhz(out.cpu().tolist(), khz), 1),
+                      "method": "s_memtime cycles / wall clock over 2 ms, one probe wave on a side stream"}
+        log(f"shader clock: idle {clock_info['idle_mhz']} MHz, during the RS {clock_info['during_rs_mhz']} MHz")
+    except (RuntimeError, OSError) as e:  # a measurement aid only: the line is still printed
+        clock_info = {"error": str(e)}
+
     value = (rs_bytes + ag_bytes) / (ms_per_step * 1e-3) / 1e9
     rs_gbps = rs_bytes / (rs_mean * 1e-3) / 1e9
     ag_gbps = ag_bytes / (ag_mean * 1e-3) / 1e9
@@ -831,6 +856,7 @@ def main():
         },
         "kernel_source_sha256_16": kernel_source_hash(),
         "software": {"torch": torch.__version__, "hip": torch.version.hip},
+        "shader_clock": clock_info,
         "device": {"name": torch.cuda.get_device_name(dev),
                    "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count},
     }

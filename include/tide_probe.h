@@ -51,6 +51,18 @@ enum {
 int32_t tide_probe_launch(int32_t num_wgs, int32_t shape, int64_t spin_ticks, tide_probe_record* records,
                           void* stream);
 
+/*
+ * Shader clock probe: one 64-thread workgroup on `stream` sleeps until `spin_ticks` wall-clock ticks
+ * have passed (at most 2^26 polls) and writes out[0..3] = wall clock at start and end, shader cycle
+ * counter (s_memtime) at start and end.  (out[3]-out[2]) / (out[1]-out[0]) * wall-clock kHz is the
+ * mean shader clock of its CU over the interval; launched beside other work on another stream it
+ * records the clock that work ran at ([Endgame] Table 4 fixes the SM clock; MI355X boxes without
+ * that privilege record it instead).
+ *   out  device array of 4 uint64_t, written with vector stores.
+ * Returns 0 or a hipError_t value; -1 for spin_ticks < 0 or a NULL `out`.
+ */
+int32_t tide_probe_clock(int64_t spin_ticks, uint64_t* out, void* stream);
+
 /* Device wall-clock rate in kHz (hipDeviceAttributeWallClockRate of the current device), or -1. */
 int64_t tide_probe_wall_clock_khz(void);
 

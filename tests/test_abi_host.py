@@ -342,9 +342,12 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     text = open(os.path.join(ROOT, "include", "tide_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(tide_probe_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["tide_probe_launch", "tide_probe_wall_clock_khz"]
+    assert names == ["tide_probe_clock", "tide_probe_launch", "tide_probe_wall_clock_khz"]
     for n in names:
         assert hasattr(lib, n)
     assert lib.tide_probe_launch(0, 0, 10, None, None) == -1
     assert lib.tide_probe_launch(4, 7, 10, None, None) == -1
     assert lib.tide_probe_launch(4, 0, -1, None, None) == -1
+    assert lib.tide_probe_clock(-1, 1 << 40, None) == -1
+    assert lib.tide_probe_clock(10, None, None) == -1
+    assert pr.clock_mhz([0, 100000, 5, 5 + 2_400_000], 100000) == 2400.0  # 1 ms of wall clock, 2.4M cycles

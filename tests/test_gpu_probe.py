@@ -26,3 +26,17 @@ def test_probe_records(gpu_available, shape):
         # 64 KiB of LDS and 256 VGPRs per wave: alone on the device, one workgroup per CU in one wave
         assert len(np.unique(d["cu_key"])) == n
         assert (d["start"].max() - d["start"].min()) / tpu < 20.0
+
+
+def test_clock_probe_reads_a_shader_clock(gpu_available):
+    """The clock probe's cycle count over 1 ms of wall clock is a shader clock in the range an MI355X
+    runs at (idle or busy), and its wall-clock interval covers the requested sleep."""
+    khz = pr.wall_clock_khz()
+    out = torch.zeros(4, dtype=torch.int64, device="cuda")
+    pr.clock_probe(khz, out)  # 1 ms
+    torch.cuda.synchronize()
+    w0, w1, c0, c1 = out.cpu().tolist()
+    assert w1 - w0 >= khz and c1 > c0
+    mhz = pr.clock_mhz([w0, w1, c0, c1], khz)
+    print(f"[gpu-probe] shader clock over 1 ms: {mhz:.0f} MHz", flush=True)
+    assert 100.0 < mhz < 3000.0
