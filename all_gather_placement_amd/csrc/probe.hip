@@ -70,9 +70,107 @@ __global__ __launch_bounds__(64) void probe_clock(uint64_t* out, unsigned long l
   }
 }
 
+// RS-shaped mix probe: the access shape of the reduce-scatter's full work items, with the reads or
+// the writes left out.  One 128-thread workgroup per 1024-output item, items spread over the 8 XCDs
+// in contiguous ranges; per lane one 16-byte non-temporal buffer load from each of the C
+// contributors, 8 widen-and-add sums in ascending contributor order, an LDS exchange, and two
+// 16-byte non-temporal stores of whole cache lines.  MODE 0: loads and stores; 1: loads only (the
+// stores sit behind a test no sum can pass, which keeps the loads live); 2: stores only (a pattern).
+constexpr int kMixThreads = 128;
+constexpr int kMixItem = kMixThreads * 8;
+typedef unsigned int mix_u32x4 __attribute__((ext_vector_type(4)));
+typedef float mix_f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRawBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kNtLoad = 2;                     // nt
+constexpr int kNtStore = 18;                   // nt sc1
+
+template <int CT, int MODE>
+__global__ __launch_bounds__(kMixThreads) void probe_mix(const unsigned short* const* __restrict__ src,
+                                                          float* __restrict__ dst, int64_t items) {
+  __shared__ mix_f32x4 xfer[2 * kMixThreads];
+  const int64_t b = blockIdx.x, x = b % 8, i = b / 8;
+  const int64_t item = x * (items / 8) + (x < items % 8 ? x : items % 8) + i;
+  const int tid = threadIdx.x;
+  mix_f32x4 o0, o1;
+  if (MODE == 2) {
+    o0 = mix_f32x4{float(tid), 1.0f, 2.0f, 3.0f};
+    o1 = mix_f32x4{float(tid), 4.0f, 5.0f, 6.0f};
+  } else {
+    mix_u32x4 v[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<unsigned short*>(src[c] + item * kMixItem), 0, 2 * kMixItem, kRawBufferWord3);
+      v[c] = __builtin_bit_cast(mix_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * tid, 0, kNtLoad));
+    }
+    float a[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[2 * k] = __uint_as_float(v[0][k] << 16);
+      a[2 * k + 1] = __uint_as_float(v[0][k] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int c = 1; c < CT; ++c)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a[2 * k] += __uint_as_float(v[c][k] << 16);
+        a[2 * k + 1] += __uint_as_float(v[c][k] & 0xffff0000u);
+      }
+    xfer[2 * tid] = mix_f32x4{a[0], a[1], a[2], a[3]};
+    xfer[2 * tid + 1] = mix_f32x4{a[4], a[5], a[6], a[7]};
+    __syncthreads();
+    o0 = xfer[tid];
+    o1 = xfer[tid + kMixThreads];
+    // a NaN with payload 0x1234 in its low bits: sums of widened bf16 values never produce it
+    if (MODE == 1 && __float_as_uint(o0.x) != 0x7fc01234u) return;
+  }
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc(dst + item * kMixItem, 0, 4 * kMixItem, kRawBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(mix_u32x4, o0), rd, 16 * tid, 0, kNtStore);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(mix_u32x4, o1), rd, 16 * (tid + kMixThreads), 0,
+                                         kNtStore);
+}
+
+template <int CT, int MODE>
+int launch_mix(const unsigned short* const* src, float* dst, int64_t items, int32_t lds_bytes, hipStream_t s) {
+  hipFuncAttributes attr;
+  hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&probe_mix<CT, MODE>));
+  if (e != hipSuccess) return e;
+  const int dyn = lds_bytes > static_cast<int>(attr.sharedSizeBytes) ? lds_bytes - static_cast<int>(attr.sharedSizeBytes) : 0;
+  hipLaunchKernelGGL((probe_mix<CT, MODE>), dim3(static_cast<unsigned>(items)), dim3(kMixThreads), dyn, s, src, dst,
+                     items);
+  return hipGetLastError();
+}
+
+template <int CT>
+int launch_mix_c(int32_t mode, const unsigned short* const* src, float* dst, int64_t items, int32_t lds_bytes,
+                 hipStream_t s) {
+  switch (mode) {
+    case TIDE_PROBE_MIX_BOTH: return launch_mix<CT, 0>(src, dst, items, lds_bytes, s);
+    case TIDE_PROBE_MIX_READS: return launch_mix<CT, 1>(src, dst, items, lds_bytes, s);
+    default: return launch_mix<CT, 2>(src, dst, items, lds_bytes, s);
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t tide_probe_mix(int32_t C, int32_t mode, const void* const* src, float* dst, int64_t items, int32_t lds_bytes,
+                       void* stream) {
+  if ((C != 1 && C != 2 && C != 4 && C != 8) || mode < TIDE_PROBE_MIX_BOTH || mode > TIDE_PROBE_MIX_WRITES ||
+      items < 1 || items > 0x7fffffff || lds_bytes < 0 || dst == nullptr ||
+      (mode != TIDE_PROBE_MIX_WRITES && src == nullptr))
+    return -1;
+  const unsigned short* const* s = reinterpret_cast<const unsigned short* const*>(src);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  switch (C) {
+    case 1: return launch_mix_c<1>(mode, s, dst, items, lds_bytes, hs);
+    case 2: return launch_mix_c<2>(mode, s, dst, items, lds_bytes, hs);
+    case 4: return launch_mix_c<4>(mode, s, dst, items, lds_bytes, hs);
+    default: return launch_mix_c<8>(mode, s, dst, items, lds_bytes, hs);
+  }
+}
 
 int32_t tide_probe_clock(int64_t spin_ticks, uint64_t* out, void* stream) {
   if (spin_ticks < 0 || out == nullptr) return -1;

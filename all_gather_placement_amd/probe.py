@@ -11,6 +11,9 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 TIDE_PROBE_GEMM_SHAPED = 0
 TIDE_PROBE_SMALL = 1
+TIDE_PROBE_MIX_BOTH = 0
+TIDE_PROBE_MIX_READS = 1
+TIDE_PROBE_MIX_WRITES = 2
 RECORD_BYTES = 32
 _lib = None
 
@@ -25,6 +28,9 @@ def load_probe_library():
         lib.tide_probe_launch.restype = ctypes.c_int32
         lib.tide_probe_launch.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p]
+        lib.tide_probe_mix.restype = ctypes.c_int32
+        lib.tide_probe_mix.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
         lib.tide_probe_clock.restype = ctypes.c_int32
         lib.tide_probe_clock.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
         lib.tide_probe_wall_clock_khz.restype = ctypes.c_int64
@@ -47,6 +53,25 @@ def probe_launch(num_wgs: int, shape: int, spin_ticks: int, records=None, stream
                                None if records is None else records.data_ptr(), handle)
     if rc != 0:
         raise RuntimeError(f"tide_probe_launch failed: {rc}")
+
+
+def mix_launch(C: int, mode: int, src, dst, items: int, lds_bytes: int = 0, stream=None):
+    """Launch the RS-shaped mix probe.  src: int64 cuda tensor of C contributor pointers (bf16, 1024*items
+    each, 16-byte aligned); dst: fp32 cuda tensor of 1024*items elements, 16-byte aligned."""
+    lib = load_probe_library()
+    if dst.dtype.itemsize != 4 or dst.numel() < 1024 * items or not dst.is_cuda or dst.data_ptr() % 16:
+        raise ValueError("dst must be a 16-byte-aligned 4-byte cuda tensor of at least 1024*items elements")
+    if mode != TIDE_PROBE_MIX_WRITES and (src is None or src.numel() < C or not src.is_cuda):
+        raise ValueError("src must be a cuda tensor of at least C pointers")
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream()
+    handle = stream if isinstance(stream, int) else stream.cuda_stream
+    rc = lib.tide_probe_mix(int(C), int(mode), None if src is None else src.data_ptr(), dst.data_ptr(), int(items),
+                            int(lds_bytes), handle)
+    if rc != 0:
+        raise RuntimeError(f"tide_probe_mix failed: {rc}")
 
 
 def clock_probe(spin_ticks: int, out, stream=None):

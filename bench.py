@@ -63,6 +63,8 @@ def parse():
                     help="instead of the step benchmark: occupancy probe, spin-kernel curve and more victims")
     ap.add_argument("--engines", action="store_true",
                     help="instead of the step benchmark: AG placement on CUs vs copy engines, served GB/s and victim slowdown")
+    ap.add_argument("--mix-bound", action="store_true",
+                    help="the RS's access shape with reads or writes left out, beside the library RS (C = 1-8)")
     ap.add_argument("--copy-sizes", action="store_true",
                     help="placement of one flat parameter of 1-256 MiB over R = 1 and 8 ranks on each engine")
     ap.add_argument("--slot-reuse", action="store_true",
@@ -604,6 +606,75 @@ def copy_sizes(args, log):
     print(json.dumps({"experiment": "placement engines vs copy size", "rows": rows}), flush=True)
 
 
+def mix_bound(args, log):
+    """The RS's access shape with its writes or its reads left out (the mix probe of libtide_probe.so),
+    beside the library RS on the same buffers: one flat parameter of 2^27 elements, R = 1, C = 1, 2,
+    4 and 8 separate contributor buffers, each launch at the library's RS launch shape for that C.
+    The HBM bus carries reads and writes in turn, so reads-only + writes-only time bounds the RS from
+    below.  Medians of 21 HIP-event timings per row, three interleaved rounds; the row keeps the
+    round medians' median."""
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import Layout, tide_rs_launch_shape
+    from all_gather_placement_amd import probe as pr
+
+    items = 1 << 17
+    n = items * 1024
+    grads = [torch.full((n,), 0.01, dtype=torch.bfloat16, device="cuda") for _ in range(8)]
+    dst = torch.empty(n, dtype=torch.float32, device="cuda")
+    src = torch.tensor([g.data_ptr() for g in grads], dtype=torch.int64, device="cuda")
+    L = Layout([(n,)], 1)
+    modes = (("reads_only", pr.TIDE_PROBE_MIX_READS), ("writes_only", pr.TIDE_PROBE_MIX_WRITES),
+             ("both", pr.TIDE_PROBE_MIX_BOTH))
+
+    def med(fn, reps=21):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.median(ts)
+
+    times = {}
+    for rnd in range(3):
+        for C in (1, 2, 4, 8):
+            lds = tide_rs_launch_shape(C)["lds_bytes"]
+            for name, mode in modes:
+                t = med(lambda: pr.mix_launch(C, mode, src, dst, items, lds))
+                times.setdefault((C, name), []).append(t)
+            call = L.bind_rs([[g] for g in grads[:C]], [dst])
+            times.setdefault((C, "library_rs"), []).append(med(call.launch))
+            call.close()
+            log(f"round {rnd} C={C}: " + ", ".join(f"{k} {times[(C, k)][-1]:.4f} ms"
+                                                    for k in ("reads_only", "writes_only", "both", "library_rs")))
+    rows = []
+    for C in (1, 2, 4, 8):
+        t = {k: statistics.median(times[(C, k)]) for k in ("reads_only", "writes_only", "both", "library_rs")}
+        rb, wb = 2 * C * n, 4 * n
+        row = {"C": C, "rs_lds_bytes": tide_rs_launch_shape(C)["lds_bytes"]}
+        for k, v in t.items():
+            row[f"{k}_ms"] = round(v, 4)
+        row["reads_only_gbps"] = round(rb / (t["reads_only"] * 1e-3) / 1e9, 1)
+        row["writes_only_gbps"] = round(wb / (t["writes_only"] * 1e-3) / 1e9, 1)
+        for k in ("both", "library_rs"):
+            row[f"{k}_gbps"] = round((rb + wb) / (t[k] * 1e-3) / 1e9, 1)
+        bound = t["reads_only"] + t["writes_only"]
+        row["sum_bound_ms"] = round(bound, 4)
+        row["sum_bound_gbps"] = round((rb + wb) / (bound * 1e-3) / 1e9, 1)
+        row["library_rs_over_sum_bound"] = round(bound / t["library_rs"], 4)
+        rows.append(row)
+    L.close()
+    print(json.dumps({"experiment": "RS read/write mix bound", "outputs": n, "rows": rows}), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -649,6 +720,10 @@ def main():
     if args.copy_sizes:
         torch.cuda.set_device(0)
         copy_sizes(args, log)
+        return
+    if args.mix_bound:
+        torch.cuda.set_device(0)
+        mix_bound(args, log)
         return
     cfg = CONFIGS[args.workload]
     if args.contributors:

@@ -63,6 +63,34 @@ int32_t tide_probe_launch(int32_t num_wgs, int32_t shape, int64_t spin_ticks, ti
  */
 int32_t tide_probe_clock(int64_t spin_ticks, uint64_t* out, void* stream);
 
+/* Modes of the mix probe. */
+enum {
+  TIDE_PROBE_MIX_BOTH = 0,   /* contributor loads, sums and stores: the reduce-scatter's full items */
+  TIDE_PROBE_MIX_READS = 1,  /* the loads and sums only */
+  TIDE_PROBE_MIX_WRITES = 2  /* the stores only (a fixed pattern) */
+};
+
+/*
+ * Mix probe: the reduce-scatter's access shape for flat, 16-byte-aligned buffers, with its reads or
+ * its writes left out, so that the memory system's read-only, write-only and mixed rates can be
+ * measured in the shape the reduction uses ([Endgame] Figure 6a's node-local fp32 sums).  One
+ * 128-thread workgroup per item of 1024 outputs; item k of contributor c is elements
+ * [1024k, 1024k+1024) of src[c], its outputs are elements [1024k, 1024k+1024) of dst; items are
+ * spread over the 8 XCDs in contiguous ranges.
+ *   C          1, 2, 4 or 8.
+ *   src        device array of C device pointers (NULL allowed for TIDE_PROBE_MIX_WRITES); each
+ *              contributor holds 1024*items bf16, 16-byte aligned.
+ *   dst        device, 1024*items fp32, 16-byte aligned.  TIDE_PROBE_MIX_BOTH writes the ordered
+ *              sums (as the reduce-scatter would), TIDE_PROBE_MIX_WRITES a pattern,
+ *              TIDE_PROBE_MIX_READS nothing.
+ *   lds_bytes  local memory each workgroup requests (static + dynamic): sets how many workgroups
+ *              fit in a CU; 0 = the kernel's own only.
+ * Returns 0 or a hipError_t value; -1 for bad arguments (C, mode, items < 1 or > 2^31-1, NULL dst,
+ * NULL src with loads, lds_bytes < 0).
+ */
+int32_t tide_probe_mix(int32_t C, int32_t mode, const void* const* src, float* dst, int64_t items, int32_t lds_bytes,
+                       void* stream);
+
 /* Device wall-clock rate in kHz (hipDeviceAttributeWallClockRate of the current device), or -1. */
 int64_t tide_probe_wall_clock_khz(void);
 

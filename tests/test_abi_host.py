@@ -342,7 +342,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     text = open(os.path.join(ROOT, "include", "tide_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(tide_probe_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["tide_probe_clock", "tide_probe_launch", "tide_probe_wall_clock_khz"]
+    assert names == ["tide_probe_clock", "tide_probe_launch", "tide_probe_mix", "tide_probe_wall_clock_khz"]
     for n in names:
         assert hasattr(lib, n)
     assert lib.tide_probe_launch(0, 0, 10, None, None) == -1
@@ -350,4 +350,12 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.tide_probe_launch(4, 0, -1, None, None) == -1
     assert lib.tide_probe_clock(-1, 1 << 40, None) == -1
     assert lib.tide_probe_clock(10, None, None) == -1
+    fake = 1 << 40
+    assert lib.tide_probe_mix(3, 0, fake, fake, 8, 0, None) == -1           # C not 1, 2, 4 or 8
+    assert lib.tide_probe_mix(8, 3, fake, fake, 8, 0, None) == -1           # bad mode
+    assert lib.tide_probe_mix(8, 0, fake, fake, 0, 0, None) == -1           # no items
+    assert lib.tide_probe_mix(8, 0, fake, fake, 1 << 31, 0, None) == -1     # grid too large
+    assert lib.tide_probe_mix(8, 0, fake, None, 8, 0, None) == -1           # no destination
+    assert lib.tide_probe_mix(8, 1, None, fake, 8, 0, None) == -1           # loads without sources
+    assert lib.tide_probe_mix(8, 0, fake, fake, 8, -1, None) == -1          # negative local memory
     assert pr.clock_mhz([0, 100000, 5, 5 + 2_400_000], 100000) == 2400.0  # 1 ms of wall clock, 2.4M cycles

@@ -40,3 +40,36 @@ def test_clock_probe_reads_a_shader_clock(gpu_available):
     mhz = pr.clock_mhz([w0, w1, c0, c1], khz)
     print(f"[gpu-probe] shader clock over 1 ms: {mhz:.0f} MHz", flush=True)
     assert 100.0 < mhz < 3000.0
+
+
+def test_mix_probe_modes(gpu_available):
+    """The mix probe in the RS's access shape: both = the oracle's ordered fp32 sums bit for bit
+    (24 items, not a multiple of the 8 XCD ranges, so every item is mapped exactly once); writes only
+    = its pattern in every item; reads only = no store at all."""
+    import oracle
+    from workloads import normal_bf16_bits
+
+    items, C = 24, 4
+    n = items * 1024
+    bits = [[normal_bf16_bits((n,), 1.0, 170, c, 0)] for c in range(C)]
+    grads = [torch.from_numpy(b[0].view(np.int16).copy()).cuda().view(torch.bfloat16) for b in bits]
+    src = torch.tensor([g.data_ptr() for g in grads], dtype=torch.int64, device="cuda")
+    want = oracle.reduce_scatter(bits, [(n,)], 1)[0].view(np.uint32)
+    dst = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    pr.mix_launch(C, pr.TIDE_PROBE_MIX_BOTH, src, dst, items, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.view(torch.int32).cpu().numpy().view(np.uint32), want)
+
+    dst.fill_(float("nan"))
+    pr.mix_launch(C, pr.TIDE_PROBE_MIX_READS, src, dst, items, 27136)
+    torch.cuda.synchronize()
+    assert torch.isnan(dst).all()
+
+    pr.mix_launch(C, pr.TIDE_PROBE_MIX_WRITES, None, dst, items, 27136)
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().reshape(items, 2, 128, 4)  # item, store, lane, 4 floats
+    lanes = np.arange(128, dtype=np.float32)
+    for st, tail in ((0, (1.0, 2.0, 3.0)), (1, (4.0, 5.0, 6.0))):
+        assert np.array_equal(got[:, st, :, 0], np.broadcast_to(lanes, (items, 128)))
+        for j, v in enumerate(tail):
+            assert np.all(got[:, st, :, j + 1] == v)
