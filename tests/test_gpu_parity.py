@@ -118,7 +118,8 @@ def test_tiny_ag_bit_exact(gpu_available, mode):
 
 
 GROUPS = [
-    # (shapes, R, C): ragged tails, rows < R, empty parameters, 1-D/3-D, runtime C > 8
+    # (shapes, R, C): ragged tails, rows < R, empty parameters, 1-D/3-D; C <= 16 runs a kernel
+    # compiled for that C (16 the largest), C > 16 the runtime-C kernel
     ([(7, 5), (16, 3), (1, 9)], 4, 4),
     ([(1000, 37), (4099,), (333, 65), (0, 4), (3, 2, 5)], 8, 8),
     ([(5, 1), (2,), (9, 3, 3)], 9, 3),
@@ -127,6 +128,9 @@ GROUPS = [
     ([(77, 31), (3,)], 16, 10),
     ([(40000, 3), (11, 4097)], 5, 5),
     ([(2, 3)], 7, 12),
+    ([(300, 70), (17,), (2048, 3)], 4, 16),
+    ([(129, 33), (5000,), (0, 3)], 6, 18),
+    ([(33, 9), (70001,)], 3, 40),
 ]
 
 
@@ -156,10 +160,12 @@ def test_groups_ag_bit_exact(gpu_available, case, mode):
 
 @pytest.mark.parametrize("g_off", [0, 1, 3, 7])
 @pytest.mark.parametrize("s_off", [0, 1, 2])
-def test_rs_alignment_sweep(gpu_available, g_off, s_off):
-    """Base pointers shifted off 16-byte alignment: the element path must agree bit for bit."""
-    shapes, R, C = [(300, 17), (1025,), (8, 64)], 4, 6
-    say(f"alignment g_off={g_off} s_off={s_off}")
+@pytest.mark.parametrize("C", [6, 20])
+def test_rs_alignment_sweep(gpu_available, g_off, s_off, C):
+    """Base pointers shifted off 16-byte alignment: the element path must agree bit for bit, for a
+    compiled contributor count and for the runtime-C kernel."""
+    shapes, R = [(300, 17), (1025,), (8, 64)], 4
+    say(f"alignment g_off={g_off} s_off={s_off} C={C}")
     g = [[normal_bf16_bits(s, 1.0, 70, c, p) for p, s in enumerate(shapes)] for c in range(C)]
     want = oracle.reduce_scatter(g, shapes, R)
     # mixed offsets across contributors when g_off > 0; one launch, and short bounded launches

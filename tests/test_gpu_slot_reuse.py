@@ -76,9 +76,10 @@ def test_rs_from_slots_bit_exact(gpu_available, case):
             assert_rs_equal(np.stack([host_bits_f32(x) for x in shards]), want)
 
 
-def test_rs_from_slots_unaligned(gpu_available):
-    shapes, R, C = [(300, 17), (1025,), (8, 64)], 4, 5
-    say("rs from slots, unaligned bases")
+@pytest.mark.parametrize("C", [5, 20])
+def test_rs_from_slots_unaligned(gpu_available, C):
+    shapes, R = [(300, 17), (1025,), (8, 64)], 4
+    say(f"rs from slots, unaligned bases, C={C}")
     geo, S = ogeo.group_geometry(shapes, R)
     g = [[normal_bf16_bits(s, 1.0, 93, c, p) for p, s in enumerate(shapes)] for c in range(C)]
     slots_bits = [oracle.pack_slot(g[c], shapes, R) for c in range(C)]
