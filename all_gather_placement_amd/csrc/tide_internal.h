@@ -133,12 +133,10 @@ static_assert(kAgChunk % (8 * TIDE_AG_THREADS) == 0, "a full AG item is whole ve
 // CU): the GEMM's waves cannot share a SIMD with a resident RS wave, so a GEMM workgroup waits
 // until the RS workgroups on its CU exit.  Workgroups that live for the whole call (0) slowed the
 // GEMM ~7x even at B = 256; 64 items 0.5-2.5x; 16 items 4-27%; 4 items 4-8%.  Short-lived it is.
-// Between 4, 6 and 8 items (Llama-3.1-70B group, budget 512, three interleaved runs of 31
-// repetitions): RS 5.15-5.22 / 5.41-5.50 / 5.58-5.68 TB/s, GEMM +5.5-6.2% / +3.0-7.6% / +14-15%.
 #ifndef TIDE_RS_BOUNDED_ITEMS
-#define TIDE_RS_BOUNDED_ITEMS 6
+#define TIDE_RS_BOUNDED_ITEMS 4
 #endif
-// AG: 8 items (64 KiB of traffic per workgroup, like the RS's 120 KiB at C = 8).  Measured on the Llama-3.1-70B group
+// AG: 8 items (64 KiB of traffic per workgroup, like the RS's 80 KiB).  Measured on the Llama-3.1-70B group
 // at budget 512 against the one-wave GEMM: 16 items 5.55 TB/s, GEMM +10.9%; 8 items 4.94 TB/s, +3.7%;
 // 4 items 4.06 TB/s, +5.5%.
 #ifndef TIDE_AG_BOUNDED_ITEMS

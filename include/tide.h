@@ -149,8 +149,8 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              -N (1 <= N <= TIDE_RS_MAX_WGS_PER_CU): as 0, with at most N per CU for any C (an N
  *              at or above the hardware's own limit leaves that limit).
  *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of
- *              128 threads); each processes a bounded number of work items (6, 120 KiB of
- *              traffic at C = 8) and exits, and the call issues as many launches as needed, so
+ *              128 threads); each processes a bounded number of work items (4 by default, 80 KiB
+ *              of traffic at C = 8) and exits, and the call issues as many launches as needed, so
  *              a concurrent kernel's workgroups find free CUs within one short launch.
  *              The budget changes speed and residency only, never results.
  *   stream     hipStream_t as void*.
