@@ -28,11 +28,12 @@ _lib = None
 
 
 class TideError(RuntimeError):
-    def __init__(self, status: int, where: str, hip_error: int = 0):
+    def __init__(self, status: int, where: str, hip_error: int = 0, detail: str = ""):
         self.status = status
         self.hip_error = hip_error
         name = _lib.tide_status_str(status).decode() if _lib is not None else str(status)
         extra = f" (hipError {hip_error})" if hip_error else ""
+        extra += f": {detail}" if detail else ""
         super().__init__(f"{where}: {name}{extra}")
 
 
@@ -104,6 +105,25 @@ def _ptr(x) -> int | None:
     return x.data_ptr()
 
 
+def _expect_counts(layout: int, where: str, rows=None, per_param=None, per_rank=None):
+    """The C entry points read host pointer arrays of exactly the sizes the layout implies (C*P, P,
+    R); check the Python sequences before handing them over, so no array is read past its end."""
+    lib = load_library()
+    P, R = lib.tide_layout_num_params(layout), lib.tide_layout_num_ranks(layout)
+    bad = []
+    if rows is not None:
+        if len(rows) < 1:
+            bad.append("no contributors")
+        bad += [f"contributor {c} has {len(r)} tensors, the layout has {P} parameters"
+                for c, r in enumerate(rows) if len(r) != P]
+    if per_param is not None and len(per_param) != P:
+        bad.append(f"{len(per_param)} tensors for {P} parameters")
+    if per_rank is not None and len(per_rank) != R:
+        bad.append(f"{len(per_rank)} shards for {R} ranks")
+    if bad:
+        raise TideError(TIDE_ERR_INVALID, where, 0, "; ".join(bad[:3]))
+
+
 def _stream_handle(stream) -> int | None:
     if stream is None:
         import torch
@@ -134,6 +154,7 @@ def tide_layout_create(shapes: Sequence[Sequence[int]], R: int) -> int:
 def tide_rs_bf16_to_fp32(layout: int, grads, shards, cu_budget: int = 0, stream=None):
     """grads: C lists of P bf16 tensors (or addresses); shards: R fp32 tensors (or addresses)."""
     lib = load_library()
+    _expect_counts(layout, "tide_rs_bf16_to_fp32", rows=grads, per_rank=shards)
     C = len(grads)
     flat = [_ptr(g) for row in grads for g in row]
     g_arr = (ctypes.c_void_p * max(len(flat), 1))(*flat)
@@ -146,6 +167,7 @@ def tide_rs_bf16_to_fp32(layout: int, grads, shards, cu_budget: int = 0, stream=
 def tide_ag_place(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0, stream=None):
     """stage: R*S bf16 tensor (or address); params: P bf16 tensors (or addresses)."""
     lib = load_library()
+    _expect_counts(layout, "tide_ag_place", per_param=params)
     p_list = [_ptr(p) for p in params]
     p_arr = (ctypes.c_void_p * max(len(p_list), 1))(*p_list)
     _check(lib.tide_ag_place(layout, _ptr(stage), p_arr, int(mode), int(cu_budget), _stream_handle(stream)),
@@ -155,6 +177,7 @@ def tide_ag_place(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_bud
 def tide_slot_pack(layout: int, grads, slot, cu_budget: int = 0, stream=None):
     """grads: P bf16 tensors of one contributor (or addresses); slot: R*S bf16 tensor (or address)."""
     lib = load_library()
+    _expect_counts(layout, "tide_slot_pack", per_param=grads)
     g_list = [_ptr(g) for g in grads]
     g_arr = (ctypes.c_void_p * max(len(g_list), 1))(*g_list)
     _check(lib.tide_slot_pack(layout, g_arr, _ptr(slot), int(cu_budget), _stream_handle(stream)), "tide_slot_pack")
@@ -163,6 +186,7 @@ def tide_slot_pack(layout: int, grads, slot, cu_budget: int = 0, stream=None):
 def tide_rs_slots_bf16_to_fp32(layout: int, slots, shards, cu_budget: int = 0, stream=None):
     """slots: C packed R*S bf16 tensors (or addresses); shards: R fp32 tensors (or addresses)."""
     lib = load_library()
+    _expect_counts(layout, "tide_rs_slots_bf16_to_fp32", per_rank=shards)
     sl = [_ptr(x) for x in slots]
     sl_arr = (ctypes.c_void_p * max(len(sl), 1))(*sl)
     sh = [_ptr(x) for x in shards]
@@ -179,6 +203,7 @@ def _ptr_array(xs):
 def tide_rs_prepare(layout: int, grads, shards, cu_budget: int = 0) -> int:
     """Prepared RS call (see tide_call_launch); returns the raw tide_call handle."""
     lib = load_library()
+    _expect_counts(layout, "tide_rs_prepare", rows=grads, per_rank=shards)
     out = ctypes.c_void_p()
     _check(lib.tide_rs_prepare(layout, len(grads), _ptr_array([g for row in grads for g in row]),
                                _ptr_array(shards), int(cu_budget), ctypes.byref(out)), "tide_rs_prepare")
@@ -187,6 +212,7 @@ def tide_rs_prepare(layout: int, grads, shards, cu_budget: int = 0) -> int:
 
 def tide_ag_prepare(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0) -> int:
     lib = load_library()
+    _expect_counts(layout, "tide_ag_prepare", per_param=params)
     out = ctypes.c_void_p()
     _check(lib.tide_ag_prepare(layout, _ptr(stage), _ptr_array(params), int(mode), int(cu_budget), ctypes.byref(out)),
            "tide_ag_prepare")
@@ -195,6 +221,7 @@ def tide_ag_prepare(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_b
 
 def tide_slot_pack_prepare(layout: int, grads, slot, cu_budget: int = 0) -> int:
     lib = load_library()
+    _expect_counts(layout, "tide_slot_pack_prepare", per_param=grads)
     out = ctypes.c_void_p()
     _check(lib.tide_slot_pack_prepare(layout, _ptr_array(grads), _ptr(slot), int(cu_budget), ctypes.byref(out)),
            "tide_slot_pack_prepare")
@@ -203,6 +230,7 @@ def tide_slot_pack_prepare(layout: int, grads, slot, cu_budget: int = 0) -> int:
 
 def tide_rs_slots_prepare(layout: int, slots, shards, cu_budget: int = 0) -> int:
     lib = load_library()
+    _expect_counts(layout, "tide_rs_slots_prepare", per_rank=shards)
     out = ctypes.c_void_p()
     _check(lib.tide_rs_slots_prepare(layout, len(slots), _ptr_array(slots), _ptr_array(shards), int(cu_budget),
                                      ctypes.byref(out)), "tide_rs_slots_prepare")

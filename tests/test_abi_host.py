@@ -359,3 +359,30 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.tide_probe_mix(8, 1, None, fake, 8, 0, None) == -1           # loads without sources
     assert lib.tide_probe_mix(8, 0, fake, fake, 8, -1, None) == -1          # negative local memory
     assert pr.clock_mhz([0, 100000, 5, 5 + 2_400_000], 100000) == 2400.0  # 1 ms of wall clock, 2.4M cycles
+
+
+def test_binding_checks_pointer_array_lengths_before_the_call():
+    """The C entry points read host arrays of C*P, P and R pointers; the binding refuses Python
+    sequences of other lengths instead of letting the library read past them (no HIP call made)."""
+    lib = tb.load_library()
+    with tide.Layout(TINY.shapes, TINY.R) as L:
+        P, R = len(TINY.shapes), TINY.R
+        base = 1 << 40
+        grads = [[base + (c * P + p) * 4096 for p in range(P)] for c in range(2)]
+        shards = [base + (1 << 30) + r * 4096 for r in range(R)]
+        cases = [
+            lambda: tb.tide_rs_bf16_to_fp32(L.handle, [grads[0][:-1], grads[1]], shards),
+            lambda: tb.tide_rs_bf16_to_fp32(L.handle, grads, shards[:-1]),
+            lambda: tb.tide_rs_bf16_to_fp32(L.handle, [], shards),
+            lambda: tb.tide_ag_place(L.handle, base, grads[0][:-1]),
+            lambda: tb.tide_slot_pack(L.handle, grads[0] + [base], base + (1 << 32)),
+            lambda: tb.tide_rs_slots_bf16_to_fp32(L.handle, [base], shards + [base]),
+            lambda: tb.tide_rs_prepare(L.handle, grads, shards[:1]),
+            lambda: tb.tide_ag_prepare(L.handle, base, []),
+            lambda: tb.tide_slot_pack_prepare(L.handle, grads[0][:1], base),
+            lambda: tb.tide_rs_slots_prepare(L.handle, [base], []),
+        ]
+        for case in cases:
+            with pytest.raises(tide.TideError, match="INVALID"):
+                case()
+        assert lib.tide_last_hip_error() == 0
