@@ -57,7 +57,7 @@ typedef enum tide_status {
   TIDE_ERR_INVALID = 1,     /* bad argument: null pointer, bad size, misalignment, overlap */
   TIDE_ERR_NOMEM = 2,       /* host or device allocation failed */
   TIDE_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
-  TIDE_ERR_UNSUPPORTED = 4  /* valid request this build cannot serve */
+  TIDE_ERR_UNSUPPORTED = 4  /* valid request the runtime or device refused */
 } tide_status;
 
 /* Placement engines for tide_ag_place. */
