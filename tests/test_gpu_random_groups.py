@@ -1,8 +1,9 @@
 """Randomised GPU parity: many small seeded groups, each checked bit for bit against the oracle.
 
-Every group draws R, C, the parameter shapes (1-3 dimensions, rows 0-3000, so empty parameters,
-rows < R and ragged tails all occur), a CU budget and per-buffer base offsets (0-7 elements, so both
-the vector and the element paths run), then runs the reduce-scatter, the placement and the
+Every group draws R, C (1-12; 13-40 in a second set, which reaches the runtime-C kernel and
+negative RS budgets), the parameter shapes (1-3 dimensions, rows 0-3000, so empty parameters,
+rows < R and ragged tails all occur), a CU budget and per-buffer base offsets (0-7 elements, so
+both the vector and the element paths run), then runs the reduce-scatter, the placement and the
 Slot-Reuse packing through the C ABI.
 """
 import numpy as np
@@ -19,9 +20,9 @@ pytestmark = pytest.mark.gpu
 N_GROUPS = 40
 
 
-def _random_group(rng):
+def _random_group(rng, c_lo=1, c_hi=13):
     R = int(rng.integers(1, 18))
-    C = int(rng.integers(1, 13))
+    C = int(rng.integers(c_lo, c_hi))
     shapes = []
     for _ in range(int(rng.integers(1, 6))):
         nd = int(rng.integers(1, 4))
@@ -45,8 +46,23 @@ def _random_inputs(rng, shapes, R, C, S):
 def test_random_group_bit_exact(gpu_available, case):
     rng = np.random.default_rng(1000 + case)
     shapes, R, C, budget = _random_group(rng)
+    _check_group(rng, case, shapes, R, C, budget, budget)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_group_many_contributors(gpu_available, case):
+    """C from 13 to 40: the largest compiled contributor counts and the runtime-C kernel, with
+    bounded budgets and explicit per-CU caps (negative RS budgets)."""
+    rng = np.random.default_rng(5000 + case)
+    shapes, R, C, budget = _random_group(rng, 13, 41)
+    rs_budget = int(rng.choice([budget, -1, -3, -64]))
+    _check_group(rng, case, shapes, R, C, rs_budget, budget)
+
+
+def _check_group(rng, case, shapes, R, C, rs_budget, ag_budget):
     offset = (lambda: int(rng.integers(0, 8))) if case % 3 == 0 else (lambda: 0)
-    say(f"random group {case}: shapes={shapes} R={R} C={C} budget={budget} offsets={'on' if case % 3 == 0 else 'off'}")
+    say(f"random group {case}: shapes={shapes} R={R} C={C} budgets rs={rs_budget} ag={ag_budget} "
+        f"offsets={'on' if case % 3 == 0 else 'off'}")
     geo, S = ogeo.group_geometry(shapes, R)
     g, stage_bits = _random_inputs(rng, shapes, R, C, S)
     want = oracle.reduce_scatter(g, shapes, R)
@@ -54,7 +70,7 @@ def test_random_group_bit_exact(gpu_available, case):
     with Layout(shapes, R) as L:
         grads = [[dev_bf16(x, offset()) for x in row] for row in g]
         shards = poisoned_shards(R, S, offset())
-        L.rs_bf16_to_fp32(grads, shards, cu_budget=budget)
+        L.rs_bf16_to_fp32(grads, shards, cu_budget=rs_budget)
         stage = dev_bf16(stage_bits, offset())
         params = []
         for s in shapes:
@@ -62,11 +78,11 @@ def test_random_group_bit_exact(gpu_available, case):
             o = offset()
             buf = torch.full((n + o + 8,), POISON_BF16, dtype=torch.int16, device="cuda")
             params.append(buf[o: o + n].view(torch.bfloat16).reshape(s))
-        L.ag_place(stage, params, cu_budget=budget)
+        L.ag_place(stage, params, cu_budget=ag_budget)
         o = offset()
         slot_buf = torch.full((R * S + o + 8,), POISON_BF16, dtype=torch.int16, device="cuda")
         slot = slot_buf[o: o + R * S].view(torch.bfloat16)
-        L.slot_pack(grads[0], slot, cu_budget=budget)
+        L.slot_pack(grads[0], slot, cu_budget=ag_budget)
         torch.cuda.synchronize()
         got = np.stack([host_bits_f32(x) for x in shards]) if S else np.zeros((R, 0), np.uint32)
         assert_rs_equal(got, want)
