@@ -4,7 +4,8 @@
 // one (parameter, rank) segment, so a workgroup reads its item descriptor and the item's source
 // pointers once, as wave-uniform scalar loads into SGPRs, and then streams contiguous memory: no
 // per-element index search, no atomics, no inter-workgroup communication.  Every output element
-// has exactly one writer, and every workgroup is short-lived (one work item, then exit).
+// has exactly one writer, and every workgroup is short-lived: one work item (a few in bounded
+// launches), then exit.
 //
 // RS ([Endgame] Figure 6a, node-local fp32 sums; abstract, bf16 gradients reduced into fp32
 // shards): every output is the sum of its C contributors' bf16 inputs, each widened exactly to
@@ -17,7 +18,7 @@
 // is shaped for bytes in flight and clean traffic, not arithmetic (no matrix cores: nothing here
 // is a contraction).
 //
-// AG ([Endgame] Figure 5b, one strided copy per parameter; Table 7, direct landing): a bit copy
+// AG ([Endgame] Figure 5b, each parameter filled by a single strided copy; Table 7, direct landing): a bit copy
 // of each rank's valid rows from the rank-major stage into the parameter's storage, 16 bytes per
 // lane per access when source and destination share their 16-byte phase.
 #include <hip/hip_runtime.h>

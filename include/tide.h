@@ -4,15 +4,15 @@
  * Method: "The Endgame of FSDP Communication: Layout-Aware Collectives on Copy Engines, RDMA, and
  * NVSwitch" (arXiv 2610.38228; [Endgame] below).  FSDP2 keeps parameters and gradients as
  * per-parameter tensors while its collectives work on flat rank-major buffers; TIDE folds the
- * layout conversion into the collectives' addressing so that every piece is written once, at its
- * final address ([Endgame] abstract; Figure 1).  This library implements, on one GPU, the
+ * layout conversion into the collectives' addressing, so each piece of data is stored a single
+ * time, directly in its destination ([Endgame] abstract; Figure 1).  This library implements, on one GPU, the
  * node-local level of that idea:
  *
  *   - reduce-scatter (RS): C contributors' per-parameter bf16 gradients are read in place (no
- *     full-group pack; [Endgame] Table 1 "In-Place Read"), summed in fp32 (the mixed-precision mode
+ *     full-group pack; the in-place input mode of [Endgame] Table 1), summed in fp32 (the mixed-precision mode
  *     of the abstract; Figure 6a's node-local fp32 partials) and written into R flat fp32 shards;
  *   - all-gather placement (AG): a rank-major bf16 stage buffer is landed directly into
- *     per-parameter storage ([Endgame] Figure 5b, one strided copy per parameter).
+ *     per-parameter storage ([Endgame] Figure 5b: each parameter filled by a single strided copy).
  *
  * Geometry ([Endgame] Table 2; symbols were lost in the text we have, names are ours):
  *   parameter p has shape (rows_p, d1, d2, ...); row length L_p = d1*d2*... (1 for 1-D);
@@ -134,8 +134,8 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
 
 /*
  * Reduce-scatter, bf16 in, fp32 out ([Endgame] abstract: per-parameter bf16 gradients reduced
- * into fp32 shards; Figure 6a: node-local fp32 sums; Table 1: In-Place Read; Figure 1: each piece
- * written once at its final address).
+ * into fp32 shards; Figure 6a: node-local fp32 sums; Table 1: the in-place input mode; Figure 1:
+ * every output stored once, in its destination).
  *   C          number of contributors, >= 1
  *   grads      host [C*P]: grads[c*P + p] is contributor c's gradient of parameter p, a contiguous
  *              row-major bf16 device tensor of rows_p * L_p elements, 2-byte aligned (NULL allowed
@@ -170,8 +170,8 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
                                  float* const* shards, int32_t cu_budget, void* stream);
 
 /*
- * All-gather placement ([Endgame] Figure 5b: one strided copy per parameter from the stage slots
- * into parameter storage; abstract: shards delivered directly to parameter storage).
+ * All-gather placement ([Endgame] Figure 5b: each parameter filled from the stage slots by a single
+ * strided copy; abstract: shards land directly in parameter storage).
  *   stage      device, R*S bf16 elements, rank-major: rank r's shard starts at element r*S.
  *   params     host [P]: params[p] is parameter p's contiguous bf16 device storage of rows_p * L_p
  *              elements (NULL allowed only for empty parameters).

@@ -15,9 +15,9 @@ but lost every math symbol, so the definitions here are the plainest reading of 
                boundary between per-parameter tensors and flat rank-major buffers);
 * reduce-scatter -- the stock FSDP2 formulation named in the abstract: pack every contributor's
                gradients into a full-group fp32 rank-major buffer, then sum the buffers.  TIDE's
-               in-place path reaches the same values while skipping the pack (abstract; Table 1
-               "RS input preparation: In-Place Read"; Figure 1 "writes each piece once, at its
-               final address");
+               in-place path reaches the same values while skipping the pack (abstract; Table 1,
+               the in-place input mode of the RS; Figure 1, every piece stored once, directly in
+               its destination);
 * Slot-Reuse staging -- gradients packed into a vacated all-gather slot, then reduced from the
                slots (abstract; Figure 7); see oracle/slot.py;
 * all-gather placement -- FSDP2's copy-out of the rank-major all-gather output into

@@ -2,8 +2,8 @@
 
 [Endgame] Figure 1 puts FSDP2's contract boundary between the flat rank-major all-gather output
 and per-parameter storage; stock FSDP2 converts with a copy-out (Table 7's caption names its fused
-split_with_sizes_copy), and TIDE-AG lands each rank's piece straight into parameter storage with
-one strided copy per parameter (Figure 5b; abstract).  Both give the same parameter contents,
+split_with_sizes_copy), and TIDE-AG lands each rank's piece straight into parameter storage,
+filling each parameter by a single strided copy (Figure 5b; abstract).  Both give the same parameter contents,
 defined here as the copy-out:
 
   stage viewed as (R, S); take columns [o_p, o_p + e_p) -> (R, m_p, L_p) -> (R*m_p, L_p);

@@ -5,7 +5,7 @@ Table 8's caption, whose FSDP2 columns include the full-group pack): every contr
 per-parameter gradients are packed into one full-group fp32 buffer laid out rank-major (R slots of
 S elements, parameter p of slot r at offset o_p, padding zero), and the packed buffers of the C
 contributors are summed elementwise; slot r of the sum is rank r's fp32 shard.  TIDE's in-place
-reduce-scatter (abstract; Figure 6a, node-local fp32 sums; Table 1, "In-Place Read") computes the
+reduce-scatter (abstract; Figure 6a, node-local fp32 sums; Table 1, in-place input) computes the
 same values without the pack, which is why this formulation serves as the definition.
 
 Summation order (reading R4): y = x_0, then y = y + x_c for c = 1..C-1, each add one numpy float32
