@@ -537,6 +537,8 @@ void tide_call_destroy(tide_call* call) {
     int cur = 0;
     const bool have = hipGetDevice(&cur) == hipSuccess;
     if (have && cur != call->device) (void)hipSetDevice(call->device);
+    // launches carry no event (they must stay capturable), so wait for the device instead
+    (void)hipDeviceSynchronize();
     (void)hipFree(call->dev_table);
     if (have && cur != call->device) (void)hipSetDevice(cur);
   }

@@ -224,6 +224,9 @@ void tide_layout_destroy(tide_layout* layout) {
   const bool have_dev = !layout->devices.empty() && hipGetDevice(&cur) == hipSuccess;
   for (auto& kv : layout->devices) {
     if (hipSetDevice(kv.first) != hipSuccess) continue;
+    // Prepared calls launch without events, so work still queued on any stream may read the
+    // tables below: wait for the device before freeing them.
+    (void)hipDeviceSynchronize();
     tide::DeviceState& st = kv.second;
     for (auto& s : st.slots) {
       if (s.done) {

@@ -391,7 +391,7 @@ class BoundCall:
         _check(self._lib.tide_call_launch(self.handle, _stream_handle(stream)), "tide_call_launch")
 
     def close(self):
-        """Free the call.  Streams that launched it must have been synchronised."""
+        """Free the call (the library waits for the device's queued work first)."""
         if getattr(self, "handle", None):
             self._lib.tide_call_destroy(self.handle)
             self.handle = None

@@ -88,8 +88,9 @@ enum {
 tide_status tide_layout_create(int32_t num_params, const int32_t* ndims, const int64_t* dims,
                                int32_t num_ranks, tide_layout** out);
 
-/* Free a layout and its device tables.  Every stream that used it must have been synchronised.
- * NULL is ignored. */
+/* Free a layout and its device tables.  Waits for all work on every device the layout was used on
+ * (hipDeviceSynchronize) before freeing, so work still queued that reads its tables finishes first;
+ * prepared calls of the layout must not be launched afterwards.  NULL is ignored. */
 void tide_layout_destroy(tide_layout* layout);
 
 /* Upload the layout's device tables to the current device (idempotent).  After this, RS and AG
@@ -257,9 +258,10 @@ tide_status tide_rs_slots_prepare(const tide_layout* layout, int32_t C, const vo
 /* Enqueue a prepared call on `stream` (hipStream_t as void*). */
 tide_status tide_call_launch(const tide_call* call, void* stream);
 
-/* Free a prepared call (its device table, on the call's device).  Every stream that launched it
- * must have been synchronised, and no graph holding its launches may be replayed afterwards.
- * NULL is ignored. */
+/* Free a prepared call (its device table, on the call's device).  Waits for all work on that
+ * device first (launches carry no event, so that they stay capturable), so a call destroyed with
+ * launches in flight is safe; no graph holding its launches may be replayed afterwards.  NULL is
+ * ignored. */
 void tide_call_destroy(tide_call* call);
 
 /* Launch shape of RS calls with C contributors at `cu_budget` on the current device: threads per

@@ -336,3 +336,30 @@ def test_rs_negative_budget_sets_the_cap_and_changes_speed_only(gpu_available):
                 call.close()
                 assert_rs_equal(shards_bits(shards), want)
         assert static < 160 * 1024 // 16
+
+
+def test_destroy_with_work_in_flight(gpu_available):
+    """Closing a prepared call, or a layout, right after launching (no synchronisation) is safe:
+    destroy waits for the device before freeing the tables the queued kernels read."""
+    shapes, R, C = GROUPS[1]
+    geo, S = ogeo.group_geometry(shapes, R)
+    g = [[normal_bf16_bits(s, 1.0, 180, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    grads = [[dev_bf16(x) for x in row] for row in g]
+    want = oracle.reduce_scatter(g, shapes, R)
+    say("destroy with work in flight")
+    with Layout(shapes, R) as L:
+        shards = poisoned_shards(R, S)
+        call = L.bind_rs(grads, shards, cu_budget=2)  # many short launches queued
+        for _ in range(3):
+            call.launch()
+        call.close()
+        scratch = [torch.full((1 << 16,), -1, dtype=torch.int64, device="cuda") for _ in range(8)]
+        torch.cuda.synchronize()
+        assert_rs_equal(shards_bits(shards), want)
+        del scratch
+    shards = poisoned_shards(R, S)
+    L = Layout(shapes, R)
+    L.rs_bf16_to_fp32(grads, shards, cu_budget=2)
+    L.close()
+    torch.cuda.synchronize()
+    assert_rs_equal(shards_bits(shards), want)
