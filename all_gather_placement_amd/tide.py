@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import weakref
 from typing import Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -264,11 +265,21 @@ class Layout:
         self.handle = tide_layout_create(self.shapes, self.R)
         self.P = self._lib.tide_layout_num_params(self.handle)
         self.S = self._lib.tide_layout_shard_numel(self.handle)
+        self._calls = weakref.WeakSet()  # prepared calls made from this layout
 
     def close(self):
+        """Free the layout.  Prepared calls made from it are closed first (they address its
+        tables), so launching one afterwards raises instead of touching freed memory."""
         if getattr(self, "handle", None):
+            for call in list(getattr(self, "_calls", ())):
+                call.close()
             self._lib.tide_layout_destroy(self.handle)
             self.handle = None
+
+    def _bound(self, handle: int, keep) -> "BoundCall":
+        call = BoundCall(handle, keep)
+        self._calls.add(call)
+        return call
 
     def __del__(self):
         try:
@@ -350,21 +361,21 @@ class Layout:
     # prepared calls (validate once, launch many times; graph-capturable kernel paths) ---------
     def bind_rs(self, grads, shards, cu_budget: int = 0) -> BoundCall:
         _check_shapes_rs(self, grads, shards)
-        return BoundCall(tide_rs_prepare(self.handle, grads, shards, cu_budget), (grads, shards, self))
+        return self._bound(tide_rs_prepare(self.handle, grads, shards, cu_budget), (grads, shards, self))
 
     def bind_ag(self, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0) -> BoundCall:
         _check_shapes_ag(self, stage, params)
-        return BoundCall(tide_ag_prepare(self.handle, stage, params, mode, cu_budget), (stage, params, self))
+        return self._bound(tide_ag_prepare(self.handle, stage, params, mode, cu_budget), (stage, params, self))
 
     def bind_slot_pack(self, grads, slot, cu_budget: int = 0) -> BoundCall:
         _check_shapes_ag(self, slot, grads)
-        return BoundCall(tide_slot_pack_prepare(self.handle, grads, slot, cu_budget), (grads, slot, self))
+        return self._bound(tide_slot_pack_prepare(self.handle, grads, slot, cu_budget), (grads, slot, self))
 
     def bind_rs_slots(self, slots, shards, cu_budget: int = 0) -> BoundCall:
         _check_shapes_rs(self, [], shards)
         for sl in slots:
             _check_stage(self, sl)
-        return BoundCall(tide_rs_slots_prepare(self.handle, slots, shards, cu_budget), (slots, shards, self))
+        return self._bound(tide_rs_slots_prepare(self.handle, slots, shards, cu_budget), (slots, shards, self))
 
     def slot_pack(self, grads, slot, cu_budget: int = 0, stream=None):
         _check_shapes_ag(self, slot, grads)
@@ -388,6 +399,8 @@ class BoundCall:
         self._keep = keep
 
     def launch(self, stream=None):
+        if not self.handle:
+            raise TideError(TIDE_ERR_INVALID, "tide_call_launch", 0, "the call or its layout was closed")
         _check(self._lib.tide_call_launch(self.handle, _stream_handle(stream)), "tide_call_launch")
 
     def close(self):

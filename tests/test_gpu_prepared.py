@@ -363,3 +363,21 @@ def test_destroy_with_work_in_flight(gpu_available):
     L.close()
     torch.cuda.synchronize()
     assert_rs_equal(shards_bits(shards), want)
+
+
+def test_closing_the_layout_closes_its_calls(gpu_available):
+    """Prepared calls address their layout's tables: closing the layout closes them, and a later
+    launch raises instead of reading freed memory."""
+    shapes, R, C = GROUPS[0]
+    geo, S = ogeo.group_geometry(shapes, R)
+    grads = [[torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes] for _ in range(C)]
+    shards = poisoned_shards(R, S)
+    say("layout close closes its calls")
+    L = Layout(shapes, R)
+    call = L.bind_rs(grads, shards)
+    call.launch()
+    L.close()
+    with pytest.raises(TideError, match="closed"):
+        call.launch()
+    torch.cuda.synchronize()
+    assert np.all(shards_bits(shards) == 0)  # the launch before the close completed: all +0.0
