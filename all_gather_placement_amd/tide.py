@@ -420,9 +420,24 @@ def _is_tensor(x) -> bool:
     return hasattr(x, "data_ptr") and hasattr(x, "dtype")
 
 
-def _check_shapes_rs(L: Layout, grads, shards):
-    """Host-side shape/dtype checks of torch arguments (the C ABI sees only addresses)."""
+def _check_device(tensors):
+    """Every tensor argument on the current device: the library launches there, so an address on
+    another device would reach its kernels as a foreign pointer."""
     import torch
+
+    devs = {t.device.index for t in tensors if _is_tensor(t)}
+    if not devs:
+        return
+    cur = torch.cuda.current_device() if torch.cuda.is_available() else None
+    if len(devs) > 1 or (cur is not None and devs != {cur}):
+        raise ValueError(f"all tensors must be on the current device (cuda:{cur}); got devices {sorted(devs)}")
+
+
+def _check_shapes_rs(L: Layout, grads, shards):
+    """Host-side shape/dtype/device checks of torch arguments (the C ABI sees only addresses)."""
+    import torch
+
+    _check_device([g for row in grads for g in row] + list(shards))
 
     if len(shards) != L.R:
         raise ValueError(f"expected {L.R} shards, got {len(shards)}")
@@ -442,6 +457,8 @@ def _check_shapes_rs(L: Layout, grads, shards):
 def _check_stage(L: Layout, stage):
     import torch
 
+    _check_device([stage])
+
     if _is_tensor(stage):
         if stage.dtype != torch.bfloat16 or not stage.is_cuda or not stage.is_contiguous() or stage.numel() != L.R * L.S:
             raise ValueError(f"stage/slot must be a contiguous cuda bf16 tensor of R*S = {L.R * L.S} elements")
@@ -452,6 +469,7 @@ def _check_shapes_ag(L: Layout, stage, params):
 
     if len(params) != L.P:
         raise ValueError(f"expected {L.P} parameters, got {len(params)}")
+    _check_device([stage] + list(params))
     _check_stage(L, stage)
     for q, shape in zip(params, L.shapes):
         if _is_tensor(q):

@@ -386,3 +386,25 @@ def test_binding_checks_pointer_array_lengths_before_the_call():
             with pytest.raises(tide.TideError, match="INVALID"):
                 case()
         assert lib.tide_last_hip_error() == 0
+
+
+def test_binding_rejects_tensors_on_mixed_devices():
+    """Tensor arguments must all sit on one device (the current one when a GPU is present)."""
+    import torch
+
+    class FakeTensor:  # duck-typed like a torch tensor, on a chosen device; never dereferenced
+        def __init__(self, dev):
+            self.device = torch.device("cuda", dev)
+            self.dtype = torch.bfloat16
+            self.is_cuda = True
+
+        def data_ptr(self):
+            return 1 << 40
+
+    with tide.Layout(TINY.shapes, TINY.R) as L:
+        grads = [[FakeTensor(0) for _ in range(L.P)] for _ in range(2)]
+        shards = [FakeTensor(0) for _ in range(L.R - 1)] + [FakeTensor(1)]
+        with pytest.raises(ValueError, match="current device"):
+            L.rs_bf16_to_fp32(grads, shards)
+        with pytest.raises(ValueError, match="current device"):
+            L.ag_place(FakeTensor(1), [FakeTensor(0) for _ in range(L.P)])
