@@ -197,6 +197,54 @@ __device__ __forceinline__ void full_item_finish(const u32x4 x[CT], float* dst, 
 #endif
 }
 
+// Full work item, runtime contributor count (C > kRsMaxCt): contributors in blocks of 8, each
+// block's 8 loads issued together (a lane past C gets a zero-sized buffer range and its value is
+// never added), sums in ascending contributor order, then the same exchange and stores as above.
+constexpr int kRtLoadAux = TIDE_RS_LOAD_AUX >= 0 ? TIDE_RS_LOAD_AUX : 2;     // nt
+constexpr int kRtStoreAux = TIDE_RS_STORE_AUX >= 0 ? TIDE_RS_STORE_AUX : 18;  // nt sc1
+__device__ __forceinline__ void full_item_rt(void* const* gptr, int32_t P, const RsChunk& ch, int C, float* dst,
+                                             f32x4* xfer, int tid) {
+  constexpr int B = 8;
+  float a[8] = {};
+  for (int c0 = 0; c0 < C; c0 += B) {
+    const int nb = min(B, C - c0);
+    u32x4 x[B];
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      const int c = k < nb ? c0 + k : c0;
+      const unsigned short* src =
+          reinterpret_cast<const unsigned short*>(gptr[static_cast<int64_t>(c) * P + ch.p]) + ch.src;
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned short*>(src), 0,
+                                                                           k < nb ? 16 * kThreads : 0, 0x00020000);
+      x[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, 16 * tid, 0, kRtLoadAux));
+    }
+    // keep all B loads ahead of their first use: without this the compiler moves each load next to
+    // its conditional add below, one round trip per contributor (emits no instruction)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < B; ++k) {
+      if (k >= nb) break;
+      const float v[8] = {widen_lo(x[k].x), widen_hi(x[k].x), widen_lo(x[k].y), widen_hi(x[k].y),
+                          widen_lo(x[k].z), widen_hi(x[k].z), widen_lo(x[k].w), widen_hi(x[k].w)};
+      if (c0 + k == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = v[e];  // start from x_0 itself (keeps -0.0)
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] += v[e];
+      }
+    }
+  }
+  __syncthreads();  // the previous item's readers are done with xfer
+  xfer[2 * tid] = f32x4{a[0], a[1], a[2], a[3]};
+  xfer[2 * tid + 1] = f32x4{a[4], a[5], a[6], a[7]};
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, 32 * kThreads, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid]), rsrc, 16 * tid, 0, kRtStoreAux);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid + kThreads]), rsrc, 16 * (tid + kThreads),
+                                         0, kRtStoreAux);
+}
+
 // RS kernel.  CT in 1..kRsMaxCt: contributor count fixed at compile time; CT == 0: any C >= 1.
 // VEC: all source and shard base pointers are 16-byte aligned (checked on the host), so the
 // alignment of an element depends only on its offset inside its buffer.
@@ -261,6 +309,12 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
           store_hbm(dst + k, sum1<CT>(src, nc, k));
         }
       } else {
+#if TIDE_RS_WIDE
+        if (full_item(ch)) {
+          full_item_rt(ptrs, P, ch, nc, dst, xfer, tid);
+          continue;  // no tail, no padding in a full item
+        }
+#endif
         for (int i = tid; i < head; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
         for (int q = tid; q < ng; q += kThreads) {
           const int64_t k = head + 4 * static_cast<int64_t>(q);

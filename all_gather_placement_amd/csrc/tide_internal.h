@@ -36,11 +36,14 @@ namespace tide {
 // workgroups on the Llama-3.1-8B group: C = 8: 6 per CU beat 3, 4, 5, 7, 8 and no cap by 1-5%;
 // C = 4: 8 beat 6, 12 and 16 (+2.4% over 6); C = 2 and 1: 12 beat 8, 16 and no cap (C = 1: 4.1
 // TB/s at 6 -> 6.4 TB/s); C = 12: 6 beat 3, 4, 5 and no cap (5.93 TB/s); C = 16: 4 and 5 beat 2,
-// 3 and no cap (5.82 TB/s).  Contributor counts up to kRsMaxCt are compiled in (full-item path);
-// above, the runtime-C path loads one contributor at a time and streams best uncapped (at C = 12,
-// before 9..16 were compiled in: 3.5 TB/s capped at 6, 5.5 TB/s uncapped).
+// 3 and no cap (5.82 TB/s).  Contributor counts up to kRsMaxCt are compiled in; above, the
+// runtime-C kernel's full items load the contributors in blocks of 8: C = 20: 6 per CU 5.80 TB/s
+// (3: 4.51, 4: 5.61, 5: 5.73, 8: 5.69, no cap 5.61); C = 32: 4 per CU 5.74 TB/s (3: 4.87, 5: 5.73,
+// 6: 5.71, 8: 5.60, no cap 5.58).
 constexpr int kRsMaxCt = 16;
-constexpr int rs_wgs_per_cu(int C) { return C <= 2 ? 12 : C <= 4 ? 8 : C <= 12 ? 6 : C <= kRsMaxCt ? 4 : 0; }
+constexpr int rs_wgs_per_cu(int C) {
+  return C <= 2 ? 12 : C <= 4 ? 8 : C <= 12 ? 6 : C <= kRsMaxCt ? 4 : C <= 24 ? 6 : 4;
+}
 #ifndef TIDE_RS_NQ
 #define TIDE_RS_NQ 2
 #endif

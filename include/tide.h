@@ -144,9 +144,10 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *   shards     host [R]: shards[r] is rank r's flat fp32 device shard of S elements, 4-byte aligned.
  *   cu_budget  0: one launch, one short-lived workgroup per work item, with at most N of them
  *              resident per CU: N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 12, 4 for C <= 16,
- *              no cap above (each requests 1/N of the CU's local memory; fewer requests in flight
- *              stream HBM better than a full CU, and a workgroup's traffic grows with C).
- *              C <= 16 runs a kernel compiled for that C; larger C a slower runtime-C kernel.
+ *              6 for C <= 24, 4 above (each requests 1/N of the CU's local memory; fewer requests
+ *              in flight stream HBM better than a full CU, and a workgroup's traffic grows with C).
+ *              C <= 16 runs a kernel compiled for that C; larger C a runtime-C kernel that loads
+ *              the contributors in blocks of 8.
  *              -N (1 <= N <= TIDE_RS_MAX_WGS_PER_CU): as 0, with at most N per CU for any C (an N
  *              at or above the hardware's own limit leaves that limit).
  *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of

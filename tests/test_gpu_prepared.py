@@ -294,17 +294,14 @@ def test_prepared_calls_from_threads(gpu_available):
 
 def test_rs_launch_shape_caps_occupancy(gpu_available):
     """Unbounded RS launches request 1/N of a gfx950 CU's 160 KiB of local memory per 128-thread
-    workgroup, N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 12, 4 for C <= 16; no cap above 16."""
+    workgroup, N = 12 for C <= 2, 8 for C <= 4, 6 for C <= 12, 4 for C <= 16, 6 for C <= 24, 4 above."""
     lds_per_cu = 160 * 1024
-    for C, n in ((1, 12), (2, 12), (3, 8), (4, 8), (5, 6), (8, 6), (9, 6), (12, 6), (13, 4), (16, 4), (17, 0),
-                 (40, 0)):
+    for C, n in ((1, 12), (2, 12), (3, 8), (4, 8), (5, 6), (8, 6), (9, 6), (12, 6), (13, 4), (16, 4), (17, 6),
+                 (24, 6), (25, 4), (40, 4)):
         shape = tide_rs_launch_shape(C)
         say(f"RS launch shape C={C}: {shape}")
         assert shape["threads"] == 128 and shape["item_outputs"] == 1024
-        if n:
-            assert shape["lds_bytes"] * n <= lds_per_cu < shape["lds_bytes"] * (n + 1), (C, shape)
-        else:
-            assert shape["lds_bytes"] * 16 <= lds_per_cu, (C, shape)  # only the kernel's own
+        assert shape["lds_bytes"] * n <= lds_per_cu < shape["lds_bytes"] * (n + 1), (C, shape)
 
 
 def test_rs_negative_budget_sets_the_cap_and_changes_speed_only(gpu_available):
