@@ -63,6 +63,8 @@ def parse():
                     help="instead of the step benchmark: occupancy probe, spin-kernel curve and more victims")
     ap.add_argument("--engines", action="store_true",
                     help="instead of the step benchmark: AG placement on CUs vs copy engines, served GB/s and victim slowdown")
+    ap.add_argument("--overlap", action="store_true",
+                    help="the RS on one stream beside back-to-back one-wave GEMMs on another, per --budgets")
     ap.add_argument("--mix-bound", action="store_true",
                     help="the RS's access shape with reads or writes left out, beside the library RS (C = 1-8)")
     ap.add_argument("--copy-sizes", action="store_true",
@@ -606,6 +608,85 @@ def copy_sizes(args, log):
     print(json.dumps({"experiment": "placement engines vs copy size", "rows": rows}), flush=True)
 
 
+def overlap(args, log):
+    """The RS hidden behind compute, as FSDP overlaps it with backward: n back-to-back one-wave bf16
+    GEMMs on one stream, the RS (one call at each CU budget) on another, both enqueued at once.
+    Reports each part alone, the overlapped makespan (first start to last end), the GEMM stream's
+    own time while overlapped, and how much of the shorter part was hidden:
+    hidden = (alone_gemms + alone_rs - makespan) / min(alone_gemms, alone_rs).  Medians of reps."""
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import Layout
+    from oracle.geometry import group_geometry  # sizes only
+    from workloads import CONFIGS, normal_bf16_cuda
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    M, N, K = (int(x) for x in args.gemm.split(","))
+    a = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
+    grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
+             for c in range(cfg.C)]
+    _, S = group_geometry(cfg.shapes, cfg.R)
+    shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
+    L = Layout(cfg.shapes, cfg.R)
+    L.prepare()
+    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def gemms(n):
+        for _ in range(n):
+            torch.matmul(a, b)
+
+    def timed(fn, stream):
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    t_one = statistics.median(timed(lambda: gemms(1), sA) for _ in range(args.reps))
+    rows = []
+    for budget in (int(x) for x in args.budgets.split(",")):
+        call = L.bind_rs(grads, shards, cu_budget=budget)
+        t_rs = statistics.median(timed(lambda: call.launch(sB), sB) for _ in range(args.reps))
+        n = max(1, round(t_rs / t_one))  # GEMM work about as long as the RS
+        t_g = statistics.median(timed(lambda: gemms(n), sA) for _ in range(args.reps))
+        spans, gemm_spans = [], []
+        for _ in range(args.reps):
+            torch.cuda.synchronize()
+            g0, g1, r0, r1 = ev(), ev(), ev(), ev()
+            with torch.cuda.stream(sA):
+                g0.record(sA)
+                gemms(n)
+                g1.record(sA)
+            r0.record(sB)
+            call.launch(sB)
+            r1.record(sB)
+            torch.cuda.synchronize()
+            first = g0 if g0.elapsed_time(r0) >= 0 else r0  # whichever stream started first
+            last = g1 if r1.elapsed_time(g1) >= 0 else r1   # whichever ended last
+            spans.append(first.elapsed_time(last))
+            gemm_spans.append(g0.elapsed_time(g1))
+        call.close()
+        span, t_gc = statistics.median(spans), statistics.median(gemm_spans)
+        row = {"cu_budget": budget, "gemms": n, "gemms_alone_ms": round(t_g, 4), "rs_alone_ms": round(t_rs, 4),
+               "overlapped_makespan_ms": round(span, 4), "gemms_while_overlapped_ms": round(t_gc, 4),
+               "gemm_slowdown_pct": round((t_gc / t_g - 1) * 100, 2),
+               "serial_ms": round(t_g + t_rs, 4),
+               "hidden_fraction": round((t_g + t_rs - span) / min(t_g, t_rs), 3)}
+        log(json.dumps(row))
+        rows.append(row)
+    L.close()
+    print(json.dumps({"experiment": "RS overlapped with back-to-back one-wave GEMMs", "workload": cfg.name,
+                      "gemm": [M, N, K], "gemm_alone_ms": round(t_one, 4), "rows": rows}), flush=True)
+
+
 def mix_bound(args, log):
     """The RS's access shape with its writes or its reads left out (the mix probe of libtide_probe.so),
     beside the library RS on the same buffers: one flat parameter of 2^27 elements, R = 1, C = 1, 2,
@@ -724,6 +805,10 @@ def main():
     if args.mix_bound:
         torch.cuda.set_device(0)
         mix_bound(args, log)
+        return
+    if args.overlap:
+        torch.cuda.set_device(0)
+        overlap(args, log)
         return
     cfg = CONFIGS[args.workload]
     if args.contributors:
