@@ -64,7 +64,8 @@ def parse():
     ap.add_argument("--engines", action="store_true",
                     help="instead of the step benchmark: AG placement on CUs vs copy engines, served GB/s and victim slowdown")
     ap.add_argument("--overlap", action="store_true",
-                    help="the RS on one stream beside back-to-back one-wave GEMMs on another, per --budgets")
+                    help="communication on one stream beside back-to-back GEMMs on another, per --budgets")
+    ap.add_argument("--overlap-comm", choices=["rs", "ag_kernel", "ag_sdma", "ag_copy2d"], default="rs")
     ap.add_argument("--mix-bound", action="store_true",
                     help="the RS's access shape with reads or writes left out, beside the library RS (C = 1-8)")
     ap.add_argument("--copy-sizes", action="store_true",
@@ -609,8 +610,10 @@ def copy_sizes(args, log):
 
 
 def overlap(args, log):
-    """The RS hidden behind compute, as FSDP overlaps it with backward: n back-to-back one-wave bf16
-    GEMMs on one stream, the RS (one call at each CU budget) on another, both enqueued at once.
+    """Communication hidden behind compute, as FSDP overlaps it with forward and backward: n
+    back-to-back bf16 GEMMs on one stream, the communication (--overlap-comm: the RS, or the AG
+    placement on the compute units or the DMA engines; one call at each CU budget) on another,
+    both enqueued at once.
     Reports each part alone, the overlapped makespan (first start to last end), the GEMM stream's
     own time while overlapped, and how much of the shorter part was hidden:
     hidden = (alone_gemms + alone_rs - makespan) / min(alone_gemms, alone_rs).  Medians of reps."""
@@ -627,12 +630,22 @@ def overlap(args, log):
     M, N, K = (int(x) for x in args.gemm.split(","))
     a = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
     b = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
-    grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
-             for c in range(cfg.C)]
+    from all_gather_placement_amd import TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
+
+    kind = args.overlap_comm
     _, S = group_geometry(cfg.shapes, cfg.R)
-    shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
     L = Layout(cfg.shapes, cfg.R)
     L.prepare()
+    if kind == "rs":
+        grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
+                 for c in range(cfg.C)]
+        shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
+        bind = lambda budget: L.bind_rs(grads, shards, cu_budget=budget)
+    else:
+        stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
+        params = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in cfg.shapes]
+        mode = {"ag_kernel": TIDE_AG_KERNEL, "ag_sdma": TIDE_AG_SDMA, "ag_copy2d": TIDE_AG_COPY2D}[kind]
+        bind = lambda budget: L.bind_ag(stage, params, mode=mode, cu_budget=budget if kind == "ag_kernel" else 0)
     sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -652,9 +665,10 @@ def overlap(args, log):
 
     t_one = statistics.median(timed(lambda: gemms(1), sA) for _ in range(args.reps))
     rows = []
-    for budget in (int(x) for x in args.budgets.split(",")):
-        call = L.bind_rs(grads, shards, cu_budget=budget)
-        t_rs = statistics.median(timed(lambda: call.launch(sB), sB) for _ in range(args.reps))
+    budgets = [int(x) for x in args.budgets.split(",")] if kind in ("rs", "ag_kernel") else [0]
+    for budget in budgets:
+        call = bind(budget)
+        t_rs = statistics.median(timed(lambda: call.launch(sB), sB) for _ in range(args.reps))  # the comm alone
         n = max(1, round(t_rs / t_one))  # GEMM work about as long as the RS
         t_g = statistics.median(timed(lambda: gemms(n), sA) for _ in range(args.reps))
         spans, gemm_spans = [], []
@@ -675,7 +689,7 @@ def overlap(args, log):
             gemm_spans.append(g0.elapsed_time(g1))
         call.close()
         span, t_gc = statistics.median(spans), statistics.median(gemm_spans)
-        row = {"cu_budget": budget, "gemms": n, "gemms_alone_ms": round(t_g, 4), "rs_alone_ms": round(t_rs, 4),
+        row = {"cu_budget": budget, "gemms": n, "gemms_alone_ms": round(t_g, 4), "comm_alone_ms": round(t_rs, 4),
                "overlapped_makespan_ms": round(span, 4), "gemms_while_overlapped_ms": round(t_gc, 4),
                "gemm_slowdown_pct": round((t_gc / t_g - 1) * 100, 2),
                "serial_ms": round(t_g + t_rs, 4),
@@ -683,8 +697,9 @@ def overlap(args, log):
         log(json.dumps(row))
         rows.append(row)
     L.close()
-    print(json.dumps({"experiment": "RS overlapped with back-to-back one-wave GEMMs", "workload": cfg.name,
-                      "gemm": [M, N, K], "gemm_alone_ms": round(t_one, 4), "rows": rows}), flush=True)
+    print(json.dumps({"experiment": "communication overlapped with back-to-back GEMMs", "comm": kind,
+                      "workload": cfg.name, "gemm": [M, N, K], "gemm_alone_ms": round(t_one, 4), "rows": rows}),
+          flush=True)
 
 
 def mix_bound(args, log):
