@@ -1,6 +1,8 @@
 // Occupancy and interference probes for gfx950 (libtide_probe.so); see include/tide_probe.h.
 #include <hip/hip_runtime.h>
 
+#include <vector>
+
 #include "../../include/tide_probe.h"
 
 namespace {
@@ -189,6 +191,26 @@ int32_t tide_probe_launch(int32_t num_wgs, int32_t shape, int64_t spin_ticks, ti
   else
     hipLaunchKernelGGL(probe_small, dim3(num_wgs), dim3(kProbeThreads), 0, s, records, ticks);
   return static_cast<int32_t>(hipGetLastError());
+}
+
+int32_t tide_probe_stream_create_cu_mask(int32_t first_cu, int32_t n_cus, void** stream) {
+  int dev = 0, cus = 0;
+  if (stream == nullptr || first_cu < 0 || n_cus < 1) return -1;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return -1;
+  if (static_cast<int64_t>(first_cu) + n_cus > cus) return -1;
+  std::vector<uint32_t> mask((cus + 31) / 32, 0u);
+  for (int i = first_cu; i < first_cu + n_cus; ++i) mask[i / 32] |= 1u << (i % 32);
+  hipStream_t s = nullptr;
+  const hipError_t e = hipExtStreamCreateWithCUMask(&s, static_cast<uint32_t>(mask.size()), mask.data());
+  if (e != hipSuccess) return static_cast<int32_t>(e);
+  *stream = s;
+  return 0;
+}
+
+int32_t tide_probe_stream_destroy(void* stream) {
+  if (stream == nullptr) return -1;
+  return static_cast<int32_t>(hipStreamDestroy(static_cast<hipStream_t>(stream)));
 }
 
 int64_t tide_probe_wall_clock_khz(void) {

@@ -33,6 +33,10 @@ def load_probe_library():
                                        ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
         lib.tide_probe_clock.restype = ctypes.c_int32
         lib.tide_probe_clock.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        lib.tide_probe_stream_create_cu_mask.restype = ctypes.c_int32
+        lib.tide_probe_stream_create_cu_mask.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+        lib.tide_probe_stream_destroy.restype = ctypes.c_int32
+        lib.tide_probe_stream_destroy.argtypes = [ctypes.c_void_p]
         lib.tide_probe_wall_clock_khz.restype = ctypes.c_int64
         lib.tide_probe_wall_clock_khz.argtypes = []
         _lib = lib
@@ -93,6 +97,24 @@ def clock_mhz(out_host, wall_khz: int) -> float:
     """Mean shader clock (MHz) from the probe's four values (a host sequence of 4 integers)."""
     w0, w1, c0, c1 = (int(x) & 0xFFFFFFFFFFFFFFFF for x in list(out_host)[:4])
     return (c1 - c0) / max(w1 - w0, 1) * wall_khz / 1e3
+
+
+def cu_mask_stream(first_cu: int, n_cus: int):
+    """A torch stream whose kernels may run only on CU-mask bits [first_cu, first_cu + n_cus).
+    Returns (torch stream, handle); release the handle with destroy_stream once its work is done."""
+    import torch
+
+    h = ctypes.c_void_p()
+    rc = load_probe_library().tide_probe_stream_create_cu_mask(int(first_cu), int(n_cus), ctypes.byref(h))
+    if rc != 0:
+        raise RuntimeError(f"tide_probe_stream_create_cu_mask({first_cu}, {n_cus}) failed: {rc}")
+    return torch.cuda.ExternalStream(h.value), h.value
+
+
+def destroy_stream(handle: int) -> None:
+    rc = load_probe_library().tide_probe_stream_destroy(handle)
+    if rc != 0:
+        raise RuntimeError(f"tide_probe_stream_destroy failed: {rc}")
 
 
 def wall_clock_khz() -> int:

@@ -57,6 +57,9 @@ def parse():
                     help="instead of the step benchmark: slowdown of a concurrent one-wave bf16 GEMM per cu_budget")
     ap.add_argument("--budgets", default="0,8,16,32,64,128,256,512,768,1024,1536,2048")
     ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
+    ap.add_argument("--cu-masks", default="16,32,64,128",
+                    help="--interference: also the RS confined to K CUs by a CU-masked stream, and the GEMM on "
+                         "the other CUs (comma list of K; empty: none)")
     ap.add_argument("--reps", type=int, default=31,
                     help="repetitions per row of the interference measurements (medians)")
     ap.add_argument("--probes", action="store_true",
@@ -155,6 +158,76 @@ def cpu_baseline(cfg, log, min_seconds: float = 10.0):
     }
 
 
+def cu_placement(stream, n_wgs: int) -> dict:
+    """Where `stream`'s workgroups run: n_wgs small probe workgroups (~50 us each) record their
+    CU; returns the number of distinct CUs and the distinct CUs per XCD."""
+    import numpy as np
+    import torch
+
+    from all_gather_placement_amd import probe as pr
+
+    rec = torch.zeros(n_wgs * pr.RECORD_BYTES, dtype=torch.uint8, device="cuda")
+    ticks = max(1, pr.wall_clock_khz() // 20)  # 50 us
+    pr.probe_launch(n_wgs, pr.TIDE_PROBE_SMALL, ticks, rec, stream)
+    torch.cuda.synchronize()
+    d = pr.decode(rec.cpu().numpy().view(np.uint64))
+    keys = np.unique(d["cu_key"])
+    per_xcc = [int(len(np.unique(d["cu_key"][d["xcc"] == x]))) for x in range(8)]
+    return {"cus": int(len(keys)), "cus_per_xcd": per_xcc}
+
+
+def cu_mask_rows(masks, comm_alone, gemm_once, gemm_alone, rs_bytes, reps, log):
+    """Interference rows for the RS confined by CU masks (see interference())."""
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import probe as pr
+
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = []
+    for k in masks:
+        if not 0 < k < n_cus:
+            raise SystemExit(f"--cu-masks: K must be in 1..{n_cus - 1}, got {k}")
+        rs_stream, rs_h = pr.cu_mask_stream(0, k)
+        gemm_stream, gemm_h = pr.cu_mask_stream(k, n_cus - k)
+        try:
+            where_rs = cu_placement(rs_stream, 8 * k)
+            where_gemm = cu_placement(gemm_stream, 8 * (n_cus - k))
+            t_comm = comm_alone("rs", 0, rs_stream)
+            g_masked = statistics.median(gemm_once(gemm_stream=gemm_stream)[0] for _ in range(reps))
+            for kind, gs in (("rs_cumask", None), ("rs_cumask_partition", gemm_stream)):
+                conc, outlast = [], 0
+                for _ in range(reps):
+                    t, started_first, outlasted = gemm_once("rs", 0, gemm_stream=gs, comm_stream=rs_stream)
+                    if started_first:
+                        conc.append(t)
+                        outlast += int(outlasted)
+                med = statistics.median(conc) if conc else None
+                row = {
+                    "comm": kind, "cu_budget": 0, "cu_mask_cus": k,
+                    "comm_ms": round(t_comm, 4),
+                    "comm_gbps": round(rs_bytes / (t_comm * 1e-3) / 1e9, 1),
+                    "gemm_alone_us": round(gemm_alone * 1e3, 2),
+                    "gemm_concurrent_us": round(med * 1e3, 2) if med else None,
+                    "gemm_concurrent_min_max_us": [round(min(conc) * 1e3, 2), round(max(conc) * 1e3, 2)] if conc else None,
+                    "slowdown_pct": round((med / gemm_alone - 1) * 100, 2) if med else None,
+                    "reps": len(conc),
+                    "comm_outlasts_gemm": round(outlast / len(conc), 2) if conc else None,
+                    "rs_stream_placement": where_rs,
+                }
+                if gs is not None:
+                    row["gemm_masked_alone_us"] = round(g_masked * 1e3, 2)
+                    row["gemm_stream_placement"] = where_gemm
+                log(json.dumps(row))
+                rows.append(row)
+        finally:
+            torch.cuda.synchronize()
+            pr.destroy_stream(rs_h)
+            pr.destroy_stream(gemm_h)
+    return rows
+
+
 def interference(args, log):
     """Slowdown of a concurrent one-wave bf16 GEMM while the RS runs at each CU budget.
 
@@ -166,6 +239,13 @@ def interference(args, log):
     it was still running when the GEMM finished (when it is not, the GEMM waited for the RS to
     drain).  slowdown = median(GEMM with RS) / median(GEMM alone) - 1, the pages' statistic
     (medians of launches).  The same is measured for the AG placement on each engine.
+
+    CU masks (--cu-masks K,...) are the other way to keep communication off compute units: the RS
+    (one unbounded launch) on a stream whose CU mask allows K CUs, (a) beside the GEMM on all CUs
+    ("rs_cumask") and (b) with the GEMM's own stream masked to the other CUs ("rs_cumask_partition";
+    its slowdown is against the unmasked GEMM alone, and `gemm_masked_alone_us` is the GEMM alone on
+    its share).  A CU-id probe on each masked stream records how many CUs, on which XCDs, its
+    workgroups ran on.
     """
     import statistics
 
@@ -199,7 +279,8 @@ def interference(args, log):
 
     bound = {}
 
-    def comm(kind, budget):
+    def comm(kind, budget, stream=None):
+        stream = sB if stream is None else stream
         if (kind, budget) not in bound:
             if kind == "rs":
                 bound[kind, budget] = L.bind_rs(grads, shards, cu_budget=budget)
@@ -208,34 +289,37 @@ def interference(args, log):
                 bound[kind, budget] = L.bind_ag(stage, params, mode=mode, cu_budget=budget)
         reps = 1 if kind in ("rs", "ag_sdma") else 4  # long enough to cover the GEMM
         for _ in range(reps):
-            bound[kind, budget].launch(sB)
+            bound[kind, budget].launch(stream)
 
-    def gemm_once(kind=None, budget=0):
+    def gemm_once(kind=None, budget=0, gemm_stream=None, comm_stream=None):
+        gs = sA if gemm_stream is None else gemm_stream
+        cs = sB if comm_stream is None else comm_stream
         torch.cuda.synchronize()
         e0, e1, r0, r1 = ev(), ev(), ev(), ev()
-        with torch.cuda.stream(sA):
+        with torch.cuda.stream(gs):
             torch.cuda._sleep(spin_cycles)
-            e0.record(sA)
+            e0.record(gs)
             torch.matmul(a, b)
-            e1.record(sA)
+            e1.record(gs)
         if kind is not None:
-            r0.record(sB)
-            comm(kind, budget)
-            r1.record(sB)
+            r0.record(cs)
+            comm(kind, budget, cs)
+            r1.record(cs)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1)
         if kind is None:
             return t, True, True
         return t, r0.elapsed_time(e0) > 0, e1.elapsed_time(r1) > 0
 
-    def comm_alone(kind, budget):
+    def comm_alone(kind, budget, stream=None):
+        cs = sB if stream is None else stream
         ts = []
         for _ in range(3):
             torch.cuda.synchronize()
             r0, r1 = ev(), ev()
-            r0.record(sB)
-            comm(kind, budget)
-            r1.record(sB)
+            r0.record(cs)
+            comm(kind, budget, cs)
+            r1.record(cs)
             torch.cuda.synchronize()
             ts.append(r0.elapsed_time(r1))
         return statistics.median(ts)
@@ -271,6 +355,9 @@ def interference(args, log):
         }
         log(json.dumps(row))
         rows.append(row)
+    masks = [int(x) for x in args.cu_masks.split(",") if x.strip()]
+    if masks:
+        rows += cu_mask_rows(masks, comm_alone, gemm_once, alone, rs_bytes, args.reps, log)
     L.close()
     out = {"experiment": "concurrent one-wave GEMM slowdown vs communication CU budget", "workload": cfg.name,
            "gemm": [M, N, K], "gemm_alone_us_min_max": [round(min(alone_all) * 1e3, 2), round(max(alone_all) * 1e3, 2)],

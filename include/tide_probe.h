@@ -91,6 +91,23 @@ enum {
 int32_t tide_probe_mix(int32_t C, int32_t mode, const void* const* src, float* dst, int64_t items, int32_t lds_bytes,
                        void* stream);
 
+/*
+ * A stream whose kernels may run only on the compute units selected by bits [first_cu, first_cu +
+ * n_cus) of a CU mask (hipExtStreamCreateWithCUMask; the runtime maps mask bits onto the XCDs' CUs,
+ * and tide_probe_launch's records show where they landed).  Instruments the alternative to a CU
+ * budget -- confining communication to a fixed set of CUs -- beside [Endgame] Figure 3's account of
+ * resident communication workgroups holding CUs a concurrent GEMM needs.  Default priority.
+ *   first_cu, n_cus  0 <= first_cu, 1 <= n_cus, first_cu + n_cus <= the current device's CU count.
+ *   stream           receives the hipStream_t (as void*); release it with tide_probe_stream_destroy
+ *                    after the work on it has finished.
+ * Returns 0 or a hipError_t value; -1 for bad arguments (ranges above, NULL stream) or when the
+ * device's CU count cannot be read.
+ */
+int32_t tide_probe_stream_create_cu_mask(int32_t first_cu, int32_t n_cus, void** stream);
+
+/* Destroy a stream made by tide_probe_stream_create_cu_mask.  Returns 0 or a hipError_t value; -1 for NULL. */
+int32_t tide_probe_stream_destroy(void* stream);
+
 /* Device wall-clock rate in kHz (hipDeviceAttributeWallClockRate of the current device), or -1. */
 int64_t tide_probe_wall_clock_khz(void);
 

@@ -342,7 +342,8 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     text = open(os.path.join(ROOT, "include", "tide_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(tide_probe_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["tide_probe_clock", "tide_probe_launch", "tide_probe_mix", "tide_probe_wall_clock_khz"]
+    assert names == ["tide_probe_clock", "tide_probe_launch", "tide_probe_mix", "tide_probe_stream_create_cu_mask",
+                     "tide_probe_stream_destroy", "tide_probe_wall_clock_khz"]
     for n in names:
         assert hasattr(lib, n)
     assert lib.tide_probe_launch(0, 0, 10, None, None) == -1
@@ -358,6 +359,12 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.tide_probe_mix(8, 0, fake, None, 8, 0, None) == -1           # no destination
     assert lib.tide_probe_mix(8, 1, None, fake, 8, 0, None) == -1           # loads without sources
     assert lib.tide_probe_mix(8, 0, fake, fake, 8, -1, None) == -1          # negative local memory
+    h = ctypes.c_void_p()
+    assert lib.tide_probe_stream_create_cu_mask(0, 0, ctypes.byref(h)) == -1   # no CUs
+    assert lib.tide_probe_stream_create_cu_mask(-1, 4, ctypes.byref(h)) == -1  # negative first CU
+    assert lib.tide_probe_stream_create_cu_mask(0, 4, None) == -1              # nowhere to put the stream
+    assert lib.tide_probe_stream_destroy(None) == -1
+    assert h.value is None
     assert pr.clock_mhz([0, 100000, 5, 5 + 2_400_000], 100000) == 2400.0  # 1 ms of wall clock, 2.4M cycles
 
 

@@ -73,3 +73,45 @@ def test_mix_probe_modes(gpu_available):
         assert np.array_equal(got[:, st, :, 0], np.broadcast_to(lanes, (items, 128)))
         for j, v in enumerate(tail):
             assert np.all(got[:, st, :, j + 1] == v)
+
+
+def test_cu_mask_stream_confines_work_and_keeps_results(gpu_available):
+    """A stream masked to K CUs runs its workgroups on at most K distinct CUs (disjoint from the
+    complementary mask's), and an RS launched on it equals the same RS on torch's stream bit for bit."""
+    from all_gather_placement_amd import Layout
+    from workloads import normal_bf16_cuda
+
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    khz = pr.wall_clock_khz()
+    shapes, R, C = [(3000, 64), (257,)], 8, 8
+    grads = [[normal_bf16_cuda(s, 1e-3, 171, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    for k in (8, 64):
+        s_in, h_in = pr.cu_mask_stream(0, k)
+        s_out, h_out = pr.cu_mask_stream(k, n_cus - k)
+        try:
+            keys = []
+            for st, n_wgs in ((s_in, 8 * k), (s_out, 8 * (n_cus - k))):
+                recs = torch.zeros(n_wgs * 4, dtype=torch.int64, device="cuda")
+                pr.probe_launch(n_wgs, pr.TIDE_PROBE_SMALL, khz // 50, recs, st)  # 20 us each
+                torch.cuda.synchronize()
+                keys.append(set(pr.decode(recs.cpu().numpy().view(np.uint64))["cu_key"].tolist()))
+            print(f"[gpu-probe] mask of {k} CUs: workgroups on {len(keys[0])} CUs; complement on {len(keys[1])}",
+                  flush=True)
+            assert 0 < len(keys[0]) <= k
+            assert 0 < len(keys[1]) <= n_cus - k
+            assert not (keys[0] & keys[1])
+            with Layout(shapes, R) as L:
+                ref = [torch.full((L.S,), float("nan"), device="cuda") for _ in range(R)]
+                got = [torch.full((L.S,), float("nan"), device="cuda") for _ in range(R)]
+                L.rs_bf16_to_fp32(grads, ref)
+                torch.cuda.synchronize()
+                call = L.bind_rs(grads, got, cu_budget=0)
+                call.launch(s_in)
+                torch.cuda.synchronize()
+                call.close()
+                for a, b in zip(ref, got):
+                    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        finally:
+            torch.cuda.synchronize()
+            pr.destroy_stream(h_in)
+            pr.destroy_stream(h_out)
