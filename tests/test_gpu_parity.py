@@ -244,6 +244,42 @@ def test_identical_contributor_buffers(gpu_available):
     assert_rs_equal(got, oracle.reduce_scatter([[x]] * C, shapes, R))
 
 
+@pytest.mark.parametrize("C", [257, 1000])
+@pytest.mark.parametrize("budget", [0, 3, -2])
+def test_many_contributors(gpu_available, C, budget):
+    """C far beyond the compiled counts (the runtime-C kernel, blocks of 8 with a ragged last block):
+    seven distinct N(0, 1) buffers passed in turn as the C contributors, so the ascending-order fp32
+    sum over C terms, where every reordering changes bits, is checked against the oracle."""
+    say(f"many contributors C={C} budget={budget}")
+    shapes, R = [(300, 40), (1500,), (17, 3)], 8
+    distinct = [[normal_bf16_bits(s, 1.0, 175, d, p) for p, s in enumerate(shapes)] for d in range(7)]
+    dev = [[dev_bf16(b) for b in row] for row in distinct]
+    grads = [dev[c % 7] for c in range(C)]
+    with Layout(shapes, R) as L:
+        shards = poisoned_shards(R, L.S)
+        L.rs_bf16_to_fp32(grads, shards, cu_budget=budget)
+        torch.cuda.synchronize()
+        got = np.stack([host_bits_f32(s) for s in shards])
+    assert_rs_equal(got, oracle.reduce_scatter([distinct[c % 7] for c in range(C)], shapes, R))
+
+
+def test_many_ranks(gpu_available):
+    """R = 1000 ranks over parameters with fewer rows than ranks: ranks past the data hold padding
+    only (+0.0), every shard is written in full, and the placement skips the padding."""
+    say("many ranks R=1000")
+    shapes, R, C = [(5000, 3), (70,), (999, 2)], 1000, 3
+    bits = [[normal_bf16_bits(s, 1.0, 176, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    assert_rs_equal(run_rs(shapes, R, bits), oracle.reduce_scatter(bits, shapes, R))
+    with Layout(shapes, R) as L:
+        S = L.S
+    stage_bits = normal_bf16_bits((R * S,), 1.0, 177, 0)
+    want = oracle.all_gather_place(stage_bits, shapes, R)
+    for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D):
+        got = run_ag(shapes, R, stage_bits, mode=mode)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w), mode
+
+
 def test_overlap_rejected(gpu_available):
     shapes, R = [(64,)], 2
     g = dev_bf16(normal_bf16_bits((64,), 1.0, 74, 0))
