@@ -78,6 +78,14 @@ def parse():
     return ap.parse_args()
 
 
+def shard_numel(shapes, R: int) -> int:
+    """S, the elements of one rank's flat shard, from the library's own layout (host only)."""
+    from all_gather_placement_amd import Layout
+
+    with Layout(shapes, R) as L:
+        return L.S
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("kernels.hip", "tide_internal.h"):
@@ -252,7 +260,6 @@ def interference(args, log):
     import torch
 
     from all_gather_placement_amd import Layout
-    from oracle.geometry import group_geometry
     from workloads import CONFIGS, normal_bf16_cuda
 
     cfg = CONFIGS[args.workload]
@@ -262,7 +269,7 @@ def interference(args, log):
     b = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
     grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
              for c in range(cfg.C)]
-    _, S = group_geometry(cfg.shapes, cfg.R)
+    S = shard_numel(cfg.shapes, cfg.R)
     shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
     rs_bytes = 2 * cfg.C * cfg.numel() + 4 * cfg.R * S
     L = Layout(cfg.shapes, cfg.R)
@@ -378,12 +385,11 @@ def slot_reuse(args, log):
     import torch
 
     from all_gather_placement_amd import Layout
-    from oracle.geometry import group_geometry
     from workloads import CONFIGS, normal_bf16_cuda
 
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
-    _, S = group_geometry(cfg.shapes, cfg.R)
+    S = shard_numel(cfg.shapes, cfg.R)
     numel = cfg.numel()
     grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
              for c in range(cfg.C)]
@@ -450,7 +456,6 @@ def probes(args, log):
 
     from all_gather_placement_amd import Layout
     from all_gather_placement_amd import probe as pr
-    from oracle.geometry import group_geometry
     from workloads import CONFIGS, normal_bf16_cuda
 
     cfg = CONFIGS[args.workload]
@@ -459,7 +464,7 @@ def probes(args, log):
     tpu = khz / 1000.0  # wall-clock ticks per microsecond
     grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
              for c in range(cfg.C)]
-    _, S = group_geometry(cfg.shapes, cfg.R)
+    S = shard_numel(cfg.shapes, cfg.R)
     shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
     L = Layout(cfg.shapes, cfg.R)
     L.prepare()
@@ -584,12 +589,11 @@ def engines(args, log):
     import torch
 
     from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
-    from oracle.geometry import group_geometry
     from workloads import CONFIGS, normal_bf16_cuda
 
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
-    _, S = group_geometry(cfg.shapes, cfg.R)
+    S = shard_numel(cfg.shapes, cfg.R)
     stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
     params = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in cfg.shapes]
     ag_bytes = 4 * cfg.numel()
@@ -709,7 +713,6 @@ def overlap(args, log):
     import torch
 
     from all_gather_placement_amd import Layout
-    from oracle.geometry import group_geometry  # sizes only
     from workloads import CONFIGS, normal_bf16_cuda
 
     cfg = CONFIGS[args.workload]
@@ -720,7 +723,7 @@ def overlap(args, log):
     from all_gather_placement_amd import TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
 
     kind = args.overlap_comm
-    _, S = group_geometry(cfg.shapes, cfg.R)
+    S = shard_numel(cfg.shapes, cfg.R)
     L = Layout(cfg.shapes, cfg.R)
     L.prepare()
     if kind == "rs":
@@ -877,7 +880,6 @@ def main():
     import torch
 
     from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, tide_rs_launch_shape
-    from oracle.geometry import group_geometry  # sizes only, for the byte formulas
     from workloads import CONFIGS, normal_bf16_cuda
 
     from all_gather_placement_amd.build import ensure_built
@@ -922,7 +924,7 @@ def main():
     log(f"workload {cfg.name}: P={cfg.P} R={cfg.R} C={cfg.C}")
 
     numel = cfg.numel()
-    _, S = group_geometry(cfg.shapes, cfg.R)
+    S = shard_numel(cfg.shapes, cfg.R)
     rs_bytes = 2 * cfg.C * numel + 4 * cfg.R * S
     ag_bytes = 4 * numel
 

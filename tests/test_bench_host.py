@@ -30,3 +30,36 @@ def test_traffic_only_from_counters_taken_on_this_kernel_source(tmp_path, monkey
     # the counters moved every algorithmic byte about once (reads + writes within 1% of 20 B per output)
     algorithmic = int(re.search(r"algorithmic_bytes_per_launch:\s*([0-9]+)", text).group(1))
     assert abs(hbm / algorithmic - 1.0) < 0.01
+
+
+def _oracle_imports(path):
+    """(enclosing function or None, line) of every import of the oracle package in a source file."""
+    import ast
+
+    tree = ast.parse(open(path).read())
+    found = []
+
+    def visit(node, fn):
+        for child in ast.iter_child_nodes(node):
+            if isinstance(child, (ast.FunctionDef, ast.AsyncFunctionDef)):
+                visit(child, child.name)
+                continue
+            if isinstance(child, ast.Import) and any(a.name.split(".")[0] == "oracle" for a in child.names):
+                found.append((fn, child.lineno))
+            if isinstance(child, ast.ImportFrom) and (child.module or "").split(".")[0] == "oracle":
+                found.append((fn, child.lineno))
+            visit(child, fn)
+
+    visit(tree, None)
+    return found
+
+
+def test_oracle_only_in_the_cpu_baseline_leg_and_never_in_the_package():
+    """The oracle is test infrastructure: bench.py touches it only in cpu_baseline, and nothing in the
+    package or the input generators imports it."""
+    uses = _oracle_imports(os.path.join(ROOT, "bench.py"))
+    assert uses and all(fn == "cpu_baseline" for fn, _ in uses), uses
+    for d in ("all_gather_placement_amd", "workloads"):
+        for f in sorted(os.listdir(os.path.join(ROOT, d))):
+            if f.endswith(".py"):
+                assert _oracle_imports(os.path.join(ROOT, d, f)) == [], (d, f)
