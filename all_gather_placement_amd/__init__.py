@@ -8,6 +8,8 @@ from .tide import (  # noqa: F401
     TIDE_AG_COPY2D,
     TIDE_AG_KERNEL,
     TIDE_AG_SDMA,
+    TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS,
+    TIDE_RS_MAX_WGS_PER_CU,
     Layout,
     TideError,
     library_path,
@@ -19,6 +21,7 @@ from .tide import (  # noqa: F401
     tide_call_launch,
     tide_layout_create,
     tide_rs_bf16_to_fp32,
+    tide_rs_cu_exclusive,
     tide_rs_launch_shape,
     tide_rs_prepare,
     tide_rs_slots_bf16_to_fp32,

@@ -19,6 +19,10 @@
 namespace tide {
 namespace {
 
+// Smallest RS cu_budget: the per-CU caps -1 .. -TIDE_RS_MAX_WGS_PER_CU, then the CU-exclusive modes.
+constexpr int32_t kRsMinBudget = TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS);
+static_assert(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS == kRsCuMaxItems, "header and kernel agree on the widest workgroup");
+
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
 };
@@ -70,7 +74,7 @@ struct Request {
 
 tide_status validate_rs(const tide_layout* L, int32_t C, const void* const* grads, float* const* shards,
                         int32_t cu_budget, Request* q) {
-  if (L == nullptr || grads == nullptr || shards == nullptr || C < 1 || cu_budget < -TIDE_RS_MAX_WGS_PER_CU)
+  if (L == nullptr || grads == nullptr || shards == nullptr || C < 1 || cu_budget < kRsMinBudget)
     return TIDE_ERR_INVALID;
   const int32_t P = L->P, R = L->R;
   const int64_t S = L->S;
@@ -106,7 +110,7 @@ tide_status validate_rs(const tide_layout* L, int32_t C, const void* const* grad
 
 tide_status validate_rs_slots(const tide_layout* L, int32_t C, const void* const* slots, float* const* shards,
                               int32_t cu_budget, Request* q) {
-  if (L == nullptr || slots == nullptr || shards == nullptr || C < 1 || cu_budget < -TIDE_RS_MAX_WGS_PER_CU)
+  if (L == nullptr || slots == nullptr || shards == nullptr || C < 1 || cu_budget < kRsMinBudget)
     return TIDE_ERR_INVALID;
   if (C > (1 << 24)) return TIDE_ERR_INVALID;
   const int32_t R = L->R;
@@ -273,6 +277,10 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
   if (q.kind == kRs || q.kind == kRsSlots) {
     const int64_t count = int64_t(L->rs_chunks.size());
     const bool flat = q.kind == kRsSlots;
+    if (const int w = rs_cu_items(q.cu_budget)) {
+      // one launch of CU-exclusive workgroups of w items (the table's order: items are rank-major)
+      return launch_rs_cu(st->rs, count, w, tbl, flat ? 1 : L->P, q.C, L->S, flat, q.vec, rs_cu_launch_lds(*st), hs);
+    }
     const int64_t rs_wgs = int64_t(q.cu_budget) * kBudgetThreads / kThreads;
     const Plan plan = plan_for(count, q.cu_budget, rs_wgs, kRsBoundedItems);
     // Unbounded launches cap the RS workgroups per CU (by C, or -cu_budget); bounded ones are
@@ -517,7 +525,7 @@ tide_status tide_call_launch(const tide_call* call, void* stream) {
 
 tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads, int32_t* item_outputs,
                                  int32_t* lds_bytes) {
-  if (C < 1 || cu_budget < -TIDE_RS_MAX_WGS_PER_CU || threads == nullptr || item_outputs == nullptr ||
+  if (C < 1 || cu_budget < tide::kRsMinBudget || threads == nullptr || item_outputs == nullptr ||
       lds_bytes == nullptr)
     return TIDE_ERR_INVALID;
   tide::DeviceState st;
@@ -525,8 +533,13 @@ tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads,
   int e = hipGetDevice(&dev);
   if (e == hipSuccess) e = tide::rs_device_info(dev, &st);
   if (e != hipSuccess) return tide::hip_fail(e);
-  *threads = tide::kThreads;
   *item_outputs = int32_t(tide::kRsChunk);
+  if (const int w = tide::rs_cu_items(cu_budget)) {
+    *threads = tide::kThreads * w;
+    *lds_bytes = st.rs_static_lds_cu + tide::rs_cu_launch_lds(st);
+    return TIDE_OK;
+  }
+  *threads = tide::kThreads;
   *lds_bytes = (C <= tide::kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt) + tide::rs_launch_lds(st, C, cu_budget);
   return TIDE_OK;
 }

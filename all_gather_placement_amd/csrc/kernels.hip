@@ -173,8 +173,7 @@ __device__ __forceinline__ void full_item_load(const unsigned short* const* src,
 // exchanged through LDS so that each 16-byte store instruction of a wave covers 1 KiB of whole
 // cache lines.  All threads of the workgroup call it (it synchronises the workgroup).
 template <int CT>
-__device__ __forceinline__ void full_item_finish(const u32x4 x[CT], float* dst, f32x4* xfer, int tid) {
-  float a[8];
+__device__ __forceinline__ void full_item_sums(const u32x4 x[CT], float a[8]) {
   a[0] = widen_lo(x[0].x); a[1] = widen_hi(x[0].x); a[2] = widen_lo(x[0].y); a[3] = widen_hi(x[0].y);
   a[4] = widen_lo(x[0].z); a[5] = widen_hi(x[0].z); a[6] = widen_lo(x[0].w); a[7] = widen_hi(x[0].w);
 #pragma unroll
@@ -182,10 +181,17 @@ __device__ __forceinline__ void full_item_finish(const u32x4 x[CT], float* dst, 
     a[0] += widen_lo(x[c].x); a[1] += widen_hi(x[c].x); a[2] += widen_lo(x[c].y); a[3] += widen_hi(x[c].y);
     a[4] += widen_lo(x[c].z); a[5] += widen_hi(x[c].z); a[6] += widen_lo(x[c].w); a[7] += widen_hi(x[c].w);
   }
-  __syncthreads();  // the previous item's readers are done with xfer
+}
+
+// A lane's 8 sums into the exchange buffer: outputs 8*tid .. 8*tid+7 of the item.
+__device__ __forceinline__ void full_item_put(const float a[8], f32x4* xfer, int tid) {
   xfer[2 * tid] = f32x4{a[0], a[1], a[2], a[3]};
   xfer[2 * tid + 1] = f32x4{a[4], a[5], a[6], a[7]};
-  __syncthreads();
+}
+
+// The item's 1024 fp32 outputs from the exchange buffer: two 16-byte stores per lane, so each wave
+// store instruction covers 1 KiB of whole cache lines.
+__device__ __forceinline__ void full_item_store(const f32x4* xfer, float* dst, int tid) {
 #if TIDE_RS_STORE_AUX >= 0
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, 32 * kThreads, 0x00020000);
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid]), rsrc, 16 * tid, 0, TIDE_RS_STORE_AUX);
@@ -197,13 +203,23 @@ __device__ __forceinline__ void full_item_finish(const u32x4 x[CT], float* dst, 
 #endif
 }
 
+template <int CT>
+__device__ __forceinline__ void full_item_finish(const u32x4 x[CT], float* dst, f32x4* xfer, int tid) {
+  float a[8];
+  full_item_sums<CT>(x, a);
+  __syncthreads();  // the previous item's readers are done with xfer
+  full_item_put(a, xfer, tid);
+  __syncthreads();
+  full_item_store(xfer, dst, tid);
+}
+
 // Full work item, runtime contributor count (C > kRsMaxCt): contributors in blocks of 8, each
 // block's 8 loads issued together (a lane past C gets a zero-sized buffer range and its value is
 // never added), sums in ascending contributor order, then the same exchange and stores as above.
 constexpr int kRtLoadAux = TIDE_RS_LOAD_AUX >= 0 ? TIDE_RS_LOAD_AUX : 2;     // nt
 constexpr int kRtStoreAux = TIDE_RS_STORE_AUX >= 0 ? TIDE_RS_STORE_AUX : 18;  // nt sc1
-__device__ __forceinline__ void full_item_rt(void* const* gptr, int32_t P, const RsChunk& ch, int C, float* dst,
-                                             f32x4* xfer, int tid) {
+__device__ __forceinline__ void full_item_rt_sums(void* const* gptr, int32_t P, const RsChunk& ch, int C, int tid,
+                                                  float out[8]) {
   constexpr int B = 8;
   float a[8] = {};
   for (int c0 = 0; c0 < C; c0 += B) {
@@ -235,14 +251,25 @@ __device__ __forceinline__ void full_item_rt(void* const* gptr, int32_t P, const
       }
     }
   }
-  __syncthreads();  // the previous item's readers are done with xfer
-  xfer[2 * tid] = f32x4{a[0], a[1], a[2], a[3]};
-  xfer[2 * tid + 1] = f32x4{a[4], a[5], a[6], a[7]};
-  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = a[e];
+}
+
+__device__ __forceinline__ void full_item_rt_store(const f32x4* xfer, float* dst, int tid) {
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst, 0, 32 * kThreads, 0x00020000);
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid]), rsrc, 16 * tid, 0, kRtStoreAux);
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, xfer[tid + kThreads]), rsrc, 16 * (tid + kThreads),
                                          0, kRtStoreAux);
+}
+
+__device__ __forceinline__ void full_item_rt(void* const* gptr, int32_t P, const RsChunk& ch, int C, float* dst,
+                                             f32x4* xfer, int tid) {
+  float a[8];
+  full_item_rt_sums(gptr, P, ch, C, tid, a);
+  __syncthreads();  // the previous item's readers are done with xfer
+  full_item_put(a, xfer, tid);
+  __syncthreads();
+  full_item_rt_store(xfer, dst, tid);
 }
 
 // RS kernel.  CT in 1..kRsMaxCt: contributor count fixed at compile time; CT == 0: any C >= 1.
@@ -333,6 +360,139 @@ __global__ __launch_bounds__(kThreads) void rs_kernel(const RsChunk* __restrict_
     // Padding rows of this rank's slice: +0.0.
     for (int i = tid; i < ch.npad; i += kThreads) store_hbm(dst + n + i, 0.0f);
   }
+}
+
+// The CT contributor base pointers of parameter p, all loaded before any is used: one scalar-load
+// batch and one wait (an empty asm statement that takes every pointer as an SGPR operand keeps the
+// compiler from pairing each load with its first use, which would serialise them; it emits no
+// instruction).
+template <int CT>
+__device__ __forceinline__ void load_bases(const unsigned short* const* __restrict__ gptr, int32_t P, int32_t p,
+                                           const unsigned short* (&b)[CT]) {
+#pragma unroll
+  for (int c = 0; c < CT; ++c) b[c] = gptr[static_cast<int64_t>(c) * P + p];
+  if constexpr (CT == 1) {
+    asm volatile("" : "+s"(b[0]));
+  } else if constexpr (CT == 2) {
+    asm volatile("" : "+s"(b[0]), "+s"(b[1]));
+  } else if constexpr (CT == 4) {
+    asm volatile("" : "+s"(b[0]), "+s"(b[1]), "+s"(b[2]), "+s"(b[3]));
+  } else if constexpr (CT == 8) {
+    asm volatile("" : "+s"(b[0]), "+s"(b[1]), "+s"(b[2]), "+s"(b[3]), "+s"(b[4]), "+s"(b[5]), "+s"(b[6]),
+                 "+s"(b[7]));
+  }
+}
+
+// CU-exclusive RS kernel: one launch over all work items in workgroups of W = blockDim.x / 128
+// groups of 128 threads (W <= kRsCuMaxItems); group g of workgroup slot s takes item s*W + g, the
+// same per-item work as rs_kernel.  The host gives every workgroup the largest local memory one may
+// request, so a CU holds a single RS workgroup and is empty again whenever it exits: a concurrent
+// kernel's workgroup waiting for a whole CU (a one-wave GEMM's, for instance) takes it within one
+// RS workgroup lifetime, while the RS itself runs as one launch with W items resident per CU.
+// There is one workgroup barrier, outside every per-group branch: groups with a full item leave
+// their sums in their own exchange slot and store them after it; the others finish before it.
+template <int CT, bool VEC, bool FLAT>
+__global__ __launch_bounds__(kThreads * kRsCuMaxItems) void rs_cu_kernel(const RsChunk* __restrict__ chunks,
+                                                                         int64_t count,
+                                                                         void* const* __restrict__ ptrs,
+                                                                         int32_t P, int32_t C, int64_t S) {
+#if TIDE_RS_WIDE
+  __shared__ f32x4 xfer_all[kRsCuMaxItems][2 * kThreads];
+#endif
+  const int W = static_cast<int>(blockDim.x) / kThreads;
+  const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kThreads);
+  const int tid = static_cast<int>(threadIdx.x) % kThreads;
+  const unsigned short* const* __restrict__ gptr = reinterpret_cast<const unsigned short* const*>(ptrs);
+  float* const* __restrict__ sptr = reinterpret_cast<float* const*>(ptrs + static_cast<int64_t>(C) * P);
+  const int nc = CT > 0 ? CT : C;
+  // workgroup slots, one per grid position: each XCD walks one contiguous range of them
+  int64_t slot = blockIdx.x;
+  if (TIDE_RS_XCD_REMAP != 0) {
+    const int64_t n = gridDim.x, x = slot % kXcds, i = slot / kXcds;
+    slot = x * (n / kXcds) + min<int64_t>(x, n % kXcds) + i;
+  }
+  const int64_t item = slot * W + grp;
+  float* full_dst = nullptr;  // set for a full item, stored after the barrier
+
+  if (item < count) {
+    RsChunk ch = chunks[item];
+    if (FLAT) {
+      ch.src = static_cast<int64_t>(ch.r) * S + ch.dst;
+      ch.p = 0;
+    }
+    float* dst = sptr[ch.r] + ch.dst;
+    const int n = ch.nvalid;
+
+    if (VEC) {
+      const int head = min(n, static_cast<int>((-ch.src) & 7));
+      const int nb = (n - head) >> 3;
+      const int ng = 2 * nb;
+      const int tail = (n - head) & 7;
+      const bool dst16 = ((ch.dst + head) & 3) == 0;
+      if constexpr (CT > 0) {
+        const unsigned short* src[CT];
+        load_bases<CT>(gptr, P, ch.p, src);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) src[c] += ch.src;
+#if TIDE_RS_WIDE
+        if (full_item(ch)) {
+          u32x4 x[CT];
+          float a[8];
+          full_item_load<CT>(src, tid, x);
+          full_item_sums<CT>(x, a);
+          full_item_put(a, xfer_all[grp], tid);
+          full_dst = dst;
+        } else
+#endif
+        {
+          if (tid < head) store_hbm(dst + tid, sum1<CT>(src, nc, tid));
+          constexpr int NQ = TIDE_RS_NQ;
+          int q = tid;
+          for (; q + (NQ - 1) * kThreads < ng; q += NQ * kThreads)
+            sum_groups<CT, NQ>(src, static_cast<uint32_t>(head + 4 * q), dst, dst16);
+          for (; q < ng; q += kThreads) sum_groups<CT, 1>(src, static_cast<uint32_t>(head + 4 * q), dst, dst16);
+          if (tid < tail) {
+            const int64_t k = head + 8 * static_cast<int64_t>(nb) + tid;
+            store_hbm(dst + k, sum1<CT>(src, nc, k));
+          }
+        }
+      } else {
+#if TIDE_RS_WIDE
+        if (full_item(ch)) {
+          float a[8];
+          full_item_rt_sums(ptrs, P, ch, nc, tid, a);
+          full_item_put(a, xfer_all[grp], tid);
+          full_dst = dst;
+        } else
+#endif
+        {
+          for (int i = tid; i < head; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
+          for (int q = tid; q < ng; q += kThreads) {
+            const int64_t k = head + 4 * static_cast<int64_t>(q);
+            sum_group_rt(gptr, P, ch.p, nc, ch.src + k, dst + k, dst16);
+          }
+          for (int i = tid; i < tail; i += kThreads) {
+            const int64_t k = head + 8 * static_cast<int64_t>(nb) + i;
+            store_hbm(dst + k, sum1_rt(gptr, P, ch.p, nc, ch.src + k));
+          }
+        }
+      }
+    } else {
+      for (int i = tid; i < n; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
+    }
+    // padding rows of this rank's slice (a full item has none)
+    for (int i = tid; i < ch.npad; i += kThreads) store_hbm(dst + n + i, 0.0f);
+  }
+
+#if TIDE_RS_WIDE
+  __syncthreads();  // every group's exchange slot is written
+  if (full_dst != nullptr) {
+    if (CT > 0)
+      full_item_store(xfer_all[grp], full_dst, tid);
+    else
+      full_item_rt_store(xfer_all[grp], full_dst, tid);
+  }
+#endif
 }
 
 // AG kernel: bit copy of n bf16 elements per item.  VEC: stage and parameter bases are 16-byte
@@ -470,7 +630,44 @@ hipError_t launch_rs_c(const RsChunk* chunks, int64_t first, int64_t count, int 
   }
 }
 
+template <int CT, bool FLAT>
+hipError_t launch_rs_cu_ct(const RsChunk* chunks, int64_t count, int grid, int threads, void* const* ptrs, int32_t P,
+                           int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
+  if (vec)
+    hipLaunchKernelGGL((rs_cu_kernel<CT, true, FLAT>), dim3(grid), dim3(threads), lds, s, chunks, count, ptrs, P, C, S);
+  else
+    hipLaunchKernelGGL((rs_cu_kernel<CT, false, FLAT>), dim3(grid), dim3(threads), lds, s, chunks, count, ptrs, P, C,
+                       S);
+  return hipGetLastError();
+}
+
+// The CU-exclusive kernel is compiled for the counts a layer group is reduced over most (C = 1, 2,
+// 4, 8); any other C takes its runtime-C form.
+template <bool FLAT>
+hipError_t launch_rs_cu_c(const RsChunk* chunks, int64_t count, int grid, int threads, void* const* ptrs, int32_t P,
+                          int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
+  switch (C) {
+    case 1: return launch_rs_cu_ct<1, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+    case 2: return launch_rs_cu_ct<2, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+    case 4: return launch_rs_cu_ct<4, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+    case 8: return launch_rs_cu_ct<8, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+    default: return launch_rs_cu_ct<0, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+  }
+}
+
 }  // namespace
+
+int launch_rs_cu(const RsChunk* chunks, int64_t count, int items_per_wg, const void* const* dev_ptrs, int32_t P,
+                 int32_t C, int64_t S, bool flat, bool vec, int dyn_lds, void* hip_stream) {
+  if (items_per_wg < 1 || items_per_wg > kRsCuMaxItems || count < 1) return hipErrorInvalidValue;
+  const int64_t grid = (count + items_per_wg - 1) / items_per_wg;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  void* const* ptrs = const_cast<void* const*>(dev_ptrs);
+  const int threads = kThreads * items_per_wg;
+  if (flat) return launch_rs_cu_c<true>(chunks, count, int(grid), threads, ptrs, 1, C, S, vec, dyn_lds, s);
+  return launch_rs_cu_c<false>(chunks, count, int(grid), threads, ptrs, P, C, S, vec, dyn_lds, s);
+}
 
 int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,
               const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, int dyn_lds,
@@ -479,6 +676,13 @@ int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int
   void* const* ptrs = const_cast<void* const*>(dev_ptrs);
   if (flat) return launch_rs_c<true>(chunks, first, count, grid, items_per_wg, ptrs, 1, C, S, vec, dyn_lds, s);
   return launch_rs_c<false>(chunks, first, count, grid, items_per_wg, ptrs, P, C, S, vec, dyn_lds, s);
+}
+
+int rs_cu_static_lds(int* static_lds) {
+  hipFuncAttributes attr;
+  const hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&rs_cu_kernel<8, true, false>));
+  if (e == hipSuccess) *static_lds = static_cast<int>(attr.sharedSizeBytes);
+  return e;
 }
 
 int rs_lds_info(int device, int* lds_per_cu, int* static_lds_ct, int* static_lds_rt) {

@@ -53,13 +53,29 @@ struct DeviceState {
   int lds_per_wg = 0;       // largest local memory one workgroup may request (bytes)
   int rs_static_lds_ct = 0; // static local memory of the RS kernel, C <= kRsMaxCt
   int rs_static_lds_rt = 0; // static local memory of the RS kernel, C > kRsMaxCt
+  int rs_static_lds_cu = 0; // static local memory of the CU-exclusive RS kernel
 };
+
+// cu_budget values TIDE_RS_CU_EXCLUSIVE(W): the number of items per CU-exclusive workgroup, else 0.
+inline int rs_cu_items(int cu_budget) {
+  const int w = -cu_budget - TIDE_RS_MAX_WGS_PER_CU;
+  return w >= 1 && w <= TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS ? w : 0;
+}
+
+// Dynamic local memory of a CU-exclusive RS workgroup: together with its static local memory, the
+// most one workgroup may request (all of a CU's on MI355X), so no second one fits beside it.
+inline int rs_cu_launch_lds(const DeviceState& st) {
+  const int cap = st.lds_per_wg < st.lds_per_cu ? st.lds_per_wg : st.lds_per_cu;
+  const int dyn = cap - st.rs_static_lds_cu;
+  return dyn > 0 ? dyn : 0;
+}
 
 // Dynamic local memory of an RS launch with C contributors at `cu_budget` on this device: 0 caps
 // the RS workgroups per CU at rs_wgs_per_cu(C), -N at N; bounded launches (> 0) add none.  Needs
 // lds_per_cu, lds_per_wg and the static sizes filled in (rs_device_info).
 inline int rs_launch_lds(const DeviceState& st, int C, int cu_budget) {
   if (cu_budget > 0) return 0;
+  if (rs_cu_items(cu_budget) > 0) return rs_cu_launch_lds(st);
   const int wgs = cu_budget < 0 ? -cu_budget : rs_wgs_per_cu(C);
   const int static_lds = C <= kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt;
   const int dyn = rs_dynamic_lds(st.lds_per_cu, static_lds, wgs);

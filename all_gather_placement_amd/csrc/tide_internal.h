@@ -146,6 +146,15 @@ static_assert(kAgChunk % (8 * TIDE_AG_THREADS) == 0, "a full AG item is whole ve
 #define TIDE_AG_BOUNDED_ITEMS 8
 #endif
 constexpr int kRsBoundedItems = TIDE_RS_BOUNDED_ITEMS;
+
+// CU-exclusive RS launches (cu_budget TIDE_RS_CU_EXCLUSIVE(W)): one launch of workgroups of W
+// 128-thread groups, one work item each, and the largest local memory a workgroup may request, so
+// each CU holds one RS workgroup and is empty whenever it exits.  Measured on MI355X (one flat
+// C = 8 parameter, 2^27 outputs, beside the one-wave bf16 GEMM): W = 2 5.04 TB/s, GEMM +2.5%;
+// 4: 6.25 TB/s, +4.4%; 6: 6.27, +7.9%; 8: 6.36, +10.5%; bounded budget 512 (same resident threads
+// as W = 4): 5.33 TB/s, -0.2%; W = 4 with only its own local memory (several per CU): +261%.
+constexpr int kRsCuMaxItems = 8;
+static_assert(kThreads * kRsCuMaxItems <= 1024, "a CU-exclusive workgroup fits the workgroup size limit");
 constexpr int kAgBoundedItems = TIDE_AG_BOUNDED_ITEMS;
 
 // One RS work item: nvalid summed elements of parameter p, starting at element `src` of the
@@ -185,6 +194,11 @@ int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int
               const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, int dyn_lds,
               void* hip_stream);
 int rs_lds_info(int device, int* lds_per_cu, int* static_lds_ct, int* static_lds_rt);
+// launch_rs_cu: the CU-exclusive RS over all `count` items in one launch, items_per_wg (1 ..
+// kRsCuMaxItems) items per workgroup; rs_cu_static_lds: that kernel's static local memory.
+int launch_rs_cu(const RsChunk* chunks, int64_t count, int items_per_wg, const void* const* dev_ptrs, int32_t P,
+                 int32_t C, int64_t S, bool flat, bool vec, int dyn_lds, void* hip_stream);
+int rs_cu_static_lds(int* static_lds);
 inline int rs_dynamic_lds(int lds_per_cu, int static_lds, int wgs_per_cu) {
   if (wgs_per_cu <= 0 || lds_per_cu <= 0) return 0;
   // rounded down to 512 bytes per workgroup, so wgs_per_cu of them fit in a CU (and, for counts up

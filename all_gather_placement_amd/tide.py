@@ -24,6 +24,18 @@ TIDE_ERR_UNSUPPORTED = 4
 TIDE_AG_KERNEL = 0
 TIDE_AG_SDMA = 1
 TIDE_AG_COPY2D = 2
+TIDE_RS_MAX_WGS_PER_CU = 64
+TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS = 8
+
+
+def tide_rs_cu_exclusive(items_per_workgroup: int) -> int:
+    """RS cu_budget of the CU-exclusive launch (include/tide.h TIDE_RS_CU_EXCLUSIVE(W)): workgroups of
+    128*W threads taking W work items each and a whole CU's local memory, one per CU."""
+    w = int(items_per_workgroup)
+    if not 1 <= w <= TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS:
+        raise ValueError(f"items per CU-exclusive workgroup must be 1..{TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS}, got {w}")
+    return -(TIDE_RS_MAX_WGS_PER_CU + w)
+
 
 _lib = None
 

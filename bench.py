@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--cu-budget", type=int, default=0)
     ap.add_argument("--rs-wgs-per-cu", type=int, default=0,
                     help="unbounded RS with at most N workgroups per CU (RS cu_budget -N; 0 = the library's cap by C)")
+    ap.add_argument("--rs-cu-exclusive", type=int, default=0,
+                    help="the RS as one launch of CU-exclusive workgroups of W items (RS cu_budget "
+                         "TIDE_RS_CU_EXCLUSIVE(W) = -(64 + W), W = 1..8)")
     ap.add_argument("--ag-mode", choices=["kernel", "sdma", "copy2d"], default="kernel")
     ap.add_argument("--contributors", type=int, default=0,
                     help="override the workload's contributor count C (default: the workload's own)")
@@ -55,7 +58,7 @@ def parse():
                     help="also capture the step (prepared RS + AG calls) in a HIP graph and time its replays")
     ap.add_argument("--interference", action="store_true",
                     help="instead of the step benchmark: slowdown of a concurrent one-wave bf16 GEMM per cu_budget")
-    ap.add_argument("--budgets", default="0,8,16,32,64,128,256,512,768,1024,1536,2048")
+    ap.add_argument("--budgets", default="0,-1,-2,-4,-65,-66,-68,-70,-72,8,16,32,64,128,256,512,768,1024,1536,2048")
     ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
     ap.add_argument("--cu-masks", default="16,32,64,128",
                     help="--interference: also the RS confined to K CUs by a CU-masked stream, and the GEMM on "
@@ -76,6 +79,17 @@ def parse():
     ap.add_argument("--slot-reuse", action="store_true",
                     help="instead of the step benchmark: Slot-Reuse (pack into slots + RS from slots) vs in-place RS")
     return ap.parse_args()
+
+
+def rs_mode(cu_budget: int) -> str:
+    """How an RS call at `cu_budget` launches (include/tide.h, tide_rs_bf16_to_fp32)."""
+    if cu_budget == 0:
+        return "one launch, per-CU cap by C"
+    if cu_budget > 0:
+        return f"bounded launches, {256 * cu_budget} threads"
+    if cu_budget >= -64:
+        return f"one launch, at most {-cu_budget} per CU"
+    return f"one launch, CU-exclusive workgroups of {-cu_budget - 64} items"
 
 
 def shard_numel(shapes, R: int) -> int:
@@ -351,6 +365,7 @@ def interference(args, log):
         med = statistics.median(conc) if conc else None
         row = {
             "comm": kind, "cu_budget": budget,
+            "mode": rs_mode(budget) if kind == "rs" else None,
             "comm_ms": round(t_alone, 4),
             "comm_gbps": round(nbytes / (t_alone * 1e-3) / 1e9, 1),
             "gemm_alone_us": round(alone * 1e3, 2),
@@ -756,6 +771,8 @@ def overlap(args, log):
     t_one = statistics.median(timed(lambda: gemms(1), sA) for _ in range(args.reps))
     rows = []
     budgets = [int(x) for x in args.budgets.split(",")] if kind in ("rs", "ag_kernel") else [0]
+    if kind == "ag_kernel":
+        budgets = [b for b in budgets if b >= 0]  # per-CU caps (-N) are the RS's only
     for budget in budgets:
         call = bind(budget)
         t_rs = statistics.median(timed(lambda: call.launch(sB), sB) for _ in range(args.reps))  # the comm alone
@@ -872,6 +889,10 @@ def main():
         print("--rs-wgs-per-cu takes 1..64 and applies to the unbounded RS only (--cu-budget 0)",
               file=sys.stderr, flush=True)
         sys.exit(2)
+    if args.rs_cu_exclusive and (args.cu_budget or args.rs_wgs_per_cu or not 0 < args.rs_cu_exclusive <= 8):
+        print("--rs-cu-exclusive takes 1..8 and replaces --cu-budget and --rs-wgs-per-cu for the RS",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
 
     def log(msg):
         if not args.quiet:
@@ -944,6 +965,8 @@ def main():
     stream = torch.cuda.current_stream()
     # Arguments are validated and marshalled once; each call below is one C-ABI call.
     rs_budget = -args.rs_wgs_per_cu if args.rs_wgs_per_cu else args.cu_budget
+    if args.rs_cu_exclusive:
+        rs_budget = -(64 + args.rs_cu_exclusive)
     rs_call = L.bind_rs(grads, shards, cu_budget=rs_budget)
     ag_call = L.bind_ag(stage, params, mode=ag_mode, cu_budget=args.cu_budget)
 
@@ -1094,7 +1117,8 @@ def main():
         "config": {
             "workload": f"{cfg.name} RS+AG step (R={cfg.R}, C={cfg.C}, P={cfg.P})",
             "R": cfg.R, "C": cfg.C, "P": cfg.P, "numel": numel, "S": S,
-            "cu_budget": args.cu_budget, "rs_cu_budget": rs_budget, "ag_mode": args.ag_mode,
+            "cu_budget": args.cu_budget, "rs_cu_budget": rs_budget, "rs_mode": rs_mode(rs_budget),
+            "ag_mode": args.ag_mode,
             "rs_bytes": rs_bytes, "ag_bytes": ag_bytes, "parallelism": "none (1 GPU, node-local level)",
         },
         "rs_gbps": round(rs_gbps, 2),
@@ -1111,7 +1135,8 @@ def main():
                         "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
         "roofline": {
             "bound": "hbm",
-            "kernel": f"rs_kernel<{cfg.C if cfg.C <= 16 else 0}, true, false>",
+            "kernel": (f"rs_cu_kernel<{cfg.C if cfg.C in (1, 2, 4, 8) else 0}, true, false>" if rs_budget < -64
+                       else f"rs_kernel<{cfg.C if cfg.C <= 16 else 0}, true, false>"),
             "achieved": round(rs_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

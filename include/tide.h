@@ -52,6 +52,11 @@ typedef struct tide_layout tide_layout;
 /* Largest per-CU cap an RS call may ask for with a negative cu_budget. */
 #define TIDE_RS_MAX_WGS_PER_CU 64
 
+/* RS cu_budget of the CU-exclusive launch with W work items per workgroup (1 <= W <=
+ * TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS): -65 .. -72, below the per-CU caps.  See tide_rs_bf16_to_fp32. */
+#define TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS 8
+#define TIDE_RS_CU_EXCLUSIVE(W) (-(TIDE_RS_MAX_WGS_PER_CU + (W)))
+
 typedef enum tide_status {
   TIDE_OK = 0,
   TIDE_ERR_INVALID = 1,     /* bad argument: null pointer, bad size, misalignment, overlap */
@@ -150,6 +155,14 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              the contributors in blocks of 8.
  *              -N (1 <= N <= TIDE_RS_MAX_WGS_PER_CU): as 0, with at most N per CU for any C (an N
  *              at or above the hardware's own limit leaves that limit).
+ *              TIDE_RS_CU_EXCLUSIVE(W) (1 <= W <= 8): one launch of workgroups of 128*W threads, each
+ *              taking W work items and the largest local memory a workgroup may request (a whole
+ *              CU's on MI355X), so every CU holds one RS workgroup -- W items in flight -- and is
+ *              empty whenever it exits: a concurrent kernel waiting for whole CUs (a one-wave
+ *              GEMM) gets each CU within one RS workgroup lifetime, while the RS runs as a single
+ *              launch ([Endgame] Figure 3: communication workgroups that stay resident push the
+ *              GEMM's into a second wave).  Compiled for C = 1, 2, 4 and 8; other C take the
+ *              runtime-C form.
  *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of
  *              128 threads); each processes a bounded number of work items (4 by default, 80 KiB
  *              of traffic at C = 8) and exits, and the call issues as many launches as needed, so
@@ -164,7 +177,7 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  * 16-byte-aligned grads and shards take the vector path; any other legal alignment takes a
  * slower element path with identical results.
  * Errors: TIDE_ERR_INVALID (null layout/arrays, C < 1, C*P > 2^24,
- * cu_budget < -TIDE_RS_MAX_WGS_PER_CU, null or
+ * cu_budget < TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS), null or
  * misaligned pointer, any shard overlapping another shard or any gradient), TIDE_ERR_NOMEM,
  * TIDE_ERR_HIP.
  */
@@ -268,8 +281,9 @@ void tide_call_destroy(tide_call* call);
 /* Launch shape of RS calls with C contributors at `cu_budget` on the current device: threads per
  * workgroup, outputs per full work item, and the local memory (static + dynamic, bytes) each
  * workgroup requests -- a CU holds as many RS workgroups as fit in its local memory, so for
- * cu_budget <= 0 this sets the per-CU cap.  Errors: TIDE_ERR_INVALID (C < 1,
- * cu_budget < -TIDE_RS_MAX_WGS_PER_CU or a NULL pointer), TIDE_ERR_HIP. */
+ * cu_budget <= 0 this sets the per-CU cap (for TIDE_RS_CU_EXCLUSIVE(W): 128*W threads, one workgroup
+ * per CU).  Errors: TIDE_ERR_INVALID (C < 1,
+ * cu_budget < TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) or a NULL pointer), TIDE_ERR_HIP. */
 tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads, int32_t* item_outputs,
                                  int32_t* lds_bytes);
 

@@ -29,6 +29,14 @@ int launch_fill_zero(const AgChunk*, int64_t, void*, void*) {
   std::fprintf(stderr, "launch_fill_zero reached in a host-only check\n");
   std::abort();
 }
+int launch_rs_cu(const RsChunk*, int64_t, int, const void* const*, int32_t, int32_t, int64_t, bool, bool, int, void*) {
+  std::fprintf(stderr, "launch_rs_cu reached in a host-only check\n");
+  std::abort();
+}
+int rs_cu_static_lds(int*) {
+  std::fprintf(stderr, "rs_cu_static_lds reached in a host-only check\n");
+  std::abort();
+}
 }  // namespace tide
 
 static int failures = 0;
@@ -127,7 +135,7 @@ int main() {
   tide_call* call = nullptr;
   CHECK(tide_rs_prepare(L, 1, g, sh, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
   CHECK(tide_rs_prepare(L, 0, g, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
-  CHECK(tide_rs_prepare(L, 1, g, sh2, -TIDE_RS_MAX_WGS_PER_CU - 1, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_rs_prepare(L, 1, g, sh2, TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) - 1, &call) == TIDE_ERR_INVALID && call == nullptr);
   CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, -1, &call) == TIDE_ERR_INVALID);
   CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, 0, &call) == TIDE_ERR_INVALID);
   CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, 7, 0, &call) == TIDE_ERR_INVALID);
@@ -139,7 +147,7 @@ int main() {
   CHECK(tide_rs_launch_shape(8, 0, nullptr, nullptr, nullptr) == TIDE_ERR_INVALID);
   int32_t th = 0, it = 0, lds = 0;
   CHECK(tide_rs_launch_shape(0, 0, &th, &it, &lds) == TIDE_ERR_INVALID);
-  CHECK(tide_rs_launch_shape(8, -TIDE_RS_MAX_WGS_PER_CU - 1, &th, &it, &lds) == TIDE_ERR_INVALID);
+  CHECK(tide_rs_launch_shape(8, TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) - 1, &th, &it, &lds) == TIDE_ERR_INVALID);
   tide_call_destroy(nullptr);
   CHECK(tide_last_hip_error() == 0);
   tide_layout_destroy(L);

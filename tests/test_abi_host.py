@@ -270,7 +270,7 @@ def test_rs_rejects_bad_arguments_before_any_hip_call():
         assert lib.tide_rs_bf16_to_fp32(None, 4, _vp_array(g), _vp_array(s), 0, None) == INV
         assert lib.tide_rs_bf16_to_fp32(L.handle, 4, None, _vp_array(s), 0, None) == INV
         assert call(g, s, C=0) == INV
-        assert call(g, s, budget=-65) == INV           # beyond TIDE_RS_MAX_WGS_PER_CU
+        assert call(g, s, budget=-73) == INV           # below TIDE_RS_CU_EXCLUSIVE(8)
         g2 = list(g); g2[5] = None
         assert call(g2, s) == INV                     # null gradient of a non-empty parameter
         g3 = list(g); g3[1] += 1
@@ -325,7 +325,7 @@ def test_slot_entry_points_reject_bad_arguments_before_any_hip_call():
         shards = [(1 << 35) + r * (1 << 20) for r in range(L.R)]
         rs = lambda sl, sh, C=4, budget=0: lib.tide_rs_slots_bf16_to_fp32(L.handle, C, _vp_array(sl), _vp_array(sh), budget, None)
         assert rs(slots, shards, C=0) == INV
-        assert rs(slots, shards, budget=-65) == INV
+        assert rs(slots, shards, budget=-73) == INV
         ss = list(slots); ss[2] = None
         assert rs(ss, shards) == INV
         sh = list(shards); sh[0] = slots[1] + 8
@@ -415,3 +415,17 @@ def test_binding_rejects_tensors_on_mixed_devices():
             L.rs_bf16_to_fp32(grads, shards)
         with pytest.raises(ValueError, match="current device"):
             L.ag_place(FakeTensor(1), [FakeTensor(0) for _ in range(L.P)])
+
+
+def test_cu_exclusive_encoding_matches_the_header():
+    """TIDE_RS_CU_EXCLUSIVE(W) in include/tide.h and the binding's tide_rs_cu_exclusive agree, and sit
+    below the per-CU caps -1 .. -TIDE_RS_MAX_WGS_PER_CU."""
+    text = open(os.path.join(ROOT, "include", "tide.h")).read()
+    max_wgs = int(re.search(r"#define TIDE_RS_MAX_WGS_PER_CU (\d+)", text).group(1))
+    max_items = int(re.search(r"#define TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS (\d+)", text).group(1))
+    assert "#define TIDE_RS_CU_EXCLUSIVE(W) (-(TIDE_RS_MAX_WGS_PER_CU + (W)))" in text
+    assert (tide.TIDE_RS_MAX_WGS_PER_CU, tide.TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) == (max_wgs, max_items)
+    assert [tide.tide_rs_cu_exclusive(w) for w in range(1, max_items + 1)] == list(range(-max_wgs - 1, -max_wgs - max_items - 1, -1))
+    for bad in (0, max_items + 1):
+        with pytest.raises(ValueError):
+            tide.tide_rs_cu_exclusive(bad)

@@ -17,7 +17,7 @@ import oracle
 from oracle import geometry as ogeo
 from oracle import rs as ors
 from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError,
-                                      tide_rs_launch_shape)
+                                      tide_rs_cu_exclusive, tide_rs_launch_shape)
 from workloads import CONFIGS, normal_bf16_bits, normal_bf16_cuda
 from tests.test_gpu_parity import (GROUPS, POISON_BF16, POISON_F32, assert_rs_equal, dev_bf16, host_bits_bf16,
                                    host_bits_f32, poisoned_shards, say, _locate_many, _sample_positions)
@@ -115,7 +115,7 @@ def test_prepare_rejects_what_the_immediate_call_rejects(gpu_available):
         with pytest.raises(TideError, match="INVALID"):
             L.bind_rs(grads, bad)
         with pytest.raises(TideError, match="INVALID"):
-            L.bind_rs(grads, shards, cu_budget=-65)
+            L.bind_rs(grads, shards, cu_budget=-73)  # below the CU-exclusive modes
         stage = torch.zeros(R * S, dtype=torch.bfloat16, device="cuda")
         params = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
         with pytest.raises(TideError, match="INVALID"):
@@ -135,11 +135,13 @@ def _capture(calls, stream):
     return g
 
 
-@pytest.mark.parametrize("budget", [0, 3])
-def test_graph_replay_kernel_paths(gpu_available, budget):
-    """RS, AG placement (kernel), Slot-Reuse pack + RS from slots, captured once, replayed 4 times."""
+@pytest.mark.parametrize("budget,rs_budget", [(0, 0), (3, 3), (0, tide_rs_cu_exclusive(4))],
+                         ids=["unbounded", "bounded3", "rs_cu_exclusive4"])
+def test_graph_replay_kernel_paths(gpu_available, budget, rs_budget):
+    """RS, AG placement (kernel), Slot-Reuse pack + RS from slots, captured once, replayed 4 times
+    (the two RS calls at rs_budget, the placement and the packing at budget)."""
     shapes, R, C = GROUPS[1]
-    say(f"graph capture and replay, budget={budget}")
+    say(f"graph capture and replay, budget={budget} rs_budget={rs_budget}")
     geo, S = ogeo.group_geometry(shapes, R)
     with Layout(shapes, R) as L:
         grads = [[torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes] for _ in range(C)]
@@ -148,9 +150,9 @@ def test_graph_replay_kernel_paths(gpu_available, budget):
         shards2 = poisoned_shards(R, S)
         params = poisoned_params(shapes)
         slots = [poisoned_slot(R, S) for _ in range(C)]
-        calls = [L.bind_rs(grads, shards, cu_budget=budget), L.bind_ag(stage, params, cu_budget=budget)]
+        calls = [L.bind_rs(grads, shards, cu_budget=rs_budget), L.bind_ag(stage, params, cu_budget=budget)]
         calls += [L.bind_slot_pack(grads[c], slots[c], cu_budget=budget) for c in range(C)]
-        calls.append(L.bind_rs_slots(slots, shards2, cu_budget=budget))
+        calls.append(L.bind_rs_slots(slots, shards2, cu_budget=rs_budget))
         side = torch.cuda.Stream()
         torch.cuda.synchronize()
         graph = _capture(calls, side)
@@ -176,7 +178,7 @@ def test_graph_replay_kernel_paths(gpu_available, budget):
                 assert np.array_equal(host_bits_bf16(slots[c]), oracle.pack_slot(g[c], shapes, R)), f"replay {it}"
             # eager immediate calls on the same inputs agree with the replay
             eager = poisoned_shards(R, S)
-            L.rs_bf16_to_fp32(grads, eager, cu_budget=budget)
+            L.rs_bf16_to_fp32(grads, eager, cu_budget=rs_budget)
             torch.cuda.synchronize()
             assert np.array_equal(shards_bits(eager), shards_bits(shards))
         del graph
@@ -333,6 +335,53 @@ def test_rs_negative_budget_sets_the_cap_and_changes_speed_only(gpu_available):
                 call.close()
                 assert_rs_equal(shards_bits(shards), want)
         assert static < 160 * 1024 // 16
+
+
+def test_rs_cu_exclusive_modes(gpu_available):
+    """cu_budget TIDE_RS_CU_EXCLUSIVE(W): one launch of 128*W-thread workgroups that take the largest
+    local memory a workgroup may request (one per CU).  For every W, the compiled forms (C = 8, 4)
+    and the runtime-C form (C = 6, 18), aligned and misaligned bases, immediate and prepared calls,
+    and Slot-Reuse's source addressing, the shards equal the oracle's bit for bit."""
+    lds_per_cu = 160 * 1024
+    groups = [(GROUPS[1], 0), (([(4096, 64), (129, 7), (3,)], 8, 4), 1), (([(1000, 24), (5,), (96, 64)], 8, 6), 3),
+              (([(300, 70), (17,), (2048, 3)], 4, 18), 0)]
+    for (shapes, R, C), pad in groups:
+        geo, S = ogeo.group_geometry(shapes, R)
+        g = [[normal_bf16_bits(s, 1.0, 190, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+        want = oracle.reduce_scatter(g, shapes, R)
+        grads = [[dev_bf16(x, pad) for x in row] for row in g]
+        with Layout(shapes, R) as L:
+            slots = [poisoned_slot(R, S) for _ in range(C)]
+            for c in range(C):
+                L.slot_pack(grads[c], slots[c])
+            for w in range(1, 9):
+                budget = tide_rs_cu_exclusive(w)
+                shape = tide_rs_launch_shape(C, budget)
+                say(f"RS CU-exclusive C={C} W={w} pad={pad}: {shape}")
+                assert shape["threads"] == 128 * w and shape["item_outputs"] == 1024
+                assert lds_per_cu // 2 < shape["lds_bytes"] <= lds_per_cu, shape  # one workgroup per CU
+                shards = poisoned_shards(R, S, pad)
+                L.rs_bf16_to_fp32(grads, shards, cu_budget=budget)
+                torch.cuda.synchronize()
+                assert_rs_equal(shards_bits(shards), want)
+                if w in (1, 4, 8):
+                    shards = poisoned_shards(R, S, pad)
+                    call = L.bind_rs(grads, shards, cu_budget=budget)
+                    call.launch()
+                    torch.cuda.synchronize()
+                    call.close()
+                    assert_rs_equal(shards_bits(shards), want)
+                    shards = poisoned_shards(R, S)
+                    L.rs_slots_bf16_to_fp32(slots, shards, cu_budget=budget)
+                    torch.cuda.synchronize()
+                    assert_rs_equal(shards_bits(shards), want)
+    with Layout(*GROUPS[0][:2]) as L:
+        shards = poisoned_shards(GROUPS[0][1], L.S)
+        grads = [[torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in GROUPS[0][0]] for _ in range(4)]
+        with pytest.raises(TideError, match="INVALID"):
+            L.rs_bf16_to_fp32(grads, shards, cu_budget=tide_rs_cu_exclusive(8) - 1)
+    with pytest.raises(ValueError):
+        tide_rs_cu_exclusive(9)
 
 
 def test_destroy_with_work_in_flight(gpu_available):
