@@ -15,6 +15,7 @@ from .tide import (  # noqa: F401
     library_path,
     load_library,
     BoundCall,
+    tide_ag_cu_exclusive,
     tide_ag_place,
     tide_ag_prepare,
     tide_call_destroy,

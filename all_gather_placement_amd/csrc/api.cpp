@@ -21,7 +21,9 @@ namespace {
 
 // Smallest RS cu_budget: the per-CU caps -1 .. -TIDE_RS_MAX_WGS_PER_CU, then the CU-exclusive modes.
 constexpr int32_t kRsMinBudget = TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS);
-static_assert(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS == kRsCuMaxItems, "header and kernel agree on the widest workgroup");
+static_assert(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS == kRsCuMaxItems && TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS == kAgCuMaxItems,
+              "header and kernels agree on the widest workgroup");
+static_assert(TIDE_AG_CU_EXCLUSIVE(3) == TIDE_RS_CU_EXCLUSIVE(3), "one encoding for both collectives");
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -143,8 +145,10 @@ tide_status validate_rs_slots(const tide_layout* L, int32_t C, const void* const
 // slot) share one layout of arguments: a stage/slot of R*S bf16 and P per-parameter tensors.
 tide_status validate_ag(const tide_layout* L, const void* stage, void* const* params, int32_t mode,
                         int32_t cu_budget, bool pack, Request* q) {
-  if (L == nullptr || params == nullptr || cu_budget < 0) return TIDE_ERR_INVALID;
+  if (L == nullptr || params == nullptr) return TIDE_ERR_INVALID;
   if (!pack && mode != TIDE_AG_KERNEL && mode != TIDE_AG_SDMA && mode != TIDE_AG_COPY2D) return TIDE_ERR_INVALID;
+  // negative budgets: only the CU-exclusive launch of the kernel (placement or packing)
+  if (cu_budget < 0 && (cu_exclusive_items(cu_budget) == 0 || (!pack && mode != TIDE_AG_KERNEL))) return TIDE_ERR_INVALID;
   const int32_t P = L->P, R = L->R;
   const int64_t stage_n = int64_t(R) * L->S;
   if (stage_n > 0 && (stage == nullptr || !aligned(stage, 2))) return TIDE_ERR_INVALID;
@@ -277,7 +281,7 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
   if (q.kind == kRs || q.kind == kRsSlots) {
     const int64_t count = int64_t(L->rs_chunks.size());
     const bool flat = q.kind == kRsSlots;
-    if (const int w = rs_cu_items(q.cu_budget)) {
+    if (const int w = cu_exclusive_items(q.cu_budget)) {
       // one launch of CU-exclusive workgroups of w items (the table's order: items are rank-major)
       return launch_rs_cu(st->rs, count, w, tbl, flat ? 1 : L->P, q.C, L->S, flat, q.vec, rs_cu_launch_lds(*st), hs);
     }
@@ -294,6 +298,13 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
     return e;
   }
   const int64_t count = int64_t(L->ag_chunks.size());
+  if (const int w = cu_exclusive_items(q.cu_budget)) {
+    if (count > 0)
+      e = launch_ag_cu(st->ag, count, w, q.stage, tbl, q.kind == kPack, q.vec, ag_cu_launch_lds(*st), hs);
+    if (e == hipSuccess && q.kind == kPack)
+      e = launch_fill_zero(st->slot_pad, int64_t(L->slot_pad_items.size()), q.stage, hs);
+    return e;
+  }
   const int64_t ag_wgs = int64_t(q.cu_budget) * kBudgetThreads / kAgThreads;
   const Plan plan = plan_for(count, q.cu_budget, ag_wgs, kAgBoundedItems);
   // Few workgroups per CU (small budgets): each loads two items at a time.
@@ -534,7 +545,7 @@ tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads,
   if (e == hipSuccess) e = tide::rs_device_info(dev, &st);
   if (e != hipSuccess) return tide::hip_fail(e);
   *item_outputs = int32_t(tide::kRsChunk);
-  if (const int w = tide::rs_cu_items(cu_budget)) {
+  if (const int w = tide::cu_exclusive_items(cu_budget)) {
     *threads = tide::kThreads * w;
     *lds_bytes = st.rs_static_lds_cu + tide::rs_cu_launch_lds(st);
     return TIDE_OK;

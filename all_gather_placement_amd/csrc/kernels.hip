@@ -585,6 +585,51 @@ __global__ __launch_bounds__(kAgThreads) void ag_kernel(const AgChunk* __restric
   }
 }
 
+// CU-exclusive AG kernel (placement, or Slot-Reuse packing with PACK): one launch over all items in
+// workgroups of W = blockDim.x / 128 groups of 128 threads (W <= kAgCuMaxItems); group g of
+// workgroup b copies item b*W + g.  Like the CU-exclusive RS, every workgroup is given the largest
+// local memory one may request, so a CU holds one and is empty whenever it exits (a concurrent
+// one-wave GEMM takes it then).  A full item's two 16-byte vectors per lane are both loaded before
+// either is stored; other items take the same head / vector / tail path as ag_kernel.  No barrier.
+template <bool VEC, bool PACK>
+__global__ __launch_bounds__(kAgThreads * kAgCuMaxItems) void ag_cu_kernel(const AgChunk* __restrict__ chunks,
+                                                                          int64_t count,
+                                                                          unsigned short* __restrict__ stage,
+                                                                          unsigned short* const* __restrict__ params) {
+  const int W = static_cast<int>(blockDim.x) / kAgThreads;
+  const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kAgThreads);
+  const int tid = static_cast<int>(threadIdx.x) % kAgThreads;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * W + grp;
+  if (item >= count) return;
+  const AgChunk ch = chunks[item];
+  const unsigned short* src = PACK ? params[ch.p] + ch.dst : stage + ch.src;
+  unsigned short* dst = PACK ? stage + ch.src : params[ch.p] + ch.dst;
+  const int64_t src_off = PACK ? ch.dst : ch.src;
+  const int n = ch.n;
+  if (VEC && n == kAgChunk && (ch.src & 7) == 0 && (ch.dst & 7) == 0) {
+    constexpr int NV = kAgChunk / 8 / kAgThreads;  // vectors per lane of a full item
+    u32x4 x[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) x[k] = load_hbm(at_bytes<u32x4>(src, 16u * (tid + k * kAgThreads)));
+#pragma unroll
+    for (int k = 0; k < NV; ++k) store_hbm(at_bytes<u32x4>(dst, 16u * (tid + k * kAgThreads)), x[k]);
+  } else if (VEC && ((ch.src - ch.dst) & 7) == 0) {
+    const int head = min(n, static_cast<int>((-src_off) & 7));
+    const int nb = (n - head) >> 3;
+    const int tail = (n - head) & 7;
+    if (tid < head) store_hbm(dst + tid, load_hbm(src + tid));
+    const u32x4* sv = reinterpret_cast<const u32x4*>(src + head);
+    u32x4* dv = reinterpret_cast<u32x4*>(dst + head);
+    for (int v = tid; v < nb; v += kAgThreads) store_hbm(at_bytes<u32x4>(dv, 16u * v), load_hbm(at_bytes<u32x4>(sv, 16u * v)));
+    if (tid < tail) {
+      const int k = head + 8 * nb + tid;
+      store_hbm(dst + k, load_hbm(src + k));
+    }
+  } else {
+    for (int i = tid; i < n; i += kAgThreads) store_hbm(dst + i, load_hbm(src + i));
+  }
+}
+
 // Zero-fill kernel for the padding of a packed slot: items (src = slot element offset, n).
 __global__ __launch_bounds__(kAgThreads) void fill_zero_kernel(const AgChunk* __restrict__ items, int64_t count,
                                                                 unsigned short* __restrict__ slot) {
@@ -667,6 +712,29 @@ int launch_rs_cu(const RsChunk* chunks, int64_t count, int items_per_wg, const v
   const int threads = kThreads * items_per_wg;
   if (flat) return launch_rs_cu_c<true>(chunks, count, int(grid), threads, ptrs, 1, C, S, vec, dyn_lds, s);
   return launch_rs_cu_c<false>(chunks, count, int(grid), threads, ptrs, P, C, S, vec, dyn_lds, s);
+}
+
+int launch_ag_cu(const AgChunk* chunks, int64_t count, int items_per_wg, void* stage, const void* const* dev_params,
+                 bool pack, bool vec, int dyn_lds, void* hip_stream) {
+  if (items_per_wg < 1 || items_per_wg > kAgCuMaxItems || count < 1) return hipErrorInvalidValue;
+  const int64_t grid = (count + items_per_wg - 1) / items_per_wg;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  unsigned short* st = static_cast<unsigned short*>(stage);
+  unsigned short* const* pp = reinterpret_cast<unsigned short* const*>(const_cast<void* const*>(dev_params));
+  const dim3 g(static_cast<unsigned>(grid)), b(kAgThreads * items_per_wg);
+  if (pack) {
+    if (vec)
+      hipLaunchKernelGGL((ag_cu_kernel<true, true>), g, b, dyn_lds, s, chunks, count, st, pp);
+    else
+      hipLaunchKernelGGL((ag_cu_kernel<false, true>), g, b, dyn_lds, s, chunks, count, st, pp);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((ag_cu_kernel<true, false>), g, b, dyn_lds, s, chunks, count, st, pp);
+    else
+      hipLaunchKernelGGL((ag_cu_kernel<false, false>), g, b, dyn_lds, s, chunks, count, st, pp);
+  }
+  return hipGetLastError();
 }
 
 int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg,

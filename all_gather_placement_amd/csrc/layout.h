@@ -56,8 +56,9 @@ struct DeviceState {
   int rs_static_lds_cu = 0; // static local memory of the CU-exclusive RS kernel
 };
 
-// cu_budget values TIDE_RS_CU_EXCLUSIVE(W): the number of items per CU-exclusive workgroup, else 0.
-inline int rs_cu_items(int cu_budget) {
+// cu_budget values TIDE_RS_CU_EXCLUSIVE(W) (TIDE_AG_CU_EXCLUSIVE(W) for the placement kernel and the
+// packing): the number of items per CU-exclusive workgroup, else 0.
+inline int cu_exclusive_items(int cu_budget) {
   const int w = -cu_budget - TIDE_RS_MAX_WGS_PER_CU;
   return w >= 1 && w <= TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS ? w : 0;
 }
@@ -69,13 +70,16 @@ inline int rs_cu_launch_lds(const DeviceState& st) {
   const int dyn = cap - st.rs_static_lds_cu;
   return dyn > 0 ? dyn : 0;
 }
+inline int ag_cu_launch_lds(const DeviceState& st) {  // the AG kernels have no static local memory
+  return st.lds_per_wg < st.lds_per_cu ? st.lds_per_wg : st.lds_per_cu;
+}
 
 // Dynamic local memory of an RS launch with C contributors at `cu_budget` on this device: 0 caps
 // the RS workgroups per CU at rs_wgs_per_cu(C), -N at N; bounded launches (> 0) add none.  Needs
 // lds_per_cu, lds_per_wg and the static sizes filled in (rs_device_info).
 inline int rs_launch_lds(const DeviceState& st, int C, int cu_budget) {
   if (cu_budget > 0) return 0;
-  if (rs_cu_items(cu_budget) > 0) return rs_cu_launch_lds(st);
+  if (cu_exclusive_items(cu_budget) > 0) return rs_cu_launch_lds(st);
   const int wgs = cu_budget < 0 ? -cu_budget : rs_wgs_per_cu(C);
   const int static_lds = C <= kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt;
   const int dyn = rs_dynamic_lds(st.lds_per_cu, static_lds, wgs);

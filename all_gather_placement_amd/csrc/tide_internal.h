@@ -154,6 +154,7 @@ constexpr int kRsBoundedItems = TIDE_RS_BOUNDED_ITEMS;
 // 4: 6.25 TB/s, +4.4%; 6: 6.27, +7.9%; 8: 6.36, +10.5%; bounded budget 512 (same resident threads
 // as W = 4): 5.33 TB/s, -0.2%; W = 4 with only its own local memory (several per CU): +261%.
 constexpr int kRsCuMaxItems = 8;
+constexpr int kAgCuMaxItems = 8;  // AG placement / Slot-Reuse packing in the same CU-exclusive form
 static_assert(kThreads * kRsCuMaxItems <= 1024, "a CU-exclusive workgroup fits the workgroup size limit");
 constexpr int kAgBoundedItems = TIDE_AG_BOUNDED_ITEMS;
 
@@ -199,6 +200,10 @@ int rs_lds_info(int device, int* lds_per_cu, int* static_lds_ct, int* static_lds
 int launch_rs_cu(const RsChunk* chunks, int64_t count, int items_per_wg, const void* const* dev_ptrs, int32_t P,
                  int32_t C, int64_t S, bool flat, bool vec, int dyn_lds, void* hip_stream);
 int rs_cu_static_lds(int* static_lds);
+// launch_ag_cu: the CU-exclusive AG placement (pack = false) or packing (pack = true) over all
+// `count` items in one launch, items_per_wg (1 .. kAgCuMaxItems) items per workgroup.
+int launch_ag_cu(const AgChunk* chunks, int64_t count, int items_per_wg, void* stage, const void* const* dev_params,
+                 bool pack, bool vec, int dyn_lds, void* hip_stream);
 inline int rs_dynamic_lds(int lds_per_cu, int static_lds, int wgs_per_cu) {
   if (wgs_per_cu <= 0 || lds_per_cu <= 0) return 0;
   // rounded down to 512 bytes per workgroup, so wgs_per_cu of them fit in a CU (and, for counts up

@@ -37,6 +37,12 @@ def tide_rs_cu_exclusive(items_per_workgroup: int) -> int:
     return -(TIDE_RS_MAX_WGS_PER_CU + w)
 
 
+def tide_ag_cu_exclusive(items_per_workgroup: int) -> int:
+    """AG cu_budget of the CU-exclusive placement / packing kernel (include/tide.h TIDE_AG_CU_EXCLUSIVE(W)),
+    the same encoding as the RS's."""
+    return tide_rs_cu_exclusive(items_per_workgroup)
+
+
 _lib = None
 
 

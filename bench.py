@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--rs-cu-exclusive", type=int, default=0,
                     help="the RS as one launch of CU-exclusive workgroups of W items (RS cu_budget "
                          "TIDE_RS_CU_EXCLUSIVE(W) = -(64 + W), W = 1..8)")
+    ap.add_argument("--ag-cu-exclusive", type=int, default=0,
+                    help="the AG placement kernel as one launch of CU-exclusive workgroups of W items (AG cu_budget "
+                         "TIDE_AG_CU_EXCLUSIVE(W) = -(64 + W), W = 1..8)")
     ap.add_argument("--ag-mode", choices=["kernel", "sdma", "copy2d"], default="kernel")
     ap.add_argument("--contributors", type=int, default=0,
                     help="override the workload's contributor count C (default: the workload's own)")
@@ -81,10 +84,10 @@ def parse():
     return ap.parse_args()
 
 
-def rs_mode(cu_budget: int) -> str:
-    """How an RS call at `cu_budget` launches (include/tide.h, tide_rs_bf16_to_fp32)."""
+def rs_mode(cu_budget: int, kind: str = "rs") -> str:
+    """How an RS (or, kind "ag", a placement-kernel) call at `cu_budget` launches (include/tide.h)."""
     if cu_budget == 0:
-        return "one launch, per-CU cap by C"
+        return "one launch, per-CU cap by C" if kind == "rs" else "one launch, one workgroup per item"
     if cu_budget > 0:
         return f"bounded launches, {256 * cu_budget} threads"
     if cu_budget >= -64:
@@ -352,7 +355,8 @@ def interference(args, log):
     log(f"victim GEMM {M}x{N}x{K} bf16 alone: {alone * 1e3:.1f} us (median of {len(alone_all)})")
     rows = []
     cases = [("rs", int(x)) for x in args.budgets.split(",")]
-    cases += [("ag_kernel", 0), ("ag_kernel", 512), ("ag_kernel", 768), ("ag_copy2d", 0), ("ag_sdma", 0)]
+    cases += [("ag_kernel", 0), ("ag_kernel", 512), ("ag_kernel", 768), ("ag_kernel", -66), ("ag_kernel", -68),
+              ("ag_kernel", -70), ("ag_copy2d", 0), ("ag_sdma", 0)]
     for kind, budget in cases:
         t_alone = comm_alone(kind, budget)
         conc, outlast = [], 0
@@ -365,7 +369,7 @@ def interference(args, log):
         med = statistics.median(conc) if conc else None
         row = {
             "comm": kind, "cu_budget": budget,
-            "mode": rs_mode(budget) if kind == "rs" else None,
+            "mode": rs_mode(budget, "rs" if kind == "rs" else "ag") if kind in ("rs", "ag_kernel") else None,
             "comm_ms": round(t_alone, 4),
             "comm_gbps": round(nbytes / (t_alone * 1e-3) / 1e9, 1),
             "gemm_alone_us": round(alone * 1e3, 2),
@@ -889,6 +893,10 @@ def main():
         print("--rs-wgs-per-cu takes 1..64 and applies to the unbounded RS only (--cu-budget 0)",
               file=sys.stderr, flush=True)
         sys.exit(2)
+    if args.ag_cu_exclusive and (args.cu_budget or args.ag_mode != "kernel" or not 0 < args.ag_cu_exclusive <= 8):
+        print("--ag-cu-exclusive takes 1..8, applies to the kernel engine and replaces --cu-budget for the AG",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
     if args.rs_cu_exclusive and (args.cu_budget or args.rs_wgs_per_cu or not 0 < args.rs_cu_exclusive <= 8):
         print("--rs-cu-exclusive takes 1..8 and replaces --cu-budget and --rs-wgs-per-cu for the RS",
               file=sys.stderr, flush=True)
@@ -968,7 +976,8 @@ def main():
     if args.rs_cu_exclusive:
         rs_budget = -(64 + args.rs_cu_exclusive)
     rs_call = L.bind_rs(grads, shards, cu_budget=rs_budget)
-    ag_call = L.bind_ag(stage, params, mode=ag_mode, cu_budget=args.cu_budget)
+    ag_budget = -(64 + args.ag_cu_exclusive) if args.ag_cu_exclusive else args.cu_budget
+    ag_call = L.bind_ag(stage, params, mode=ag_mode, cu_budget=ag_budget)
 
     def step(ev_rs=None, ev_ag=None):
         if ev_rs:
@@ -1118,7 +1127,7 @@ def main():
             "workload": f"{cfg.name} RS+AG step (R={cfg.R}, C={cfg.C}, P={cfg.P})",
             "R": cfg.R, "C": cfg.C, "P": cfg.P, "numel": numel, "S": S,
             "cu_budget": args.cu_budget, "rs_cu_budget": rs_budget, "rs_mode": rs_mode(rs_budget),
-            "ag_mode": args.ag_mode,
+            "ag_mode": args.ag_mode, "ag_cu_budget": ag_budget,
             "rs_bytes": rs_bytes, "ag_bytes": ag_bytes, "parallelism": "none (1 GPU, node-local level)",
         },
         "rs_gbps": round(rs_gbps, 2),

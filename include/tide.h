@@ -56,6 +56,8 @@ typedef struct tide_layout tide_layout;
  * TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS): -65 .. -72, below the per-CU caps.  See tide_rs_bf16_to_fp32. */
 #define TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS 8
 #define TIDE_RS_CU_EXCLUSIVE(W) (-(TIDE_RS_MAX_WGS_PER_CU + (W)))
+/* The same launch form for the placement kernel and Slot-Reuse packing (tide_ag_place, tide_slot_pack). */
+#define TIDE_AG_CU_EXCLUSIVE(W) TIDE_RS_CU_EXCLUSIVE(W)
 
 typedef enum tide_status {
   TIDE_OK = 0,
@@ -195,13 +197,17 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
  *              are 128 threads, so B admits 2B of them, each copying 8 work items -- 64 KiB of
  *              traffic -- before it exits; with at most 4 of them per CU, two items are loaded
  *              before either is stored).  0: one workgroup per work item, no cap.
+ *              TIDE_AG_CU_EXCLUSIVE(W) (1 <= W <= 8, TIDE_AG_KERNEL only): one launch of workgroups of
+ *              128*W threads, each copying W work items and holding a whole CU's local memory, as the
+ *              RS's TIDE_RS_CU_EXCLUSIVE(W): a concurrent one-wave GEMM gets each CU back within one
+ *              workgroup lifetime.
  * Result: params[p][r*m_p*L_p + k] = stage[r*S + o_p + k] for every r and k < v*L_p, copied as
  * bits; stage padding is never read into a parameter; every parameter element is written once.
  * All pointers must be 2-byte aligned; 16-byte alignment selects the vector path.
  * TIDE_AG_SDMA work is ordered after the caller's earlier work on `stream`, and later work on
  * `stream` waits for it (event fork/join with the internal copy streams).
- * Errors: TIDE_ERR_INVALID (null/misaligned pointer, bad mode, cu_budget < 0, a parameter
- * overlapping the stage or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a copy kind), TIDE_ERR_NOMEM,
+ * Errors: TIDE_ERR_INVALID (null/misaligned pointer, bad mode, a negative cu_budget other than
+ * TIDE_AG_CU_EXCLUSIVE(1..8) with TIDE_AG_KERNEL, a parameter overlapping the stage or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a copy kind), TIDE_ERR_NOMEM,
  * TIDE_ERR_HIP.
  */
 tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params,

@@ -33,6 +33,10 @@ int launch_rs_cu(const RsChunk*, int64_t, int, const void* const*, int32_t, int3
   std::fprintf(stderr, "launch_rs_cu reached in a host-only check\n");
   std::abort();
 }
+int launch_ag_cu(const AgChunk*, int64_t, int, void*, const void* const*, bool, bool, int, void*) {
+  std::fprintf(stderr, "launch_ag_cu reached in a host-only check\n");
+  std::abort();
+}
 int rs_cu_static_lds(int*) {
   std::fprintf(stderr, "rs_cu_static_lds reached in a host-only check\n");
   std::abort();
@@ -137,6 +141,10 @@ int main() {
   CHECK(tide_rs_prepare(L, 0, g, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
   CHECK(tide_rs_prepare(L, 1, g, sh2, TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) - 1, &call) == TIDE_ERR_INVALID && call == nullptr);
   CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, -1, &call) == TIDE_ERR_INVALID);
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_SDMA, TIDE_AG_CU_EXCLUSIVE(4), &call) ==
+        TIDE_ERR_INVALID);
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, TIDE_AG_CU_EXCLUSIVE(9), &call) ==
+        TIDE_ERR_INVALID);
   CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, 0, &call) == TIDE_ERR_INVALID);
   CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, 7, 0, &call) == TIDE_ERR_INVALID);
   CHECK(tide_slot_pack_prepare(L, const_cast<const void* const*>(pp), reinterpret_cast<void*>(base), 0, &call) ==

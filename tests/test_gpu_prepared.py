@@ -17,7 +17,7 @@ import oracle
 from oracle import geometry as ogeo
 from oracle import rs as ors
 from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError,
-                                      tide_rs_cu_exclusive, tide_rs_launch_shape)
+                                      tide_ag_cu_exclusive, tide_rs_cu_exclusive, tide_rs_launch_shape)
 from workloads import CONFIGS, normal_bf16_bits, normal_bf16_cuda
 from tests.test_gpu_parity import (GROUPS, POISON_BF16, POISON_F32, assert_rs_equal, dev_bf16, host_bits_bf16,
                                    host_bits_f32, poisoned_shards, say, _locate_many, _sample_positions)
@@ -135,8 +135,8 @@ def _capture(calls, stream):
     return g
 
 
-@pytest.mark.parametrize("budget,rs_budget", [(0, 0), (3, 3), (0, tide_rs_cu_exclusive(4))],
-                         ids=["unbounded", "bounded3", "rs_cu_exclusive4"])
+@pytest.mark.parametrize("budget,rs_budget", [(0, 0), (3, 3), (tide_ag_cu_exclusive(4), tide_rs_cu_exclusive(4))],
+                         ids=["unbounded", "bounded3", "cu_exclusive4"])
 def test_graph_replay_kernel_paths(gpu_available, budget, rs_budget):
     """RS, AG placement (kernel), Slot-Reuse pack + RS from slots, captured once, replayed 4 times
     (the two RS calls at rs_budget, the placement and the packing at budget)."""
@@ -382,6 +382,46 @@ def test_rs_cu_exclusive_modes(gpu_available):
             L.rs_bf16_to_fp32(grads, shards, cu_budget=tide_rs_cu_exclusive(8) - 1)
     with pytest.raises(ValueError):
         tide_rs_cu_exclusive(9)
+
+
+def test_ag_cu_exclusive_modes(gpu_available):
+    """cu_budget TIDE_AG_CU_EXCLUSIVE(W) for the placement kernel and Slot-Reuse packing: for every W,
+    aligned and misaligned bases, immediate and prepared calls, the parameters and the packed slot equal
+    the oracle's bit for bit; the DMA engines and the runtime 2-D copy reject it."""
+    groups = [(GROUPS[1], 0), (GROUPS[6], 0), (([(1000, 24), (5,), (96, 64)], 8, 6), 3), (GROUPS[0], 1)]
+    for (shapes, R, C), pad in groups:
+        geo, S = ogeo.group_geometry(shapes, R)
+        st_bits = normal_bf16_bits((R * S,), 1.0, 195, 0)
+        want = oracle.all_gather_place(st_bits, shapes, R)
+        g = [normal_bf16_bits(s, 1.0, 196, 0, p) for p, s in enumerate(shapes)]
+        want_slot = oracle.pack_slot(g, shapes, R)
+        stage = dev_bf16(st_bits, pad)
+        grads = [dev_bf16(x, pad) for x in g]
+        with Layout(shapes, R) as L:
+            for w in range(1, 9):
+                budget = tide_ag_cu_exclusive(w)
+                say(f"AG CU-exclusive W={w} R={R} pad={pad}")
+                params = poisoned_params(shapes)
+                L.ag_place(stage, params, cu_budget=budget)
+                slot = poisoned_slot(R, S)
+                L.slot_pack(grads, slot, cu_budget=budget)
+                torch.cuda.synchronize()
+                for a, b in zip([host_bits_bf16(q) for q in params], want):
+                    assert np.array_equal(a, b), (w, pad)
+                assert np.array_equal(host_bits_bf16(slot), want_slot), (w, pad)
+                if w in (1, 4, 8):
+                    params = poisoned_params(shapes)
+                    call = L.bind_ag(stage, params, cu_budget=budget)
+                    call.launch()
+                    torch.cuda.synchronize()
+                    call.close()
+                    for a, b in zip([host_bits_bf16(q) for q in params], want):
+                        assert np.array_equal(a, b), (w, pad)
+            for mode in (TIDE_AG_SDMA, TIDE_AG_COPY2D):
+                with pytest.raises(TideError, match="INVALID"):
+                    L.ag_place(stage, poisoned_params(shapes), mode=mode, cu_budget=tide_ag_cu_exclusive(4))
+            with pytest.raises(TideError, match="INVALID"):
+                L.ag_place(stage, poisoned_params(shapes), cu_budget=-1)
 
 
 def test_destroy_with_work_in_flight(gpu_available):

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from oracle import geometry as ogeo
-from all_gather_placement_amd import Layout, tide_rs_cu_exclusive
+from all_gather_placement_amd import Layout, tide_ag_cu_exclusive, tide_rs_cu_exclusive
 from tests.test_gpu_parity import POISON_BF16, assert_rs_equal, dev_bf16, host_bits_bf16, host_bits_f32, poisoned_shards, say
 
 pytestmark = pytest.mark.gpu
@@ -62,10 +62,12 @@ def test_random_group_many_contributors(gpu_available, case):
 @pytest.mark.parametrize("case", range(16))
 def test_random_group_cu_exclusive(gpu_available, case):
     """The CU-exclusive RS (W = 1 .. 8 items per CU-wide workgroup) on random groups, C 1-12 and
-    13-40 in turn (compiled and runtime-C forms), misaligned bases in a third of them."""
+    13-40 in turn (compiled and runtime-C forms), misaligned bases in a third of them; the placement
+    and the packing in the same form in every other group."""
     rng = np.random.default_rng(7000 + case)
     shapes, R, C, budget = _random_group(rng, *((1, 13) if case % 2 == 0 else (13, 41)))
-    _check_group(rng, case, shapes, R, C, tide_rs_cu_exclusive(1 + case % 8), budget)
+    ag_budget = tide_ag_cu_exclusive(1 + (3 * case) % 8) if case % 4 < 2 else budget
+    _check_group(rng, case, shapes, R, C, tide_rs_cu_exclusive(1 + case % 8), ag_budget)
 
 
 def _check_group(rng, case, shapes, R, C, rs_budget, ag_budget):
