@@ -776,7 +776,7 @@ def overlap(args, log):
     rows = []
     budgets = [int(x) for x in args.budgets.split(",")] if kind in ("rs", "ag_kernel") else [0]
     if kind == "ag_kernel":
-        budgets = [b for b in budgets if b >= 0]  # per-CU caps (-N) are the RS's only
+        budgets = [b for b in budgets if b >= 0 or b <= -65]  # per-CU caps (-1 .. -64) are the RS's only
     for budget in budgets:
         call = bind(budget)
         t_rs = statistics.median(timed(lambda: call.launch(sB), sB) for _ in range(args.reps))  # the comm alone
