@@ -14,7 +14,8 @@ import torch
 
 from oracle import geometry as ogeo
 from oracle import rs as ors
-from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
+from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, tide_ag_cu_exclusive,
+                                      tide_rs_cu_exclusive)
 from workloads import normal_bf16_cuda
 from tests.test_gpu_parity import host_bits_bf16, host_bits_f32, poisoned_shards, say, _locate_many
 
@@ -89,16 +90,26 @@ def test_parameter_beyond_2_31_elements(gpu_available):
             lo, hi = r * g.m * g.L, (r * g.m + v) * g.L
             assert torch.equal(seg[: v * g.L].view(torch.int32), acc[lo:hi].view(torch.int32)), r
             assert bool((seg[v * g.L:].view(torch.int32) == 0).all()), r
-        del acc, grads, shards
-        torch.cuda.empty_cache()
+        del acc
         say("large parameter: full comparison OK")
+
+        # the CU-exclusive launch (one launch, 64-bit item and element offsets) gives the same shards
+        say("large parameter: RS, CU-exclusive workgroups of 4 items")
+        shards_x = poisoned_shards(R, S)
+        L.rs_bf16_to_fp32(grads, shards_x, cu_budget=tide_rs_cu_exclusive(4))
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert torch.equal(shards_x[r].view(torch.int32), shards[r].view(torch.int32)), r
+        del grads, shards, shards_x
+        torch.cuda.empty_cache()
 
         stage = normal_bf16_cuda((R * S,), 1.0, 202, 0)
         ref = stage.view(R, S)[:, g.o: g.o + g.e].reshape(R * g.m, g.L)[: g.rows]
-        for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D):
-            say(f"large parameter: AG mode={mode}")
+        for mode, budget in ((TIDE_AG_KERNEL, 0), (TIDE_AG_SDMA, 0), (TIDE_AG_COPY2D, 0),
+                             (TIDE_AG_KERNEL, tide_ag_cu_exclusive(4))):
+            say(f"large parameter: AG mode={mode} cu_budget={budget}")
             param = torch.full(SHAPES[0], float("nan"), dtype=torch.bfloat16, device="cuda")
-            L.ag_place(stage, [param], mode=mode)
+            L.ag_place(stage, [param], mode=mode, cu_budget=budget)
             torch.cuda.synchronize()
             assert torch.equal(param.view(torch.int16), ref.view(torch.int16)), mode
             del param

@@ -12,7 +12,8 @@ import torch
 import oracle
 from oracle import geometry as ogeo
 from oracle import rs as ors
-from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError
+from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError,
+                                      tide_ag_cu_exclusive, tide_rs_cu_exclusive)
 from workloads import ORDERED, TINY, normal_bf16_bits, normal_bf16_cuda, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -399,14 +400,24 @@ def test_full_size_rs_and_ag(gpu_available, cfg):
                 assert bool((seg[v * g.L:].view(torch.int32) == 0).all())
             del acc
         say(f"full size {cfg.name}: full comparison OK")
+
+        # the CU-exclusive launch (the setting used beside compute) gives the same shards bit for bit
+        shards_x = poisoned_shards(cfg.R, S)
+        L.rs_bf16_to_fp32(grads, shards_x, cu_budget=tide_rs_cu_exclusive(4))
+        torch.cuda.synchronize()
+        for r in range(cfg.R):
+            assert torch.equal(shards_x[r].view(torch.int32), shards[r].view(torch.int32)), r
+        del shards_x
+        say(f"full size {cfg.name}: CU-exclusive RS equal")
         del grads
 
         # (3) AG placement, both engines, bit-exact against torch slicing; then the round trip
         stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
-        for mode in (TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D):
+        for mode, budget in ((TIDE_AG_KERNEL, 0), (TIDE_AG_SDMA, 0), (TIDE_AG_COPY2D, 0),
+                             (TIDE_AG_KERNEL, tide_ag_cu_exclusive(4))):
             params = [torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda") for s in cfg.shapes]
-            say(f"full size {cfg.name}: AG mode={mode}")
-            L.ag_place(stage, params, mode=mode)
+            say(f"full size {cfg.name}: AG mode={mode} cu_budget={budget}")
+            L.ag_place(stage, params, mode=mode, cu_budget=budget)
             torch.cuda.synchronize()
             st2 = stage.view(cfg.R, S)
             for p, g in enumerate(geo):
@@ -422,7 +433,7 @@ def test_full_size_rs_and_ag(gpu_available, cfg):
                 sb = host_bits_bf16(stage[torch.from_numpy(sidx).cuda()])
                 pb = host_bits_bf16(params[p].reshape(-1)[torch.from_numpy(k).cuda()])
                 assert np.array_equal(sb, pb)
-            if mode == TIDE_AG_KERNEL:
+            if mode == TIDE_AG_KERNEL and budget == 0:
                 L.rs_bf16_to_fp32([params], shards)
                 torch.cuda.synchronize()
                 for r in range(cfg.R):
