@@ -63,6 +63,8 @@ def parse():
                     help="instead of the step benchmark: slowdown of a concurrent one-wave bf16 GEMM per cu_budget")
     ap.add_argument("--budgets", default="0,-1,-2,-4,-65,-66,-68,-70,-72,8,16,32,64,128,256,512,768,1024,1536,2048")
     ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
+    ap.add_argument("--probe-budgets", default="none,0,16,64,256,512,768,1024,2048",
+                    help="--probes: RS cu_budgets of the occupancy-probe rows (none = no RS)")
     ap.add_argument("--cu-masks", default="16,32,64,128",
                     help="--interference: also the RS confined to K CUs by a CU-masked stream, and the GEMM on "
                          "the other CUs (comma list of K; empty: none)")
@@ -523,7 +525,8 @@ def probes(args, log):
     for _ in range(2):
         probe_once(None)
     table5 = []
-    for budget in [None, 0, 16, 64, 256, 512, 768, 1024, 2048]:
+    probe_budgets = [None if x.strip() == "none" else int(x) for x in args.probe_budgets.split(",") if x.strip()]
+    for budget in probe_budgets:
         res = [probe_once(budget) for _ in range(max(args.reps, 15))]
         disp = [r[0] for r in res]
         row = {"cu_budget": budget, "displaced_median": statistics.median(disp), "displaced_max": max(disp),
