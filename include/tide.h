@@ -164,7 +164,8 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              GEMM) gets each CU within one RS workgroup lifetime, while the RS runs as a single
  *              launch ([Endgame] Figure 3: communication workgroups that stay resident push the
  *              GEMM's into a second wave).  Compiled for C = 1, 2, 4 and 8; other C take the
- *              runtime-C form.
+ *              runtime-C form.  A CU keeps W items' loads (C*2 KiB each) in flight, so fewer
+ *              contributors want a wider W (on MI355X: W = 4 at C = 8 matches W = 8 at C = 4).
  *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of
  *              128 threads); each processes a bounded number of work items (4 by default, 80 KiB
  *              of traffic at C = 8) and exits, and the call issues as many launches as needed, so
