@@ -281,7 +281,7 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
   if (q.kind == kRs || q.kind == kRsSlots) {
     const int64_t count = int64_t(L->rs_chunks.size());
     const bool flat = q.kind == kRsSlots;
-    if (const int w = cu_exclusive_items(q.cu_budget)) {
+    if (const int w = rs_cu_launch_items(q.C, q.cu_budget)) {
       // one launch of CU-exclusive workgroups of w items (the table's order: items are rank-major)
       return launch_rs_cu(st->rs, count, w, tbl, flat ? 1 : L->P, q.C, L->S, flat, q.vec, rs_cu_launch_lds(*st), hs);
     }
@@ -545,7 +545,7 @@ tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads,
   if (e == hipSuccess) e = tide::rs_device_info(dev, &st);
   if (e != hipSuccess) return tide::hip_fail(e);
   *item_outputs = int32_t(tide::kRsChunk);
-  if (const int w = tide::cu_exclusive_items(cu_budget)) {
+  if (const int w = tide::rs_cu_launch_items(C, cu_budget)) {
     *threads = tide::kThreads * w;
     *lds_bytes = st.rs_static_lds_cu + tide::rs_cu_launch_lds(st);
     return TIDE_OK;

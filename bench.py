@@ -89,7 +89,8 @@ def parse():
 def rs_mode(cu_budget: int, kind: str = "rs") -> str:
     """How an RS (or, kind "ag", a placement-kernel) call at `cu_budget` launches (include/tide.h)."""
     if cu_budget == 0:
-        return "one launch, per-CU cap by C" if kind == "rs" else "one launch, one workgroup per item"
+        return "one launch, per-CU cap by C (C >= 12: CU-exclusive, 8 items)" if kind == "rs" else \
+            "one launch, one workgroup per item"
     if cu_budget > 0:
         return f"bounded launches, {256 * cu_budget} threads"
     if cu_budget >= -64:
@@ -1147,7 +1148,8 @@ def main():
                         "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"rs_cu_kernel<{cfg.C if cfg.C in (1, 2, 4, 8) else 0}, true, false>" if rs_budget < -64
+            "kernel": (f"rs_cu_kernel<{cfg.C if cfg.C in (1, 2, 4, 8) else 0}, true, false>"
+                       if rs_budget < -64 or (rs_budget == 0 and cfg.C >= 12)
                        else f"rs_kernel<{cfg.C if cfg.C <= 16 else 0}, true, false>"),
             "achieved": round(rs_gbps, 2),
             "peak": HBM_PEAK_GBPS,
