@@ -119,8 +119,9 @@ def test_tiny_ag_bit_exact(gpu_available, mode):
 
 
 GROUPS = [
-    # (shapes, R, C): ragged tails, rows < R, empty parameters, 1-D/3-D; C <= 16 runs a kernel
-    # compiled for that C (16 the largest), C > 16 the runtime-C kernel
+    # (shapes, R, C): ragged tails, rows < R, empty parameters, 1-D/3-D; at the bounded budget C <= 16
+    # runs a kernel compiled for that C (16 the largest), C > 16 the runtime-C kernel; at cu_budget 0,
+    # C >= 12 runs the CU-exclusive kernel's runtime-C form
     ([(7, 5), (16, 3), (1, 9)], 4, 4),
     ([(1000, 37), (4099,), (333, 65), (0, 4), (3, 2, 5)], 8, 8),
     ([(5, 1), (2,), (9, 3, 3)], 9, 3),
