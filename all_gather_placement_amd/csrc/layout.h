@@ -70,17 +70,21 @@ inline int rs_cu_launch_lds(const DeviceState& st) {
   const int dyn = cap - st.rs_static_lds_cu;
   return dyn > 0 ? dyn : 0;
 }
-// Default RS launch (cu_budget 0) from this many contributors on: the CU-exclusive form with the
-// widest workgroups (kRsCuMaxItems items) instead of single-item workgroups under a per-CU cap.
-// Measured on MI355X (Llama-3.1-8B shapes, R = 8, HIP-event means): C = 12 / 16 / 20 / 24 / 32 run
-// +2.3 / +5.2 / +1.9 / +1.8 / +1.6% faster so; C = 9 / 10 -3.1 / -1.4% and C <= 4 -4 to -26%
-// slower, so below 12 the per-CU cap stays (C = 8: +0.2 to +1.4%, within the run-to-run spread).
+// Default RS launch (cu_budget 0) in the CU-exclusive form with the widest workgroups (kRsCuMaxItems
+// items) instead of single-item workgroups under a per-CU cap, where it measured faster on MI355X
+// (Llama-3.1-8B shapes, R = 8, HIP-event means): C = 8, compiled (the four layer groups: +0.2 to
+// +1.5% over three interleaved sessions), and C >= 12 in its runtime-C form (C = 12 / 16 / 20 / 24 /
+// 32: +2.3 / +5.2 / +1.9 / +1.8 / +1.6%).  Elsewhere the cap stays: C = 9 / 10 -3.1 / -1.4% (a
+// compiled capped kernel against the runtime-C form), C <= 4 -4 to -26% (a CU then holds too few
+// bytes in flight).  The CU-exclusive default also leaves a concurrent one-wave GEMM its CUs
+// (+12-15% instead of waiting for the whole call).
 constexpr int kRsCuDefaultMinC = 12;
+inline bool rs_cu_default(int C) { return C == 8 || C >= kRsCuDefaultMinC; }
 
 // Items per CU-exclusive RS workgroup for C contributors at cu_budget, or 0 for the other forms.
 inline int rs_cu_launch_items(int C, int cu_budget) {
   if (const int w = cu_exclusive_items(cu_budget)) return w;
-  return cu_budget == 0 && C >= kRsCuDefaultMinC ? kRsCuMaxItems : 0;
+  return cu_budget == 0 && rs_cu_default(C) ? kRsCuMaxItems : 0;
 }
 
 inline int ag_cu_launch_lds(const DeviceState& st) {  // the AG kernels have no static local memory

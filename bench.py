@@ -89,7 +89,7 @@ def parse():
 def rs_mode(cu_budget: int, kind: str = "rs") -> str:
     """How an RS (or, kind "ag", a placement-kernel) call at `cu_budget` launches (include/tide.h)."""
     if cu_budget == 0:
-        return "one launch, per-CU cap by C (C >= 12: CU-exclusive, 8 items)" if kind == "rs" else \
+        return "one launch: C = 8 and C >= 12 CU-exclusive, 8 items; else per-CU cap by C" if kind == "rs" else \
             "one launch, one workgroup per item"
     if cu_budget > 0:
         return f"bounded launches, {256 * cu_budget} threads"
@@ -114,15 +114,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per RS launch from the committed counter summary, if it matches this kernel."""
+def read_traffic(workload: str, kernel: str):
+    """HBM bytes per RS launch from the committed counter summary, if it was taken on this kernel
+    (same kernel source and the same kernel, as the launch form depends on host code too)."""
     path = os.path.join(ROOT, "profiles", f"rs_kernel_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_k = re.search(r"rs_kernel_name:\s*(.+)", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_src and m_b) or m_src.group(1) != kernel_source_hash():
+    if not (m_src and m_k and m_b) or m_src.group(1) != kernel_source_hash() or m_k.group(1).strip() != kernel:
         return None
     return float(m_b.group(1))
 
@@ -1112,7 +1114,10 @@ def main():
     rs_gbps = rs_bytes / (rs_mean * 1e-3) / 1e9
     ag_gbps = ag_bytes / (ag_mean * 1e-3) / 1e9
     # counters were taken for the workload's own contributor count and the unbounded launch
-    traffic = read_traffic(cfg.name) if rs_budget == 0 and not args.contributors else None
+    rs_kernel_name = (f"rs_cu_kernel<{cfg.C if cfg.C in (1, 2, 4, 8) else 0}, true, false>"
+                      if rs_budget < -64 or (rs_budget == 0 and (cfg.C >= 12 or cfg.C == 8))
+                      else f"rs_kernel<{cfg.C if cfg.C <= 16 else 0}, true, false>")
+    traffic = read_traffic(cfg.name, rs_kernel_name) if rs_budget == 0 and not args.contributors else None
 
     out = {
         "metric": METRIC,
@@ -1148,9 +1153,7 @@ def main():
                         "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"rs_cu_kernel<{cfg.C if cfg.C in (1, 2, 4, 8) else 0}, true, false>"
-                       if rs_budget < -64 or (rs_budget == 0 and cfg.C >= 12)
-                       else f"rs_kernel<{cfg.C if cfg.C <= 16 else 0}, true, false>"),
+            "kernel": rs_kernel_name,
             "achieved": round(rs_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

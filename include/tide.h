@@ -149,12 +149,13 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              row-major bf16 device tensor of rows_p * L_p elements, 2-byte aligned (NULL allowed
  *              only for empty parameters).  Read in place, never written.
  *   shards     host [R]: shards[r] is rank r's flat fp32 device shard of S elements, 4-byte aligned.
- *   cu_budget  0: one launch.  C <= 11: one short-lived workgroup per work item, with at most N
- *              of them resident per CU: N = 12 for C <= 2, 8 for C <= 4, 6 above (each requests
- *              1/N of the CU's local memory; fewer requests in flight stream HBM better than a full
- *              CU, and a workgroup's traffic grows with C), in a kernel compiled for that C.
- *              C >= 12: as TIDE_RS_CU_EXCLUSIVE(8) below (faster there by 2-5% on MI355X), in its
- *              runtime-C form, which loads the contributors in blocks of 8.
+ *   cu_budget  0: one launch.  C = 8 and C >= 12: as TIDE_RS_CU_EXCLUSIVE(8) below (on MI355X the
+ *              fastest form there, and it leaves a concurrent GEMM its CUs); C >= 12 in its runtime-C
+ *              form, which loads the contributors in blocks of 8.  Other C: one short-lived workgroup
+ *              per work item, with at most N of them resident per CU: N = 12 for C <= 2, 8 for
+ *              C <= 4, 6 above (each requests 1/N of the CU's local memory; fewer requests in flight
+ *              stream HBM better than a full CU, and a workgroup's traffic grows with C), in a
+ *              kernel compiled for that C.
  *              -N (1 <= N <= TIDE_RS_MAX_WGS_PER_CU): as 0, with at most N per CU for any C (an N
  *              at or above the hardware's own limit leaves that limit).
  *              TIDE_RS_CU_EXCLUSIVE(W) (1 <= W <= 8): one launch of workgroups of 128*W threads, each

@@ -295,16 +295,16 @@ def test_prepared_calls_from_threads(gpu_available):
 
 
 def test_rs_launch_shape_caps_occupancy(gpu_available):
-    """Default RS launches (cu_budget 0): up to 11 contributors, 128-thread workgroups requesting 1/N
-    of a gfx950 CU's 160 KiB of local memory, N = 12 for C <= 2, 8 for C <= 4, 6 up to C = 11; from
+    """Default RS launches (cu_budget 0): 128-thread workgroups requesting 1/N of a gfx950 CU's 160 KiB
+    of local memory, N = 12 for C <= 2, 8 for C <= 4, 6 for C = 5-7 and 9-11; at C = 8 and from
     C = 12 on, CU-exclusive workgroups of 8 items (1024 threads, the whole local memory)."""
     lds_per_cu = 160 * 1024
-    for C, n in ((1, 12), (2, 12), (3, 8), (4, 8), (5, 6), (8, 6), (9, 6), (11, 6)):
+    for C, n in ((1, 12), (2, 12), (3, 8), (4, 8), (5, 6), (7, 6), (9, 6), (11, 6)):
         shape = tide_rs_launch_shape(C)
         say(f"RS launch shape C={C}: {shape}")
         assert shape["threads"] == 128 and shape["item_outputs"] == 1024
         assert shape["lds_bytes"] * n <= lds_per_cu < shape["lds_bytes"] * (n + 1), (C, shape)
-    for C in (12, 13, 16, 17, 24, 25, 40):
+    for C in (8, 12, 13, 16, 17, 24, 25, 40):
         shape = tide_rs_launch_shape(C)
         say(f"RS launch shape C={C}: {shape}")
         assert shape == tide_rs_launch_shape(C, tide_rs_cu_exclusive(8)), (C, shape)
