@@ -179,11 +179,11 @@ tide_status validate_ag(const tide_layout* L, const void* stage, void* const* pa
 // Stage `n` device pointers for a launch on `stream`; returns the slot that holds them.
 int acquire_ptrs(DeviceState* st, void* const* ptrs, size_t n, hipStream_t stream, PtrSlot** out) {
   // A slot that already holds this exact table and was last used on this stream can be reused
-  // without a copy: stream order keeps its earlier readers ahead of the new launch.  Calls that
+  // without a refill: stream order keeps its earlier readers ahead of the new launch.  Calls that
   // alternate between tables (an RS and an AG on the same group) hit different slots.
   for (int k = 0; k < kPtrSlots; ++k) {
     PtrSlot& s = st->slots[k];
-    if (s.n == n && s.host != nullptr && s.stream == stream && std::memcmp(s.host, ptrs, n * sizeof(void*)) == 0) {
+    if (s.n == n && s.dev != nullptr && s.stream == stream && std::memcmp(s.host.data(), ptrs, n * sizeof(void*)) == 0) {
       *out = &s;
       return hipSuccess;
     }
@@ -199,25 +199,20 @@ int acquire_ptrs(DeviceState* st, void* const* ptrs, size_t n, hipStream_t strea
     if ((e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming)) != hipSuccess) return e;
   }
   if (s.cap < n) {
-    if (s.dev) (void)hipFree(s.dev);
-    if (s.host) (void)hipHostFree(s.host);
+    dev_free(s.dev, st->aux);  // not pending: nothing reads it any more
     s.dev = nullptr;
-    s.host = nullptr;
     s.cap = 0;
+    s.n = 0;
     const size_t cap = std::max<size_t>(n, 256);
-    if ((e = hipMalloc(reinterpret_cast<void**>(&s.dev), cap * sizeof(void*))) != hipSuccess) return e;
-    if ((e = hipHostMalloc(reinterpret_cast<void**>(&s.host), cap * sizeof(void*), hipHostMallocDefault)) !=
-        hipSuccess) {
-      (void)hipFree(s.dev);
-      s.dev = nullptr;
-      return e;
-    }
+    void* p = nullptr;
+    if ((e = static_cast<hipError_t>(dev_alloc_copy(st->aux, nullptr, cap * sizeof(void*), &p))) != hipSuccess) return e;
+    s.dev = static_cast<void**>(p);
     s.cap = cap;
   }
-  std::memcpy(s.host, ptrs, n * sizeof(void*));
+  s.host.assign(ptrs, ptrs + n);
   s.n = n;
   s.stream = stream;
-  if ((e = hipMemcpyAsync(s.dev, s.host, n * sizeof(void*), hipMemcpyHostToDevice, stream)) != hipSuccess) {
+  if ((e = static_cast<hipError_t>(launch_put_ptrs(s.dev, ptrs, int64_t(n), stream))) != hipSuccess) {
     s.n = 0;
     return e;
   }
@@ -423,7 +418,59 @@ struct tide_call {
   int device = -1;
   void** dev_table = nullptr;
   tide::DeviceState* st = nullptr;  // node of layout->devices; std::map nodes do not move
+  // Completion marks of the kernel launches: one event per stream the call was launched on,
+  // recorded again after each launch, so that destroying the call (or its layout) waits for this
+  // call's work and nothing else.  A launch captured into a graph, or one whose stream could not be
+  // queried, cannot be tracked that way: `untracked` makes destroy wait for the whole device.
+  std::mutex mu;
+  std::vector<std::pair<hipStream_t, hipEvent_t>> marks;
+  bool untracked = false;
 };
+
+namespace tide {
+namespace {
+
+// Record the completion mark of a kernel launch on `hs` (see tide_call::marks).
+int mark_launch(tide_call* call, hipStream_t hs) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t q = hipStreamIsCapturing(hs, &cs);
+  std::lock_guard<std::mutex> lock(call->mu);
+  if (q != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    call->untracked = true;
+    return hipSuccess;
+  }
+  for (auto& m : call->marks)
+    if (m.first == hs) return hipEventRecord(m.second, hs);
+  hipEvent_t ev = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e != hipSuccess) return e;
+  call->marks.emplace_back(hs, ev);
+  return hipEventRecord(ev, hs);
+}
+
+// Wait until every launch of `call` has finished (the call's device current).
+void wait_call(tide_call* call) {
+  std::lock_guard<std::mutex> lock(call->mu);
+  if (call->untracked) {
+    (void)hipDeviceSynchronize();
+    call->untracked = false;
+  }
+  for (auto& m : call->marks) (void)hipEventSynchronize(m.second);
+}
+
+}  // namespace
+
+void wait_for_calls(const tide_layout* layout) {
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  for (tide_call* call : layout->calls) {
+    if (have && call->device != cur) (void)hipSetDevice(call->device);
+    wait_call(call);
+    if (have && call->device != cur) (void)hipSetDevice(cur);
+  }
+}
+
+}  // namespace tide
 
 namespace {
 
@@ -442,13 +489,17 @@ tide_status prepare(const tide_layout* L, tide::Request&& q, tide_call** out) {
   const bool kernels = !(call->q.kind == tide::kAg && call->q.mode != TIDE_AG_KERNEL);
   if (e == hipSuccess && kernels && !call->q.table.empty()) {
     const size_t bytes = call->q.table.size() * sizeof(void*);
-    e = hipMalloc(reinterpret_cast<void**>(&call->dev_table), bytes);
-    if (e == hipSuccess) e = hipMemcpy(call->dev_table, call->q.table.data(), bytes, hipMemcpyHostToDevice);
+    void* p = nullptr;
+    e = tide::dev_alloc_copy(call->st->aux, call->q.table.data(), bytes, &p);
+    call->dev_table = static_cast<void**>(p);
   }
   if (e != hipSuccess) {
-    if (call->dev_table) (void)hipFree(call->dev_table);
     delete call;
     return tide::hip_fail(e);
+  }
+  {
+    std::lock_guard<std::mutex> lock(L->mu);
+    L->calls.push_back(call);
   }
   *out = call;
   return TIDE_OK;
@@ -531,6 +582,7 @@ tide_status tide_call_launch(const tide_call* call, void* stream) {
   }
   if (!tide::needs_kernels(call->layout, q)) return TIDE_OK;
   e = tide::enqueue_kernels(call->layout, call->st, q, call->dev_table, hs);
+  if (e == hipSuccess) e = tide::mark_launch(const_cast<tide_call*>(call), hs);
   return e == hipSuccess ? TIDE_OK : tide::hip_fail(e);
 }
 
@@ -557,15 +609,19 @@ tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads,
 
 void tide_call_destroy(tide_call* call) {
   if (call == nullptr) return;
-  if (call->dev_table) {
-    int cur = 0;
-    const bool have = hipGetDevice(&cur) == hipSuccess;
-    if (have && cur != call->device) (void)hipSetDevice(call->device);
-    // launches carry no event (they must stay capturable), so wait for the device instead
-    (void)hipDeviceSynchronize();
-    (void)hipFree(call->dev_table);
-    if (have && cur != call->device) (void)hipSetDevice(cur);
+  {
+    std::lock_guard<std::mutex> lock(call->layout->mu);
+    auto& v = call->layout->calls;
+    v.erase(std::remove(v.begin(), v.end(), call), v.end());
   }
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  if (have && cur != call->device) (void)hipSetDevice(call->device);
+  // this call's own launches only (their marks); other work on the device is not waited for
+  tide::wait_call(call);
+  for (auto& m : call->marks) (void)hipEventDestroy(m.second);
+  tide::dev_free(call->dev_table, call->st->aux);  // stream-ordered: waits for no other work
+  if (have && cur != call->device) (void)hipSetDevice(cur);
   delete call;
 }
 

@@ -78,12 +78,15 @@ __device__ __forceinline__ void store4(float* d, const float a[4], bool dst16) {
 }
 
 // Work item taken by this workgroup.  Workgroups are dispatched round-robin over the XCDs
-// (workgroup b runs on XCD b mod kXcds).  With REMAP, when each workgroup takes one item, the items
-// are renumbered so that every XCD walks one contiguous range of the table, keeping its L2 and TLB
-// on one stream of pages; the map is a bijection on [0, count).
+// (workgroup b runs on XCD b mod kXcds).  With REMAP, when the grid has one workgroup per item, the
+// items are renumbered so that every XCD walks one contiguous range of the table, keeping its L2 and
+// TLB on one stream of pages; the map is a bijection on [0, count).  Such a grid has no item for
+// j > 0 (a launch may still pass items_per_wg > 1, e.g. a bounded launch's short tail), so the
+// caller's loop ends there and every item is taken exactly once.
 template <bool REMAP>
 __device__ __forceinline__ int64_t item_of(int j, int64_t count) {
   if (REMAP && gridDim.x == count) {
+    if (j > 0) return count;
     const int64_t b = blockIdx.x;
     const int64_t x = b % kXcds, i = b / kXcds;
     return x * (count / kXcds) + min<int64_t>(x, count % kXcds) + i;
@@ -630,6 +633,18 @@ __global__ __launch_bounds__(kAgThreads * kAgCuMaxItems) void ag_cu_kernel(const
   }
 }
 
+// One batch of pointers as a kernel argument (2 KiB), written by one workgroup with vector stores.
+constexpr int kPutPtrsBatch = 256;
+struct PtrBatch {
+  unsigned long long v[kPutPtrsBatch];
+};
+
+__global__ __launch_bounds__(kPutPtrsBatch) void put_ptrs_kernel(unsigned long long* __restrict__ dst, PtrBatch b,
+                                                                 int n) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = b.v[i];
+}
+
 // Zero-fill kernel for the padding of a packed slot: items (src = slot element offset, n).
 __global__ __launch_bounds__(kAgThreads) void fill_zero_kernel(const AgChunk* __restrict__ items, int64_t count,
                                                                 unsigned short* __restrict__ slot) {
@@ -787,6 +802,21 @@ int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int
                          items_per_wg, batch, st, pp);
   }
   return hipGetLastError();
+}
+
+int launch_put_ptrs(void* dst, void* const* ptrs, int64_t n, void* hip_stream) {
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  unsigned long long* d = static_cast<unsigned long long*>(dst);
+  for (int64_t first = 0; first < n; first += kPutPtrsBatch) {
+    const int k = static_cast<int>(n - first < kPutPtrsBatch ? n - first : kPutPtrsBatch);
+    PtrBatch b;
+    for (int i = 0; i < kPutPtrsBatch; ++i)
+      b.v[i] = i < k ? static_cast<unsigned long long>(reinterpret_cast<uintptr_t>(ptrs[first + i])) : 0ull;
+    hipLaunchKernelGGL(put_ptrs_kernel, dim3(1), dim3(kPutPtrsBatch), 0, s, d + first, b, k);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 int launch_fill_zero(const AgChunk* items, int64_t count, void* slot, void* hip_stream) {

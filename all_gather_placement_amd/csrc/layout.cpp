@@ -45,17 +45,13 @@ thread_local int g_last_hip_error = 0;
 
 // Copy a host table to new device memory (nothing for an empty table).
 template <typename T>
-hipError_t upload(const std::vector<T>& v, T** out) {
+hipError_t upload(hipStream_t aux, const std::vector<T>& v, T** out) {
   *out = nullptr;
   if (v.empty()) return hipSuccess;
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(out), v.size() * sizeof(T));
-  if (e != hipSuccess) return e;
-  e = hipMemcpy(*out, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(*out);
-    *out = nullptr;
-  }
-  return e;
+  void* p = nullptr;
+  const int e = dev_alloc_copy(aux, v.data(), v.size() * sizeof(T), &p);
+  *out = static_cast<T*>(p);
+  return static_cast<hipError_t>(e);
 }
 
 // Order in which workgroups take work items (before any XCD renumbering in the kernels):
@@ -91,6 +87,25 @@ void order_items(tide_layout* L) {
 
 void set_last_hip_error(int err) { g_last_hip_error = err; }
 
+int dev_alloc_copy(hipStream_t aux, const void* host, size_t bytes, void** out) {
+  *out = nullptr;
+  void* p = nullptr;
+  hipError_t e = hipMallocAsync(&p, bytes, aux);
+  if (e != hipSuccess) return e;
+  if (host != nullptr) e = hipMemcpyAsync(p, host, bytes, hipMemcpyHostToDevice, aux);
+  if (e == hipSuccess) e = hipStreamSynchronize(aux);
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(p, aux);
+    return e;
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+void dev_free(void* p, hipStream_t aux) {
+  if (p != nullptr) (void)hipFreeAsync(p, aux);
+}
+
 int rs_device_info(int device, DeviceState* st) {
   hipError_t e = static_cast<hipError_t>(
       rs_lds_info(device, &st->lds_per_cu, &st->rs_static_lds_ct, &st->rs_static_lds_rt));
@@ -111,14 +126,17 @@ int device_state(const tide_layout* layout, DeviceState** out) {
   }
   DeviceState st;
   e = static_cast<hipError_t>(rs_device_info(dev, &st));
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&st.aux, hipStreamNonBlocking);
   if (e != hipSuccess) return e;
-  e = upload(layout->rs_chunks, &st.rs);
-  if (e == hipSuccess) e = upload(layout->ag_chunks, &st.ag);
-  if (e == hipSuccess) e = upload(layout->slot_pad_items, &st.slot_pad);
+  e = upload(st.aux, layout->rs_chunks, &st.rs);
+  if (e == hipSuccess) e = upload(st.aux, layout->ag_chunks, &st.ag);
+  if (e == hipSuccess) e = upload(st.aux, layout->slot_pad_items, &st.slot_pad);
   if (e != hipSuccess) {
-    if (st.rs) (void)hipFree(st.rs);
-    if (st.ag) (void)hipFree(st.ag);
-    if (st.slot_pad) (void)hipFree(st.slot_pad);
+    dev_free(st.rs, st.aux);
+    dev_free(st.ag, st.aux);
+    dev_free(st.slot_pad, st.aux);
+    (void)hipStreamSynchronize(st.aux);
+    (void)hipStreamDestroy(st.aux);
     return e;
   }
   auto res = layout->devices.emplace(dev, st);
@@ -223,19 +241,24 @@ void tide_layout_destroy(tide_layout* layout) {
   int cur = 0;
   // No HIP call at all for a layout that never reached a device (host-only use).
   const bool have_dev = !layout->devices.empty() && hipGetDevice(&cur) == hipSuccess;
+  if (have_dev) {
+    // Prepared calls not destroyed yet (the contract asks for them to go first): their queued
+    // launches read the tables below.
+    std::lock_guard<std::mutex> lock(layout->mu);
+    tide::wait_for_calls(layout);
+  }
   for (auto& kv : layout->devices) {
     if (hipSetDevice(kv.first) != hipSuccess) continue;
-    // Prepared calls launch without events, so work still queued on any stream may read the
-    // tables below: wait for the device before freeing them.
-    (void)hipDeviceSynchronize();
+    // What else may still read the tables: immediate calls' kernels (each ring slot's event is
+    // recorded after the kernels that read it) and DMA copies (the internal streams).  Work of
+    // other streams that never used the layout is not waited for.
     tide::DeviceState& st = kv.second;
     for (auto& s : st.slots) {
       if (s.done) {
         if (s.pending) (void)hipEventSynchronize(s.done);
         (void)hipEventDestroy(s.done);
       }
-      if (s.dev) (void)hipFree(s.dev);
-      if (s.host) (void)hipHostFree(s.host);
+      tide::dev_free(s.dev, st.aux);
     }
     for (int k = 0; k < tide::kDmaStreams; ++k) {
       if (st.dma[k]) {
@@ -245,9 +268,12 @@ void tide_layout_destroy(tide_layout* layout) {
       if (st.dma_join[k]) (void)hipEventDestroy(st.dma_join[k]);
     }
     if (st.dma_fork) (void)hipEventDestroy(st.dma_fork);
-    if (st.rs) (void)hipFree(st.rs);
-    if (st.ag) (void)hipFree(st.ag);
-    if (st.slot_pad) (void)hipFree(st.slot_pad);
+    // stream-ordered frees on the internal stream: they wait for nothing but that stream
+    tide::dev_free(st.rs, st.aux);
+    tide::dev_free(st.ag, st.aux);
+    tide::dev_free(st.slot_pad, st.aux);
+    (void)hipStreamSynchronize(st.aux);
+    (void)hipStreamDestroy(st.aux);
   }
   if (have_dev && !layout->devices.empty()) (void)hipSetDevice(cur);
   delete layout;
@@ -351,5 +377,10 @@ const char* tide_status_str(int32_t status) {
 }
 
 int32_t tide_last_hip_error(void) { return tide::g_last_hip_error; }
+
+#ifndef TIDE_BUILD_ID
+#define TIDE_BUILD_ID "unknown"
+#endif
+const char* tide_build_id(void) { return TIDE_BUILD_ID; }
 
 }  // extern "C"

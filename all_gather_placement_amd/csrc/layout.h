@@ -21,10 +21,11 @@ struct ParamGeom {
 };
 
 // A ring of device pointer tables.  Each RS/AG call needs its C*P + R (or P) device pointers in
-// device memory; a slot is refilled from pinned host memory with one stream-ordered copy, and a
-// call whose pointers equal the previous call's on the same stream reuses that slot with no copy.
+// device memory; a slot is refilled by small kernels on the caller's stream that carry the pointers
+// as kernel arguments (no host staging buffer), and a call whose pointers equal the previous call's
+// on the same stream reuses that slot with no refill.
 struct PtrSlot {
-  void** host = nullptr;  // pinned
+  std::vector<void*> host;  // host copy of what the slot holds (to recognise a repeated table)
   void** dev = nullptr;
   size_t cap = 0;         // pointers
   size_t n = 0;           // pointers currently held
@@ -40,6 +41,10 @@ constexpr int kPtrSlots = 8;
 constexpr int kDmaStreams = 2;
 
 struct DeviceState {
+  // Internal stream of the library's own device memory: tables are allocated from the device's
+  // stream-ordered pool and freed on it, so freeing them waits for nothing else (hipFree and
+  // hipHostFree synchronise the whole device).
+  hipStream_t aux = nullptr;
   RsChunk* rs = nullptr;
   AgChunk* ag = nullptr;
   AgChunk* slot_pad = nullptr;
@@ -109,7 +114,15 @@ inline int rs_launch_lds(const DeviceState& st, int C, int cu_budget) {
 // Returns a hipError_t.
 int rs_device_info(int device, DeviceState* st);
 
+// `bytes` of device memory from the device's stream-ordered pool, allocated on `aux` and filled from
+// `host` (if not NULL); usable from every stream once this returns (it waits for `aux`).
+int dev_alloc_copy(hipStream_t aux, const void* host, size_t bytes, void** out);
+// Stream-ordered free on `aux`, for memory that nothing reads any more (the caller has waited).
+void dev_free(void* p, hipStream_t aux);
+
 }  // namespace tide
+
+struct tide_call;
 
 struct tide_layout {
   int32_t P = 0;
@@ -122,6 +135,9 @@ struct tide_layout {
   std::vector<tide::AgChunk> slot_pad_items;
   mutable std::mutex mu;
   mutable std::map<int, tide::DeviceState> devices;
+  // Prepared calls made from this layout and not yet destroyed (guarded by mu): their launches
+  // read the layout's device tables, so destroying the layout waits for them too.
+  mutable std::vector<tide_call*> calls;
 };
 
 namespace tide {
@@ -131,4 +147,6 @@ int device_state(const tide_layout* layout, DeviceState** out);
 // Reorders the work-item tables into the order workgroups take them.
 void order_items(tide_layout* layout);
 void set_last_hip_error(int err);
+// Waits for the launches of every prepared call still registered with the layout (layout->mu held).
+void wait_for_calls(const tide_layout* layout);
 }  // namespace tide

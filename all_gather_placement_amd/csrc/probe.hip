@@ -220,4 +220,9 @@ int64_t tide_probe_wall_clock_khz(void) {
   return khz;
 }
 
+#ifndef TIDE_BUILD_ID
+#define TIDE_BUILD_ID "unknown"
+#endif
+const char* tide_probe_build_id(void) { return TIDE_BUILD_ID; }
+
 }  // extern "C"

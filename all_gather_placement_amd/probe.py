@@ -25,6 +25,9 @@ def load_probe_library():
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run `python -m all_gather_placement_amd.build`")
         lib = ctypes.CDLL(path)
+        from .build import PROBE_LIB, check_current
+
+        check_current(PROBE_LIB, loaded=lib)
         lib.tide_probe_launch.restype = ctypes.c_int32
         lib.tide_probe_launch.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p]

@@ -69,6 +69,11 @@ def load_library(path: str | None = None):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m all_gather_placement_amd.build`")
     lib = ctypes.CDLL(path)
+    if path == library_path():
+        # a library built from other sources than the ones beside it is refused, never run
+        from .build import LIB, check_current
+
+        check_current(LIB, loaded=lib)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     P_i32, P_i64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
     sig = {
@@ -99,6 +104,7 @@ def load_library(path: str | None = None):
         "tide_rs_launch_shape": (i32, [i32, i32, P_i32, P_i32, P_i32]),
         "tide_status_str": (ctypes.c_char_p, [i32]),
         "tide_last_hip_error": (i32, []),
+        "tide_build_id": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

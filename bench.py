@@ -5,11 +5,14 @@
 
 One step = one pass of the whole hot path over one parameter group already resident in HBM: the
 in-place reduce-scatter (C bf16 contributors -> R fp32 shards) followed by the all-gather placement
-(rank-major bf16 stage -> per-parameter storage).  The JSON line reports:
+(rank-major bf16 stage -> per-parameter storage).  The default group is the Llama-3.1-70B decoder
+layer (R = 8, C = 8, 17.1 GB of RS traffic per call), the largest of the layer groups.  The JSON line
+reports:
 
-  value       effective HBM GB/s of the step: algorithmic bytes of RS and AG / step time;
-  roofline    the RS kernel (the dominant one): algorithmic bytes per launch / its mean duration,
-              measured with HIP events on the launch stream, against the 8 TB/s HBM peak;
+  value       the RS's effective HBM GB/s: its algorithmic bytes / the mean duration of its launches,
+              measured with HIP events on the launch stream (the metric's own quantity);
+  step_gbps   the whole step's algorithmic bytes (RS + AG) / the step time; ag_gbps the placement's;
+  roofline    the RS kernel (the dominant one): the same achieved rate against the 8 TB/s HBM peak;
   calibration a runtime device-to-device copy moving the RS's bytes, timed in the same run (the
               rate a plain stream reaches on this device), and the RS's ratio to it;
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload (same byte formula).
@@ -20,7 +23,6 @@ AG = 2*numel (reads) + 2*numel (writes).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -40,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3_1_8b_layer")
+    ap.add_argument("--workload", default="llama3_1_70b_layer")
     ap.add_argument("--cu-budget", type=int, default=0)
     ap.add_argument("--rs-wgs-per-cu", type=int, default=0,
                     help="unbounded RS with at most N workgroups per CU (RS cu_budget -N; 0 = the library's cap by C)")
@@ -107,11 +109,12 @@ def shard_numel(shapes, R: int) -> int:
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for f in ("kernels.hip", "tide_internal.h"):
-        with open(os.path.join(ROOT, "all_gather_placement_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    """Build id of libtide.so for the sources in the tree: kernels, launch plan (entry points and
+    layout code), headers and compile flags.  Profiles record it, so any change to what runs on the
+    device, or how it is launched, marks them stale."""
+    from all_gather_placement_amd.build import LIB, source_hash
+
+    return source_hash(LIB)
 
 
 def read_traffic(workload: str, kernel: str):
@@ -132,9 +135,11 @@ def read_traffic(workload: str, kernel: str):
 def cpu_baseline(cfg, log, min_seconds: float = 10.0):
     """Time the oracle on a bounded sample of the workload (about 10-30 s of CPU work).
 
-    The sample is the group's leading parameters (storage order) up to ~45M elements, with the
-    workload's R, C and value scale; the oracle's RS and AG run over it repeatedly until at least
-    `min_seconds` have passed.  Threads used = process CPU time / wall time over the timed passes.
+    The sample is the group's leading parameters (storage order) up to ~45M elements (at least the
+    first parameter), with the workload's R, C and value scale; the oracle's RS and AG run over it
+    repeatedly until at least `min_seconds` have passed.  `value` is the oracle RS's rate by the
+    metric's byte formula (the quantity the GPU line reports); `ag_gbps` the copy-out's.  Threads
+    used = process CPU time / wall time over the timed passes.
     """
     import resource
 
@@ -175,14 +180,13 @@ def cpu_baseline(cfg, log, min_seconds: float = 10.0):
     log(f"cpu oracle sample: {len(shapes)} params, {total} elems, {passes} passes: RS {t_rs:.2f} s, "
         f"AG {t_ag:.2f} s, cpu/wall {cpu / wall:.2f}")
     return {
-        "value": round(passes * (rs_bytes + ag_bytes) / (t_rs + t_ag) / 1e9, 3),
+        "value": round(passes * rs_bytes / t_rs / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": (f"{cfg.name}: parameters {[n for n, _ in cfg.params[:len(shapes)]]} "
                    f"({total} elements, R={cfg.R}, C={cfg.C}); numpy pack-then-sum RS + copy-out AG, "
                    f"{passes} passes in {t_rs + t_ag:.1f} s; host has {os.cpu_count()} logical CPUs"),
-        "rs_gbps": round(passes * rs_bytes / t_rs / 1e9, 3),
         "ag_gbps": round(passes * ag_bytes / t_ag / 1e9, 3),
         "cpu_over_wall": round(cpu / wall, 3),
     }
@@ -1062,8 +1066,8 @@ def main():
         g1.synchronize()
         graph_ms = g0.elapsed_time(g1) / K
         graph_info = {"ms_per_step": round(graph_ms, 5),
-                      "value": round((rs_bytes + ag_bytes) / (graph_ms * 1e-3) / 1e9, 2)}
-        log(f"graph replay: {graph_ms:.4f} ms per step ({graph_info['value']:.0f} GB/s)")
+                      "step_gbps": round((rs_bytes + ag_bytes) / (graph_ms * 1e-3) / 1e9, 2)}
+        log(f"graph replay: {graph_ms:.4f} ms per step ({graph_info['step_gbps']:.0f} GB/s)")
         del graph
         torch.cuda.synchronize()
 
@@ -1110,7 +1114,7 @@ def main():
     except (RuntimeError, OSError) as e:  # a measurement aid only: the line is still printed
         clock_info = {"error": str(e)}
 
-    value = (rs_bytes + ag_bytes) / (ms_per_step * 1e-3) / 1e9
+    step_gbps = (rs_bytes + ag_bytes) / (ms_per_step * 1e-3) / 1e9
     rs_gbps = rs_bytes / (rs_mean * 1e-3) / 1e9
     ag_gbps = ag_bytes / (ag_mean * 1e-3) / 1e9
     # counters were taken for the workload's own contributor count and the unbounded launch
@@ -1121,7 +1125,7 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(rs_gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
@@ -1141,6 +1145,7 @@ def main():
         },
         "rs_gbps": round(rs_gbps, 2),
         "rs_frac_of_peak": round(rs_gbps / HBM_PEAK_GBPS, 4),
+        "step_gbps": round(step_gbps, 2),
         "rs_ms_mean": round(rs_mean, 5),
         "rs_ms_min_median": [round(rs_sorted[0], 5), round(rs_sorted[K // 2], 5)],
         "ag_gbps": round(ag_gbps, 2),

@@ -95,9 +95,11 @@ enum {
 tide_status tide_layout_create(int32_t num_params, const int32_t* ndims, const int64_t* dims,
                                int32_t num_ranks, tide_layout** out);
 
-/* Free a layout and its device tables.  Waits for all work on every device the layout was used on
- * (hipDeviceSynchronize) before freeing, so work still queued that reads its tables finishes first;
- * prepared calls of the layout must not be launched afterwards.  NULL is ignored. */
+/* Free a layout and its device tables.  First waits for the work still queued that reads them --
+ * the kernels of its immediate calls (each pointer-table slot's event), its DMA-engine copies (the
+ * library's internal copy streams) and the launches of prepared calls not yet destroyed (as
+ * tide_call_destroy) -- but not for other work on the device.  Prepared calls of the layout should
+ * be destroyed first and must not be launched afterwards.  NULL is ignored. */
 void tide_layout_destroy(tide_layout* layout);
 
 /* Upload the layout's device tables to the current device (idempotent).  After this, RS and AG
@@ -216,9 +218,9 @@ tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* co
                           int32_t mode, int32_t cu_budget, void* stream);
 
 /*
- * Slot-Reuse, step 1: pack one contributor's per-parameter bf16 gradients into a vacated rank-major
- * all-gather slot ([Endgame] abstract: Slot-Reuse stages gradients in vacated all-gather slots;
- * Figure 7: gradients are copied into a vacated slot whose reuse waits for the reduce-scatter's read).
+ * Slot-Reuse, step 1: pack one contributor's per-parameter bf16 gradients into a rank-major
+ * all-gather buffer that is no longer needed (the optional Slot-Reuse mode of the [Endgame] abstract;
+ * Figure 7: the reduce-scatter then reads the buffer, which is reused only after that read).
  *   grads      host [P]: grads[p] is parameter p's contiguous bf16 gradient (rows_p * L_p elements,
  *              2-byte aligned; NULL allowed only for empty parameters).  Read, never written.
  *   slot       device, R*S bf16 elements in the stage layout (rank r's shard at element r*S).
@@ -251,9 +253,10 @@ tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, con
  * and uploads a device table of the buffer addresses that the call owns; tide_call_launch then
  * enqueues the work on a stream with the result the immediate call would have given.
  *   - For the kernel paths (RS, RS from slots, slot packing, TIDE_AG_KERNEL placement),
- *     tide_call_launch only launches kernels: no allocation, no copy, no event, no check beyond
- *     the current device.  Such launches may be captured into a HIP graph and the graph replayed;
- *     each replay recomputes the result from the buffers' current contents.
+ *     tide_call_launch launches kernels and, outside graph capture, records the call's completion
+ *     event on the stream (created on the first launch on each stream): no device allocation, no
+ *     copy, no check beyond the current device.  Such launches may be captured into a HIP graph and
+ *     the graph replayed; each replay recomputes the result from the buffers' current contents.
  *   - TIDE_AG_COPY2D and TIDE_AG_SDMA calls enqueue runtime copies as the immediate call does
  *     (TIDE_AG_SDMA through the layout's internal copy streams).
  *   - The buffers named at prepare time must stay allocated while the call may launch; their
@@ -280,10 +283,11 @@ tide_status tide_rs_slots_prepare(const tide_layout* layout, int32_t C, const vo
 /* Enqueue a prepared call on `stream` (hipStream_t as void*). */
 tide_status tide_call_launch(const tide_call* call, void* stream);
 
-/* Free a prepared call (its device table, on the call's device).  Waits for all work on that
- * device first (launches carry no event, so that they stay capturable), so a call destroyed with
- * launches in flight is safe; no graph holding its launches may be replayed afterwards.  NULL is
- * ignored. */
+/* Free a prepared call (its device table, on the call's device).  Waits first for the call's own
+ * launches -- each kernel launch records an event on its stream, one event per stream -- so a call
+ * destroyed with launches in flight is safe and work of other streams is not waited for.  Launches
+ * captured into a graph carry no event; if the call was ever captured, destroy waits for the whole
+ * device instead, and no graph holding its launches may be replayed afterwards.  NULL is ignored. */
 void tide_call_destroy(tide_call* call);
 
 /* Launch shape of RS calls with C contributors at `cu_budget` on the current device: threads per
@@ -301,6 +305,12 @@ const char* tide_status_str(int32_t status);
 /* HIP error code (hipError_t value) behind the calling thread's last TIDE_ERR_HIP or
  * TIDE_ERR_UNSUPPORTED (also set for TIDE_ERR_NOMEM from a device allocation), 0 if none. */
 int32_t tide_last_hip_error(void);
+
+/* Build id of this library: a static, NUL-terminated string of 16 hex digits, the first digits of
+ * the SHA-256 of the sources, headers and compile flags it was built from ("unknown" for a build
+ * that did not set one).  The Python binding compares it with the sources beside the library and
+ * refuses a library built from other sources.  Host only; makes no HIP call. */
+const char* tide_build_id(void);
 
 #ifdef __cplusplus
 }

@@ -111,6 +111,10 @@ int32_t tide_probe_stream_destroy(void* stream);
 /* Device wall-clock rate in kHz (hipDeviceAttributeWallClockRate of the current device), or -1. */
 int64_t tide_probe_wall_clock_khz(void);
 
+/* Build id of this library (16 hex digits of the SHA-256 of its sources, headers and compile flags;
+ * "unknown" if none was set): the binding refuses a library built from other sources.  Host only. */
+const char* tide_probe_build_id(void);
+
 #ifdef __cplusplus
 }
 #endif

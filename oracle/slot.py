@@ -1,8 +1,8 @@
 """Slot-Reuse staging: gradients packed into a vacated all-gather slot (oracle; test infrastructure).
 
-[Endgame] abstract: Slot-Reuse optionally stages gradients in vacated all-gather slots; Figure 7: the
-gradients are copied into a vacated all-gather slot and the reduce-scatter then reads the slot, whose
-reuse waits for that read.  A slot has the all-gather stage's rank-major layout (R slots of S bf16
+In TIDE's optional Slot-Reuse mode ([Endgame] abstract; Figure 7) a contributor's gradients are first
+copied into an all-gather buffer that is no longer needed, and the reduce-scatter reads them from there;
+the buffer is only reused after that read.  A slot has the all-gather stage's rank-major layout (R slots of S bf16
 elements, parameter p of rank r at r*S + o_p), so packing is the inverse of the all-gather copy-out:
 
   slot[r*S + o_p + k] = G[p].flat[r*m_p*L_p + k]   for k < v*L_p,   +0 (bits 0) for the padding.

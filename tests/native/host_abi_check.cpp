@@ -41,6 +41,10 @@ int rs_cu_static_lds(int*) {
   std::fprintf(stderr, "rs_cu_static_lds reached in a host-only check\n");
   std::abort();
 }
+int launch_put_ptrs(void*, void* const*, int64_t, void*) {
+  std::fprintf(stderr, "launch_put_ptrs reached in a host-only check\n");
+  std::abort();
+}
 }  // namespace tide
 
 static int failures = 0;

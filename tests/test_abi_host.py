@@ -342,8 +342,8 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     text = open(os.path.join(ROOT, "include", "tide_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(tide_probe_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["tide_probe_clock", "tide_probe_launch", "tide_probe_mix", "tide_probe_stream_create_cu_mask",
-                     "tide_probe_stream_destroy", "tide_probe_wall_clock_khz"]
+    assert names == ["tide_probe_build_id", "tide_probe_clock", "tide_probe_launch", "tide_probe_mix",
+                     "tide_probe_stream_create_cu_mask", "tide_probe_stream_destroy", "tide_probe_wall_clock_khz"]
     for n in names:
         assert hasattr(lib, n)
     assert lib.tide_probe_launch(0, 0, 10, None, None) == -1
@@ -429,3 +429,39 @@ def test_cu_exclusive_encoding_matches_the_header():
     for bad in (0, max_items + 1):
         with pytest.raises(ValueError):
             tide.tide_rs_cu_exclusive(bad)
+
+
+def test_build_id_matches_the_sources():
+    """Each library carries the build id of the sources in the tree it was built from."""
+    from all_gather_placement_amd import build
+
+    for lib in (build.LIB, build.PROBE_LIB):
+        assert build.built_id(lib) == build.source_hash(lib)
+        assert len(build.source_hash(lib)) == 16
+    assert tb.load_library().tide_build_id().decode() == build.source_hash(build.LIB)
+
+
+def test_library_built_from_other_sources_is_refused_or_rebuilt(monkeypatch):
+    """A library whose build id differs from the sources beside it is refused by the binding, and
+    ensure_built() rebuilds it.  The mismatch is faked by changing the id the sources are expected to
+    have; no file is edited."""
+    import ctypes
+
+    from all_gather_placement_amd import build, probe, tide
+
+    lib = ctypes.CDLL(build.LIB)
+    build.check_current(build.LIB, loaded=lib)  # the real one passes
+    monkeypatch.setattr(build, "source_hash", lambda lib=build.LIB, extra=(): "0123456789abcdef")
+    with pytest.raises(RuntimeError, match="other sources"):
+        build.check_current(build.LIB, loaded=lib)
+    with pytest.raises(RuntimeError, match="other sources"):
+        tide.load_library(tide.library_path())  # an explicit load re-checks
+    monkeypatch.setattr(probe, "_lib", None)
+    with pytest.raises(RuntimeError, match="other sources"):
+        probe.load_probe_library()
+    monkeypatch.setattr(probe, "_lib", None)
+    assert not build.is_current(build.LIB) and not build.is_current(build.PROBE_LIB)
+    rebuilt = []
+    monkeypatch.setattr(build, "build", lambda verbose=False: rebuilt.append(True) or build.LIB)
+    build.ensure_built()
+    assert rebuilt == [True]

@@ -431,7 +431,7 @@ def test_ag_cu_exclusive_modes(gpu_available):
 
 def test_destroy_with_work_in_flight(gpu_available):
     """Closing a prepared call, or a layout, right after launching (no synchronisation) is safe:
-    destroy waits for the device before freeing the tables the queued kernels read."""
+    destroy waits for the queued kernels that read the tables before freeing them."""
     shapes, R, C = GROUPS[1]
     geo, S = ogeo.group_geometry(shapes, R)
     g = [[normal_bf16_bits(s, 1.0, 180, c, p) for p, s in enumerate(shapes)] for c in range(C)]
@@ -454,6 +454,57 @@ def test_destroy_with_work_in_flight(gpu_available):
     L.close()
     torch.cuda.synchronize()
     assert_rs_equal(shards_bits(shards), want)
+
+
+def test_destroy_waits_for_its_own_work_only(gpu_available):
+    """Destroying a prepared call, or a layout, waits for the work that reads its tables (the
+    call's launches, the layout's immediate calls) and not for a kernel running on another stream:
+    once the call's own work has finished, a 200 ms spin workgroup started on a side stream is still
+    running when destroy returns (a device-wide wait would take the whole 200 ms).  The spin starts
+    after the call's work because streams share the device's few hardware queues: work queued behind
+    it in the same queue would wait for it whoever waits on that work."""
+    import time
+
+    from all_gather_placement_amd import probe as pr
+
+    shapes, R, C = GROUPS[1]
+    geo, S = ogeo.group_geometry(shapes, R)
+    g = [[normal_bf16_bits(s, 1.0, 181, c, p) for p, s in enumerate(shapes)] for c in range(C)]
+    grads = [[dev_bf16(x) for x in row] for row in g]
+    want = oracle.reduce_scatter(g, shapes, R)
+    khz = pr.wall_clock_khz()
+    other = torch.cuda.Stream()
+    for what in ("call", "layout"):
+        say(f"destroy ({what}) beside a spin kernel on another stream")
+        torch.cuda.synchronize()
+        L = Layout(shapes, R)
+        shards = poisoned_shards(R, S)
+        call = L.bind_rs(grads, shards) if what == "call" else None
+        if what == "call":
+            call.launch()
+        else:
+            L.rs_bf16_to_fp32(grads, shards)
+        torch.cuda.current_stream().synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(other)
+        pr.probe_launch(1, pr.TIDE_PROBE_SMALL, khz * 200, None, other)  # one workgroup, 200 ms
+        t1.record(other)
+        time.sleep(0.01)  # let the spin start
+        t = time.perf_counter()
+        if what == "call":
+            call.close()  # waits for the call's launch (its event), not for the side stream
+        else:
+            L.close()  # waits for the immediate call's kernels (its table slot's event)
+        waited = time.perf_counter() - t
+        still_running = not t1.query()
+        other.synchronize()
+        spin_ms = t0.elapsed_time(t1)
+        torch.cuda.synchronize()
+        assert_rs_equal(shards_bits(shards), want)
+        say(f"destroy ({what}): returned after {waited * 1e3:.1f} ms, the side kernel ran {spin_ms:.1f} ms")
+        assert spin_ms > 100.0, spin_ms
+        assert still_running and waited * 1e3 < 0.5 * spin_ms, (waited, spin_ms)
+        L.close()
 
 
 def test_closing_the_layout_closes_its_calls(gpu_available):
