@@ -22,6 +22,8 @@ from .tide import (  # noqa: F401
     tide_call_launch,
     tide_layout_create,
     tide_rs_bf16_to_fp32,
+    tide_rs_bf16_to_fp32_noalloc,
+    TIDE_NOALLOC_MAX_PTRS,
     tide_rs_cu_exclusive,
     tide_rs_launch_shape,
     tide_rs_prepare,

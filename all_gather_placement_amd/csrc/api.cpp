@@ -538,6 +538,31 @@ tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, con
   return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
 }
 
+tide_status tide_rs_bf16_to_fp32_noalloc(const tide_layout* layout, int32_t C, const void* const* grads,
+                                         float* const* shards, int32_t cu_budget, void* stream) {
+  tide::Request q;
+  tide_status s = tide::validate_rs(layout, C, grads, shards, cu_budget, &q);
+  if (s != TIDE_OK) return s;
+  if (int64_t(q.table.size()) > int64_t(TIDE_NOALLOC_MAX_PTRS)) return TIDE_ERR_INVALID;
+  if (!tide::needs_kernels(layout, q)) return TIDE_OK;
+  int dev = 0;
+  int e = hipGetDevice(&dev);
+  if (e != hipSuccess) return tide::hip_fail(e);
+  const tide::DeviceState* st = nullptr;
+  {
+    // the device tables must exist already: creating them here would allocate
+    std::lock_guard<std::mutex> lock(layout->mu);
+    auto it = layout->devices.find(dev);
+    if (it == layout->devices.end()) return TIDE_ERR_INVALID;
+    st = &it->second;  // std::map nodes do not move; the state is never erased before destroy
+  }
+  if (st->scratch == nullptr || int64_t(q.table.size()) > st->scratch_ptrs) return TIDE_ERR_INVALID;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  e = tide::launch_put_ptrs(st->scratch, q.table.data(), int64_t(q.table.size()), hs);
+  if (e == hipSuccess) e = tide::enqueue_kernels(layout, st, q, static_cast<void* const*>(st->scratch), hs);
+  return e == hipSuccess ? TIDE_OK : tide::hip_fail(e);
+}
+
 tide_status tide_rs_prepare(const tide_layout* layout, int32_t C, const void* const* grads, float* const* shards,
                             int32_t cu_budget, tide_call** out) {
   tide::Request q;

@@ -23,6 +23,10 @@
 // lane per access when source and destination share their 16-byte phase.
 #include <hip/hip_runtime.h>
 
+#include <map>
+#include <mutex>
+
+#include "../../include/tide.h"
 #include "tide_internal.h"
 
 namespace tide {
@@ -633,6 +637,13 @@ __global__ __launch_bounds__(kAgThreads * kAgCuMaxItems) void ag_cu_kernel(const
   }
 }
 
+// Pointer-table scratch of the allocation-free RS entry point: one fixed array per device, held by
+// the library until the process ends.  Host code never passes `scratch` itself to a kernel (in host
+// code the name is only a stand-in for the symbol); it uses the device address that
+// noalloc_scratch() obtains once per device with hipGetSymbolAddress.
+constexpr int64_t kNoAllocMaxPtrs = TIDE_NOALLOC_MAX_PTRS;
+static __device__ __align__(256) unsigned long long scratch[kNoAllocMaxPtrs];
+
 // One batch of pointers as a kernel argument (2 KiB), written by one workgroup with vector stores.
 constexpr int kPutPtrsBatch = 256;
 struct PtrBatch {
@@ -802,6 +813,25 @@ int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int
                          items_per_wg, batch, st, pp);
   }
   return hipGetLastError();
+}
+
+int noalloc_scratch(int device, void** out, int64_t* max_ptrs) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;  // device -> address of `scratch` on it
+  std::lock_guard<std::mutex> lock(mu);
+  *max_ptrs = kNoAllocMaxPtrs;
+  auto it = addr.find(device);
+  if (it != addr.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (p == nullptr) return hipErrorInvalidSymbol;
+  addr.emplace(device, p);
+  *out = p;
+  return hipSuccess;
 }
 
 int launch_put_ptrs(void* dst, void* const* ptrs, int64_t n, void* hip_stream) {

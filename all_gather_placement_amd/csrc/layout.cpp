@@ -126,6 +126,7 @@ int device_state(const tide_layout* layout, DeviceState** out) {
   }
   DeviceState st;
   e = static_cast<hipError_t>(rs_device_info(dev, &st));
+  if (e == hipSuccess) e = static_cast<hipError_t>(noalloc_scratch(dev, &st.scratch, &st.scratch_ptrs));
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&st.aux, hipStreamNonBlocking);
   if (e != hipSuccess) return e;
   e = upload(st.aux, layout->rs_chunks, &st.rs);

@@ -59,6 +59,10 @@ struct DeviceState {
   int rs_static_lds_ct = 0; // static local memory of the RS kernel, C <= kRsMaxCt
   int rs_static_lds_rt = 0; // static local memory of the RS kernel, C > kRsMaxCt
   int rs_static_lds_cu = 0; // static local memory of the CU-exclusive RS kernel
+  // Device address of the library's fixed pointer-table scratch array on this device (allocation-free
+  // RS entry point), obtained once at set-up, and its size in pointers.
+  void* scratch = nullptr;
+  int64_t scratch_ptrs = 0;
 };
 
 // cu_budget values TIDE_RS_CU_EXCLUSIVE(W) (TIDE_AG_CU_EXCLUSIVE(W) for the placement kernel and the

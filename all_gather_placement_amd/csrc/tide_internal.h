@@ -214,6 +214,9 @@ inline int rs_dynamic_lds(int lds_per_cu, int static_lds, int wgs_per_cu) {
 int launch_ag(const AgChunk* chunks, int64_t first, int64_t count, int grid, int items_per_wg, int batch,
               void* stage, const void* const* dev_params, bool pack, bool vec, void* hip_stream);
 int launch_fill_zero(const AgChunk* items, int64_t count, void* slot, void* hip_stream);
+// Device address of the fixed pointer-table scratch array of the allocation-free RS entry point on
+// the current device (hipGetSymbolAddress once per device, then cached); `max_ptrs` gets its size.
+int noalloc_scratch(int device, void** out, int64_t* max_ptrs);
 // Writes the n pointers `ptrs` (host) into the device array `dst` with kernel launches on
 // `hip_stream` (the values travel as kernel arguments: no copy from host memory, no allocation).
 int launch_put_ptrs(void* dst, void* const* ptrs, int64_t n, void* hip_stream);

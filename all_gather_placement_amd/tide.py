@@ -26,6 +26,7 @@ TIDE_AG_SDMA = 1
 TIDE_AG_COPY2D = 2
 TIDE_RS_MAX_WGS_PER_CU = 64
 TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS = 8
+TIDE_NOALLOC_MAX_PTRS = 65536
 
 
 def tide_rs_cu_exclusive(items_per_workgroup: int) -> int:
@@ -88,6 +89,7 @@ def load_library(path: str | None = None):
         "tide_layout_param": (i32, [vp, i32, P_i64, P_i64, P_i64, P_i64]),
         "tide_layout_segment": (i32, [vp, i32, i32, P_i64, P_i64, P_i64, P_i64]),
         "tide_rs_bf16_to_fp32": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]),
+        "tide_rs_bf16_to_fp32_noalloc": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]),
         "tide_ag_place": (i32, [vp, vp, ctypes.POINTER(vp), i32, i32, vp]),
         "tide_layout_copy_rs_items": (i32, [vp, i64, i64, P_i64]),
         "tide_layout_copy_ag_items": (i32, [vp, i64, i64, P_i64]),
@@ -187,6 +189,25 @@ def tide_rs_bf16_to_fp32(layout: int, grads, shards, cu_budget: int = 0, stream=
     s_arr = (ctypes.c_void_p * max(len(s_list), 1))(*s_list)
     _check(lib.tide_rs_bf16_to_fp32(layout, C, g_arr, s_arr, int(cu_budget), _stream_handle(stream)),
            "tide_rs_bf16_to_fp32")
+
+
+def tide_rs_bf16_to_fp32_noalloc(layout: int, grads, shards, cu_budget: int = 0, stream=None):
+    """As tide_rs_bf16_to_fp32, allocating nothing: the address table goes into the library's fixed
+    per-device scratch array (at most TIDE_NOALLOC_MAX_PTRS = C*P + R pointers); the layout must have
+    been prepared on the current device.  Calls that overlap on one device race on that array."""
+    lib = load_library()
+    _expect_counts(layout, "tide_rs_bf16_to_fp32_noalloc", rows=grads, per_rank=shards)
+    C = len(grads)
+    flat = [_ptr(g) for row in grads for g in row]
+    n = len(flat) + len(shards)
+    if n > TIDE_NOALLOC_MAX_PTRS:
+        raise TideError(TIDE_ERR_INVALID, "tide_rs_bf16_to_fp32_noalloc", 0,
+                        f"C*P + R = {n} pointers exceed the scratch table's {TIDE_NOALLOC_MAX_PTRS}")
+    g_arr = (ctypes.c_void_p * max(len(flat), 1))(*flat)
+    s_list = [_ptr(s) for s in shards]
+    s_arr = (ctypes.c_void_p * max(len(s_list), 1))(*s_list)
+    _check(lib.tide_rs_bf16_to_fp32_noalloc(layout, C, g_arr, s_arr, int(cu_budget), _stream_handle(stream)),
+           "tide_rs_bf16_to_fp32_noalloc")
 
 
 def tide_ag_place(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0, stream=None):

@@ -246,6 +246,28 @@ tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, con
                                        float* const* shards, int32_t cu_budget, void* stream);
 
 /*
+ * Allocation-free reduce-scatter, for callers that cannot allocate device memory: code running
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   Arguments and result: exactly those of tide_rs_bf16_to_fp32 (same kernels, same launch forms,
+ *   bit-identical shards).
+ *   Scratch: the call's table of buffer addresses (C*P + R pointers) is written, by a small kernel
+ *   on `stream`, into a fixed device array of TIDE_NOALLOC_MAX_PTRS pointers (512 KiB) that the
+ *   library holds on each device it runs on until the process ends, instead of the layout's
+ *   allocated ring of tables.  The call makes no hipMalloc, hipFree, hipHostMalloc or copy from host
+ *   memory; it only launches kernels (host bookkeeping aside).  The table is rewritten in full by
+ *   every call, so nothing needs clearing between calls.
+ *   Concurrency: every call on a device shares that device's array, so calls that may overlap on one
+ *   device (other streams, other threads) race on it; calls on one stream are ordered.
+ *   Requirements: the layout has been prepared on the current device (tide_layout_prepare, which
+ *   allocates its device tables); C*P + R <= TIDE_NOALLOC_MAX_PTRS.
+ * Errors: those of tide_rs_bf16_to_fp32; TIDE_ERR_INVALID also when C*P + R exceeds
+ * TIDE_NOALLOC_MAX_PTRS or the layout was not prepared on the current device (no work enqueued).
+ */
+#define TIDE_NOALLOC_MAX_PTRS 65536
+tide_status tide_rs_bf16_to_fp32_noalloc(const tide_layout* layout, int32_t C, const void* const* grads,
+                                         float* const* shards, int32_t cu_budget, void* stream);
+
+/*
  * Prepared calls.  A training step issues the same collectives on the same buffers every step
  * (FSDP2 keeps its gradient, shard and stage buffers for the whole run), so the argument checks
  * and the device table of buffer addresses can be done once.  tide_*_prepare takes exactly the

@@ -41,6 +41,10 @@ int rs_cu_static_lds(int*) {
   std::fprintf(stderr, "rs_cu_static_lds reached in a host-only check\n");
   std::abort();
 }
+int noalloc_scratch(int, void**, int64_t*) {
+  std::fprintf(stderr, "noalloc_scratch reached in a host-only check\n");
+  std::abort();
+}
 int launch_put_ptrs(void*, void* const*, int64_t, void*) {
   std::fprintf(stderr, "launch_put_ptrs reached in a host-only check\n");
   std::abort();
@@ -139,6 +143,14 @@ int main() {
   float* sh2[4];
   for (int r = 0; r < 4; ++r) sh2[r] = reinterpret_cast<float*>(base + (uintptr_t(1) << 20) * (r + 1));
   CHECK(tide_rs_slots_bf16_to_fp32(L, 2, sl, sh2, 0, nullptr) == TIDE_ERR_INVALID);  // odd slot address
+  // the allocation-free RS applies the same checks, and refuses a pointer table beyond its scratch
+  CHECK(tide_rs_bf16_to_fp32_noalloc(L, 1, g, sh, 0, nullptr) == TIDE_ERR_INVALID);  // shard inside a gradient
+  CHECK(tide_rs_bf16_to_fp32_noalloc(L, 0, g, sh2, 0, nullptr) == TIDE_ERR_INVALID);
+  {
+    // C = TIDE_NOALLOC_MAX_PTRS contributors (all aliasing one valid gradient) + R shards: one too many
+    std::vector<const void*> many(TIDE_NOALLOC_MAX_PTRS, g[0]);
+    CHECK(tide_rs_bf16_to_fp32_noalloc(L, TIDE_NOALLOC_MAX_PTRS, many.data(), sh2, 0, nullptr) == TIDE_ERR_INVALID);
+  }
   // prepared calls apply the same checks, and leave *out untouched
   tide_call* call = nullptr;
   CHECK(tide_rs_prepare(L, 1, g, sh, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
