@@ -8,14 +8,18 @@ from .tide import (  # noqa: F401
     TIDE_AG_COPY2D,
     TIDE_AG_KERNEL,
     TIDE_AG_SDMA,
-    TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS,
-    TIDE_RS_MAX_WGS_PER_CU,
+    TIDE_CU_EXCLUSIVE_MAX_ITEMS,
+    TIDE_LAUNCH_BOUNDED,
+    TIDE_LAUNCH_CU_EXCLUSIVE,
+    TIDE_LAUNCH_DEFAULT,
+    TIDE_LAUNCH_PER_CU_CAP,
+    TIDE_MAX_WGS_PER_CU,
+    Launch,
     Layout,
     TideError,
     library_path,
     load_library,
     BoundCall,
-    tide_ag_cu_exclusive,
     tide_ag_place,
     tide_ag_prepare,
     tide_call_destroy,
@@ -24,7 +28,6 @@ from .tide import (  # noqa: F401
     tide_rs_bf16_to_fp32,
     tide_rs_bf16_to_fp32_noalloc,
     TIDE_NOALLOC_MAX_PTRS,
-    tide_rs_cu_exclusive,
     tide_rs_launch_shape,
     tide_rs_prepare,
     tide_rs_slots_bf16_to_fp32,

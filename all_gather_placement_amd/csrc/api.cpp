@@ -19,11 +19,8 @@
 namespace tide {
 namespace {
 
-// Smallest RS cu_budget: the per-CU caps -1 .. -TIDE_RS_MAX_WGS_PER_CU, then the CU-exclusive modes.
-constexpr int32_t kRsMinBudget = TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS);
-static_assert(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS == kRsCuMaxItems && TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS == kAgCuMaxItems,
-              "header and kernels agree on the widest workgroup");
-static_assert(TIDE_AG_CU_EXCLUSIVE(3) == TIDE_RS_CU_EXCLUSIVE(3), "one encoding for both collectives");
+static_assert(TIDE_CU_EXCLUSIVE_MAX_ITEMS == 2 * kRsCuMaxGroups && rs_cu_items_ok(4, 2) && !rs_cu_items_ok(5, 2),
+              "header and kernels agree on the widest CU-exclusive RS workgroup");
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -66,7 +63,8 @@ struct Request {
   Kind kind = kRs;
   int32_t C = 0;          // contributors (RS kinds)
   int32_t mode = TIDE_AG_KERNEL;
-  int32_t cu_budget = 0;
+  int32_t form = TIDE_LAUNCH_DEFAULT;  // launch form and count (include/tide.h tide_launch_form)
+  int32_t count = 0;
   bool vec = true;        // every base pointer 16-byte aligned
   void* stage = nullptr;  // AG stage / packed slot
   // Device pointers the kernels read, host copy:
@@ -75,15 +73,16 @@ struct Request {
 };
 
 tide_status validate_rs(const tide_layout* L, int32_t C, const void* const* grads, float* const* shards,
-                        int32_t cu_budget, Request* q) {
-  if (L == nullptr || grads == nullptr || shards == nullptr || C < 1 || cu_budget < kRsMinBudget)
+                        int32_t form, int32_t count, Request* q) {
+  if (L == nullptr || grads == nullptr || shards == nullptr || C < 1 || !rs_launch_ok(C, form, count))
     return TIDE_ERR_INVALID;
   const int32_t P = L->P, R = L->R;
   const int64_t S = L->S;
   if (int64_t(C) * P > (int64_t(1) << 24)) return TIDE_ERR_INVALID;
   q->kind = kRs;
   q->C = C;
-  q->cu_budget = cu_budget;
+  q->form = form;
+  q->count = count;
   q->vec = true;
   std::vector<Range> ins, outs;
   ins.reserve(size_t(C) * P);
@@ -111,15 +110,16 @@ tide_status validate_rs(const tide_layout* L, int32_t C, const void* const* grad
 }
 
 tide_status validate_rs_slots(const tide_layout* L, int32_t C, const void* const* slots, float* const* shards,
-                              int32_t cu_budget, Request* q) {
-  if (L == nullptr || slots == nullptr || shards == nullptr || C < 1 || cu_budget < kRsMinBudget)
+                              int32_t form, int32_t count, Request* q) {
+  if (L == nullptr || slots == nullptr || shards == nullptr || C < 1 || !rs_launch_ok(C, form, count))
     return TIDE_ERR_INVALID;
   if (C > (1 << 24)) return TIDE_ERR_INVALID;
   const int32_t R = L->R;
   const int64_t S = L->S;
   q->kind = kRsSlots;
   q->C = C;
-  q->cu_budget = cu_budget;
+  q->form = form;
+  q->count = count;
   q->vec = true;
   std::vector<Range> ins, outs;
   if (S > 0) {
@@ -144,17 +144,19 @@ tide_status validate_rs_slots(const tide_layout* L, int32_t C, const void* const
 // AG placement (pack = false: stage -> params) and Slot-Reuse packing (pack = true: params ->
 // slot) share one layout of arguments: a stage/slot of R*S bf16 and P per-parameter tensors.
 tide_status validate_ag(const tide_layout* L, const void* stage, void* const* params, int32_t mode,
-                        int32_t cu_budget, bool pack, Request* q) {
+                        int32_t form, int32_t count, bool pack, Request* q) {
   if (L == nullptr || params == nullptr) return TIDE_ERR_INVALID;
   if (!pack && mode != TIDE_AG_KERNEL && mode != TIDE_AG_SDMA && mode != TIDE_AG_COPY2D) return TIDE_ERR_INVALID;
-  // negative budgets: only the CU-exclusive launch of the kernel (placement or packing)
-  if (cu_budget < 0 && (cu_exclusive_items(cu_budget) == 0 || (!pack && mode != TIDE_AG_KERNEL))) return TIDE_ERR_INVALID;
+  // launch forms shape the kernel only: the DMA modes take the default
+  if (!ag_launch_ok(form, count) || (!pack && mode != TIDE_AG_KERNEL && form != TIDE_LAUNCH_DEFAULT))
+    return TIDE_ERR_INVALID;
   const int32_t P = L->P, R = L->R;
   const int64_t stage_n = int64_t(R) * L->S;
   if (stage_n > 0 && (stage == nullptr || !aligned(stage, 2))) return TIDE_ERR_INVALID;
   q->kind = pack ? kPack : kAg;
   q->mode = pack ? TIDE_AG_KERNEL : mode;
-  q->cu_budget = cu_budget;
+  q->form = form;
+  q->count = count;
   q->vec = stage_n == 0 || aligned(stage, 16);
   q->stage = const_cast<void*>(stage);
   std::vector<Range> stage_r, tensors;
@@ -246,17 +248,17 @@ int ensure_dma(DeviceState* st) {
 // Enqueueing validated work
 // ---------------------------------------------------------------------------------------------
 
-// Launch plan for `count` work items: cu_budget <= 0 = one item per workgroup in one launch;
-// B > 0 = grids of at most `max_wgs` workgroups, each taking `bounded_items` items and exiting
-// (bounded_items 0: one launch, workgroups walk every item).
+// Launch plan for `count` work items: bounded = grids of at most `max_wgs` workgroups, each taking
+// `bounded_items` items and exiting (bounded_items 0: one launch, workgroups walk every item);
+// otherwise one launch of single-item workgroups (or kPersistentWorkgroups walking them).
 struct Plan {
   int grid;
   int items;
   int64_t per_launch;
 };
 
-Plan plan_for(int64_t count, int32_t cu_budget, int64_t max_wgs, int bounded_items) {
-  if (cu_budget <= 0) {
+Plan plan_for(int64_t count, bool bounded, int64_t max_wgs, int bounded_items) {
+  if (!bounded) {
     const int64_t cap = kPersistentWorkgroups > 0 ? kPersistentWorkgroups : (int64_t(1) << 30);
     const int64_t g = std::min<int64_t>(count, cap);
     const int items = int((count + g - 1) / g);
@@ -272,19 +274,20 @@ Plan plan_for(int64_t count, int32_t cu_budget, int64_t max_wgs, int bounded_ite
 int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& q, void* const* dev_table,
                     hipStream_t hs) {
   const void* const* tbl = const_cast<const void* const*>(dev_table);
+  const bool bounded = q.form == TIDE_LAUNCH_BOUNDED;
   int e = hipSuccess;
   if (q.kind == kRs || q.kind == kRsSlots) {
     const int64_t count = int64_t(L->rs_chunks.size());
     const bool flat = q.kind == kRsSlots;
-    if (const int w = rs_cu_launch_items(q.C, q.cu_budget)) {
-      // one launch of CU-exclusive workgroups of w items (the table's order: items are rank-major)
-      return launch_rs_cu(st->rs, count, w, tbl, flat ? 1 : L->P, q.C, L->S, flat, q.vec, rs_cu_launch_lds(*st), hs);
+    if (const int n = rs_cu_launch_items(q.C, q.form, q.count)) {
+      // one launch of CU-exclusive workgroups of n items (the table's order: items are rank-major)
+      return launch_rs_cu(st->rs, count, rs_cu_groups(n), rs_cu_items_per_group(n), tbl, flat ? 1 : L->P, q.C, L->S,
+                          flat, q.vec, cu_exclusive_lds(*st), hs);
     }
-    const int64_t rs_wgs = int64_t(q.cu_budget) * kBudgetThreads / kThreads;
-    const Plan plan = plan_for(count, q.cu_budget, rs_wgs, kRsBoundedItems);
-    // Unbounded launches cap the RS workgroups per CU (by C, or -cu_budget); bounded ones are
-    // capped by the budget.
-    const int lds = rs_launch_lds(*st, q.C, q.cu_budget);
+    const int64_t rs_wgs = bounded ? int64_t(q.count) * kBudgetThreads / kThreads : 0;
+    const Plan plan = plan_for(count, bounded, rs_wgs, kRsBoundedItems);
+    // single-item workgroups under a per-CU cap, or bounded launches (capped by their budget)
+    const int lds = rs_launch_lds(*st, q.C, q.form, q.count);
     for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
       const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
       e = launch_rs(st->rs, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, tbl, flat ? 1 : L->P, q.C,
@@ -293,17 +296,17 @@ int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& 
     return e;
   }
   const int64_t count = int64_t(L->ag_chunks.size());
-  if (const int w = cu_exclusive_items(q.cu_budget)) {
+  if (q.form == TIDE_LAUNCH_CU_EXCLUSIVE) {
     if (count > 0)
-      e = launch_ag_cu(st->ag, count, w, q.stage, tbl, q.kind == kPack, q.vec, ag_cu_launch_lds(*st), hs);
+      e = launch_ag_cu(st->ag, count, q.count, q.stage, tbl, q.kind == kPack, q.vec, cu_exclusive_lds(*st), hs);
     if (e == hipSuccess && q.kind == kPack)
       e = launch_fill_zero(st->slot_pad, int64_t(L->slot_pad_items.size()), q.stage, hs);
     return e;
   }
-  const int64_t ag_wgs = int64_t(q.cu_budget) * kBudgetThreads / kAgThreads;
-  const Plan plan = plan_for(count, q.cu_budget, ag_wgs, kAgBoundedItems);
+  const int64_t ag_wgs = bounded ? int64_t(q.count) * kBudgetThreads / kAgThreads : 0;
+  const Plan plan = plan_for(count, bounded, ag_wgs, kAgBoundedItems);
   // Few workgroups per CU (small budgets): each loads two items at a time.
-  const int batch = q.cu_budget > 0 && ag_wgs <= int64_t(kAgBatchMaxWgsPerCu) * std::max(st->cus, 1) ? 2 : 1;
+  const int batch = bounded && ag_wgs <= int64_t(kAgBatchMaxWgsPerCu) * std::max(st->cus, 1) ? 2 : 1;
   for (int64_t first = 0; first < count && e == hipSuccess; first += plan.per_launch) {
     const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
     e = launch_ag(st->ag, first, n, int(std::min<int64_t>(plan.grid, n)), plan.items, batch, q.stage, tbl,
@@ -510,38 +513,41 @@ tide_status prepare(const tide_layout* L, tide::Request&& q, tide_call** out) {
 extern "C" {
 
 tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* grads,
-                                 float* const* shards, int32_t cu_budget, void* stream) {
+                                 float* const* shards, int32_t launch_form, int32_t launch_count, void* stream) {
   tide::Request q;
-  const tide_status s = tide::validate_rs(layout, C, grads, shards, cu_budget, &q);
+  const tide_status s = tide::validate_rs(layout, C, grads, shards, launch_form, launch_count, &q);
   return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
 }
 
 tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params, int32_t mode,
-                          int32_t cu_budget, void* stream) {
+                          int32_t launch_form, int32_t launch_count, void* stream) {
   tide::Request q;
-  const tide_status s = tide::validate_ag(layout, stage, params, mode, cu_budget, /*pack=*/false, &q);
+  const tide_status s =
+      tide::validate_ag(layout, stage, params, mode, launch_form, launch_count, /*pack=*/false, &q);
   return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
 }
 
-tide_status tide_slot_pack(const tide_layout* layout, const void* const* grads, void* slot, int32_t cu_budget,
-                           void* stream) {
+tide_status tide_slot_pack(const tide_layout* layout, const void* const* grads, void* slot, int32_t launch_form,
+                           int32_t launch_count, void* stream) {
   tide::Request q;
-  const tide_status s = tide::validate_ag(layout, slot, const_cast<void* const*>(grads), TIDE_AG_KERNEL, cu_budget,
-                                          /*pack=*/true, &q);
+  const tide_status s = tide::validate_ag(layout, slot, const_cast<void* const*>(grads), TIDE_AG_KERNEL, launch_form,
+                                          launch_count, /*pack=*/true, &q);
   return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
 }
 
 tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* slots,
-                                       float* const* shards, int32_t cu_budget, void* stream) {
+                                       float* const* shards, int32_t launch_form, int32_t launch_count,
+                                       void* stream) {
   tide::Request q;
-  const tide_status s = tide::validate_rs_slots(layout, C, slots, shards, cu_budget, &q);
+  const tide_status s = tide::validate_rs_slots(layout, C, slots, shards, launch_form, launch_count, &q);
   return s != TIDE_OK ? s : tide::run_now(layout, q, stream);
 }
 
 tide_status tide_rs_bf16_to_fp32_noalloc(const tide_layout* layout, int32_t C, const void* const* grads,
-                                         float* const* shards, int32_t cu_budget, void* stream) {
+                                         float* const* shards, int32_t launch_form, int32_t launch_count,
+                                         void* stream) {
   tide::Request q;
-  tide_status s = tide::validate_rs(layout, C, grads, shards, cu_budget, &q);
+  tide_status s = tide::validate_rs(layout, C, grads, shards, launch_form, launch_count, &q);
   if (s != TIDE_OK) return s;
   if (int64_t(q.table.size()) > int64_t(TIDE_NOALLOC_MAX_PTRS)) return TIDE_ERR_INVALID;
   if (!tide::needs_kernels(layout, q)) return TIDE_OK;
@@ -564,31 +570,32 @@ tide_status tide_rs_bf16_to_fp32_noalloc(const tide_layout* layout, int32_t C, c
 }
 
 tide_status tide_rs_prepare(const tide_layout* layout, int32_t C, const void* const* grads, float* const* shards,
-                            int32_t cu_budget, tide_call** out) {
+                            int32_t launch_form, int32_t launch_count, tide_call** out) {
   tide::Request q;
-  const tide_status s = tide::validate_rs(layout, C, grads, shards, cu_budget, &q);
+  const tide_status s = tide::validate_rs(layout, C, grads, shards, launch_form, launch_count, &q);
   return s != TIDE_OK ? s : prepare(layout, std::move(q), out);
 }
 
 tide_status tide_ag_prepare(const tide_layout* layout, const void* stage, void* const* params, int32_t mode,
-                            int32_t cu_budget, tide_call** out) {
+                            int32_t launch_form, int32_t launch_count, tide_call** out) {
   tide::Request q;
-  const tide_status s = tide::validate_ag(layout, stage, params, mode, cu_budget, /*pack=*/false, &q);
+  const tide_status s =
+      tide::validate_ag(layout, stage, params, mode, launch_form, launch_count, /*pack=*/false, &q);
   return s != TIDE_OK ? s : prepare(layout, std::move(q), out);
 }
 
 tide_status tide_slot_pack_prepare(const tide_layout* layout, const void* const* grads, void* slot,
-                                   int32_t cu_budget, tide_call** out) {
+                                   int32_t launch_form, int32_t launch_count, tide_call** out) {
   tide::Request q;
-  const tide_status s = tide::validate_ag(layout, slot, const_cast<void* const*>(grads), TIDE_AG_KERNEL, cu_budget,
-                                          /*pack=*/true, &q);
+  const tide_status s = tide::validate_ag(layout, slot, const_cast<void* const*>(grads), TIDE_AG_KERNEL, launch_form,
+                                          launch_count, /*pack=*/true, &q);
   return s != TIDE_OK ? s : prepare(layout, std::move(q), out);
 }
 
 tide_status tide_rs_slots_prepare(const tide_layout* layout, int32_t C, const void* const* slots,
-                                  float* const* shards, int32_t cu_budget, tide_call** out) {
+                                  float* const* shards, int32_t launch_form, int32_t launch_count, tide_call** out) {
   tide::Request q;
-  const tide_status s = tide::validate_rs_slots(layout, C, slots, shards, cu_budget, &q);
+  const tide_status s = tide::validate_rs_slots(layout, C, slots, shards, launch_form, launch_count, &q);
   return s != TIDE_OK ? s : prepare(layout, std::move(q), out);
 }
 
@@ -611,24 +618,28 @@ tide_status tide_call_launch(const tide_call* call, void* stream) {
   return e == hipSuccess ? TIDE_OK : tide::hip_fail(e);
 }
 
-tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads, int32_t* item_outputs,
-                                 int32_t* lds_bytes) {
-  if (C < 1 || cu_budget < tide::kRsMinBudget || threads == nullptr || item_outputs == nullptr ||
-      lds_bytes == nullptr)
-    return TIDE_ERR_INVALID;
+tide_status tide_rs_launch_shape(int32_t C, int32_t launch_form, int32_t launch_count, int32_t* threads,
+                                 int32_t* items_per_workgroup, int32_t* item_outputs, int32_t* lds_bytes) {
+  if (C < 1 || !tide::rs_launch_ok(C, launch_form, launch_count)) return TIDE_ERR_INVALID;
   tide::DeviceState st;
   int dev = 0;
   int e = hipGetDevice(&dev);
   if (e == hipSuccess) e = tide::rs_device_info(dev, &st);
   if (e != hipSuccess) return tide::hip_fail(e);
-  *item_outputs = int32_t(tide::kRsChunk);
-  if (const int w = tide::rs_cu_launch_items(C, cu_budget)) {
-    *threads = tide::kThreads * w;
-    *lds_bytes = st.rs_static_lds_cu + tide::rs_cu_launch_lds(st);
-    return TIDE_OK;
+  int th = tide::kThreads, items = 1, lds = 0;
+  if (const int n = tide::rs_cu_launch_items(C, launch_form, launch_count)) {
+    th = tide::kThreads * tide::rs_cu_groups(n);
+    items = n;
+    lds = tide::cu_exclusive_lds(st);
+  } else {
+    if (launch_form == TIDE_LAUNCH_BOUNDED) items = tide::kRsBoundedItems;
+    lds = (C <= tide::kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt) +
+          tide::rs_launch_lds(st, C, launch_form, launch_count);
   }
-  *threads = tide::kThreads;
-  *lds_bytes = (C <= tide::kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt) + tide::rs_launch_lds(st, C, cu_budget);
+  if (threads) *threads = th;
+  if (items_per_workgroup) *items_per_workgroup = items;
+  if (item_outputs) *item_outputs = int32_t(tide::kRsChunk);
+  if (lds_bytes) *lds_bytes = lds;
   return TIDE_OK;
 }
 

@@ -390,114 +390,178 @@ __device__ __forceinline__ void load_bases(const unsigned short* const* __restri
   }
 }
 
-// CU-exclusive RS kernel: one launch over all work items in workgroups of W = blockDim.x / 128
-// groups of 128 threads (W <= kRsCuMaxItems); group g of workgroup slot s takes item s*W + g, the
-// same per-item work as rs_kernel.  The host gives every workgroup the largest local memory one may
-// request, so a CU holds a single RS workgroup and is empty again whenever it exits: a concurrent
-// kernel's workgroup waiting for a whole CU (a one-wave GEMM's, for instance) takes it within one
-// RS workgroup lifetime, while the RS itself runs as one launch with W items resident per CU.
-// There is one workgroup barrier, outside every per-group branch: groups with a full item leave
-// their sums in their own exchange slot and store them after it; the others finish before it.
+// One RS work item of a CU-exclusive workgroup's group (the per-item work of rs_kernel): a full item
+// leaves its sums in the group's exchange slot `xfer` and returns the destination to store them to
+// after the workgroup barrier; any other item is written directly and returns nullptr.
 template <int CT, bool VEC, bool FLAT>
-__global__ __launch_bounds__(kThreads * kRsCuMaxItems) void rs_cu_kernel(const RsChunk* __restrict__ chunks,
-                                                                         int64_t count,
-                                                                         void* const* __restrict__ ptrs,
-                                                                         int32_t P, int32_t C, int64_t S) {
-#if TIDE_RS_WIDE
-  __shared__ f32x4 xfer_all[kRsCuMaxItems][2 * kThreads];
-#endif
-  const int W = static_cast<int>(blockDim.x) / kThreads;
-  const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kThreads);
-  const int tid = static_cast<int>(threadIdx.x) % kThreads;
+__device__ __forceinline__ float* rs_cu_item(const RsChunk* __restrict__ chunks, int64_t item,
+                                             void* const* __restrict__ ptrs, int32_t P, int32_t C, int64_t S,
+                                             f32x4* xfer, int tid) {
   const unsigned short* const* __restrict__ gptr = reinterpret_cast<const unsigned short* const*>(ptrs);
   float* const* __restrict__ sptr = reinterpret_cast<float* const*>(ptrs + static_cast<int64_t>(C) * P);
   const int nc = CT > 0 ? CT : C;
+  RsChunk ch = chunks[item];
+  if (FLAT) {
+    ch.src = static_cast<int64_t>(ch.r) * S + ch.dst;
+    ch.p = 0;
+  }
+  float* dst = sptr[ch.r] + ch.dst;
+  const int n = ch.nvalid;
+  float* full_dst = nullptr;
+
+  if (VEC) {
+    const int head = min(n, static_cast<int>((-ch.src) & 7));
+    const int nb = (n - head) >> 3;
+    const int ng = 2 * nb;
+    const int tail = (n - head) & 7;
+    const bool dst16 = ((ch.dst + head) & 3) == 0;
+    if constexpr (CT > 0) {
+      const unsigned short* src[CT];
+      load_bases<CT>(gptr, P, ch.p, src);
+#pragma unroll
+      for (int c = 0; c < CT; ++c) src[c] += ch.src;
+#if TIDE_RS_WIDE
+      if (full_item(ch)) {
+        u32x4 x[CT];
+        float a[8];
+        full_item_load<CT>(src, tid, x);
+        full_item_sums<CT>(x, a);
+        full_item_put(a, xfer, tid);
+        full_dst = dst;
+      } else
+#endif
+      {
+        if (tid < head) store_hbm(dst + tid, sum1<CT>(src, nc, tid));
+        constexpr int NQ = TIDE_RS_NQ;
+        int q = tid;
+        for (; q + (NQ - 1) * kThreads < ng; q += NQ * kThreads)
+          sum_groups<CT, NQ>(src, static_cast<uint32_t>(head + 4 * q), dst, dst16);
+        for (; q < ng; q += kThreads) sum_groups<CT, 1>(src, static_cast<uint32_t>(head + 4 * q), dst, dst16);
+        if (tid < tail) {
+          const int64_t k = head + 8 * static_cast<int64_t>(nb) + tid;
+          store_hbm(dst + k, sum1<CT>(src, nc, k));
+        }
+      }
+    } else {
+#if TIDE_RS_WIDE
+      if (full_item(ch)) {
+        float a[8];
+        full_item_rt_sums(ptrs, P, ch, nc, tid, a);
+        full_item_put(a, xfer, tid);
+        full_dst = dst;
+      } else
+#endif
+      {
+        for (int i = tid; i < head; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
+        for (int q = tid; q < ng; q += kThreads) {
+          const int64_t k = head + 4 * static_cast<int64_t>(q);
+          sum_group_rt(gptr, P, ch.p, nc, ch.src + k, dst + k, dst16);
+        }
+        for (int i = tid; i < tail; i += kThreads) {
+          const int64_t k = head + 8 * static_cast<int64_t>(nb) + i;
+          store_hbm(dst + k, sum1_rt(gptr, P, ch.p, nc, ch.src + k));
+        }
+      }
+    }
+  } else {
+    for (int i = tid; i < n; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
+  }
+  // padding rows of this rank's slice (a full item has none)
+  for (int i = tid; i < ch.npad; i += kThreads) store_hbm(dst + n + i, 0.0f);
+  return full_dst;
+}
+
+// CU-exclusive RS kernel: one launch over all work items in workgroups of W = blockDim.x / 128
+// groups of 128 threads (W <= kRsCuMaxGroups), each group taking KI consecutive items; group g of
+// workgroup slot s takes items (s*W + g)*KI .. +KI-1, with the same per-item work as rs_kernel.  The
+// host gives every workgroup the largest local memory one may request (here all of it dynamic: the
+// W*KI exchange slots of 4 KiB and the rest unused), so a CU holds a single RS workgroup and is empty
+// again whenever it exits: a concurrent kernel's workgroup waiting for a whole CU (a one-wave GEMM's,
+// for instance) takes it within one RS workgroup lifetime, while the RS itself runs as one launch
+// with W*KI items resident per CU.  With KI > 1 (few contributors, whose items carry few bytes), a
+// group whose KI items are all full issues every load of all of them before its first sum, so the
+// CU keeps as many bytes in flight as with more contributors.  There is one workgroup barrier,
+// outside every per-group branch: full items leave their sums in their exchange slots and are
+// stored after it; the others are finished before it.
+template <int CT, int KI, bool VEC, bool FLAT>
+__global__ __launch_bounds__(kThreads * kRsCuMaxGroups) void rs_cu_kernel(const RsChunk* __restrict__ chunks,
+                                                                          int64_t count,
+                                                                          void* const* __restrict__ ptrs,
+                                                                          int32_t P, int32_t C, int64_t S) {
+  extern __shared__ f32x4 xfer_dyn[];  // W*KI exchange slots of 2*kThreads vectors
+  const int W = static_cast<int>(blockDim.x) / kThreads;
+  const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kThreads);
+  const int tid = static_cast<int>(threadIdx.x) % kThreads;
   // workgroup slots, one per grid position: each XCD walks one contiguous range of them
   int64_t slot = blockIdx.x;
   if (TIDE_RS_XCD_REMAP != 0) {
     const int64_t n = gridDim.x, x = slot % kXcds, i = slot / kXcds;
     slot = x * (n / kXcds) + min<int64_t>(x, n % kXcds) + i;
   }
-  const int64_t item = slot * W + grp;
-  float* full_dst = nullptr;  // set for a full item, stored after the barrier
-
-  if (item < count) {
-    RsChunk ch = chunks[item];
-    if (FLAT) {
-      ch.src = static_cast<int64_t>(ch.r) * S + ch.dst;
-      ch.p = 0;
-    }
-    float* dst = sptr[ch.r] + ch.dst;
-    const int n = ch.nvalid;
-
-    if (VEC) {
-      const int head = min(n, static_cast<int>((-ch.src) & 7));
-      const int nb = (n - head) >> 3;
-      const int ng = 2 * nb;
-      const int tail = (n - head) & 7;
-      const bool dst16 = ((ch.dst + head) & 3) == 0;
-      if constexpr (CT > 0) {
-        const unsigned short* src[CT];
-        load_bases<CT>(gptr, P, ch.p, src);
+  const int64_t first = (slot * W + grp) * KI;
+  f32x4* xfer = xfer_dyn + static_cast<int64_t>(grp) * KI * 2 * kThreads;
+  float* full_dst[KI];
 #pragma unroll
-        for (int c = 0; c < CT; ++c) src[c] += ch.src;
+  for (int k = 0; k < KI; ++k) full_dst[k] = nullptr;
+
+  bool done = false;
 #if TIDE_RS_WIDE
-        if (full_item(ch)) {
-          u32x4 x[CT];
-          float a[8];
-          full_item_load<CT>(src, tid, x);
-          full_item_sums<CT>(x, a);
-          full_item_put(a, xfer_all[grp], tid);
-          full_dst = dst;
-        } else
-#endif
-        {
-          if (tid < head) store_hbm(dst + tid, sum1<CT>(src, nc, tid));
-          constexpr int NQ = TIDE_RS_NQ;
-          int q = tid;
-          for (; q + (NQ - 1) * kThreads < ng; q += NQ * kThreads)
-            sum_groups<CT, NQ>(src, static_cast<uint32_t>(head + 4 * q), dst, dst16);
-          for (; q < ng; q += kThreads) sum_groups<CT, 1>(src, static_cast<uint32_t>(head + 4 * q), dst, dst16);
-          if (tid < tail) {
-            const int64_t k = head + 8 * static_cast<int64_t>(nb) + tid;
-            store_hbm(dst + k, sum1<CT>(src, nc, k));
-          }
+  if constexpr (KI > 1 && CT > 0 && VEC) {
+    // all KI items full: every load of every item in flight before the first sum
+    if (first + KI <= count) {
+      RsChunk ch[KI];
+      bool all_full = true;
+#pragma unroll
+      for (int k = 0; k < KI; ++k) {
+        ch[k] = chunks[first + k];
+        if (FLAT) {
+          ch[k].src = static_cast<int64_t>(ch[k].r) * S + ch[k].dst;
+          ch[k].p = 0;
         }
-      } else {
-#if TIDE_RS_WIDE
-        if (full_item(ch)) {
-          float a[8];
-          full_item_rt_sums(ptrs, P, ch, nc, tid, a);
-          full_item_put(a, xfer_all[grp], tid);
-          full_dst = dst;
-        } else
-#endif
-        {
-          for (int i = tid; i < head; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
-          for (int q = tid; q < ng; q += kThreads) {
-            const int64_t k = head + 4 * static_cast<int64_t>(q);
-            sum_group_rt(gptr, P, ch.p, nc, ch.src + k, dst + k, dst16);
-          }
-          for (int i = tid; i < tail; i += kThreads) {
-            const int64_t k = head + 8 * static_cast<int64_t>(nb) + i;
-            store_hbm(dst + k, sum1_rt(gptr, P, ch.p, nc, ch.src + k));
-          }
-        }
+        all_full = all_full && full_item(ch[k]);
       }
-    } else {
-      for (int i = tid; i < n; i += kThreads) store_hbm(dst + i, sum1_rt(gptr, P, ch.p, nc, ch.src + i));
+      if (all_full) {
+        const unsigned short* const* __restrict__ gptr = reinterpret_cast<const unsigned short* const*>(ptrs);
+        float* const* __restrict__ sptr = reinterpret_cast<float* const*>(ptrs + static_cast<int64_t>(C) * P);
+        u32x4 x[KI][CT];
+#pragma unroll
+        for (int k = 0; k < KI; ++k) {
+          const unsigned short* src[CT];
+          load_bases<CT>(gptr, P, ch[k].p, src);
+#pragma unroll
+          for (int c = 0; c < CT; ++c) src[c] += ch[k].src;
+          full_item_load<CT>(src, tid, x[k]);
+          full_dst[k] = sptr[ch[k].r] + ch[k].dst;
+        }
+#pragma unroll
+        for (int k = 0; k < KI; ++k) {
+          float a[8];
+          full_item_sums<CT>(x[k], a);
+          full_item_put(a, xfer + k * 2 * kThreads, tid);
+        }
+        done = true;
+      }
     }
-    // padding rows of this rank's slice (a full item has none)
-    for (int i = tid; i < ch.npad; i += kThreads) store_hbm(dst + n + i, 0.0f);
+  }
+#endif
+  if (!done) {
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+      if (first + k < count)
+        full_dst[k] = rs_cu_item<CT, VEC, FLAT>(chunks, first + k, ptrs, P, C, S, xfer + k * 2 * kThreads, tid);
+    }
   }
 
 #if TIDE_RS_WIDE
-  __syncthreads();  // every group's exchange slot is written
-  if (full_dst != nullptr) {
-    if (CT > 0)
-      full_item_store(xfer_all[grp], full_dst, tid);
-    else
-      full_item_rt_store(xfer_all[grp], full_dst, tid);
+  __syncthreads();  // every group's exchange slots are written
+#pragma unroll
+  for (int k = 0; k < KI; ++k) {
+    if (full_dst[k] != nullptr) {
+      if (CT > 0)
+        full_item_store(xfer + k * 2 * kThreads, full_dst[k], tid);
+      else
+        full_item_rt_store(xfer + k * 2 * kThreads, full_dst[k], tid);
+    }
   }
 #endif
 }
@@ -701,43 +765,61 @@ hipError_t launch_rs_c(const RsChunk* chunks, int64_t first, int64_t count, int 
   }
 }
 
-template <int CT, bool FLAT>
+template <int CT, int KI, bool FLAT>
 hipError_t launch_rs_cu_ct(const RsChunk* chunks, int64_t count, int grid, int threads, void* const* ptrs, int32_t P,
                            int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
   if (vec)
-    hipLaunchKernelGGL((rs_cu_kernel<CT, true, FLAT>), dim3(grid), dim3(threads), lds, s, chunks, count, ptrs, P, C, S);
+    hipLaunchKernelGGL((rs_cu_kernel<CT, KI, true, FLAT>), dim3(grid), dim3(threads), lds, s, chunks, count, ptrs, P,
+                       C, S);
   else
-    hipLaunchKernelGGL((rs_cu_kernel<CT, false, FLAT>), dim3(grid), dim3(threads), lds, s, chunks, count, ptrs, P, C,
-                       S);
+    hipLaunchKernelGGL((rs_cu_kernel<CT, KI, false, FLAT>), dim3(grid), dim3(threads), lds, s, chunks, count, ptrs, P,
+                       C, S);
   return hipGetLastError();
 }
 
-// The CU-exclusive kernel is compiled for the counts a layer group is reduced over most (C = 1, 2,
-// 4, 8); any other C takes its runtime-C form.
-template <bool FLAT>
-hipError_t launch_rs_cu_c(const RsChunk* chunks, int64_t count, int grid, int threads, void* const* ptrs, int32_t P,
-                          int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
-  switch (C) {
-    case 1: return launch_rs_cu_ct<1, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
-    case 2: return launch_rs_cu_ct<2, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
-    case 4: return launch_rs_cu_ct<4, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
-    case 8: return launch_rs_cu_ct<8, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
-    default: return launch_rs_cu_ct<0, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+// Items per group: 1 for every C; 2 for C <= 4, whose items carry few bytes (rs_cu_items_ok).
+template <int CT, bool FLAT>
+hipError_t launch_rs_cu_ki(int ki, const RsChunk* chunks, int64_t count, int grid, int threads, void* const* ptrs,
+                           int32_t P, int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
+  if constexpr (CT >= 1 && CT <= 4) {
+    if (ki == 2) return launch_rs_cu_ct<CT, 2, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
   }
+  if (ki != 1) return hipErrorInvalidValue;
+  return launch_rs_cu_ct<CT, 1, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+}
+
+// The CU-exclusive kernel is compiled for C = 1 .. kRsMaxCt; any other C takes its runtime-C form.
+template <bool FLAT>
+hipError_t launch_rs_cu_c(int ki, const RsChunk* chunks, int64_t count, int grid, int threads, void* const* ptrs,
+                          int32_t P, int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
+#define TIDE_RS_CU_CASE(N) \
+  case N: return launch_rs_cu_ki<N, FLAT>(ki, chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+  switch (C) {
+    TIDE_RS_CU_CASE(1) TIDE_RS_CU_CASE(2) TIDE_RS_CU_CASE(3) TIDE_RS_CU_CASE(4) TIDE_RS_CU_CASE(5)
+    TIDE_RS_CU_CASE(6) TIDE_RS_CU_CASE(7) TIDE_RS_CU_CASE(8) TIDE_RS_CU_CASE(9) TIDE_RS_CU_CASE(10)
+    TIDE_RS_CU_CASE(11) TIDE_RS_CU_CASE(12) TIDE_RS_CU_CASE(13) TIDE_RS_CU_CASE(14) TIDE_RS_CU_CASE(15)
+    TIDE_RS_CU_CASE(16)
+    default: return launch_rs_cu_ki<0, FLAT>(ki, chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
+  }
+#undef TIDE_RS_CU_CASE
 }
 
 }  // namespace
 
-int launch_rs_cu(const RsChunk* chunks, int64_t count, int items_per_wg, const void* const* dev_ptrs, int32_t P,
-                 int32_t C, int64_t S, bool flat, bool vec, int dyn_lds, void* hip_stream) {
-  if (items_per_wg < 1 || items_per_wg > kRsCuMaxItems || count < 1) return hipErrorInvalidValue;
-  const int64_t grid = (count + items_per_wg - 1) / items_per_wg;
+int launch_rs_cu(const RsChunk* chunks, int64_t count, int groups, int items_per_group, const void* const* dev_ptrs,
+                 int32_t P, int32_t C, int64_t S, bool flat, bool vec, int lds, void* hip_stream) {
+  if (groups < 1 || groups > kRsCuMaxGroups || !rs_cu_items_ok(C, items_per_group) || count < 1)
+    return hipErrorInvalidValue;
+  if (lds < rs_cu_xfer_bytes(groups, items_per_group)) return hipErrorInvalidValue;
+  const int64_t per_wg = int64_t(groups) * items_per_group;
+  const int64_t grid = (count + per_wg - 1) / per_wg;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   void* const* ptrs = const_cast<void* const*>(dev_ptrs);
-  const int threads = kThreads * items_per_wg;
-  if (flat) return launch_rs_cu_c<true>(chunks, count, int(grid), threads, ptrs, 1, C, S, vec, dyn_lds, s);
-  return launch_rs_cu_c<false>(chunks, count, int(grid), threads, ptrs, P, C, S, vec, dyn_lds, s);
+  const int threads = kThreads * groups;
+  if (flat)
+    return launch_rs_cu_c<true>(items_per_group, chunks, count, int(grid), threads, ptrs, 1, C, S, vec, lds, s);
+  return launch_rs_cu_c<false>(items_per_group, chunks, count, int(grid), threads, ptrs, P, C, S, vec, lds, s);
 }
 
 int launch_ag_cu(const AgChunk* chunks, int64_t count, int items_per_wg, void* stage, const void* const* dev_params,
@@ -770,13 +852,6 @@ int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int
   void* const* ptrs = const_cast<void* const*>(dev_ptrs);
   if (flat) return launch_rs_c<true>(chunks, first, count, grid, items_per_wg, ptrs, 1, C, S, vec, dyn_lds, s);
   return launch_rs_c<false>(chunks, first, count, grid, items_per_wg, ptrs, P, C, S, vec, dyn_lds, s);
-}
-
-int rs_cu_static_lds(int* static_lds) {
-  hipFuncAttributes attr;
-  const hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(&rs_cu_kernel<8, true, false>));
-  if (e == hipSuccess) *static_lds = static_cast<int>(attr.sharedSizeBytes);
-  return e;
 }
 
 int rs_lds_info(int device, int* lds_per_cu, int* static_lds_ct, int* static_lds_rt) {

@@ -111,7 +111,6 @@ int rs_device_info(int device, DeviceState* st) {
       rs_lds_info(device, &st->lds_per_cu, &st->rs_static_lds_ct, &st->rs_static_lds_rt));
   if (e == hipSuccess) e = hipDeviceGetAttribute(&st->lds_per_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&st->cus, hipDeviceAttributeMultiprocessorCount, device);
-  if (e == hipSuccess) e = static_cast<hipError_t>(rs_cu_static_lds(&st->rs_static_lds_cu));
   return e;
 }
 

@@ -7,6 +7,7 @@
 #include <mutex>
 #include <vector>
 
+#include "../../include/tide.h"
 #include "tide_internal.h"
 
 namespace tide {
@@ -58,57 +59,69 @@ struct DeviceState {
   int lds_per_wg = 0;       // largest local memory one workgroup may request (bytes)
   int rs_static_lds_ct = 0; // static local memory of the RS kernel, C <= kRsMaxCt
   int rs_static_lds_rt = 0; // static local memory of the RS kernel, C > kRsMaxCt
-  int rs_static_lds_cu = 0; // static local memory of the CU-exclusive RS kernel
   // Device address of the library's fixed pointer-table scratch array on this device (allocation-free
   // RS entry point), obtained once at set-up, and its size in pointers.
   void* scratch = nullptr;
   int64_t scratch_ptrs = 0;
 };
 
-// cu_budget values TIDE_RS_CU_EXCLUSIVE(W) (TIDE_AG_CU_EXCLUSIVE(W) for the placement kernel and the
-// packing): the number of items per CU-exclusive workgroup, else 0.
-inline int cu_exclusive_items(int cu_budget) {
-  const int w = -cu_budget - TIDE_RS_MAX_WGS_PER_CU;
-  return w >= 1 && w <= TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS ? w : 0;
+// Launch forms (include/tide.h tide_launch_form).
+//
+// TIDE_LAUNCH_DEFAULT for the RS with C contributors: CU-exclusive workgroups of 8 groups of 128
+// threads, each group keeping 2 items' loads in flight for C <= 3 (16 items) and 1 item for C >= 4
+// (8 items): the most items whose traffic, (2C + 4) KiB each, stays within the 160 KiB of a C = 8
+// workgroup, so no workgroup lives longer than one at C = 8.  Measured on MI355X (Llama-3.1-8B
+// shapes; HIP-event means): C = 1 / 2 / 3 / 4 / 5 / 6 / 7 / 8 stream 5.9 / 6.12 / 6.17 / 6.14 / 6.28 /
+// 6.32 / 6.34 / 6.30 TB/s, against 6.29 / 6.39 / 6.42 / 6.34 / 6.32 / 6.31 / 6.26 / 6.20 for
+// single-item workgroups under their best per-CU cap, which never empties a CU during the call: a
+// concurrent one-wave GEMM then waits for the whole RS (+236% at C = 4) instead of +7.9% (C = 4)
+// or +13.5% (C = 8, the Llama-3.1-70B group).
+constexpr int rs_default_items(int C) { return C <= 3 ? 2 * kRsCuMaxGroups : kRsCuMaxGroups; }
+
+// Groups per workgroup and items per group of a CU-exclusive RS workgroup taking n items.
+inline int rs_cu_groups(int n) { return n <= kRsCuMaxGroups ? n : kRsCuMaxGroups; }
+inline int rs_cu_items_per_group(int n) { return n <= kRsCuMaxGroups ? 1 : n / kRsCuMaxGroups; }
+
+// Whether (form, count) is a valid RS launch for C contributors.
+inline bool rs_launch_ok(int C, int form, int count) {
+  switch (form) {
+    case TIDE_LAUNCH_DEFAULT: return count == 0;
+    case TIDE_LAUNCH_BOUNDED: return count >= 1;
+    case TIDE_LAUNCH_CU_EXCLUSIVE:
+      if (count >= 1 && count <= kRsCuMaxGroups) return true;
+      return count == 2 * kRsCuMaxGroups && rs_cu_items_ok(C > kRsMaxCt ? 0 : C, 2);
+    case TIDE_LAUNCH_PER_CU_CAP: return count >= 1 && count <= TIDE_MAX_WGS_PER_CU;
+    default: return false;
+  }
+}
+// Whether (form, count) is a valid launch of the placement kernel or the slot packing.
+inline bool ag_launch_ok(int form, int count) {
+  switch (form) {
+    case TIDE_LAUNCH_DEFAULT: return count == 0;
+    case TIDE_LAUNCH_BOUNDED: return count >= 1;
+    case TIDE_LAUNCH_CU_EXCLUSIVE: return count >= 1 && count <= kAgCuMaxItems;
+    default: return false;
+  }
 }
 
-// Dynamic local memory of a CU-exclusive RS workgroup: together with its static local memory, the
-// most one workgroup may request (all of a CU's on MI355X), so no second one fits beside it.
-inline int rs_cu_launch_lds(const DeviceState& st) {
-  const int cap = st.lds_per_wg < st.lds_per_cu ? st.lds_per_wg : st.lds_per_cu;
-  const int dyn = cap - st.rs_static_lds_cu;
-  return dyn > 0 ? dyn : 0;
-}
-// Default RS launch (cu_budget 0) in the CU-exclusive form with the widest workgroups (kRsCuMaxItems
-// items) instead of single-item workgroups under a per-CU cap, where it measured faster on MI355X
-// (Llama-3.1-8B shapes, R = 8, HIP-event means): C = 8, compiled (the four layer groups: +0.2 to
-// +1.5% over three interleaved sessions), and C >= 12 in its runtime-C form (C = 12 / 16 / 20 / 24 /
-// 32: +2.3 / +5.2 / +1.9 / +1.8 / +1.6%).  Elsewhere the cap stays: C = 9 / 10 -3.1 / -1.4% (a
-// compiled capped kernel against the runtime-C form), C <= 4 -4 to -26% (a CU then holds too few
-// bytes in flight).  The CU-exclusive default also leaves a concurrent one-wave GEMM its CUs
-// (+12-15% instead of waiting for the whole call).
-constexpr int kRsCuDefaultMinC = 12;
-inline bool rs_cu_default(int C) { return C == 8 || C >= kRsCuDefaultMinC; }
-
-// Items per CU-exclusive RS workgroup for C contributors at cu_budget, or 0 for the other forms.
-inline int rs_cu_launch_items(int C, int cu_budget) {
-  if (const int w = cu_exclusive_items(cu_budget)) return w;
-  return cu_budget == 0 && rs_cu_default(C) ? kRsCuMaxItems : 0;
+// Items per CU-exclusive RS workgroup of a valid launch, or 0 for the other forms.
+inline int rs_cu_launch_items(int C, int form, int count) {
+  if (form == TIDE_LAUNCH_CU_EXCLUSIVE) return count;
+  if (form == TIDE_LAUNCH_DEFAULT) return rs_default_items(C > kRsMaxCt ? kRsCuMaxGroups : C);
+  return 0;
 }
 
-inline int ag_cu_launch_lds(const DeviceState& st) {  // the AG kernels have no static local memory
-  return st.lds_per_wg < st.lds_per_cu ? st.lds_per_wg : st.lds_per_cu;
-}
+// Local memory a CU-exclusive workgroup requests: the most one workgroup may (all of a CU's on
+// MI355X), so no second one fits beside it.  The kernels have no static local memory.
+inline int cu_exclusive_lds(const DeviceState& st) { return st.lds_per_wg < st.lds_per_cu ? st.lds_per_wg : st.lds_per_cu; }
 
-// Dynamic local memory of an RS launch with C contributors at `cu_budget` on this device: 0 caps
-// the RS workgroups per CU at rs_wgs_per_cu(C), -N at N; bounded launches (> 0) add none.  Needs
+// Dynamic local memory of an RS launch of single-item workgroups (bounded launches and per-CU caps):
+// TIDE_LAUNCH_PER_CU_CAP N requests 1/N of the CU's local memory; bounded launches none.  Needs
 // lds_per_cu, lds_per_wg and the static sizes filled in (rs_device_info).
-inline int rs_launch_lds(const DeviceState& st, int C, int cu_budget) {
-  if (cu_budget > 0) return 0;
-  if (rs_cu_launch_items(C, cu_budget) > 0) return rs_cu_launch_lds(st);
-  const int wgs = cu_budget < 0 ? -cu_budget : rs_wgs_per_cu(C);
+inline int rs_launch_lds(const DeviceState& st, int C, int form, int count) {
+  if (form != TIDE_LAUNCH_PER_CU_CAP) return 0;
   const int static_lds = C <= kRsMaxCt ? st.rs_static_lds_ct : st.rs_static_lds_rt;
-  const int dyn = rs_dynamic_lds(st.lds_per_cu, static_lds, wgs);
+  const int dyn = rs_dynamic_lds(st.lds_per_cu, static_lds, count);
   // caps below what one workgroup's local memory can express become the smallest that it can
   const int room = st.lds_per_wg - static_lds;
   return dyn < room ? dyn : (room > 0 ? room : 0);

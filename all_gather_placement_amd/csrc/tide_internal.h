@@ -29,8 +29,8 @@ namespace tide {
 #ifndef TIDE_AG_CHUNK
 #define TIDE_AG_CHUNK 2048
 #endif
-// RS occupancy cap of unbounded launches (cu_budget 0): at most rs_wgs_per_cu(C) RS workgroups per
-// CU, enforced by the local-memory size each launch requests (the CU's LDS divided by that count).
+// RS single-item workgroups under a per-CU cap (TIDE_LAUNCH_PER_CU_CAP N): at most N RS workgroups
+// per CU, enforced by the local-memory size each launch requests (the CU's LDS divided by N).
 // Fewer requests in flight stream HBM better than a full CU, and a workgroup's traffic grows with
 // C (2C + 4 bytes per output), so the best count falls as C grows.  Measured with 128-thread
 // workgroups on the Llama-3.1-8B group: C = 8: 6 per CU beat 3, 4, 5, 7, 8 and no cap by 1-5%;
@@ -41,9 +41,6 @@ namespace tide {
 // (3: 4.51, 4: 5.61, 5: 5.73, 8: 5.69, no cap 5.61); C = 32: 4 per CU 5.74 TB/s (3: 4.87, 5: 5.73,
 // 6: 5.71, 8: 5.60, no cap 5.58).
 constexpr int kRsMaxCt = 16;
-constexpr int rs_wgs_per_cu(int C) {
-  return C <= 2 ? 12 : C <= 4 ? 8 : C <= 12 ? 6 : C <= kRsMaxCt ? 4 : C <= 24 ? 6 : 4;
-}
 #ifndef TIDE_RS_NQ
 #define TIDE_RS_NQ 2
 #endif
@@ -89,7 +86,7 @@ constexpr int kAgBatchMaxWgsPerCu = TIDE_AG_BATCH_MAX_WGS_PER_CU;
 #ifndef TIDE_STORE_NT
 #define TIDE_STORE_NT 1
 #endif
-// Unbounded launches (cu_budget 0): 0 = one workgroup per work item; N > 0 = at most N
+// One-launch single-item forms (default placement, per-CU caps): 0 = one workgroup per work item; N > 0 = at most N
 // workgroups, each walking items with a grid stride.
 #ifndef TIDE_PERSISTENT_WGS
 #define TIDE_PERSISTENT_WGS 0
@@ -115,7 +112,7 @@ constexpr int64_t kXcds = 8;
 
 constexpr int kThreads = TIDE_THREADS;
 constexpr int kAgThreads = TIDE_AG_THREADS;
-// Unit of cu_budget: B admits B * kBudgetThreads threads of resident communication workgroups.
+// Unit of TIDE_LAUNCH_BOUNDED: B admits B * kBudgetThreads threads of resident communication workgroups.
 constexpr int kBudgetThreads = 256;
 static_assert(kBudgetThreads % kThreads == 0 && kBudgetThreads % TIDE_AG_THREADS == 0,
               "a budget slot holds whole workgroups");
@@ -128,7 +125,7 @@ static_assert(kRsChunk % 8 == 0 && kAgChunk % 8 == 0, "work items must be whole 
 static_assert(kRsChunk < (int64_t(1) << 31) && kAgChunk < (int64_t(1) << 31), "item sizes are int32");
 static_assert(kAgChunk % (8 * TIDE_AG_THREADS) == 0, "a full AG item is whole vectors for every lane");
 
-// Bounded launches (cu_budget B > 0): at most B * kBudgetThreads threads of RS (or AG) workgroups
+// Bounded launches (TIDE_LAUNCH_BOUNDED B): at most B * kBudgetThreads threads of RS (or AG) workgroups
 // are resident; each workgroup takes this many work items and exits, and the call issues as many
 // launches as it needs.  0 = a single launch whose workgroups walk all items (resident for the
 // whole call).
@@ -147,15 +144,23 @@ static_assert(kAgChunk % (8 * TIDE_AG_THREADS) == 0, "a full AG item is whole ve
 #endif
 constexpr int kRsBoundedItems = TIDE_RS_BOUNDED_ITEMS;
 
-// CU-exclusive RS launches (cu_budget TIDE_RS_CU_EXCLUSIVE(W)): one launch of workgroups of W
-// 128-thread groups, one work item each, and the largest local memory a workgroup may request, so
-// each CU holds one RS workgroup and is empty whenever it exits.  Measured on MI355X (one flat
+// CU-exclusive RS launches (TIDE_LAUNCH_CU_EXCLUSIVE N): one launch of workgroups of W = min(N, 8)
+// 128-thread groups taking N/W work items each, and the largest local memory a workgroup may
+// request, so each CU holds one RS workgroup and is empty whenever it exits.  Measured on MI355X (one flat
 // C = 8 parameter, 2^27 outputs, beside the one-wave bf16 GEMM): W = 2 5.04 TB/s, GEMM +2.5%;
 // 4: 6.25 TB/s, +4.4%; 6: 6.27, +7.9%; 8: 6.36, +10.5%; bounded budget 512 (same resident threads
 // as W = 4): 5.33 TB/s, -0.2%; W = 4 with only its own local memory (several per CU): +261%.
-constexpr int kRsCuMaxItems = 8;
-constexpr int kAgCuMaxItems = 8;  // AG placement / Slot-Reuse packing in the same CU-exclusive form
-static_assert(kThreads * kRsCuMaxItems <= 1024, "a CU-exclusive workgroup fits the workgroup size limit");
+constexpr int kRsCuMaxGroups = 8;  // 128-thread groups per CU-exclusive RS workgroup
+constexpr int kAgCuMaxItems = 8;   // AG placement / Slot-Reuse packing in the same CU-exclusive form
+static_assert(kThreads * kRsCuMaxGroups <= 1024, "a CU-exclusive workgroup fits the workgroup size limit");
+// Items per group of a CU-exclusive RS workgroup: 1, or 2 for C <= 4 (compiled contributor counts):
+// all of a group's loads stay in registers at once.  Measured on MI355X (Llama-3.1-8B shapes, one
+// 8-group workgroup per CU): 2 items per group over 1 at C = 1 / 2 / 3 / 4: 5.9 / 6.12 / 6.17 / 6.19
+// against 4.76 / 5.54 / 6.03 / 6.14 TB/s; 4 items per group at C = 1 / 2: 5.66 / 5.78, not kept.
+constexpr bool rs_cu_items_ok(int C, int ki) { return ki == 1 || (ki == 2 && C >= 1 && C <= 4); }
+// Local memory of the exchange slots of a CU-exclusive RS workgroup: 4 KiB per item in flight.
+constexpr int rs_cu_xfer_bytes(int groups, int ki) { return groups * ki * 2 * kThreads * 16; }
+static_assert(rs_cu_xfer_bytes(kRsCuMaxGroups, 2) <= 64 * 1024, "the widest CU-exclusive RS workgroup fits a CU");
 constexpr int kAgBoundedItems = TIDE_AG_BOUNDED_ITEMS;
 
 // One RS work item: nvalid summed elements of parameter p, starting at element `src` of the
@@ -195,11 +200,12 @@ int launch_rs(const RsChunk* chunks, int64_t first, int64_t count, int grid, int
               const void* const* dev_ptrs, int32_t P, int32_t C, int64_t S, bool flat, bool vec, int dyn_lds,
               void* hip_stream);
 int rs_lds_info(int device, int* lds_per_cu, int* static_lds_ct, int* static_lds_rt);
-// launch_rs_cu: the CU-exclusive RS over all `count` items in one launch, items_per_wg (1 ..
-// kRsCuMaxItems) items per workgroup; rs_cu_static_lds: that kernel's static local memory.
-int launch_rs_cu(const RsChunk* chunks, int64_t count, int items_per_wg, const void* const* dev_ptrs, int32_t P,
-                 int32_t C, int64_t S, bool flat, bool vec, int dyn_lds, void* hip_stream);
-int rs_cu_static_lds(int* static_lds);
+// launch_rs_cu: the CU-exclusive RS over all `count` items in one launch, `groups` (1 ..
+// kRsCuMaxGroups) groups of 128 threads per workgroup, each taking `items_per_group` items
+// (rs_cu_items_ok); `lds` is the dynamic local memory each workgroup requests (at least
+// rs_cu_xfer_bytes; the whole CU's to keep it exclusive).  The kernel has no static local memory.
+int launch_rs_cu(const RsChunk* chunks, int64_t count, int groups, int items_per_group, const void* const* dev_ptrs,
+                 int32_t P, int32_t C, int64_t S, bool flat, bool vec, int lds, void* hip_stream);
 // launch_ag_cu: the CU-exclusive AG placement (pack = false) or packing (pack = true) over all
 // `count` items in one launch, items_per_wg (1 .. kAgCuMaxItems) items per workgroup.
 int launch_ag_cu(const AgChunk* chunks, int64_t count, int items_per_wg, void* stage, const void* const* dev_params,

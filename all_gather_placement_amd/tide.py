@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 import weakref
-from typing import Sequence
+from typing import NamedTuple, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libtide.so"
@@ -24,24 +24,65 @@ TIDE_ERR_UNSUPPORTED = 4
 TIDE_AG_KERNEL = 0
 TIDE_AG_SDMA = 1
 TIDE_AG_COPY2D = 2
-TIDE_RS_MAX_WGS_PER_CU = 64
-TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS = 8
+TIDE_LAUNCH_DEFAULT = 0
+TIDE_LAUNCH_BOUNDED = 1
+TIDE_LAUNCH_CU_EXCLUSIVE = 2
+TIDE_LAUNCH_PER_CU_CAP = 3
+TIDE_MAX_WGS_PER_CU = 64
+TIDE_CU_EXCLUSIVE_MAX_ITEMS = 16
 TIDE_NOALLOC_MAX_PTRS = 65536
 
 
-def tide_rs_cu_exclusive(items_per_workgroup: int) -> int:
-    """RS cu_budget of the CU-exclusive launch (include/tide.h TIDE_RS_CU_EXCLUSIVE(W)): workgroups of
-    128*W threads taking W work items each and a whole CU's local memory, one per CU."""
-    w = int(items_per_workgroup)
-    if not 1 <= w <= TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS:
-        raise ValueError(f"items per CU-exclusive workgroup must be 1..{TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS}, got {w}")
-    return -(TIDE_RS_MAX_WGS_PER_CU + w)
+class Launch(NamedTuple):
+    """A launch form and its count (include/tide.h tide_launch_form): how many of the library's
+    workgroups are resident at once and how long each lives.  Never changes a result."""
+
+    form: int = TIDE_LAUNCH_DEFAULT
+    count: int = 0
+
+    @staticmethod
+    def default() -> "Launch":
+        """The library's choice (RS: CU-exclusive workgroups shaped for C)."""
+        return Launch(TIDE_LAUNCH_DEFAULT, 0)
+
+    @staticmethod
+    def bounded(budget: int) -> "Launch":
+        """Launches of at most 256*budget resident threads, short-lived workgroups."""
+        if int(budget) < 1:
+            raise ValueError(f"a bounded launch needs a budget >= 1, got {budget}")
+        return Launch(TIDE_LAUNCH_BOUNDED, int(budget))
+
+    @staticmethod
+    def cu_exclusive(items: int) -> "Launch":
+        """One launch of workgroups that hold a whole CU each and take `items` work items."""
+        n = int(items)
+        if not (1 <= n <= 8 or n == 16):
+            raise ValueError(f"CU-exclusive workgroups take 1..8 or 16 items, got {n}")
+        return Launch(TIDE_LAUNCH_CU_EXCLUSIVE, n)
+
+    @staticmethod
+    def per_cu_cap(n: int) -> "Launch":
+        """RS only: one launch of single-item workgroups, at most n of them per CU."""
+        if not 1 <= int(n) <= TIDE_MAX_WGS_PER_CU:
+            raise ValueError(f"a per-CU cap must be 1..{TIDE_MAX_WGS_PER_CU}, got {n}")
+        return Launch(TIDE_LAUNCH_PER_CU_CAP, int(n))
+
+    def __str__(self):
+        names = {TIDE_LAUNCH_DEFAULT: "default", TIDE_LAUNCH_BOUNDED: "bounded",
+                 TIDE_LAUNCH_CU_EXCLUSIVE: "cu_exclusive", TIDE_LAUNCH_PER_CU_CAP: "per_cu_cap"}
+        name = names.get(self.form, f"form{self.form}")
+        return name if self.form == TIDE_LAUNCH_DEFAULT else f"{name}({self.count})"
 
 
-def tide_ag_cu_exclusive(items_per_workgroup: int) -> int:
-    """AG cu_budget of the CU-exclusive placement / packing kernel (include/tide.h TIDE_AG_CU_EXCLUSIVE(W)),
-    the same encoding as the RS's."""
-    return tide_rs_cu_exclusive(items_per_workgroup)
+DEFAULT = Launch()
+
+
+def _launch(launch) -> Launch:
+    if launch is None:
+        return DEFAULT
+    if not isinstance(launch, tuple) or len(launch) != 2:
+        raise TypeError(f"launch must be a Launch (form, count), got {launch!r}")
+    return Launch(int(launch[0]), int(launch[1]))
 
 
 _lib = None
@@ -88,22 +129,23 @@ def load_library(path: str | None = None):
         "tide_layout_num_ag_chunks": (i64, [vp]),
         "tide_layout_param": (i32, [vp, i32, P_i64, P_i64, P_i64, P_i64]),
         "tide_layout_segment": (i32, [vp, i32, i32, P_i64, P_i64, P_i64, P_i64]),
-        "tide_rs_bf16_to_fp32": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]),
-        "tide_rs_bf16_to_fp32_noalloc": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]),
-        "tide_ag_place": (i32, [vp, vp, ctypes.POINTER(vp), i32, i32, vp]),
+        "tide_rs_bf16_to_fp32": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, vp]),
+        "tide_rs_bf16_to_fp32_noalloc": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, vp]),
+        "tide_ag_place": (i32, [vp, vp, ctypes.POINTER(vp), i32, i32, i32, vp]),
         "tide_layout_copy_rs_items": (i32, [vp, i64, i64, P_i64]),
         "tide_layout_copy_ag_items": (i32, [vp, i64, i64, P_i64]),
-        "tide_slot_pack": (i32, [vp, ctypes.POINTER(vp), vp, i32, vp]),
-        "tide_rs_slots_bf16_to_fp32": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp]),
+        "tide_slot_pack": (i32, [vp, ctypes.POINTER(vp), vp, i32, i32, vp]),
+        "tide_rs_slots_bf16_to_fp32": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, vp]),
         "tide_layout_num_slot_pad_items": (i64, [vp]),
         "tide_layout_copy_slot_pad_items": (i32, [vp, i64, i64, P_i64]),
-        "tide_rs_prepare": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]),
-        "tide_ag_prepare": (i32, [vp, vp, ctypes.POINTER(vp), i32, i32, ctypes.POINTER(vp)]),
-        "tide_slot_pack_prepare": (i32, [vp, ctypes.POINTER(vp), vp, i32, ctypes.POINTER(vp)]),
-        "tide_rs_slots_prepare": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, ctypes.POINTER(vp)]),
+        "tide_rs_prepare": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, ctypes.POINTER(vp)]),
+        "tide_ag_prepare": (i32, [vp, vp, ctypes.POINTER(vp), i32, i32, i32, ctypes.POINTER(vp)]),
+        "tide_slot_pack_prepare": (i32, [vp, ctypes.POINTER(vp), vp, i32, i32, ctypes.POINTER(vp)]),
+        "tide_rs_slots_prepare": (i32, [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32,
+                                        ctypes.POINTER(vp)]),
         "tide_call_launch": (i32, [vp, vp]),
         "tide_call_destroy": (None, [vp]),
-        "tide_rs_launch_shape": (i32, [i32, i32, P_i32, P_i32, P_i32]),
+        "tide_rs_launch_shape": (i32, [i32, i32, i32, P_i32, P_i32, P_i32, P_i32]),
         "tide_status_str": (ctypes.c_char_p, [i32]),
         "tide_last_hip_error": (i32, []),
         "tide_build_id": (ctypes.c_char_p, []),
@@ -178,7 +220,7 @@ def tide_layout_create(shapes: Sequence[Sequence[int]], R: int) -> int:
     return out.value
 
 
-def tide_rs_bf16_to_fp32(layout: int, grads, shards, cu_budget: int = 0, stream=None):
+def tide_rs_bf16_to_fp32(layout: int, grads, shards, launch: Launch = DEFAULT, stream=None):
     """grads: C lists of P bf16 tensors (or addresses); shards: R fp32 tensors (or addresses)."""
     lib = load_library()
     _expect_counts(layout, "tide_rs_bf16_to_fp32", rows=grads, per_rank=shards)
@@ -187,11 +229,11 @@ def tide_rs_bf16_to_fp32(layout: int, grads, shards, cu_budget: int = 0, stream=
     g_arr = (ctypes.c_void_p * max(len(flat), 1))(*flat)
     s_list = [_ptr(s) for s in shards]
     s_arr = (ctypes.c_void_p * max(len(s_list), 1))(*s_list)
-    _check(lib.tide_rs_bf16_to_fp32(layout, C, g_arr, s_arr, int(cu_budget), _stream_handle(stream)),
+    _check(lib.tide_rs_bf16_to_fp32(layout, C, g_arr, s_arr, *_launch(launch), _stream_handle(stream)),
            "tide_rs_bf16_to_fp32")
 
 
-def tide_rs_bf16_to_fp32_noalloc(layout: int, grads, shards, cu_budget: int = 0, stream=None):
+def tide_rs_bf16_to_fp32_noalloc(layout: int, grads, shards, launch: Launch = DEFAULT, stream=None):
     """As tide_rs_bf16_to_fp32, allocating nothing: the address table goes into the library's fixed
     per-device scratch array (at most TIDE_NOALLOC_MAX_PTRS = C*P + R pointers); the layout must have
     been prepared on the current device.  Calls that overlap on one device race on that array."""
@@ -206,30 +248,30 @@ def tide_rs_bf16_to_fp32_noalloc(layout: int, grads, shards, cu_budget: int = 0,
     g_arr = (ctypes.c_void_p * max(len(flat), 1))(*flat)
     s_list = [_ptr(s) for s in shards]
     s_arr = (ctypes.c_void_p * max(len(s_list), 1))(*s_list)
-    _check(lib.tide_rs_bf16_to_fp32_noalloc(layout, C, g_arr, s_arr, int(cu_budget), _stream_handle(stream)),
+    _check(lib.tide_rs_bf16_to_fp32_noalloc(layout, C, g_arr, s_arr, *_launch(launch), _stream_handle(stream)),
            "tide_rs_bf16_to_fp32_noalloc")
 
 
-def tide_ag_place(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0, stream=None):
+def tide_ag_place(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, launch: Launch = DEFAULT, stream=None):
     """stage: R*S bf16 tensor (or address); params: P bf16 tensors (or addresses)."""
     lib = load_library()
     _expect_counts(layout, "tide_ag_place", per_param=params)
     p_list = [_ptr(p) for p in params]
     p_arr = (ctypes.c_void_p * max(len(p_list), 1))(*p_list)
-    _check(lib.tide_ag_place(layout, _ptr(stage), p_arr, int(mode), int(cu_budget), _stream_handle(stream)),
+    _check(lib.tide_ag_place(layout, _ptr(stage), p_arr, int(mode), *_launch(launch), _stream_handle(stream)),
            "tide_ag_place")
 
 
-def tide_slot_pack(layout: int, grads, slot, cu_budget: int = 0, stream=None):
+def tide_slot_pack(layout: int, grads, slot, launch: Launch = DEFAULT, stream=None):
     """grads: P bf16 tensors of one contributor (or addresses); slot: R*S bf16 tensor (or address)."""
     lib = load_library()
     _expect_counts(layout, "tide_slot_pack", per_param=grads)
     g_list = [_ptr(g) for g in grads]
     g_arr = (ctypes.c_void_p * max(len(g_list), 1))(*g_list)
-    _check(lib.tide_slot_pack(layout, g_arr, _ptr(slot), int(cu_budget), _stream_handle(stream)), "tide_slot_pack")
+    _check(lib.tide_slot_pack(layout, g_arr, _ptr(slot), *_launch(launch), _stream_handle(stream)), "tide_slot_pack")
 
 
-def tide_rs_slots_bf16_to_fp32(layout: int, slots, shards, cu_budget: int = 0, stream=None):
+def tide_rs_slots_bf16_to_fp32(layout: int, slots, shards, launch: Launch = DEFAULT, stream=None):
     """slots: C packed R*S bf16 tensors (or addresses); shards: R fp32 tensors (or addresses)."""
     lib = load_library()
     _expect_counts(layout, "tide_rs_slots_bf16_to_fp32", per_rank=shards)
@@ -237,7 +279,7 @@ def tide_rs_slots_bf16_to_fp32(layout: int, slots, shards, cu_budget: int = 0, s
     sl_arr = (ctypes.c_void_p * max(len(sl), 1))(*sl)
     sh = [_ptr(x) for x in shards]
     sh_arr = (ctypes.c_void_p * max(len(sh), 1))(*sh)
-    _check(lib.tide_rs_slots_bf16_to_fp32(layout, len(sl), sl_arr, sh_arr, int(cu_budget), _stream_handle(stream)),
+    _check(lib.tide_rs_slots_bf16_to_fp32(layout, len(sl), sl_arr, sh_arr, *_launch(launch), _stream_handle(stream)),
            "tide_rs_slots_bf16_to_fp32")
 
 
@@ -246,39 +288,39 @@ def _ptr_array(xs):
     return (ctypes.c_void_p * max(len(xs), 1))(*xs)
 
 
-def tide_rs_prepare(layout: int, grads, shards, cu_budget: int = 0) -> int:
+def tide_rs_prepare(layout: int, grads, shards, launch: Launch = DEFAULT) -> int:
     """Prepared RS call (see tide_call_launch); returns the raw tide_call handle."""
     lib = load_library()
     _expect_counts(layout, "tide_rs_prepare", rows=grads, per_rank=shards)
     out = ctypes.c_void_p()
     _check(lib.tide_rs_prepare(layout, len(grads), _ptr_array([g for row in grads for g in row]),
-                               _ptr_array(shards), int(cu_budget), ctypes.byref(out)), "tide_rs_prepare")
+                               _ptr_array(shards), *_launch(launch), ctypes.byref(out)), "tide_rs_prepare")
     return out.value
 
 
-def tide_ag_prepare(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0) -> int:
+def tide_ag_prepare(layout: int, stage, params, mode: int = TIDE_AG_KERNEL, launch: Launch = DEFAULT) -> int:
     lib = load_library()
     _expect_counts(layout, "tide_ag_prepare", per_param=params)
     out = ctypes.c_void_p()
-    _check(lib.tide_ag_prepare(layout, _ptr(stage), _ptr_array(params), int(mode), int(cu_budget), ctypes.byref(out)),
+    _check(lib.tide_ag_prepare(layout, _ptr(stage), _ptr_array(params), int(mode), *_launch(launch), ctypes.byref(out)),
            "tide_ag_prepare")
     return out.value
 
 
-def tide_slot_pack_prepare(layout: int, grads, slot, cu_budget: int = 0) -> int:
+def tide_slot_pack_prepare(layout: int, grads, slot, launch: Launch = DEFAULT) -> int:
     lib = load_library()
     _expect_counts(layout, "tide_slot_pack_prepare", per_param=grads)
     out = ctypes.c_void_p()
-    _check(lib.tide_slot_pack_prepare(layout, _ptr_array(grads), _ptr(slot), int(cu_budget), ctypes.byref(out)),
+    _check(lib.tide_slot_pack_prepare(layout, _ptr_array(grads), _ptr(slot), *_launch(launch), ctypes.byref(out)),
            "tide_slot_pack_prepare")
     return out.value
 
 
-def tide_rs_slots_prepare(layout: int, slots, shards, cu_budget: int = 0) -> int:
+def tide_rs_slots_prepare(layout: int, slots, shards, launch: Launch = DEFAULT) -> int:
     lib = load_library()
     _expect_counts(layout, "tide_rs_slots_prepare", per_rank=shards)
     out = ctypes.c_void_p()
-    _check(lib.tide_rs_slots_prepare(layout, len(slots), _ptr_array(slots), _ptr_array(shards), int(cu_budget),
+    _check(lib.tide_rs_slots_prepare(layout, len(slots), _ptr_array(slots), _ptr_array(shards), *_launch(launch),
                                      ctypes.byref(out)), "tide_rs_slots_prepare")
     return out.value
 
@@ -291,13 +333,13 @@ def tide_call_destroy(call: int):
     load_library().tide_call_destroy(call)
 
 
-def tide_rs_launch_shape(C: int = 8, cu_budget: int = 0) -> dict:
-    """RS launch shape for C contributors at cu_budget on the current device: threads, item_outputs,
-    lds_bytes."""
-    v = [ctypes.c_int32() for _ in range(3)]
-    _check(load_library().tide_rs_launch_shape(int(C), int(cu_budget), *[ctypes.byref(x) for x in v]),
+def tide_rs_launch_shape(C: int = 8, launch: Launch = DEFAULT) -> dict:
+    """RS launch shape for C contributors in a launch form on the current device: threads,
+    items_per_workgroup, item_outputs, lds_bytes."""
+    v = [ctypes.c_int32() for _ in range(4)]
+    _check(load_library().tide_rs_launch_shape(int(C), *_launch(launch), *[ctypes.byref(x) for x in v]),
            "tide_rs_launch_shape")
-    return dict(zip(("threads", "item_outputs", "lds_bytes"), (x.value for x in v)))
+    return dict(zip(("threads", "items_per_workgroup", "item_outputs", "lds_bytes"), (x.value for x in v)))
 
 
 class Layout:
@@ -395,42 +437,42 @@ class Layout:
         _check(self._lib.tide_layout_prepare(self.handle), "tide_layout_prepare")
 
     # collectives -----------------------------------------------------------------------------
-    def rs_bf16_to_fp32(self, grads, shards, cu_budget: int = 0, stream=None):
+    def rs_bf16_to_fp32(self, grads, shards, launch: Launch = DEFAULT, stream=None):
         _check_shapes_rs(self, grads, shards)
-        tide_rs_bf16_to_fp32(self.handle, grads, shards, cu_budget, stream)
+        tide_rs_bf16_to_fp32(self.handle, grads, shards, launch, stream)
 
-    def ag_place(self, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0, stream=None):
+    def ag_place(self, stage, params, mode: int = TIDE_AG_KERNEL, launch: Launch = DEFAULT, stream=None):
         _check_shapes_ag(self, stage, params)
-        tide_ag_place(self.handle, stage, params, mode, cu_budget, stream)
+        tide_ag_place(self.handle, stage, params, mode, launch, stream)
 
     # prepared calls (validate once, launch many times; graph-capturable kernel paths) ---------
-    def bind_rs(self, grads, shards, cu_budget: int = 0) -> BoundCall:
+    def bind_rs(self, grads, shards, launch: Launch = DEFAULT) -> BoundCall:
         _check_shapes_rs(self, grads, shards)
-        return self._bound(tide_rs_prepare(self.handle, grads, shards, cu_budget), (grads, shards, self))
+        return self._bound(tide_rs_prepare(self.handle, grads, shards, launch), (grads, shards, self))
 
-    def bind_ag(self, stage, params, mode: int = TIDE_AG_KERNEL, cu_budget: int = 0) -> BoundCall:
+    def bind_ag(self, stage, params, mode: int = TIDE_AG_KERNEL, launch: Launch = DEFAULT) -> BoundCall:
         _check_shapes_ag(self, stage, params)
-        return self._bound(tide_ag_prepare(self.handle, stage, params, mode, cu_budget), (stage, params, self))
+        return self._bound(tide_ag_prepare(self.handle, stage, params, mode, launch), (stage, params, self))
 
-    def bind_slot_pack(self, grads, slot, cu_budget: int = 0) -> BoundCall:
+    def bind_slot_pack(self, grads, slot, launch: Launch = DEFAULT) -> BoundCall:
         _check_shapes_ag(self, slot, grads)
-        return self._bound(tide_slot_pack_prepare(self.handle, grads, slot, cu_budget), (grads, slot, self))
+        return self._bound(tide_slot_pack_prepare(self.handle, grads, slot, launch), (grads, slot, self))
 
-    def bind_rs_slots(self, slots, shards, cu_budget: int = 0) -> BoundCall:
+    def bind_rs_slots(self, slots, shards, launch: Launch = DEFAULT) -> BoundCall:
         _check_shapes_rs(self, [], shards)
         for sl in slots:
             _check_stage(self, sl)
-        return self._bound(tide_rs_slots_prepare(self.handle, slots, shards, cu_budget), (slots, shards, self))
+        return self._bound(tide_rs_slots_prepare(self.handle, slots, shards, launch), (slots, shards, self))
 
-    def slot_pack(self, grads, slot, cu_budget: int = 0, stream=None):
+    def slot_pack(self, grads, slot, launch: Launch = DEFAULT, stream=None):
         _check_shapes_ag(self, slot, grads)
-        tide_slot_pack(self.handle, grads, slot, cu_budget, stream)
+        tide_slot_pack(self.handle, grads, slot, launch, stream)
 
-    def rs_slots_bf16_to_fp32(self, slots, shards, cu_budget: int = 0, stream=None):
+    def rs_slots_bf16_to_fp32(self, slots, shards, launch: Launch = DEFAULT, stream=None):
         _check_shapes_rs(self, [], shards)
         for sl in slots:
             _check_stage(self, sl)
-        tide_rs_slots_bf16_to_fp32(self.handle, slots, shards, cu_budget, stream)
+        tide_rs_slots_bf16_to_fp32(self.handle, slots, shards, launch, stream)
 
 
 class BoundCall:

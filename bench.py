@@ -1,7 +1,9 @@
 """Benchmark of the layout-aware bf16->fp32 reduce-scatter + all-gather placement on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cu-budget B] [--ag-mode kernel|sdma|copy2d]
-                    [--graph]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--launch FORM] [--rs-launch FORM]
+                    [--ag-launch FORM] [--ag-mode kernel|sdma|copy2d] [--graph]
+
+FORM is a launch form of include/tide.h: default, bounded:B, cu_exclusive:N or per_cu_cap:N (RS only).
 
 One step = one pass of the whole hot path over one parameter group already resident in HBM: the
 in-place reduce-scatter (C bf16 contributors -> R fp32 shards) followed by the all-gather placement
@@ -43,15 +45,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama3_1_70b_layer")
-    ap.add_argument("--cu-budget", type=int, default=0)
-    ap.add_argument("--rs-wgs-per-cu", type=int, default=0,
-                    help="unbounded RS with at most N workgroups per CU (RS cu_budget -N; 0 = the library's cap by C)")
-    ap.add_argument("--rs-cu-exclusive", type=int, default=0,
-                    help="the RS as one launch of CU-exclusive workgroups of W items (RS cu_budget "
-                         "TIDE_RS_CU_EXCLUSIVE(W) = -(64 + W), W = 1..8)")
-    ap.add_argument("--ag-cu-exclusive", type=int, default=0,
-                    help="the AG placement kernel as one launch of CU-exclusive workgroups of W items (AG cu_budget "
-                         "TIDE_AG_CU_EXCLUSIVE(W) = -(64 + W), W = 1..8)")
+    ap.add_argument("--launch", default="default",
+                    help="launch form of both collectives: default, bounded:B, cu_exclusive:N, per_cu_cap:N (RS only)")
+    ap.add_argument("--rs-launch", default=None, help="launch form of the RS (overrides --launch)")
+    ap.add_argument("--ag-launch", default=None, help="launch form of the placement kernel (overrides --launch)")
     ap.add_argument("--ag-mode", choices=["kernel", "sdma", "copy2d"], default="kernel")
     ap.add_argument("--contributors", type=int, default=0,
                     help="override the workload's contributor count C (default: the workload's own)")
@@ -62,11 +59,16 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also capture the step (prepared RS + AG calls) in a HIP graph and time its replays")
     ap.add_argument("--interference", action="store_true",
-                    help="instead of the step benchmark: slowdown of a concurrent one-wave bf16 GEMM per cu_budget")
-    ap.add_argument("--budgets", default="0,-1,-2,-4,-65,-66,-68,-70,-72,8,16,32,64,128,256,512,768,1024,1536,2048")
+                    help="instead of the step benchmark: slowdown of a concurrent one-wave bf16 GEMM per launch form")
+    ap.add_argument("--launches", default=",".join(
+        ["default", "per_cu_cap:1", "per_cu_cap:2", "per_cu_cap:4"] + [f"cu_exclusive:{n}" for n in (1, 2, 4, 6, 8)]
+        + [f"bounded:{b}" for b in (8, 16, 32, 64, 128, 256, 512, 768, 1024, 1536, 2048)]),
+        help="--interference / --overlap: the launch forms to measure (comma list)")
     ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
-    ap.add_argument("--probe-budgets", default="none,0,16,64,256,512,768,1024,2048",
-                    help="--probes: RS cu_budgets of the occupancy-probe rows (none = no RS)")
+    ap.add_argument("--probe-launches",
+                    default="none,default,bounded:16,bounded:64,bounded:256,bounded:512,bounded:768,bounded:1024,"
+                            "bounded:2048,cu_exclusive:1,cu_exclusive:4,cu_exclusive:8,per_cu_cap:2",
+                    help="--probes: RS launch forms of the occupancy-probe rows (none = no RS)")
     ap.add_argument("--cu-masks", default="16,32,64,128",
                     help="--interference: also the RS confined to K CUs by a CU-masked stream, and the GEMM on "
                          "the other CUs (comma list of K; empty: none)")
@@ -77,7 +79,7 @@ def parse():
     ap.add_argument("--engines", action="store_true",
                     help="instead of the step benchmark: AG placement on CUs vs copy engines, served GB/s and victim slowdown")
     ap.add_argument("--overlap", action="store_true",
-                    help="communication on one stream beside back-to-back GEMMs on another, per --budgets")
+                    help="communication on one stream beside back-to-back GEMMs on another, per --launches")
     ap.add_argument("--overlap-comm", choices=["rs", "ag_kernel", "ag_sdma", "ag_copy2d"], default="rs")
     ap.add_argument("--mix-bound", action="store_true",
                     help="the RS's access shape with reads or writes left out, beside the library RS (C = 1-8)")
@@ -88,16 +90,45 @@ def parse():
     return ap.parse_args()
 
 
-def rs_mode(cu_budget: int, kind: str = "rs") -> str:
-    """How an RS (or, kind "ag", a placement-kernel) call at `cu_budget` launches (include/tide.h)."""
-    if cu_budget == 0:
-        return "one launch: C = 8 and C >= 12 CU-exclusive, 8 items; else per-CU cap by C" if kind == "rs" else \
-            "one launch, one workgroup per item"
-    if cu_budget > 0:
-        return f"bounded launches, {256 * cu_budget} threads"
-    if cu_budget >= -64:
-        return f"one launch, at most {-cu_budget} per CU"
-    return f"one launch, CU-exclusive workgroups of {-cu_budget - 64} items"
+def parse_launch(text: str):
+    """A launch form from the command line: default, bounded:B, cu_exclusive:N or per_cu_cap:N."""
+    from all_gather_placement_amd import Launch
+
+    t = text.strip()
+    if t == "default":
+        return Launch.default()
+    name, _, n = t.partition(":")
+    make = {"bounded": Launch.bounded, "cu_exclusive": Launch.cu_exclusive, "per_cu_cap": Launch.per_cu_cap}.get(name)
+    if make is None or not n.isdigit():
+        raise SystemExit(f"unknown launch form {text!r}: use default, bounded:B, cu_exclusive:N or per_cu_cap:N")
+    return make(int(n))
+
+
+def launch_mode(launch, C: int = 8, kind: str = "rs") -> str:
+    """How an RS (or, kind "ag", a placement-kernel) call in `launch` runs (include/tide.h)."""
+    from all_gather_placement_amd import TIDE_LAUNCH_BOUNDED, TIDE_LAUNCH_CU_EXCLUSIVE, TIDE_LAUNCH_DEFAULT
+
+    if launch.form == TIDE_LAUNCH_DEFAULT:
+        if kind != "rs":
+            return "one launch, one workgroup per item"
+        n = 16 if C <= 3 else 8
+        return f"one launch, CU-exclusive workgroups of {n} items (the default for C = {C})"
+    if launch.form == TIDE_LAUNCH_BOUNDED:
+        return f"bounded launches, {256 * launch.count} threads"
+    if launch.form == TIDE_LAUNCH_CU_EXCLUSIVE:
+        return f"one launch, CU-exclusive workgroups of {launch.count} items"
+    return f"one launch, single-item workgroups, at most {launch.count} per CU"
+
+
+def rs_kernel_name(C: int, launch) -> str:
+    """The RS kernel a launch runs for C contributors (aligned buffers, in-place source)."""
+    from all_gather_placement_amd import TIDE_LAUNCH_CU_EXCLUSIVE, TIDE_LAUNCH_DEFAULT
+
+    ct = C if C <= 16 else 0
+    if launch.form in (TIDE_LAUNCH_DEFAULT, TIDE_LAUNCH_CU_EXCLUSIVE):
+        n = launch.count if launch.form == TIDE_LAUNCH_CU_EXCLUSIVE else (16 if C <= 3 else 8)
+        return f"rs_cu_kernel<{ct}, {n // 8 if n > 8 else 1}, true, false>"
+    return f"rs_kernel<{ct}, true, false>"
 
 
 def shard_numel(shapes, R: int) -> int:
@@ -216,6 +247,7 @@ def cu_mask_rows(masks, comm_alone, gemm_once, gemm_alone, rs_bytes, reps, log):
 
     import torch
 
+    from all_gather_placement_amd import Launch
     from all_gather_placement_amd import probe as pr
 
     n_cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -228,18 +260,18 @@ def cu_mask_rows(masks, comm_alone, gemm_once, gemm_alone, rs_bytes, reps, log):
         try:
             where_rs = cu_placement(rs_stream, 8 * k)
             where_gemm = cu_placement(gemm_stream, 8 * (n_cus - k))
-            t_comm = comm_alone("rs", 0, rs_stream)
+            t_comm = comm_alone("rs", Launch.default(), rs_stream)
             g_masked = statistics.median(gemm_once(gemm_stream=gemm_stream)[0] for _ in range(reps))
             for kind, gs in (("rs_cumask", None), ("rs_cumask_partition", gemm_stream)):
                 conc, outlast = [], 0
                 for _ in range(reps):
-                    t, started_first, outlasted = gemm_once("rs", 0, gemm_stream=gs, comm_stream=rs_stream)
+                    t, started_first, outlasted = gemm_once("rs", Launch.default(), gemm_stream=gs, comm_stream=rs_stream)
                     if started_first:
                         conc.append(t)
                         outlast += int(outlasted)
                 med = statistics.median(conc) if conc else None
                 row = {
-                    "comm": kind, "cu_budget": 0, "cu_mask_cus": k,
+                    "comm": kind, "launch": "default", "cu_mask_cus": k,
                     "comm_ms": round(t_comm, 4),
                     "comm_gbps": round(rs_bytes / (t_comm * 1e-3) / 1e9, 1),
                     "gemm_alone_us": round(gemm_alone * 1e3, 2),
@@ -263,7 +295,7 @@ def cu_mask_rows(masks, comm_alone, gemm_once, gemm_alone, rs_bytes, reps, log):
 
 
 def interference(args, log):
-    """Slowdown of a concurrent one-wave bf16 GEMM while the RS runs at each CU budget.
+    """Slowdown of a concurrent one-wave bf16 GEMM while the RS runs in each launch form.
 
     The victim is a torch bf16 matmul (hipBLASLt) whose kernel is one wave on the device: at
     4096^3 it runs 256 workgroups of 256x256 tiles, one per CU.  For each repetition the GEMM's
@@ -285,10 +317,14 @@ def interference(args, log):
 
     import torch
 
-    from all_gather_placement_amd import Layout
+    from all_gather_placement_amd import Launch, Layout
     from workloads import CONFIGS, normal_bf16_cuda
 
     cfg = CONFIGS[args.workload]
+    if args.contributors:
+        import dataclasses
+
+        cfg = dataclasses.replace(cfg, C=args.contributors)
     dev = torch.device("cuda:0")
     M, N, K = (int(x) for x in args.gemm.split(","))
     a = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
@@ -312,19 +348,19 @@ def interference(args, log):
 
     bound = {}
 
-    def comm(kind, budget, stream=None):
+    def comm(kind, launch, stream=None):
         stream = sB if stream is None else stream
-        if (kind, budget) not in bound:
+        if (kind, launch) not in bound:
             if kind == "rs":
-                bound[kind, budget] = L.bind_rs(grads, shards, cu_budget=budget)
+                bound[kind, launch] = L.bind_rs(grads, shards, launch=launch)
             else:
                 mode = {"ag_sdma": TIDE_AG_SDMA, "ag_copy2d": TIDE_AG_COPY2D}.get(kind, TIDE_AG_KERNEL)
-                bound[kind, budget] = L.bind_ag(stage, params, mode=mode, cu_budget=budget)
+                bound[kind, launch] = L.bind_ag(stage, params, mode=mode, launch=launch)
         reps = 1 if kind in ("rs", "ag_sdma") else 4  # long enough to cover the GEMM
         for _ in range(reps):
-            bound[kind, budget].launch(stream)
+            bound[kind, launch].launch(stream)
 
-    def gemm_once(kind=None, budget=0, gemm_stream=None, comm_stream=None):
+    def gemm_once(kind=None, launch=None, gemm_stream=None, comm_stream=None):
         gs = sA if gemm_stream is None else gemm_stream
         cs = sB if comm_stream is None else comm_stream
         torch.cuda.synchronize()
@@ -336,7 +372,7 @@ def interference(args, log):
             e1.record(gs)
         if kind is not None:
             r0.record(cs)
-            comm(kind, budget, cs)
+            comm(kind, launch, cs)
             r1.record(cs)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1)
@@ -344,14 +380,14 @@ def interference(args, log):
             return t, True, True
         return t, r0.elapsed_time(e0) > 0, e1.elapsed_time(r1) > 0
 
-    def comm_alone(kind, budget, stream=None):
+    def comm_alone(kind, launch, stream=None):
         cs = sB if stream is None else stream
         ts = []
         for _ in range(3):
             torch.cuda.synchronize()
             r0, r1 = ev(), ev()
             r0.record(cs)
-            comm(kind, budget, cs)
+            comm(kind, launch, cs)
             r1.record(cs)
             torch.cuda.synchronize()
             ts.append(r0.elapsed_time(r1))
@@ -363,22 +399,23 @@ def interference(args, log):
     alone = statistics.median(alone_all)
     log(f"victim GEMM {M}x{N}x{K} bf16 alone: {alone * 1e3:.1f} us (median of {len(alone_all)})")
     rows = []
-    cases = [("rs", int(x)) for x in args.budgets.split(",")]
-    cases += [("ag_kernel", 0), ("ag_kernel", 512), ("ag_kernel", 768), ("ag_kernel", -66), ("ag_kernel", -68),
-              ("ag_kernel", -70), ("ag_copy2d", 0), ("ag_sdma", 0)]
-    for kind, budget in cases:
-        t_alone = comm_alone(kind, budget)
+    cases = [("rs", parse_launch(x)) for x in args.launches.split(",") if x.strip()]
+    cases += [("ag_kernel", Launch.default()), ("ag_kernel", Launch.bounded(512)), ("ag_kernel", Launch.bounded(768)),
+              ("ag_kernel", Launch.cu_exclusive(2)), ("ag_kernel", Launch.cu_exclusive(4)),
+              ("ag_kernel", Launch.cu_exclusive(6)), ("ag_copy2d", Launch.default()), ("ag_sdma", Launch.default())]
+    for kind, launch in cases:
+        t_alone = comm_alone(kind, launch)
         conc, outlast = [], 0
         for _ in range(args.reps):
-            t, started_first, outlasted = gemm_once(kind, budget)
+            t, started_first, outlasted = gemm_once(kind, launch)
             if started_first:
                 conc.append(t)
                 outlast += int(outlasted)
         nbytes = rs_bytes if kind == "rs" else (1 if kind == "ag_sdma" else 4) * ag_bytes
         med = statistics.median(conc) if conc else None
         row = {
-            "comm": kind, "cu_budget": budget,
-            "mode": rs_mode(budget, "rs" if kind == "rs" else "ag") if kind in ("rs", "ag_kernel") else None,
+            "comm": kind, "launch": str(launch),
+            "mode": launch_mode(launch, cfg.C, "rs" if kind == "rs" else "ag") if kind in ("rs", "ag_kernel") else None,
             "comm_ms": round(t_alone, 4),
             "comm_gbps": round(nbytes / (t_alone * 1e-3) / 1e9, 1),
             "gemm_alone_us": round(alone * 1e3, 2),
@@ -394,7 +431,8 @@ def interference(args, log):
     if masks:
         rows += cu_mask_rows(masks, comm_alone, gemm_once, alone, rs_bytes, args.reps, log)
     L.close()
-    out = {"experiment": "concurrent one-wave GEMM slowdown vs communication CU budget", "workload": cfg.name,
+    out = {"experiment": "concurrent one-wave GEMM slowdown vs communication launch form", "workload": cfg.name,
+           "C": cfg.C, "R": cfg.R,
            "gemm": [M, N, K], "gemm_alone_us_min_max": [round(min(alone_all) * 1e3, 2), round(max(alone_all) * 1e3, 2)],
            "rows": rows}
     print(json.dumps(out), flush=True)
@@ -442,16 +480,18 @@ def slot_reuse(args, log):
         torch.cuda.synchronize()
         return statistics.median(a.elapsed_time(b) for a, b in evs)
 
-    t_inplace = timed([L.bind_rs(grads, shards, cu_budget=args.cu_budget)], args.steps)
-    t_pack = timed([L.bind_slot_pack(grads[c], slots[c], cu_budget=args.cu_budget) for c in range(cfg.C)], args.steps)
-    t_rs_slots = timed([L.bind_rs_slots(slots, shards, cu_budget=args.cu_budget)], args.steps)
+    rs_launch = parse_launch(args.rs_launch or args.launch)
+    ag_launch = parse_launch(args.ag_launch or args.launch)
+    t_inplace = timed([L.bind_rs(grads, shards, launch=rs_launch)], args.steps)
+    t_pack = timed([L.bind_slot_pack(grads[c], slots[c], launch=ag_launch) for c in range(cfg.C)], args.steps)
+    t_rs_slots = timed([L.bind_rs_slots(slots, shards, launch=rs_launch)], args.steps)
     L.close()
     rs_bytes = 2 * cfg.C * numel + 4 * cfg.R * S
     pack_bytes = cfg.C * (2 * numel + 2 * cfg.R * S)
     rs_slot_bytes = 2 * cfg.C * cfg.R * S + 4 * cfg.R * S
     out = {
         "experiment": "Slot-Reuse vs In-Place reduce-scatter", "workload": cfg.name, "R": cfg.R, "C": cfg.C,
-        "cu_budget": args.cu_budget,
+        "rs_launch": str(rs_launch), "pack_launch": str(ag_launch),
         "in_place_rs_ms": round(t_inplace, 4), "in_place_rs_gbps": round(rs_bytes / t_inplace / 1e6, 1),
         "pack_all_contributors_ms": round(t_pack, 4), "pack_gbps": round(pack_bytes / t_pack / 1e6, 1),
         "rs_from_slots_ms": round(t_rs_slots, 4), "rs_from_slots_gbps": round(rs_slot_bytes / t_rs_slots / 1e6, 1),
@@ -470,19 +510,19 @@ def probes(args, log):
 
     (1) Occupancy probe (Table 5 analogue): 256 GEMM-shaped probe workgroups (256 threads, 64 KiB
         LDS, 256 VGPRs per wave: the one-wave GEMM's footprint, one per CU) spin ~100 us and record
-        their CU and start/end; launched while the RS runs at a given cu_budget.  A probe workgroup
+        their CU and start/end; launched while the RS runs in a given launch form.  A probe workgroup
         that starts more than 5 us after the first one was displaced into a second wave.
     (2) Spin-kernel curve (Figure 4 lines): k small workgroups resident for ~2 ms, the one-wave GEMM
         launched meanwhile; GEMM slowdown against k.
     (3) Victims of Table 4's other columns: a ~28-wave GEMM and a memory-bound elementwise add,
-        with the RS unbounded and at the training budget.
+        with the RS in its default launch, bounded and CU-exclusive (the training setting, 4 items).
     """
     import statistics
 
     import numpy as np
     import torch
 
-    from all_gather_placement_amd import Layout
+    from all_gather_placement_amd import Launch, Layout
     from all_gather_placement_amd import probe as pr
     from workloads import CONFIGS, normal_bf16_cuda
 
@@ -500,10 +540,10 @@ def probes(args, log):
     spin_cycles = 400_000
     rs_calls = {}
 
-    def rs_call(b):
-        if b not in rs_calls:
-            rs_calls[b] = L.bind_rs(grads, shards, cu_budget=b)
-        return rs_calls[b]
+    def rs_call(launch):
+        if launch not in rs_calls:
+            rs_calls[launch] = L.bind_rs(grads, shards, launch=launch)
+        return rs_calls[launch]
 
     # (1) occupancy probe.  A one-wave marker workgroup (one wave, 8 VGPRs: it fits beside
     # anything but a full SIMD) runs on the probe's stream just before it and records when the
@@ -512,14 +552,14 @@ def probes(args, log):
     marker = torch.zeros(4, dtype=torch.int64, device=dev)
     probe_ticks = int(100 * tpu)
 
-    def probe_once(budget):
+    def probe_once(launch):
         torch.cuda.synchronize()
         with torch.cuda.stream(sA):
             torch.cuda._sleep(spin_cycles)
             pr.probe_launch(1, pr.TIDE_PROBE_SMALL, 0, marker, sA)
             pr.probe_launch(256, pr.TIDE_PROBE_GEMM_SHAPED, probe_ticks, recs, sA)
-        if budget is not None:
-            rs_call(budget).launch(sB)
+        if launch is not None:
+            rs_call(launch).launch(sB)
         torch.cuda.synchronize()
         d = pr.decode(recs.cpu().numpy().view(np.uint64))
         m = pr.decode(marker.cpu().numpy().view(np.uint64))
@@ -532,11 +572,12 @@ def probes(args, log):
     for _ in range(2):
         probe_once(None)
     table5 = []
-    probe_budgets = [None if x.strip() == "none" else int(x) for x in args.probe_budgets.split(",") if x.strip()]
-    for budget in probe_budgets:
-        res = [probe_once(budget) for _ in range(max(args.reps, 15))]
+    probe_launches = [None if x.strip() == "none" else parse_launch(x) for x in args.probe_launches.split(",")
+                      if x.strip()]
+    for launch in probe_launches:
+        res = [probe_once(launch) for _ in range(max(args.reps, 15))]
         disp = [r[0] for r in res]
-        row = {"cu_budget": budget, "displaced_median": statistics.median(disp), "displaced_max": max(disp),
+        row = {"launch": None if launch is None else str(launch), "displaced_median": statistics.median(disp), "displaced_max": max(disp),
                "reps_with_displacement_pct": round(100 * sum(1 for x in disp if x) / len(disp), 1),
                "start_delay_us_median": round(statistics.median(r[4] for r in res), 1),
                "start_delay_us_max": round(max(r[4] for r in res), 1),
@@ -592,9 +633,9 @@ def probes(args, log):
             victim_once(fn, None)
         t_alone = statistics.median(victim_once(fn, None) for _ in range(args.reps))
         row = {"victim": name, "alone_us": round(t_alone * 1e3, 1)}
-        for budget in (0, 512):
-            t = statistics.median(victim_once(fn, lambda: rs_call(budget).launch(sB)) for _ in range(args.reps))
-            row[f"slowdown_pct_rs_budget_{budget}"] = round((t / t_alone - 1) * 100, 2)
+        for launch in (Launch.default(), Launch.bounded(512), Launch.cu_exclusive(4)):
+            t = statistics.median(victim_once(fn, lambda: rs_call(launch).launch(sB)) for _ in range(args.reps))
+            row[f"slowdown_pct_rs_{launch}"] = round((t / t_alone - 1) * 100, 2)
         log("victim " + json.dumps(row))
         table4.append(row)
     L.close()
@@ -617,7 +658,7 @@ def engines(args, log):
 
     import torch
 
-    from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
+    from all_gather_placement_amd import Launch, Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
     from workloads import CONFIGS, normal_bf16_cuda
 
     cfg = CONFIGS[args.workload]
@@ -637,9 +678,10 @@ def engines(args, log):
     ec = torch.empty_like(ea)
     victims = {"gemm_one_wave_4096^3": lambda: torch.matmul(a, b),
                "elementwise_add_256M_bf16": lambda: torch.add(ea, eb, out=ec)}
-    engines_ = {"cu_kernel": (TIDE_AG_KERNEL, 0), "cu_kernel_budget_512": (TIDE_AG_KERNEL, 512),
-                "copy_engine_sdma": (TIDE_AG_SDMA, 0), "runtime_copy2d": (TIDE_AG_COPY2D, 0)}
-    calls = {k: L.bind_ag(stage, params, mode=m, cu_budget=bud) for k, (m, bud) in engines_.items()}
+    engines_ = {"cu_kernel": (TIDE_AG_KERNEL, Launch.default()), "cu_kernel_bounded_512": (TIDE_AG_KERNEL, Launch.bounded(512)),
+                "cu_kernel_cu_exclusive_4": (TIDE_AG_KERNEL, Launch.cu_exclusive(4)),
+                "copy_engine_sdma": (TIDE_AG_SDMA, Launch.default()), "runtime_copy2d": (TIDE_AG_COPY2D, Launch.default())}
+    calls = {k: L.bind_ag(stage, params, mode=m, launch=lc) for k, (m, lc) in engines_.items()}
 
     def alone_ms(call, reps):
         for _ in range(2):  # first calls on a stream stage the pointer table
@@ -732,7 +774,7 @@ def copy_sizes(args, log):
 def overlap(args, log):
     """Communication hidden behind compute, as FSDP overlaps it with forward and backward: n
     back-to-back bf16 GEMMs on one stream, the communication (--overlap-comm: the RS, or the AG
-    placement on the compute units or the DMA engines; one call at each CU budget) on another,
+    placement on the compute units or the DMA engines; one call in each launch form) on another,
     both enqueued at once.
     Reports each part alone, the overlapped makespan (first start to last end), the GEMM stream's
     own time while overlapped, and how much of the shorter part was hidden:
@@ -741,7 +783,7 @@ def overlap(args, log):
 
     import torch
 
-    from all_gather_placement_amd import Layout
+    from all_gather_placement_amd import TIDE_LAUNCH_CU_EXCLUSIVE, TIDE_LAUNCH_PER_CU_CAP, Launch, Layout
     from workloads import CONFIGS, normal_bf16_cuda
 
     cfg = CONFIGS[args.workload]
@@ -759,12 +801,12 @@ def overlap(args, log):
         grads = [[normal_bf16_cuda(s, cfg.sigma, cfg.cfg_id, c, p) for p, s in enumerate(cfg.shapes)]
                  for c in range(cfg.C)]
         shards = [torch.empty(S, dtype=torch.float32, device=dev) for _ in range(cfg.R)]
-        bind = lambda budget: L.bind_rs(grads, shards, cu_budget=budget)
+        bind = lambda launch: L.bind_rs(grads, shards, launch=launch)
     else:
         stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
         params = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in cfg.shapes]
         mode = {"ag_kernel": TIDE_AG_KERNEL, "ag_sdma": TIDE_AG_SDMA, "ag_copy2d": TIDE_AG_COPY2D}[kind]
-        bind = lambda budget: L.bind_ag(stage, params, mode=mode, cu_budget=budget if kind == "ag_kernel" else 0)
+        bind = lambda launch: L.bind_ag(stage, params, mode=mode, launch=launch if kind == "ag_kernel" else Launch())
     sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -784,11 +826,13 @@ def overlap(args, log):
 
     t_one = statistics.median(timed(lambda: gemms(1), sA) for _ in range(args.reps))
     rows = []
-    budgets = [int(x) for x in args.budgets.split(",")] if kind in ("rs", "ag_kernel") else [0]
-    if kind == "ag_kernel":
-        budgets = [b for b in budgets if b >= 0 or b <= -65]  # per-CU caps (-1 .. -64) are the RS's only
-    for budget in budgets:
-        call = bind(budget)
+    launches = [parse_launch(x) for x in args.launches.split(",") if x.strip()] if kind in ("rs", "ag_kernel") \
+        else [Launch()]
+    if kind == "ag_kernel":  # per-CU caps and more than 8 items per workgroup are the RS's only
+        launches = [lc for lc in launches if lc.form != TIDE_LAUNCH_PER_CU_CAP and not
+                    (lc.form == TIDE_LAUNCH_CU_EXCLUSIVE and lc.count > 8)]
+    for launch in launches:
+        call = bind(launch)
         t_rs = statistics.median(timed(lambda: call.launch(sB), sB) for _ in range(args.reps))  # the comm alone
         n = max(1, round(t_rs / t_one))  # GEMM work about as long as the RS
         t_g = statistics.median(timed(lambda: gemms(n), sA) for _ in range(args.reps))
@@ -810,7 +854,7 @@ def overlap(args, log):
             gemm_spans.append(g0.elapsed_time(g1))
         call.close()
         span, t_gc = statistics.median(spans), statistics.median(gemm_spans)
-        row = {"cu_budget": budget, "gemms": n, "gemms_alone_ms": round(t_g, 4), "comm_alone_ms": round(t_rs, 4),
+        row = {"launch": str(launch), "gemms": n, "gemms_alone_ms": round(t_g, 4), "comm_alone_ms": round(t_rs, 4),
                "overlapped_makespan_ms": round(span, 4), "gemms_while_overlapped_ms": round(t_gc, 4),
                "gemm_slowdown_pct": round((t_gc / t_g - 1) * 100, 2),
                "serial_ms": round(t_g + t_rs, 4),
@@ -899,18 +943,6 @@ def main():
         print("bench.py measures the node-local level on one GPU only; runs on more than one GPU "
               "(--gpus > 1) are not supported.", file=sys.stderr, flush=True)
         sys.exit(2)
-    if args.rs_wgs_per_cu and (args.cu_budget or not 0 < args.rs_wgs_per_cu <= 64):
-        print("--rs-wgs-per-cu takes 1..64 and applies to the unbounded RS only (--cu-budget 0)",
-              file=sys.stderr, flush=True)
-        sys.exit(2)
-    if args.ag_cu_exclusive and (args.cu_budget or args.ag_mode != "kernel" or not 0 < args.ag_cu_exclusive <= 8):
-        print("--ag-cu-exclusive takes 1..8, applies to the kernel engine and replaces --cu-budget for the AG",
-              file=sys.stderr, flush=True)
-        sys.exit(2)
-    if args.rs_cu_exclusive and (args.cu_budget or args.rs_wgs_per_cu or not 0 < args.rs_cu_exclusive <= 8):
-        print("--rs-cu-exclusive takes 1..8 and replaces --cu-budget and --rs-wgs-per-cu for the RS",
-              file=sys.stderr, flush=True)
-        sys.exit(2)
 
     def log(msg):
         if not args.quiet:
@@ -918,7 +950,7 @@ def main():
 
     import torch
 
-    from all_gather_placement_amd import Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, tide_rs_launch_shape
+    from all_gather_placement_amd import Launch, Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, tide_rs_launch_shape
     from workloads import CONFIGS, normal_bf16_cuda
 
     from all_gather_placement_amd.build import ensure_built
@@ -982,12 +1014,10 @@ def main():
     L.prepare()
     stream = torch.cuda.current_stream()
     # Arguments are validated and marshalled once; each call below is one C-ABI call.
-    rs_budget = -args.rs_wgs_per_cu if args.rs_wgs_per_cu else args.cu_budget
-    if args.rs_cu_exclusive:
-        rs_budget = -(64 + args.rs_cu_exclusive)
-    rs_call = L.bind_rs(grads, shards, cu_budget=rs_budget)
-    ag_budget = -(64 + args.ag_cu_exclusive) if args.ag_cu_exclusive else args.cu_budget
-    ag_call = L.bind_ag(stage, params, mode=ag_mode, cu_budget=ag_budget)
+    rs_launch = parse_launch(args.rs_launch or args.launch)
+    ag_launch = parse_launch(args.ag_launch or args.launch) if args.ag_mode == "kernel" else Launch()
+    rs_call = L.bind_rs(grads, shards, launch=rs_launch)
+    ag_call = L.bind_ag(stage, params, mode=ag_mode, launch=ag_launch)
 
     def step(ev_rs=None, ev_ag=None):
         if ev_rs:
@@ -1038,7 +1068,7 @@ def main():
             fn()
         return (time.perf_counter() - t) / n * 1e6
     host_bound = host_us(lambda: rs_call.launch(stream))
-    host_unbound = host_us(lambda: L.rs_bf16_to_fp32(grads, shards, cu_budget=rs_budget, stream=stream))
+    host_unbound = host_us(lambda: L.rs_bf16_to_fp32(grads, shards, launch=rs_launch, stream=stream))
     torch.cuda.synchronize()
 
     graph_info = None
@@ -1117,11 +1147,9 @@ def main():
     step_gbps = (rs_bytes + ag_bytes) / (ms_per_step * 1e-3) / 1e9
     rs_gbps = rs_bytes / (rs_mean * 1e-3) / 1e9
     ag_gbps = ag_bytes / (ag_mean * 1e-3) / 1e9
-    # counters were taken for the workload's own contributor count and the unbounded launch
-    rs_kernel_name = (f"rs_cu_kernel<{cfg.C if cfg.C in (1, 2, 4, 8) else 0}, true, false>"
-                      if rs_budget < -64 or (rs_budget == 0 and (cfg.C >= 12 or cfg.C == 8))
-                      else f"rs_kernel<{cfg.C if cfg.C <= 16 else 0}, true, false>")
-    traffic = read_traffic(cfg.name, rs_kernel_name) if rs_budget == 0 and not args.contributors else None
+    # counters were taken for the workload's own contributor count and its default launch
+    rs_kernel = rs_kernel_name(cfg.C, rs_launch)
+    traffic = read_traffic(cfg.name, rs_kernel) if rs_launch == Launch() and not args.contributors else None
 
     out = {
         "metric": METRIC,
@@ -1139,8 +1167,8 @@ def main():
         "config": {
             "workload": f"{cfg.name} RS+AG step (R={cfg.R}, C={cfg.C}, P={cfg.P})",
             "R": cfg.R, "C": cfg.C, "P": cfg.P, "numel": numel, "S": S,
-            "cu_budget": args.cu_budget, "rs_cu_budget": rs_budget, "rs_mode": rs_mode(rs_budget),
-            "ag_mode": args.ag_mode, "ag_cu_budget": ag_budget,
+            "rs_launch": str(rs_launch), "rs_mode": launch_mode(rs_launch, cfg.C),
+            "ag_mode": args.ag_mode, "ag_launch": str(ag_launch),
             "rs_bytes": rs_bytes, "ag_bytes": ag_bytes, "parallelism": "none (1 GPU, node-local level)",
         },
         "rs_gbps": round(rs_gbps, 2),
@@ -1152,13 +1180,13 @@ def main():
         "ag_frac_of_peak": round(ag_gbps / HBM_PEAK_GBPS, 4),
         "ag_ms_mean": round(ag_mean, 5),
         "rs_host_us_per_call": {"bound": round(host_bound, 1), "validate_and_marshal": round(host_unbound, 1)},
-        "rs_launch_shape": tide_rs_launch_shape(cfg.C, rs_budget),
+        "rs_launch_shape": tide_rs_launch_shape(cfg.C, rs_launch),
         "graph_replay": graph_info,
         "calibration": {"d2d_copy_gbps": round(cal_gbps, 2), "bytes_moved": 2 * (rs_bytes // 2),
                         "rs_over_d2d_copy": round(rs_gbps / cal_gbps, 4)},
         "roofline": {
             "bound": "hbm",
-            "kernel": rs_kernel_name,
+            "kernel": rs_kernel,
             "achieved": round(rs_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

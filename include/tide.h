@@ -36,7 +36,8 @@
  *     TIDE_ERR_HIP or TIDE_ERR_UNSUPPORTED.
  *   - A layout is immutable after creation and may be used from several streams and threads at
  *     once.  The library owns it; the caller owns every buffer and stream.
- *   - The library reads no environment variables: every choice (mode, cu_budget) is an argument.
+ *   - The library reads no environment variables: every choice (engine, launch form) is an
+ *     argument.
  */
 #ifndef TIDE_H
 #define TIDE_H
@@ -49,15 +50,43 @@ extern "C" {
 
 typedef struct tide_layout tide_layout;
 
-/* Largest per-CU cap an RS call may ask for with a negative cu_budget. */
-#define TIDE_RS_MAX_WGS_PER_CU 64
+/*
+ * Launch forms of the kernel paths (reduce-scatter, reduce-scatter from slots, placement kernel,
+ * slot packing).  Each of those calls takes a pair (launch_form, launch_count).  The form decides
+ * how many of the library's workgroups are resident at once and how long each one lives; it never
+ * changes a result.  [Endgame] Figure 3: communication workgroups that stay resident push a
+ * concurrent GEMM's workgroups into a second wave; Figure 4: the GEMM slows down as more
+ * communication workgroups stay resident, so TIDE bounds their number and lifetime.  On MI355X a
+ * GEMM workgroup that holds a whole SIMD register file waits until every library workgroup on its
+ * compute unit (CU) has exited, so what matters is how soon a CU is empty again.
+ */
+typedef enum tide_launch_form {
+  /* launch_count must be 0.  RS: one launch of CU-exclusive workgroups (below) whose width and
+   * items per group the library picks for C (tuned on MI355X for throughput on its own), so no
+   * workgroup outlives its few items and a CU is empty again within one workgroup lifetime.
+   * Placement kernel and slot packing: one launch, one 128-thread workgroup per work item. */
+  TIDE_LAUNCH_DEFAULT = 0,
+  /* launch_count = B >= 1: at most 256*B threads of the library's workgroups resident at a time
+   * (2B workgroups of 128 threads); each processes a few work items (RS 4 -- 80 KiB of traffic at
+   * C = 8 --, placement and packing 8 -- 64 KiB) and exits, and the call issues as many launches as
+   * needed, so a concurrent kernel finds free CUs within one short launch. */
+  TIDE_LAUNCH_BOUNDED = 1,
+  /* launch_count = N work items per workgroup: one launch of workgroups that each request the
+   * largest local memory one workgroup may (a whole CU's on MI355X), so a CU holds one of them and
+   * is empty whenever it exits; N items (N*C*2 KiB of RS loads) stay in flight per CU.
+   * RS: N = 1..8 (128*N threads, one item per 128-thread group), or N = 16 for C <= 4 (1024
+   * threads, each 128-thread group keeping 2 items' loads in flight at once).
+   * Placement kernel and slot packing: N = 1..8. */
+  TIDE_LAUNCH_CU_EXCLUSIVE = 2,
+  /* RS only.  launch_count = N in 1..TIDE_MAX_WGS_PER_CU: one launch of single-item 128-thread
+   * workgroups, at most N of them resident per CU (each requests 1/N of the CU's local memory; an N
+   * at or above the hardware's own limit leaves that limit).  From N = 2 up a CU is never empty
+   * during the call, so a kernel that waits for whole CUs waits for the whole call. */
+  TIDE_LAUNCH_PER_CU_CAP = 3
+} tide_launch_form;
 
-/* RS cu_budget of the CU-exclusive launch with W work items per workgroup (1 <= W <=
- * TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS): -65 .. -72, below the per-CU caps.  See tide_rs_bf16_to_fp32. */
-#define TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS 8
-#define TIDE_RS_CU_EXCLUSIVE(W) (-(TIDE_RS_MAX_WGS_PER_CU + (W)))
-/* The same launch form for the placement kernel and Slot-Reuse packing (tide_ag_place, tide_slot_pack). */
-#define TIDE_AG_CU_EXCLUSIVE(W) TIDE_RS_CU_EXCLUSIVE(W)
+#define TIDE_MAX_WGS_PER_CU 64          /* largest launch_count of TIDE_LAUNCH_PER_CU_CAP */
+#define TIDE_CU_EXCLUSIVE_MAX_ITEMS 16  /* largest launch_count of TIDE_LAUNCH_CU_EXCLUSIVE (RS) */
 
 typedef enum tide_status {
   TIDE_OK = 0,
@@ -151,44 +180,29 @@ tide_status tide_layout_copy_slot_pad_items(const tide_layout* layout, int64_t f
  *              row-major bf16 device tensor of rows_p * L_p elements, 2-byte aligned (NULL allowed
  *              only for empty parameters).  Read in place, never written.
  *   shards     host [R]: shards[r] is rank r's flat fp32 device shard of S elements, 4-byte aligned.
- *   cu_budget  0: one launch.  C = 8 and C >= 12: as TIDE_RS_CU_EXCLUSIVE(8) below (on MI355X the
- *              fastest form there, and it leaves a concurrent GEMM its CUs); C >= 12 in its runtime-C
- *              form, which loads the contributors in blocks of 8.  Other C: one short-lived workgroup
- *              per work item, with at most N of them resident per CU: N = 12 for C <= 2, 8 for
- *              C <= 4, 6 above (each requests 1/N of the CU's local memory; fewer requests in flight
- *              stream HBM better than a full CU, and a workgroup's traffic grows with C), in a
- *              kernel compiled for that C.
- *              -N (1 <= N <= TIDE_RS_MAX_WGS_PER_CU): as 0, with at most N per CU for any C (an N
- *              at or above the hardware's own limit leaves that limit).
- *              TIDE_RS_CU_EXCLUSIVE(W) (1 <= W <= 8): one launch of workgroups of 128*W threads, each
- *              taking W work items and the largest local memory a workgroup may request (a whole
- *              CU's on MI355X), so every CU holds one RS workgroup -- W items in flight -- and is
- *              empty whenever it exits: a concurrent kernel waiting for whole CUs (a one-wave
- *              GEMM) gets each CU within one RS workgroup lifetime, while the RS runs as a single
- *              launch ([Endgame] Figure 3: communication workgroups that stay resident push the
- *              GEMM's into a second wave).  Compiled for C = 1, 2, 4 and 8; other C take the
- *              runtime-C form.  A CU keeps W items' loads (C*2 KiB each) in flight, so fewer
- *              contributors want a wider W (on MI355X: W = 4 at C = 8 matches W = 8 at C = 4).
- *              B > 0: at most 256*B threads of RS workgroups resident at a time (2B workgroups of
- *              128 threads); each processes a bounded number of work items (4 by default, 80 KiB
- *              of traffic at C = 8) and exits, and the call issues as many launches as needed, so
- *              a concurrent kernel's workgroups find free CUs within one short launch.
- *              The budget changes speed and residency only, never results.
+ *   launch_form, launch_count  see tide_launch_form.  TIDE_LAUNCH_DEFAULT picks, for C contributors,
+ *              CU-exclusive workgroups of 1024 threads taking 8 items for C >= 4 and 16 for C <= 3
+ *              (2 items' loads in flight per 128-thread group): the most items whose traffic stays
+ *              within that of a C = 8 workgroup, so no workgroup outlives one at C = 8.  On MI355X
+ *              that streams 5.9-6.34 TB/s at C = 1-8; single-item workgroups under a per-CU cap
+ *              (TIDE_LAUNCH_PER_CU_CAP 12 for C <= 2, 8 for C = 3, 4) stream up to 6% more at C <= 4
+ *              but never empty a CU, so a concurrent GEMM waits for the whole call.  Kernels are
+ *              compiled for C = 1..16; larger C take a runtime-C form that loads contributors in
+ *              blocks of 8.
  *   stream     hipStream_t as void*.
  * Result, for every r, p and element k of the slice: shards[r][o_p + k] =
  *   x_0 (+) x_1 (+) ... (+) x_{C-1}, x_c = grads[c*P+p][r*m_p*L_p + k] widened exactly to fp32,
  *   (+) an IEEE binary32 add with round-to-nearest-even, applied in ascending c, for k < v*L_p;
  *   +0.0 for the padding elements v*L_p <= k < e_p.  Every shard element is written exactly once,
- *   independently of cu_budget; fp32 denormals are kept.
+ *   whatever the launch form; fp32 denormals are kept.
  * 16-byte-aligned grads and shards take the vector path; any other legal alignment takes a
  * slower element path with identical results.
- * Errors: TIDE_ERR_INVALID (null layout/arrays, C < 1, C*P > 2^24,
- * cu_budget < TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS), null or
- * misaligned pointer, any shard overlapping another shard or any gradient), TIDE_ERR_NOMEM,
- * TIDE_ERR_HIP.
+ * Errors: TIDE_ERR_INVALID (null layout/arrays, C < 1, C*P > 2^24, an unknown launch form or a
+ * launch_count outside its range for the form and C, null or misaligned pointer, any shard
+ * overlapping another shard or any gradient), TIDE_ERR_NOMEM, TIDE_ERR_HIP.
  */
 tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* grads,
-                                 float* const* shards, int32_t cu_budget, void* stream);
+                                 float* const* shards, int32_t launch_form, int32_t launch_count, void* stream);
 
 /*
  * All-gather placement ([Endgame] Figure 5b: each parameter filled from the stage slots by a single
@@ -197,25 +211,23 @@ tide_status tide_rs_bf16_to_fp32(const tide_layout* layout, int32_t C, const voi
  *   params     host [P]: params[p] is parameter p's contiguous bf16 device storage of rows_p * L_p
  *              elements (NULL allowed only for empty parameters).
  *   mode       TIDE_AG_KERNEL, TIDE_AG_SDMA or TIDE_AG_COPY2D.
- *   cu_budget  >= 0, as for the RS, counted in 256-thread slots (TIDE_AG_KERNEL only; its workgroups
- *              are 128 threads, so B admits 2B of them, each copying 8 work items -- 64 KiB of
- *              traffic -- before it exits; with at most 4 of them per CU, two items are loaded
- *              before either is stored).  0: one workgroup per work item, no cap.
- *              TIDE_AG_CU_EXCLUSIVE(W) (1 <= W <= 8, TIDE_AG_KERNEL only): one launch of workgroups of
- *              128*W threads, each copying W work items and holding a whole CU's local memory, as the
- *              RS's TIDE_RS_CU_EXCLUSIVE(W): a concurrent one-wave GEMM gets each CU back within one
- *              workgroup lifetime.
+ *   launch_form, launch_count  see tide_launch_form (TIDE_AG_KERNEL only; the DMA modes take
+ *              TIDE_LAUNCH_DEFAULT, 0).  Default: one 128-thread workgroup per work item.  Bounded:
+ *              each workgroup copies 8 items; with at most 4 of them per CU, two items are loaded
+ *              before either is stored.  CU-exclusive: workgroups of 128*N threads copying N items.
+ *              TIDE_LAUNCH_PER_CU_CAP is not offered for the placement.
  * Result: params[p][r*m_p*L_p + k] = stage[r*S + o_p + k] for every r and k < v*L_p, copied as
  * bits; stage padding is never read into a parameter; every parameter element is written once.
  * All pointers must be 2-byte aligned; 16-byte alignment selects the vector path.
  * TIDE_AG_SDMA work is ordered after the caller's earlier work on `stream`, and later work on
  * `stream` waits for it (event fork/join with the internal copy streams).
- * Errors: TIDE_ERR_INVALID (null/misaligned pointer, bad mode, a negative cu_budget other than
- * TIDE_AG_CU_EXCLUSIVE(1..8) with TIDE_AG_KERNEL, a parameter overlapping the stage or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a copy kind), TIDE_ERR_NOMEM,
- * TIDE_ERR_HIP.
+ * Errors: TIDE_ERR_INVALID (null/misaligned pointer, bad mode, a launch form other than the default
+ * with a DMA mode, an unknown or unsupported form or a launch_count outside its range, a parameter
+ * overlapping the stage or another parameter), TIDE_ERR_UNSUPPORTED (the runtime refused a copy
+ * kind), TIDE_ERR_NOMEM, TIDE_ERR_HIP.
  */
-tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params,
-                          int32_t mode, int32_t cu_budget, void* stream);
+tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* const* params, int32_t mode,
+                          int32_t launch_form, int32_t launch_count, void* stream);
 
 /*
  * Slot-Reuse, step 1: pack one contributor's per-parameter bf16 gradients into a rank-major
@@ -224,26 +236,27 @@ tide_status tide_ag_place(const tide_layout* layout, const void* stage, void* co
  *   grads      host [P]: grads[p] is parameter p's contiguous bf16 gradient (rows_p * L_p elements,
  *              2-byte aligned; NULL allowed only for empty parameters).  Read, never written.
  *   slot       device, R*S bf16 elements in the stage layout (rank r's shard at element r*S).
- *   cu_budget  as for tide_ag_place.
+ *   launch_form, launch_count  as for tide_ag_place with TIDE_AG_KERNEL.
  * Result: slot[r*S + o_p + k] = grads[p][r*m_p*L_p + k] for k < v*L_p (bit copy), and +0 (bits 0)
  * in every padding element; every slot element is written once.  The exact inverse of
  * tide_ag_place.  Errors: as tide_ag_place (the slot must not overlap any gradient).
  */
-tide_status tide_slot_pack(const tide_layout* layout, const void* const* grads, void* slot, int32_t cu_budget,
-                           void* stream);
+tide_status tide_slot_pack(const tide_layout* layout, const void* const* grads, void* slot, int32_t launch_form,
+                           int32_t launch_count, void* stream);
 
 /*
  * Slot-Reuse, step 2: reduce-scatter from C packed slots ([Endgame] Figure 7).
  *   slots      host [C]: slots[c] is contributor c's packed slot, R*S bf16 elements, 2-byte aligned
  *              (slots may alias each other; they are read, never written).
- *   shards, cu_budget, stream: as tide_rs_bf16_to_fp32.
+ *   shards, launch_form, launch_count, stream: as tide_rs_bf16_to_fp32.
  * Result: shards[r][k] = x_0 (+) ... (+) x_{C-1} with x_c = slots[c][r*S + k] widened, for every
  * valid element, and +0.0 for every padding element whatever the slots hold there.  Identical to
  * tide_rs_bf16_to_fp32 on the gradients the slots were packed from.
  * Errors: as tide_rs_bf16_to_fp32.
  */
 tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, const void* const* slots,
-                                       float* const* shards, int32_t cu_budget, void* stream);
+                                       float* const* shards, int32_t launch_form, int32_t launch_count,
+                                       void* stream);
 
 /*
  * Allocation-free reduce-scatter, for callers that cannot allocate device memory: code running
@@ -265,7 +278,8 @@ tide_status tide_rs_slots_bf16_to_fp32(const tide_layout* layout, int32_t C, con
  */
 #define TIDE_NOALLOC_MAX_PTRS 65536
 tide_status tide_rs_bf16_to_fp32_noalloc(const tide_layout* layout, int32_t C, const void* const* grads,
-                                         float* const* shards, int32_t cu_budget, void* stream);
+                                         float* const* shards, int32_t launch_form, int32_t launch_count,
+                                         void* stream);
 
 /*
  * Prepared calls.  A training step issues the same collectives on the same buffers every step
@@ -294,13 +308,13 @@ tide_status tide_rs_bf16_to_fp32_noalloc(const tide_layout* layout, int32_t C, c
 typedef struct tide_call tide_call;
 
 tide_status tide_rs_prepare(const tide_layout* layout, int32_t C, const void* const* grads, float* const* shards,
-                            int32_t cu_budget, tide_call** out);
+                            int32_t launch_form, int32_t launch_count, tide_call** out);
 tide_status tide_ag_prepare(const tide_layout* layout, const void* stage, void* const* params, int32_t mode,
-                            int32_t cu_budget, tide_call** out);
+                            int32_t launch_form, int32_t launch_count, tide_call** out);
 tide_status tide_slot_pack_prepare(const tide_layout* layout, const void* const* grads, void* slot,
-                                   int32_t cu_budget, tide_call** out);
+                                   int32_t launch_form, int32_t launch_count, tide_call** out);
 tide_status tide_rs_slots_prepare(const tide_layout* layout, int32_t C, const void* const* slots,
-                                  float* const* shards, int32_t cu_budget, tide_call** out);
+                                  float* const* shards, int32_t launch_form, int32_t launch_count, tide_call** out);
 
 /* Enqueue a prepared call on `stream` (hipStream_t as void*). */
 tide_status tide_call_launch(const tide_call* call, void* stream);
@@ -312,14 +326,14 @@ tide_status tide_call_launch(const tide_call* call, void* stream);
  * device instead, and no graph holding its launches may be replayed afterwards.  NULL is ignored. */
 void tide_call_destroy(tide_call* call);
 
-/* Launch shape of RS calls with C contributors at `cu_budget` on the current device: threads per
- * workgroup, outputs per full work item, and the local memory (static + dynamic, bytes) each
- * workgroup requests -- a CU holds as many RS workgroups as fit in its local memory, so for
- * cu_budget <= 0 this sets the per-CU cap (for TIDE_RS_CU_EXCLUSIVE(W): 128*W threads, one workgroup
- * per CU).  Errors: TIDE_ERR_INVALID (C < 1,
- * cu_budget < TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) or a NULL pointer), TIDE_ERR_HIP. */
-tide_status tide_rs_launch_shape(int32_t C, int32_t cu_budget, int32_t* threads, int32_t* item_outputs,
-                                 int32_t* lds_bytes);
+/* Launch shape of RS calls with C contributors in a launch form on the current device: threads per
+ * workgroup, work items per workgroup, outputs per full work item, and the local memory (static +
+ * dynamic, bytes) each workgroup requests -- a CU holds as many RS workgroups as fit in its local
+ * memory (one in the CU-exclusive forms, N with TIDE_LAUNCH_PER_CU_CAP).  Any output pointer may be
+ * NULL.  Errors: TIDE_ERR_INVALID (C < 1, an unknown form or a launch_count outside its range),
+ * TIDE_ERR_HIP. */
+tide_status tide_rs_launch_shape(int32_t C, int32_t launch_form, int32_t launch_count, int32_t* threads,
+                                 int32_t* items_per_workgroup, int32_t* item_outputs, int32_t* lds_bytes);
 
 /* Static, NUL-terminated name of a status code ("TIDE_OK", ...; "unknown" otherwise). */
 const char* tide_status_str(int32_t status);

@@ -29,16 +29,13 @@ int launch_fill_zero(const AgChunk*, int64_t, void*, void*) {
   std::fprintf(stderr, "launch_fill_zero reached in a host-only check\n");
   std::abort();
 }
-int launch_rs_cu(const RsChunk*, int64_t, int, const void* const*, int32_t, int32_t, int64_t, bool, bool, int, void*) {
+int launch_rs_cu(const RsChunk*, int64_t, int, int, const void* const*, int32_t, int32_t, int64_t, bool, bool, int,
+                 void*) {
   std::fprintf(stderr, "launch_rs_cu reached in a host-only check\n");
   std::abort();
 }
 int launch_ag_cu(const AgChunk*, int64_t, int, void*, const void* const*, bool, bool, int, void*) {
   std::fprintf(stderr, "launch_ag_cu reached in a host-only check\n");
-  std::abort();
-}
-int rs_cu_static_lds(int*) {
-  std::fprintf(stderr, "rs_cu_static_lds reached in a host-only check\n");
   std::abort();
 }
 int noalloc_scratch(int, void**, int64_t*) {
@@ -129,49 +126,75 @@ int main() {
   const void* g[1] = {reinterpret_cast<void*>(base)};
   float* sh[4];
   for (int r = 0; r < 4; ++r) sh[r] = reinterpret_cast<float*>(base + (uintptr_t(1) << 20) * (r + 1));
-  CHECK(tide_rs_bf16_to_fp32(L, 0, g, sh, 0, nullptr) == TIDE_ERR_INVALID);
+  const int D = TIDE_LAUNCH_DEFAULT;
+  CHECK(tide_rs_bf16_to_fp32(L, 0, g, sh, D, 0, nullptr) == TIDE_ERR_INVALID);
   sh[2] = sh[1];
-  CHECK(tide_rs_bf16_to_fp32(L, 1, g, sh, 0, nullptr) == TIDE_ERR_INVALID);  // shards overlap
+  CHECK(tide_rs_bf16_to_fp32(L, 1, g, sh, D, 0, nullptr) == TIDE_ERR_INVALID);  // shards overlap
   sh[2] = reinterpret_cast<float*>(base + 8);
-  CHECK(tide_rs_bf16_to_fp32(L, 1, g, sh, 0, nullptr) == TIDE_ERR_INVALID);  // shard inside a gradient
+  CHECK(tide_rs_bf16_to_fp32(L, 1, g, sh, D, 0, nullptr) == TIDE_ERR_INVALID);  // shard inside a gradient
   void* pp[1] = {reinterpret_cast<void*>(base + 2)};
-  CHECK(tide_ag_place(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, 0, nullptr) == TIDE_ERR_INVALID);
-  CHECK(tide_ag_place(L, reinterpret_cast<void*>(base), pp, 7, 0, nullptr) == TIDE_ERR_INVALID);
-  CHECK(tide_slot_pack(L, const_cast<const void* const*>(pp), reinterpret_cast<void*>(base), 0, nullptr) ==
+  CHECK(tide_ag_place(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, D, 0, nullptr) == TIDE_ERR_INVALID);
+  CHECK(tide_ag_place(L, reinterpret_cast<void*>(base), pp, 7, D, 0, nullptr) == TIDE_ERR_INVALID);
+  CHECK(tide_slot_pack(L, const_cast<const void* const*>(pp), reinterpret_cast<void*>(base), D, 0, nullptr) ==
         TIDE_ERR_INVALID);
   const void* sl[2] = {reinterpret_cast<void*>(base), reinterpret_cast<void*>(base + 1)};
   float* sh2[4];
   for (int r = 0; r < 4; ++r) sh2[r] = reinterpret_cast<float*>(base + (uintptr_t(1) << 20) * (r + 1));
-  CHECK(tide_rs_slots_bf16_to_fp32(L, 2, sl, sh2, 0, nullptr) == TIDE_ERR_INVALID);  // odd slot address
+  CHECK(tide_rs_slots_bf16_to_fp32(L, 2, sl, sh2, D, 0, nullptr) == TIDE_ERR_INVALID);  // odd slot address
+  // launch forms out of range are refused before anything else (the rest of these calls is valid)
+  {
+    const int bad_rs[][3] = {  // {C, form, count}
+        {1, 9, 0}, {1, -1, 0}, {1, TIDE_LAUNCH_DEFAULT, 1}, {1, TIDE_LAUNCH_BOUNDED, 0},
+        {1, TIDE_LAUNCH_BOUNDED, -3}, {1, TIDE_LAUNCH_CU_EXCLUSIVE, 0}, {1, TIDE_LAUNCH_CU_EXCLUSIVE, 9},
+        {1, TIDE_LAUNCH_CU_EXCLUSIVE, 24}, {1, TIDE_LAUNCH_CU_EXCLUSIVE, 64}, {3, TIDE_LAUNCH_CU_EXCLUSIVE, 32},
+        {5, TIDE_LAUNCH_CU_EXCLUSIVE, 16}, {1, TIDE_LAUNCH_PER_CU_CAP, 0},
+        {1, TIDE_LAUNCH_PER_CU_CAP, TIDE_MAX_WGS_PER_CU + 1}};
+    for (const auto& b : bad_rs) {
+      std::vector<const void*> gg(size_t(b[0]), g[0]);
+      CHECK(tide_rs_bf16_to_fp32(L, b[0], gg.data(), sh2, b[1], b[2], nullptr) == TIDE_ERR_INVALID);
+      CHECK(tide_rs_slots_bf16_to_fp32(L, b[0], gg.data(), sh2, b[1], b[2], nullptr) == TIDE_ERR_INVALID);
+      CHECK(tide_rs_launch_shape(b[0], b[1], b[2], nullptr, nullptr, nullptr, nullptr) == TIDE_ERR_INVALID);
+    }
+    void* qq[1] = {reinterpret_cast<void*>(base + (uintptr_t(1) << 30))};
+    const int bad_ag[][3] = {  // {mode, form, count}
+        {TIDE_AG_KERNEL, TIDE_LAUNCH_PER_CU_CAP, 4}, {TIDE_AG_KERNEL, TIDE_LAUNCH_CU_EXCLUSIVE, 9},
+        {TIDE_AG_KERNEL, TIDE_LAUNCH_CU_EXCLUSIVE, 0}, {TIDE_AG_KERNEL, TIDE_LAUNCH_BOUNDED, 0},
+        {TIDE_AG_KERNEL, TIDE_LAUNCH_DEFAULT, 2}, {TIDE_AG_SDMA, TIDE_LAUNCH_CU_EXCLUSIVE, 4},
+        {TIDE_AG_SDMA, TIDE_LAUNCH_BOUNDED, 8}, {TIDE_AG_COPY2D, TIDE_LAUNCH_BOUNDED, 8}};
+    for (const auto& b : bad_ag)
+      CHECK(tide_ag_place(L, reinterpret_cast<void*>(base), qq, b[0], b[1], b[2], nullptr) == TIDE_ERR_INVALID);
+    CHECK(tide_slot_pack(L, const_cast<const void* const*>(qq), reinterpret_cast<void*>(base), TIDE_LAUNCH_PER_CU_CAP,
+                         2, nullptr) == TIDE_ERR_INVALID);
+  }
   // the allocation-free RS applies the same checks, and refuses a pointer table beyond its scratch
-  CHECK(tide_rs_bf16_to_fp32_noalloc(L, 1, g, sh, 0, nullptr) == TIDE_ERR_INVALID);  // shard inside a gradient
-  CHECK(tide_rs_bf16_to_fp32_noalloc(L, 0, g, sh2, 0, nullptr) == TIDE_ERR_INVALID);
+  CHECK(tide_rs_bf16_to_fp32_noalloc(L, 1, g, sh, D, 0, nullptr) == TIDE_ERR_INVALID);  // shard inside a gradient
+  CHECK(tide_rs_bf16_to_fp32_noalloc(L, 0, g, sh2, D, 0, nullptr) == TIDE_ERR_INVALID);
+  CHECK(tide_rs_bf16_to_fp32_noalloc(L, 1, g, sh2, TIDE_LAUNCH_CU_EXCLUSIVE, 9, nullptr) == TIDE_ERR_INVALID);
   {
     // C = TIDE_NOALLOC_MAX_PTRS contributors (all aliasing one valid gradient) + R shards: one too many
     std::vector<const void*> many(TIDE_NOALLOC_MAX_PTRS, g[0]);
-    CHECK(tide_rs_bf16_to_fp32_noalloc(L, TIDE_NOALLOC_MAX_PTRS, many.data(), sh2, 0, nullptr) == TIDE_ERR_INVALID);
+    CHECK(tide_rs_bf16_to_fp32_noalloc(L, TIDE_NOALLOC_MAX_PTRS, many.data(), sh2, D, 0, nullptr) == TIDE_ERR_INVALID);
   }
   // prepared calls apply the same checks, and leave *out untouched
   tide_call* call = nullptr;
-  CHECK(tide_rs_prepare(L, 1, g, sh, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
-  CHECK(tide_rs_prepare(L, 0, g, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
-  CHECK(tide_rs_prepare(L, 1, g, sh2, TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) - 1, &call) == TIDE_ERR_INVALID && call == nullptr);
-  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, -1, &call) == TIDE_ERR_INVALID);
-  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_SDMA, TIDE_AG_CU_EXCLUSIVE(4), &call) ==
+  CHECK(tide_rs_prepare(L, 1, g, sh, D, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_rs_prepare(L, 0, g, sh2, D, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_rs_prepare(L, 1, g, sh2, TIDE_LAUNCH_CU_EXCLUSIVE, 9, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, TIDE_LAUNCH_PER_CU_CAP, 1, &call) ==
         TIDE_ERR_INVALID);
-  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, TIDE_AG_CU_EXCLUSIVE(9), &call) ==
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_SDMA, TIDE_LAUNCH_CU_EXCLUSIVE, 4, &call) ==
         TIDE_ERR_INVALID);
-  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, 0, &call) == TIDE_ERR_INVALID);
-  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, 7, 0, &call) == TIDE_ERR_INVALID);
-  CHECK(tide_slot_pack_prepare(L, const_cast<const void* const*>(pp), reinterpret_cast<void*>(base), 0, &call) ==
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, TIDE_LAUNCH_CU_EXCLUSIVE, 9, &call) ==
         TIDE_ERR_INVALID);
-  CHECK(tide_rs_slots_prepare(L, 2, sl, sh2, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
-  CHECK(tide_rs_prepare(L, 1, g, sh2, 0, nullptr) == TIDE_ERR_INVALID);  // no output handle
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, TIDE_AG_KERNEL, D, 0, &call) == TIDE_ERR_INVALID);
+  CHECK(tide_ag_prepare(L, reinterpret_cast<void*>(base), pp, 7, D, 0, &call) == TIDE_ERR_INVALID);
+  CHECK(tide_slot_pack_prepare(L, const_cast<const void* const*>(pp), reinterpret_cast<void*>(base), D, 0, &call) ==
+        TIDE_ERR_INVALID);
+  CHECK(tide_rs_slots_prepare(L, 2, sl, sh2, D, 0, &call) == TIDE_ERR_INVALID && call == nullptr);
+  CHECK(tide_rs_prepare(L, 1, g, sh2, D, 0, nullptr) == TIDE_ERR_INVALID);  // no output handle
   CHECK(tide_call_launch(nullptr, nullptr) == TIDE_ERR_INVALID);
-  CHECK(tide_rs_launch_shape(8, 0, nullptr, nullptr, nullptr) == TIDE_ERR_INVALID);
-  int32_t th = 0, it = 0, lds = 0;
-  CHECK(tide_rs_launch_shape(0, 0, &th, &it, &lds) == TIDE_ERR_INVALID);
-  CHECK(tide_rs_launch_shape(8, TIDE_RS_CU_EXCLUSIVE(TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) - 1, &th, &it, &lds) == TIDE_ERR_INVALID);
+  int32_t th = 0, it = 0, out = 0, lds = 0;
+  CHECK(tide_rs_launch_shape(0, D, 0, &th, &it, &out, &lds) == TIDE_ERR_INVALID);
   tide_call_destroy(nullptr);
   CHECK(tide_last_hip_error() == 0);
   tide_layout_destroy(L);

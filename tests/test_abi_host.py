@@ -265,12 +265,17 @@ def test_rs_rejects_bad_arguments_before_any_hip_call():
     lib = tb.load_library()
     with tide.Layout(TINY.shapes, TINY.R) as L:
         g, s = _fake_rs_args(L, 4)
-        call = lambda gg, ss, C=4, budget=0: lib.tide_rs_bf16_to_fp32(L.handle, C, _vp_array(gg), _vp_array(ss), budget, None)
+        call = lambda gg, ss, C=4, form=0, count=0: lib.tide_rs_bf16_to_fp32(L.handle, C, _vp_array(gg), _vp_array(ss),
+                                                                            form, count, None)
         INV = tb.TIDE_ERR_INVALID
-        assert lib.tide_rs_bf16_to_fp32(None, 4, _vp_array(g), _vp_array(s), 0, None) == INV
-        assert lib.tide_rs_bf16_to_fp32(L.handle, 4, None, _vp_array(s), 0, None) == INV
+        assert lib.tide_rs_bf16_to_fp32(None, 4, _vp_array(g), _vp_array(s), 0, 0, None) == INV
+        assert lib.tide_rs_bf16_to_fp32(L.handle, 4, None, _vp_array(s), 0, 0, None) == INV
         assert call(g, s, C=0) == INV
-        assert call(g, s, budget=-73) == INV           # below TIDE_RS_CU_EXCLUSIVE(8)
+        assert call(g, s, form=4) == INV                      # no such launch form
+        assert call(g, s, form=tb.TIDE_LAUNCH_DEFAULT, count=1) == INV
+        assert call(g, s, form=tb.TIDE_LAUNCH_CU_EXCLUSIVE, count=32) == INV   # at most 16 items
+        assert call(g, s, C=5, form=tb.TIDE_LAUNCH_CU_EXCLUSIVE, count=16) == INV   # 2 items per group need C <= 4
+        assert call(g, s, form=tb.TIDE_LAUNCH_PER_CU_CAP, count=65) == INV
         g2 = list(g); g2[5] = None
         assert call(g2, s) == INV                     # null gradient of a non-empty parameter
         g3 = list(g); g3[1] += 1
@@ -289,11 +294,13 @@ def test_ag_rejects_bad_arguments_before_any_hip_call():
     with tide.Layout(TINY.shapes, TINY.R) as L:
         stage = 1 << 32
         params = [(1 << 33) + p * (1 << 20) for p in range(L.P)]
-        call = lambda st_, pp, mode=0, budget=0: lib.tide_ag_place(L.handle, st_, _vp_array(pp), mode, budget, None)
+        call = lambda st_, pp, mode=0, form=0, count=0: lib.tide_ag_place(L.handle, st_, _vp_array(pp), mode, form, count,
+                                                                           None)
         INV = tb.TIDE_ERR_INVALID
         assert call(stage, params, mode=3) == INV
         assert call(stage, params, mode=-1) == INV
-        assert call(stage, params, budget=-1) == INV
+        assert call(stage, params, form=tb.TIDE_LAUNCH_PER_CU_CAP, count=2) == INV   # RS only
+        assert call(stage, params, mode=tb.TIDE_AG_SDMA, form=tb.TIDE_LAUNCH_BOUNDED, count=8) == INV
         assert call(None, params) == INV
         assert call(stage + 1, params) == INV
         pp = list(params); pp[0] = None
@@ -302,7 +309,7 @@ def test_ag_rejects_bad_arguments_before_any_hip_call():
         assert call(stage, pp) == INV                 # parameter inside the stage
         pp = list(params); pp[2] = pp[0] + 2
         assert call(stage, pp) == INV                 # parameters overlap
-        assert lib.tide_ag_place(None, stage, _vp_array(params), 0, 0, None) == INV
+        assert lib.tide_ag_place(None, stage, _vp_array(params), 0, 0, 0, None) == INV
 
 
 def test_slot_entry_points_reject_bad_arguments_before_any_hip_call():
@@ -311,21 +318,22 @@ def test_slot_entry_points_reject_bad_arguments_before_any_hip_call():
     with tide.Layout(TINY.shapes, TINY.R) as L:
         slot = 1 << 32
         grads = [(1 << 33) + p * (1 << 20) for p in range(L.P)]
-        pack = lambda gg, sl, budget=0: lib.tide_slot_pack(L.handle, _vp_array(gg), sl, budget, None)
-        assert lib.tide_slot_pack(None, _vp_array(grads), slot, 0, None) == INV
-        assert lib.tide_slot_pack(L.handle, None, slot, 0, None) == INV
+        pack = lambda gg, sl, form=0, count=0: lib.tide_slot_pack(L.handle, _vp_array(gg), sl, form, count, None)
+        assert lib.tide_slot_pack(None, _vp_array(grads), slot, 0, 0, None) == INV
+        assert lib.tide_slot_pack(L.handle, None, slot, 0, 0, None) == INV
         assert pack(grads, None) == INV
         assert pack(grads, slot + 1) == INV
-        assert pack(grads, slot, budget=-1) == INV
+        assert pack(grads, slot, form=tb.TIDE_LAUNCH_CU_EXCLUSIVE, count=9) == INV
         gg = list(grads); gg[1] = slot + 64
         assert pack(gg, slot) == INV                  # gradient inside the slot
         gg = list(grads); gg[0] = None
         assert pack(gg, slot) == INV
         slots = [(1 << 34) + c * (1 << 20) for c in range(4)]
         shards = [(1 << 35) + r * (1 << 20) for r in range(L.R)]
-        rs = lambda sl, sh, C=4, budget=0: lib.tide_rs_slots_bf16_to_fp32(L.handle, C, _vp_array(sl), _vp_array(sh), budget, None)
+        rs = lambda sl, sh, C=4, form=0, count=0: lib.tide_rs_slots_bf16_to_fp32(L.handle, C, _vp_array(sl),
+                                                                                 _vp_array(sh), form, count, None)
         assert rs(slots, shards, C=0) == INV
-        assert rs(slots, shards, budget=-73) == INV
+        assert rs(slots, shards, form=tb.TIDE_LAUNCH_BOUNDED, count=0) == INV
         ss = list(slots); ss[2] = None
         assert rs(ss, shards) == INV
         sh = list(shards); sh[0] = slots[1] + 8
@@ -417,18 +425,24 @@ def test_binding_rejects_tensors_on_mixed_devices():
             L.ag_place(FakeTensor(1), [FakeTensor(0) for _ in range(L.P)])
 
 
-def test_cu_exclusive_encoding_matches_the_header():
-    """TIDE_RS_CU_EXCLUSIVE(W) in include/tide.h and the binding's tide_rs_cu_exclusive agree, and sit
-    below the per-CU caps -1 .. -TIDE_RS_MAX_WGS_PER_CU."""
+def test_launch_forms_match_the_header():
+    """The launch-form enum and limits in include/tide.h and the binding's Launch agree."""
     text = open(os.path.join(ROOT, "include", "tide.h")).read()
-    max_wgs = int(re.search(r"#define TIDE_RS_MAX_WGS_PER_CU (\d+)", text).group(1))
-    max_items = int(re.search(r"#define TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS (\d+)", text).group(1))
-    assert "#define TIDE_RS_CU_EXCLUSIVE(W) (-(TIDE_RS_MAX_WGS_PER_CU + (W)))" in text
-    assert (tide.TIDE_RS_MAX_WGS_PER_CU, tide.TIDE_RS_CU_EXCLUSIVE_MAX_ITEMS) == (max_wgs, max_items)
-    assert [tide.tide_rs_cu_exclusive(w) for w in range(1, max_items + 1)] == list(range(-max_wgs - 1, -max_wgs - max_items - 1, -1))
-    for bad in (0, max_items + 1):
+    for name in ("TIDE_LAUNCH_DEFAULT", "TIDE_LAUNCH_BOUNDED", "TIDE_LAUNCH_CU_EXCLUSIVE", "TIDE_LAUNCH_PER_CU_CAP"):
+        value = int(re.search(name + r" = (\d+)", text).group(1))
+        assert getattr(tide, name) == value, name
+    for name in ("TIDE_MAX_WGS_PER_CU", "TIDE_CU_EXCLUSIVE_MAX_ITEMS", "TIDE_NOALLOC_MAX_PTRS"):
+        assert getattr(tide, name) == int(re.search(r"#define " + name + r" (\d+)", text).group(1)), name
+    assert tide.Launch() == tide.Launch.default() == (tide.TIDE_LAUNCH_DEFAULT, 0)
+    assert tide.Launch.bounded(512) == (tide.TIDE_LAUNCH_BOUNDED, 512)
+    assert tide.Launch.cu_exclusive(16) == (tide.TIDE_LAUNCH_CU_EXCLUSIVE, 16)
+    assert tide.Launch.per_cu_cap(6) == (tide.TIDE_LAUNCH_PER_CU_CAP, 6)
+    assert str(tide.Launch.bounded(3)) == "bounded(3)" and str(tide.Launch()) == "default"
+    for bad in (lambda: tide.Launch.bounded(0), lambda: tide.Launch.cu_exclusive(9), lambda: tide.Launch.cu_exclusive(0),
+                lambda: tide.Launch.cu_exclusive(32),
+                lambda: tide.Launch.per_cu_cap(tide.TIDE_MAX_WGS_PER_CU + 1)):
         with pytest.raises(ValueError):
-            tide.tide_rs_cu_exclusive(bad)
+            bad()
 
 
 def test_build_id_matches_the_sources():

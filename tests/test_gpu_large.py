@@ -15,8 +15,7 @@ import torch
 
 from oracle import geometry as ogeo
 from oracle import rs as ors
-from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, tide_ag_cu_exclusive,
-                                      tide_rs_cu_exclusive)
+from all_gather_placement_amd import Launch, Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA
 from workloads import normal_bf16_cuda
 from tests.test_gpu_parity import (host_bits_bf16, host_bits_f32, oracle_ag_every_element, oracle_rs_every_element,
                                    poisoned_shards, say, _locate_many)
@@ -102,7 +101,7 @@ def test_parameter_beyond_2_31_elements(gpu_available):
         # the CU-exclusive launch (one launch, 64-bit item and element offsets) gives the same shards
         say("large parameter: RS, CU-exclusive workgroups of 4 items")
         shards_x = poisoned_shards(R, S)
-        L.rs_bf16_to_fp32(grads, shards_x, cu_budget=tide_rs_cu_exclusive(4))
+        L.rs_bf16_to_fp32(grads, shards_x, launch=Launch.cu_exclusive(4))
         torch.cuda.synchronize()
         for r in range(R):
             assert torch.equal(shards_x[r].view(torch.int32), shards[r].view(torch.int32)), r
@@ -111,11 +110,11 @@ def test_parameter_beyond_2_31_elements(gpu_available):
 
         stage = normal_bf16_cuda((R * S,), 1.0, 202, 0)
         want_p = None
-        for mode, budget in ((TIDE_AG_KERNEL, 0), (TIDE_AG_SDMA, 0), (TIDE_AG_COPY2D, 0),
-                             (TIDE_AG_KERNEL, tide_ag_cu_exclusive(4))):
-            say(f"large parameter: AG mode={mode} cu_budget={budget}")
+        for mode, launch in ((TIDE_AG_KERNEL, Launch()), (TIDE_AG_SDMA, Launch()), (TIDE_AG_COPY2D, Launch()),
+                             (TIDE_AG_KERNEL, Launch.cu_exclusive(4))):
+            say(f"large parameter: AG mode={mode} launch={launch}")
             param = torch.full(SHAPES[0], float("nan"), dtype=torch.bfloat16, device="cuda")
-            L.ag_place(stage, [param], mode=mode, cu_budget=budget)
+            L.ag_place(stage, [param], mode=mode, launch=launch)
             torch.cuda.synchronize()
             want_p = oracle_ag_every_element(SHAPES, R, stage, [param], f"large parameter AG mode={mode}", want_p)
             del param

@@ -14,7 +14,7 @@ import oracle
 from oracle import geometry as ogeo
 from oracle import rs as ors
 from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError,
-                                      tide_ag_cu_exclusive, tide_rs_cu_exclusive)
+                                      Launch)
 from workloads import ORDERED, TINY, normal_bf16_bits, normal_bf16_cuda, f32_to_bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -54,14 +54,14 @@ def poisoned_shards(R, S, pad_elems=0):
     return out
 
 
-def run_rs(shapes, R, grads_bits, cu_budget=0, g_pad=None, s_pad=0, stream=None):
+def run_rs(shapes, R, grads_bits, launch=Launch(), g_pad=None, s_pad=0, stream=None):
     """Upload, run the HIP RS, return (R, S) uint32 bits."""
     C = len(grads_bits)
     g_pad = g_pad or (lambda c, p: 0)
     grads = [[dev_bf16(grads_bits[c][p], g_pad(c, p)) for p in range(len(shapes))] for c in range(C)]
     with Layout(shapes, R) as L:
         shards = poisoned_shards(R, L.S, s_pad)
-        L.rs_bf16_to_fp32(grads, shards, cu_budget=cu_budget, stream=stream)
+        L.rs_bf16_to_fp32(grads, shards, launch=launch, stream=stream)
         torch.cuda.synchronize()
         return np.stack([host_bits_f32(s) for s in shards]) if L.S else np.zeros((R, 0), np.uint32)
 
@@ -75,7 +75,7 @@ def assert_rs_equal(got_bits, want_f32):
         raise AssertionError(f"{bad[0].size} mismatches; first at {i}: got {got_bits[i]:#010x} want {want[i]:#010x}")
 
 
-def run_ag(shapes, R, stage_bits, mode=TIDE_AG_KERNEL, cu_budget=0, st_pad=0, p_pad=None):
+def run_ag(shapes, R, stage_bits, mode=TIDE_AG_KERNEL, launch=Launch(), st_pad=0, p_pad=None):
     p_pad = p_pad or (lambda p: 0)
     stage = dev_bf16(stage_bits, st_pad)
     params = []
@@ -84,7 +84,7 @@ def run_ag(shapes, R, stage_bits, mode=TIDE_AG_KERNEL, cu_budget=0, st_pad=0, p_
         buf = torch.full((n + p_pad(p) + 8,), POISON_BF16, dtype=torch.int16, device="cuda")
         params.append(buf[p_pad(p): p_pad(p) + n].view(torch.bfloat16).reshape(s))
     with Layout(shapes, R) as L:
-        L.ag_place(stage, params, mode=mode, cu_budget=cu_budget)
+        L.ag_place(stage, params, mode=mode, launch=launch)
         torch.cuda.synchronize()
     return [host_bits_bf16(q) for q in params]
 
@@ -97,8 +97,9 @@ def test_tiny_rs_bit_exact(gpu_available):
     say("tiny RS")
     g = [[normal_bf16_bits(s, TINY.sigma, TINY.cfg_id, c, p) for p, s in enumerate(TINY.shapes)] for c in range(TINY.C)]
     want = oracle.reduce_scatter(g, TINY.shapes, TINY.R)
-    for budget in (0, 1, 2, 5):
-        assert_rs_equal(run_rs(TINY.shapes, TINY.R, g, cu_budget=budget), want)
+    for launch in (Launch.default(), Launch.bounded(1), Launch.bounded(2), Launch.bounded(5), Launch.per_cu_cap(3),
+                   Launch.cu_exclusive(1), Launch.cu_exclusive(8), Launch.cu_exclusive(16)):
+        assert_rs_equal(run_rs(TINY.shapes, TINY.R, g, launch=launch), want)
 
 
 @pytest.mark.parametrize("mode", [TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_AG_COPY2D], ids=["kernel", "sdma", "copy2d"])
@@ -120,9 +121,8 @@ def test_tiny_ag_bit_exact(gpu_available, mode):
 
 
 GROUPS = [
-    # (shapes, R, C): ragged tails, rows < R, empty parameters, 1-D/3-D; at the bounded budget C <= 16
-    # runs a kernel compiled for that C (16 the largest), C > 16 the runtime-C kernel; at cu_budget 0,
-    # C >= 12 runs the CU-exclusive kernel's runtime-C form
+    # (shapes, R, C): ragged tails, rows < R, empty parameters, 1-D/3-D; C <= 16 runs kernels compiled
+    # for that C (16 the largest), C > 16 the runtime-C kernels
     ([(7, 5), (16, 3), (1, 9)], 4, 4),
     ([(1000, 37), (4099,), (333, 65), (0, 4), (3, 2, 5)], 8, 8),
     ([(5, 1), (2,), (9, 3, 3)], 9, 3),
@@ -143,8 +143,13 @@ def test_groups_rs_bit_exact(gpu_available, case):
     say(f"group {case}: shapes={shapes} R={R} C={C}")
     g = [[normal_bf16_bits(s, 1.0, 50 + case, c, p) for p, s in enumerate(shapes)] for c in range(C)]
     want = oracle.reduce_scatter(g, shapes, R)
-    assert_rs_equal(run_rs(shapes, R, g), want)
-    assert_rs_equal(run_rs(shapes, R, g, cu_budget=3), want)
+    # every launch form: the default (CU-exclusive, shaped for C), short bounded launches, single-item
+    # workgroups under a per-CU cap, and CU-exclusive workgroups of one item per group and, where C
+    # allows it, of several items per group
+    forms = [Launch.default(), Launch.bounded(3), Launch.per_cu_cap(2), Launch.cu_exclusive(3)]
+    forms += [Launch.cu_exclusive(16)] if C <= 4 else []
+    for launch in forms:
+        assert_rs_equal(run_rs(shapes, R, g, launch=launch), want)
 
 
 @pytest.mark.parametrize("case", range(len(GROUPS)))
@@ -155,10 +160,11 @@ def test_groups_ag_bit_exact(gpu_available, case, mode):
     geo, S = ogeo.group_geometry(shapes, R)
     stage = normal_bf16_bits((R * S,), 1.0, 60 + case, 0)
     want = oracle.all_gather_place(stage, shapes, R)
-    for budget in ((0, 1, 3, 1024) if mode == TIDE_AG_KERNEL else (0,)):
-        got = run_ag(shapes, R, stage, mode=mode, cu_budget=budget)
+    forms = (Launch.default(), Launch.bounded(1), Launch.bounded(3), Launch.bounded(1024), Launch.cu_exclusive(5))
+    for launch in (forms if mode == TIDE_AG_KERNEL else (Launch.default(),)):
+        got = run_ag(shapes, R, stage, mode=mode, launch=launch)
         for a, b in zip(got, want):
-            assert np.array_equal(a, b), budget
+            assert np.array_equal(a, b), launch
 
 
 @pytest.mark.parametrize("g_off", [0, 1, 3, 7])
@@ -172,8 +178,8 @@ def test_rs_alignment_sweep(gpu_available, g_off, s_off, C):
     g = [[normal_bf16_bits(s, 1.0, 70, c, p) for p, s in enumerate(shapes)] for c in range(C)]
     want = oracle.reduce_scatter(g, shapes, R)
     # mixed offsets across contributors when g_off > 0; one launch, and short bounded launches
-    for budget in (0, 2):
-        got = run_rs(shapes, R, g, cu_budget=budget, g_pad=lambda c, p: (g_off * (c + 1)) % 8, s_pad=s_off)
+    for launch in (Launch.default(), Launch.bounded(2), Launch.per_cu_cap(6)):
+        got = run_rs(shapes, R, g, launch=launch, g_pad=lambda c, p: (g_off * (c + 1)) % 8, s_pad=s_off)
         assert_rs_equal(got, want)
 
 
@@ -184,11 +190,12 @@ def test_ag_alignment_sweep(gpu_available, st_off, p_off):
     geo, S = ogeo.group_geometry(shapes, R)
     stage = normal_bf16_bits((R * S,), 1.0, 71, 0)
     want = oracle.all_gather_place(stage, shapes, R)
-    for mode, budget in ((TIDE_AG_KERNEL, 0), (TIDE_AG_KERNEL, 2), (TIDE_AG_SDMA, 0), (TIDE_AG_COPY2D, 0)):
-        got = run_ag(shapes, R, stage, mode=mode, cu_budget=budget, st_pad=st_off,
+    for mode, launch in ((TIDE_AG_KERNEL, Launch()), (TIDE_AG_KERNEL, Launch.bounded(2)),
+                         (TIDE_AG_KERNEL, Launch.cu_exclusive(3)), (TIDE_AG_SDMA, Launch()), (TIDE_AG_COPY2D, Launch())):
+        got = run_ag(shapes, R, stage, mode=mode, launch=launch, st_pad=st_off,
                      p_pad=lambda p: (p_off * (p + 1)) % 8)
         for a, b in zip(got, want):
-            assert np.array_equal(a, b), (mode, budget)
+            assert np.array_equal(a, b), (mode, launch)
 
 
 def test_rs_special_values(gpu_available):
@@ -248,19 +255,19 @@ def test_identical_contributor_buffers(gpu_available):
 
 
 @pytest.mark.parametrize("C", [257, 1000])
-@pytest.mark.parametrize("budget", [0, 3, -2])
-def test_many_contributors(gpu_available, C, budget):
+@pytest.mark.parametrize("launch", [Launch.default(), Launch.bounded(3), Launch.per_cu_cap(2)], ids=str)
+def test_many_contributors(gpu_available, C, launch):
     """C far beyond the compiled counts (the runtime-C kernel, blocks of 8 with a ragged last block):
     seven distinct N(0, 1) buffers passed in turn as the C contributors, so the ascending-order fp32
     sum over C terms, where every reordering changes bits, is checked against the oracle."""
-    say(f"many contributors C={C} budget={budget}")
+    say(f"many contributors C={C} launch={launch}")
     shapes, R = [(300, 40), (1500,), (17, 3)], 8
     distinct = [[normal_bf16_bits(s, 1.0, 175, d, p) for p, s in enumerate(shapes)] for d in range(7)]
     dev = [[dev_bf16(b) for b in row] for row in distinct]
     grads = [dev[c % 7] for c in range(C)]
     with Layout(shapes, R) as L:
         shards = poisoned_shards(R, L.S)
-        L.rs_bf16_to_fp32(grads, shards, cu_budget=budget)
+        L.rs_bf16_to_fp32(grads, shards, launch=launch)
         torch.cuda.synchronize()
         got = np.stack([host_bits_f32(s) for s in shards])
     assert_rs_equal(got, oracle.reduce_scatter([distinct[c % 7] for c in range(C)], shapes, R))
@@ -319,7 +326,7 @@ def test_ag_then_rs_round_trip(gpu_available, mode):
 
 
 # ------------------------------------------------------------------------------------------------
-# Full-size workloads (the launch configuration the benchmark times: cu_budget = 0)
+# Full-size workloads (the launch configuration the benchmark times: the default launch)
 # ------------------------------------------------------------------------------------------------
 
 FULL = [c for c in ORDERED if c.name != "tiny"]
@@ -411,7 +418,7 @@ def oracle_ag_every_element(shapes, R, stage, params, tag, want=None):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
 def test_full_size_rs_and_ag(gpu_available, cfg):
-    """The full-size workloads at the launch configuration the benchmark times (cu_budget 0): every
+    """The full-size workloads at the launch configuration the benchmark times (the default): every
     shard element and every placed parameter element against the oracle, bit for bit."""
     say(f"full size {cfg.name}: generating inputs")
     torch.cuda.empty_cache()
@@ -422,7 +429,7 @@ def test_full_size_rs_and_ag(gpu_available, cfg):
         assert L.S == S
         shards = poisoned_shards(cfg.R, S)
         say(f"full size {cfg.name}: RS")
-        L.rs_bf16_to_fp32(grads, shards, cu_budget=0)
+        L.rs_bf16_to_fp32(grads, shards)
         torch.cuda.synchronize()
 
         # (1) every element against the oracle, a run of parameters at a time
@@ -447,7 +454,7 @@ def test_full_size_rs_and_ag(gpu_available, cfg):
 
         # the CU-exclusive launch (the setting used beside compute) gives the same shards bit for bit
         shards_x = poisoned_shards(cfg.R, S)
-        L.rs_bf16_to_fp32(grads, shards_x, cu_budget=tide_rs_cu_exclusive(4))
+        L.rs_bf16_to_fp32(grads, shards_x, launch=Launch.cu_exclusive(4))
         torch.cuda.synchronize()
         for r in range(cfg.R):
             assert torch.equal(shards_x[r].view(torch.int32), shards[r].view(torch.int32)), r
@@ -458,14 +465,14 @@ def test_full_size_rs_and_ag(gpu_available, cfg):
         # (3) AG placement, every engine, every element against the oracle; then the round trip
         stage = normal_bf16_cuda((cfg.R * S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
         want_p = None
-        for mode, budget in ((TIDE_AG_KERNEL, 0), (TIDE_AG_SDMA, 0), (TIDE_AG_COPY2D, 0),
-                             (TIDE_AG_KERNEL, tide_ag_cu_exclusive(4))):
+        for mode, launch in ((TIDE_AG_KERNEL, Launch()), (TIDE_AG_SDMA, Launch()), (TIDE_AG_COPY2D, Launch()),
+                             (TIDE_AG_KERNEL, Launch.cu_exclusive(4))):
             params = [torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda") for s in cfg.shapes]
-            say(f"full size {cfg.name}: AG mode={mode} cu_budget={budget}")
-            L.ag_place(stage, params, mode=mode, cu_budget=budget)
+            say(f"full size {cfg.name}: AG mode={mode} launch={launch}")
+            L.ag_place(stage, params, mode=mode, launch=launch)
             torch.cuda.synchronize()
             want_p = oracle_ag_every_element(cfg.shapes, cfg.R, stage, params, f"{cfg.name} AG mode={mode}", want_p)
-            if mode == TIDE_AG_KERNEL and budget == 0:
+            if mode == TIDE_AG_KERNEL and launch == Launch():
                 L.rs_bf16_to_fp32([params], shards)
                 torch.cuda.synchronize()
                 for r in range(cfg.R):
@@ -479,28 +486,31 @@ def test_full_size_rs_and_ag(gpu_available, cfg):
     torch.cuda.empty_cache()
 
 
-def test_cu_budget_does_not_change_results(gpu_available):
-    say("cu_budget independence")
+def test_launch_form_does_not_change_results(gpu_available):
+    say("launch-form independence")
     shapes, R, C = [(4096, 512), (2048,), (1500, 300)], 8, 8
     grads = [[normal_bf16_cuda(s, 1e-3, 80, c, p) for p, s in enumerate(shapes)] for c in range(C)]
     with Layout(shapes, R) as L:
         ref = None
-        for budget in (0, 1, 7, 64, 256, 1024):
+        for launch in (Launch.default(), Launch.bounded(1), Launch.bounded(7), Launch.bounded(64), Launch.bounded(256),
+                       Launch.bounded(1024), Launch.per_cu_cap(1), Launch.per_cu_cap(6), Launch.per_cu_cap(64),
+                       *[Launch.cu_exclusive(w) for w in range(1, 9)]):
             shards = poisoned_shards(R, L.S)
-            L.rs_bf16_to_fp32(grads, shards, cu_budget=budget)
+            L.rs_bf16_to_fp32(grads, shards, launch=launch)
             torch.cuda.synchronize()
             got = torch.stack([s.view(torch.int32) for s in shards])
             if ref is None:
                 ref = got
             else:
-                assert torch.equal(got, ref), budget
+                assert torch.equal(got, ref), launch
         # the placement too: small budgets load two items per workgroup at a time, large ones one
         stage = normal_bf16_cuda((R * L.S,), 1.0, 81, 0)
         pref = None
-        for budget in (0, 1, 7, 64, 256, 512, 513, 1024):
+        for launch in (Launch.default(), *[Launch.bounded(b) for b in (1, 7, 64, 256, 512, 513, 1024)],
+                       *[Launch.cu_exclusive(w) for w in (1, 4, 8)]):
             params = [torch.full(s, POISON_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
                       for s in shapes]
-            L.ag_place(stage, params, cu_budget=budget)
+            L.ag_place(stage, params, launch=launch)
             torch.cuda.synchronize()
             got = [q.view(torch.int16).clone() for q in params]
             if pref is None:
@@ -511,4 +521,4 @@ def test_cu_budget_does_not_change_results(gpu_available):
                     want = st2[:, g.o: g.o + g.e].reshape(R * g.m, g.L)[: g.rows].reshape(-1)
                     assert torch.equal(got[p].reshape(-1), want.view(torch.int16)), p
             else:
-                assert all(torch.equal(a, b) for a, b in zip(got, pref)), budget
+                assert all(torch.equal(a, b) for a, b in zip(got, pref)), launch

@@ -16,8 +16,9 @@ import torch
 import oracle
 from oracle import geometry as ogeo
 from oracle import rs as ors
-from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TideError,
-                                      tide_ag_cu_exclusive, tide_rs_cu_exclusive, tide_rs_launch_shape)
+from all_gather_placement_amd import (Layout, TIDE_AG_COPY2D, TIDE_AG_KERNEL, TIDE_AG_SDMA, TIDE_LAUNCH_CU_EXCLUSIVE,
+                                      TIDE_LAUNCH_DEFAULT, TideError,
+                                      Launch, tide_rs_launch_shape)
 from workloads import CONFIGS, normal_bf16_bits, normal_bf16_cuda
 from tests.test_gpu_parity import (GROUPS, POISON_BF16, POISON_F32, assert_rs_equal, dev_bf16, host_bits_bf16,
                                    host_bits_f32, poisoned_shards, say, _locate_many, _sample_positions)
@@ -57,9 +58,9 @@ def test_prepared_calls_bit_exact(gpu_available, case):
     grads = [[dev_bf16(x) for x in row] for row in g]
     stage = dev_bf16(stage_bits)
     with Layout(shapes, R) as L:
-        for budget in (0, 3):
+        for launch in (Launch.default(), Launch.bounded(3), Launch.per_cu_cap(4)):
             shards = poisoned_shards(R, S)
-            call = L.bind_rs(grads, shards, cu_budget=budget)
+            call = L.bind_rs(grads, shards, launch=launch)
             for _ in range(2):  # a launch rewrites every element: the second must change nothing
                 call.launch()
                 torch.cuda.synchronize()
@@ -73,7 +74,7 @@ def test_prepared_calls_bit_exact(gpu_available, case):
             for a, b in zip([host_bits_bf16(q) for q in params], want_ag):
                 assert np.array_equal(a, b), name
         slots = [poisoned_slot(R, S) for _ in range(C)]
-        packs = [L.bind_slot_pack(grads[c], slots[c], cu_budget=3) for c in range(C)]
+        packs = [L.bind_slot_pack(grads[c], slots[c], launch=Launch.bounded(3)) for c in range(C)]
         for p in packs:
             p.launch()
         torch.cuda.synchronize()
@@ -114,8 +115,9 @@ def test_prepare_rejects_what_the_immediate_call_rejects(gpu_available):
         bad[1] = bad[0]  # two ranks writing one shard
         with pytest.raises(TideError, match="INVALID"):
             L.bind_rs(grads, bad)
-        with pytest.raises(TideError, match="INVALID"):
-            L.bind_rs(grads, shards, cu_budget=-73)  # below the CU-exclusive modes
+        for bad in (Launch(9, 0), Launch(TIDE_LAUNCH_CU_EXCLUSIVE, 9), Launch(TIDE_LAUNCH_DEFAULT, 2)):
+            with pytest.raises(TideError, match="INVALID"):
+                L.bind_rs(grads, shards, launch=bad)  # no such form / count
         stage = torch.zeros(R * S, dtype=torch.bfloat16, device="cuda")
         params = [torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
         with pytest.raises(TideError, match="INVALID"):
@@ -135,13 +137,15 @@ def _capture(calls, stream):
     return g
 
 
-@pytest.mark.parametrize("budget,rs_budget", [(0, 0), (3, 3), (tide_ag_cu_exclusive(4), tide_rs_cu_exclusive(4))],
-                         ids=["unbounded", "bounded3", "cu_exclusive4"])
-def test_graph_replay_kernel_paths(gpu_available, budget, rs_budget):
+@pytest.mark.parametrize("launch,rs_launch",
+                         [(Launch(), Launch()), (Launch.bounded(3), Launch.bounded(3)),
+                          (Launch.cu_exclusive(4), Launch.cu_exclusive(4)), (Launch(), Launch.per_cu_cap(6))],
+                         ids=["default", "bounded3", "cu_exclusive4", "per_cu_cap6"])
+def test_graph_replay_kernel_paths(gpu_available, launch, rs_launch):
     """RS, AG placement (kernel), Slot-Reuse pack + RS from slots, captured once, replayed 4 times
-    (the two RS calls at rs_budget, the placement and the packing at budget)."""
+    (the two RS calls in rs_launch, the placement and the packing in launch)."""
     shapes, R, C = GROUPS[1]
-    say(f"graph capture and replay, budget={budget} rs_budget={rs_budget}")
+    say(f"graph capture and replay, launch={launch} rs_launch={rs_launch}")
     geo, S = ogeo.group_geometry(shapes, R)
     with Layout(shapes, R) as L:
         grads = [[torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes] for _ in range(C)]
@@ -150,9 +154,9 @@ def test_graph_replay_kernel_paths(gpu_available, budget, rs_budget):
         shards2 = poisoned_shards(R, S)
         params = poisoned_params(shapes)
         slots = [poisoned_slot(R, S) for _ in range(C)]
-        calls = [L.bind_rs(grads, shards, cu_budget=rs_budget), L.bind_ag(stage, params, cu_budget=budget)]
-        calls += [L.bind_slot_pack(grads[c], slots[c], cu_budget=budget) for c in range(C)]
-        calls.append(L.bind_rs_slots(slots, shards2, cu_budget=rs_budget))
+        calls = [L.bind_rs(grads, shards, launch=rs_launch), L.bind_ag(stage, params, launch=launch)]
+        calls += [L.bind_slot_pack(grads[c], slots[c], launch=launch) for c in range(C)]
+        calls.append(L.bind_rs_slots(slots, shards2, launch=rs_launch))
         side = torch.cuda.Stream()
         torch.cuda.synchronize()
         graph = _capture(calls, side)
@@ -178,7 +182,7 @@ def test_graph_replay_kernel_paths(gpu_available, budget, rs_budget):
                 assert np.array_equal(host_bits_bf16(slots[c]), oracle.pack_slot(g[c], shapes, R)), f"replay {it}"
             # eager immediate calls on the same inputs agree with the replay
             eager = poisoned_shards(R, S)
-            L.rs_bf16_to_fp32(grads, eager, cu_budget=rs_budget)
+            L.rs_bf16_to_fp32(grads, eager, launch=rs_launch)
             torch.cuda.synchronize()
             assert np.array_equal(shards_bits(eager), shards_bits(shards))
         del graph
@@ -200,8 +204,8 @@ def test_graph_replay_full_size_step(gpu_available):
         stage = normal_bf16_cuda((cfg.R * S,), 1.0, cfg.cfg_id, 1 << 20)
         shards = [torch.empty(S, dtype=torch.float32, device="cuda") for _ in range(cfg.R)]
         params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in cfg.shapes]
-        rs = L.bind_rs(grads, shards, cu_budget=512)
-        ag = L.bind_ag(stage, params, cu_budget=512)
+        rs = L.bind_rs(grads, shards, launch=Launch.bounded(512))
+        ag = L.bind_ag(stage, params, launch=Launch.bounded(512))
         side = torch.cuda.Stream()
         torch.cuda.synchronize()
         graph = _capture([rs, ag], side)
@@ -218,7 +222,7 @@ def test_graph_replay_full_size_step(gpu_available):
             torch.cuda.synchronize()
             graph.replay()
             torch.cuda.synchronize()
-            L.rs_bf16_to_fp32(grads, ref_shards, cu_budget=0)
+            L.rs_bf16_to_fp32(grads, ref_shards)
             L.ag_place(stage, ref_params)
             torch.cuda.synchronize()
             for a, b in zip(shards, ref_shards):
@@ -269,7 +273,7 @@ def test_prepared_calls_from_threads(gpu_available):
         def run(w):
             try:
                 with torch.cuda.stream(w["stream"]):
-                    rs = L.bind_rs(w["grads"], w["shards"], cu_budget=7)
+                    rs = L.bind_rs(w["grads"], w["shards"], launch=Launch.bounded(7))
                     ag = L.bind_ag(w["stage"], w["params"])
                     for _ in range(iters):
                         rs.launch(w["stream"])
@@ -294,35 +298,47 @@ def test_prepared_calls_from_threads(gpu_available):
                 assert np.array_equal(a, b)
 
 
-def test_rs_launch_shape_caps_occupancy(gpu_available):
-    """Default RS launches (cu_budget 0): 128-thread workgroups requesting 1/N of a gfx950 CU's 160 KiB
-    of local memory, N = 12 for C <= 2, 8 for C <= 4, 6 for C = 5-7 and 9-11; at C = 8 and from
-    C = 12 on, CU-exclusive workgroups of 8 items (1024 threads, the whole local memory)."""
+def test_rs_launch_shapes(gpu_available):
+    """The RS launch shape of each form (tide_rs_launch_shape) on a gfx950 CU's 160 KiB of local
+    memory.  Default: CU-exclusive workgroups of 1024 threads taking 16 items (C <= 3) or 8 (C >= 4,
+    the runtime-C form included) and the whole local memory; CU-exclusive N: 128*min(N, 8)
+    threads, N items; per-CU cap N: single-item 128-thread workgroups requesting 1/N of it; bounded:
+    128 threads, 4 items, no dynamic local memory."""
     lds_per_cu = 160 * 1024
-    for C, n in ((1, 12), (2, 12), (3, 8), (4, 8), (5, 6), (7, 6), (9, 6), (11, 6)):
+    for C, items in ((1, 16), (2, 16), (3, 16), (4, 8), (5, 8), (7, 8), (8, 8), (9, 8), (16, 8), (17, 8), (40, 8)):
         shape = tide_rs_launch_shape(C)
-        say(f"RS launch shape C={C}: {shape}")
-        assert shape["threads"] == 128 and shape["item_outputs"] == 1024
-        assert shape["lds_bytes"] * n <= lds_per_cu < shape["lds_bytes"] * (n + 1), (C, shape)
-    for C in (8, 12, 13, 16, 17, 24, 25, 40):
-        shape = tide_rs_launch_shape(C)
-        say(f"RS launch shape C={C}: {shape}")
-        assert shape == tide_rs_launch_shape(C, tide_rs_cu_exclusive(8)), (C, shape)
-        assert shape["threads"] == 1024 and lds_per_cu // 2 < shape["lds_bytes"] <= lds_per_cu, (C, shape)
+        say(f"RS default launch shape C={C}: {shape}")
+        assert shape == tide_rs_launch_shape(C, Launch.cu_exclusive(items)), (C, shape)
+        assert shape["threads"] == 1024 and shape["items_per_workgroup"] == items and shape["item_outputs"] == 1024
+        assert lds_per_cu // 2 < shape["lds_bytes"] <= lds_per_cu, (C, shape)  # one workgroup per CU
+    for n in (1, 3, 8, 16):
+        shape = tide_rs_launch_shape(4, Launch.cu_exclusive(n))
+        assert shape["threads"] == 128 * min(n, 8) and shape["items_per_workgroup"] == n, (n, shape)
+    for C in (2, 8, 20):
+        b = tide_rs_launch_shape(C, Launch.bounded(5))
+        assert b["threads"] == 128 and b["items_per_workgroup"] == 4 and b["lds_bytes"] < lds_per_cu // 16, b
+        for n in (2, 6, 12):
+            shape = tide_rs_launch_shape(C, Launch.per_cu_cap(n))
+            assert shape["threads"] == 128 and shape["items_per_workgroup"] == 1
+            assert shape["lds_bytes"] * n <= lds_per_cu < shape["lds_bytes"] * (n + 1), (C, n, shape)
+    for C, bad in ((3, Launch(TIDE_LAUNCH_CU_EXCLUSIVE, 32)), (5, Launch.cu_exclusive(16)),
+                   (1, Launch(TIDE_LAUNCH_CU_EXCLUSIVE, 24))):
+        with pytest.raises(TideError, match="INVALID"):
+            tide_rs_launch_shape(C, bad)
 
 
-def test_rs_negative_budget_sets_the_cap_and_changes_speed_only(gpu_available):
-    """cu_budget = -N: one unbounded launch with at most N RS workgroups per CU, for any C (compiled-C
+def test_rs_per_cu_cap_sets_the_cap_and_changes_speed_only(gpu_available):
+    """TIDE_LAUNCH_PER_CU_CAP N: one launch with at most N RS workgroups per CU, for any C (compiled-C
     and runtime-C kernels); the shards stay bit for bit those of the oracle, immediate and prepared."""
     for shapes, R, C in (GROUPS[1], ([(300, 70), (17,), (2048, 3)], 4, 18)):
         geo, S = ogeo.group_geometry(shapes, R)
         g = [[normal_bf16_bits(s, 1.0, 160, c, p) for p, s in enumerate(shapes)] for c in range(C)]
         grads = [[dev_bf16(x) for x in row] for row in g]
         want = oracle.reduce_scatter(g, shapes, R)
-        static = tide_rs_launch_shape(C, 5)["lds_bytes"]  # bounded launches add none: the kernel's own
+        static = tide_rs_launch_shape(C, Launch.bounded(5))["lds_bytes"]  # bounded launches add none
         for n in (1, 3, 6, 16, 64):
-            shape = tide_rs_launch_shape(C, -n)
-            say(f"RS C={C} cu_budget={-n}: {shape}")
+            shape = tide_rs_launch_shape(C, Launch.per_cu_cap(n))
+            say(f"RS C={C} per-CU cap {n}: {shape}")
             want_lds = max(static, (160 * 1024 // n) // 512 * 512)
             if n == 1:  # may exceed one workgroup's limit: then the smallest cap it can express
                 assert static < shape["lds_bytes"] <= want_lds, shape
@@ -330,11 +346,11 @@ def test_rs_negative_budget_sets_the_cap_and_changes_speed_only(gpu_available):
                 assert shape["lds_bytes"] == want_lds, (n, shape)
             with Layout(shapes, R) as L:
                 shards = poisoned_shards(R, S)
-                L.rs_bf16_to_fp32(grads, shards, cu_budget=-n)
+                L.rs_bf16_to_fp32(grads, shards, launch=Launch.per_cu_cap(n))
                 torch.cuda.synchronize()
                 assert_rs_equal(shards_bits(shards), want)
                 shards = poisoned_shards(R, S)
-                call = L.bind_rs(grads, shards, cu_budget=-n)
+                call = L.bind_rs(grads, shards, launch=Launch.per_cu_cap(n))
                 call.launch()
                 torch.cuda.synchronize()
                 call.close()
@@ -343,13 +359,13 @@ def test_rs_negative_budget_sets_the_cap_and_changes_speed_only(gpu_available):
 
 
 def test_rs_cu_exclusive_modes(gpu_available):
-    """cu_budget TIDE_RS_CU_EXCLUSIVE(W): one launch of 128*W-thread workgroups that take the largest
-    local memory a workgroup may request (one per CU).  For every W, the compiled forms (C = 8, 4)
-    and the runtime-C form (C = 6, 18), aligned and misaligned bases, immediate and prepared calls,
-    and Slot-Reuse's source addressing, the shards equal the oracle's bit for bit."""
-    lds_per_cu = 160 * 1024
+    """TIDE_LAUNCH_CU_EXCLUSIVE N: one launch of workgroups that take the largest local memory a
+    workgroup may request (one per CU), N = 1..8 items (one per 128-thread group) and, where C allows,
+    16 (two items' loads in flight per group).  For every N, compiled forms (C = 8, 4, 6, 2)
+    and the runtime-C form (C = 18), aligned and misaligned bases, immediate and prepared calls, and
+    Slot-Reuse's source addressing, the shards equal the oracle's bit for bit."""
     groups = [(GROUPS[1], 0), (([(4096, 64), (129, 7), (3,)], 8, 4), 1), (([(1000, 24), (5,), (96, 64)], 8, 6), 3),
-              (([(300, 70), (17,), (2048, 3)], 4, 18), 0)]
+              (([(6000, 40), (77, 9)], 4, 2), 0), (([(300, 70), (17,), (2048, 3)], 4, 18), 0)]
     for (shapes, R, C), pad in groups:
         geo, S = ogeo.group_geometry(shapes, R)
         g = [[normal_bf16_bits(s, 1.0, 190, c, p) for p, s in enumerate(shapes)] for c in range(C)]
@@ -359,40 +375,41 @@ def test_rs_cu_exclusive_modes(gpu_available):
             slots = [poisoned_slot(R, S) for _ in range(C)]
             for c in range(C):
                 L.slot_pack(grads[c], slots[c])
-            for w in range(1, 9):
-                budget = tide_rs_cu_exclusive(w)
-                shape = tide_rs_launch_shape(C, budget)
-                say(f"RS CU-exclusive C={C} W={w} pad={pad}: {shape}")
-                assert shape["threads"] == 128 * w and shape["item_outputs"] == 1024
-                assert lds_per_cu // 2 < shape["lds_bytes"] <= lds_per_cu, shape  # one workgroup per CU
+            ns = list(range(1, 9)) + ([16] if C <= 4 else [])
+            for n in ns:
+                launch = Launch.cu_exclusive(n)
+                say(f"RS CU-exclusive C={C} N={n} pad={pad}: {tide_rs_launch_shape(C, launch)}")
                 shards = poisoned_shards(R, S, pad)
-                L.rs_bf16_to_fp32(grads, shards, cu_budget=budget)
+                L.rs_bf16_to_fp32(grads, shards, launch=launch)
                 torch.cuda.synchronize()
                 assert_rs_equal(shards_bits(shards), want)
-                if w in (1, 4, 8):
+                if n in (1, 4, 8, 16):
                     shards = poisoned_shards(R, S, pad)
-                    call = L.bind_rs(grads, shards, cu_budget=budget)
+                    call = L.bind_rs(grads, shards, launch=launch)
                     call.launch()
                     torch.cuda.synchronize()
                     call.close()
                     assert_rs_equal(shards_bits(shards), want)
                     shards = poisoned_shards(R, S)
-                    L.rs_slots_bf16_to_fp32(slots, shards, cu_budget=budget)
+                    L.rs_slots_bf16_to_fp32(slots, shards, launch=launch)
                     torch.cuda.synchronize()
                     assert_rs_equal(shards_bits(shards), want)
     with Layout(*GROUPS[0][:2]) as L:
         shards = poisoned_shards(GROUPS[0][1], L.S)
         grads = [[torch.zeros(s, dtype=torch.bfloat16, device="cuda") for s in GROUPS[0][0]] for _ in range(4)]
-        with pytest.raises(TideError, match="INVALID"):
-            L.rs_bf16_to_fp32(grads, shards, cu_budget=tide_rs_cu_exclusive(8) - 1)
+        for bad in (Launch(TIDE_LAUNCH_CU_EXCLUSIVE, 9), Launch(TIDE_LAUNCH_CU_EXCLUSIVE, 32),
+                    Launch(TIDE_LAUNCH_CU_EXCLUSIVE, 0)):
+            with pytest.raises(TideError, match="INVALID"):
+                L.rs_bf16_to_fp32(grads, shards, launch=bad)
     with pytest.raises(ValueError):
-        tide_rs_cu_exclusive(9)
+        Launch.cu_exclusive(9)
 
 
 def test_ag_cu_exclusive_modes(gpu_available):
-    """cu_budget TIDE_AG_CU_EXCLUSIVE(W) for the placement kernel and Slot-Reuse packing: for every W,
+    """TIDE_LAUNCH_CU_EXCLUSIVE W for the placement kernel and Slot-Reuse packing: for every W,
     aligned and misaligned bases, immediate and prepared calls, the parameters and the packed slot equal
-    the oracle's bit for bit; the DMA engines and the runtime 2-D copy reject it."""
+    the oracle's bit for bit; the DMA engines and the runtime 2-D copy reject it, and so does the
+    placement any per-CU cap."""
     groups = [(GROUPS[1], 0), (GROUPS[6], 0), (([(1000, 24), (5,), (96, 64)], 8, 6), 3), (GROUPS[0], 1)]
     for (shapes, R, C), pad in groups:
         geo, S = ogeo.group_geometry(shapes, R)
@@ -404,19 +421,19 @@ def test_ag_cu_exclusive_modes(gpu_available):
         grads = [dev_bf16(x, pad) for x in g]
         with Layout(shapes, R) as L:
             for w in range(1, 9):
-                budget = tide_ag_cu_exclusive(w)
+                launch = Launch.cu_exclusive(w)
                 say(f"AG CU-exclusive W={w} R={R} pad={pad}")
                 params = poisoned_params(shapes)
-                L.ag_place(stage, params, cu_budget=budget)
+                L.ag_place(stage, params, launch=launch)
                 slot = poisoned_slot(R, S)
-                L.slot_pack(grads, slot, cu_budget=budget)
+                L.slot_pack(grads, slot, launch=launch)
                 torch.cuda.synchronize()
                 for a, b in zip([host_bits_bf16(q) for q in params], want):
                     assert np.array_equal(a, b), (w, pad)
                 assert np.array_equal(host_bits_bf16(slot), want_slot), (w, pad)
                 if w in (1, 4, 8):
                     params = poisoned_params(shapes)
-                    call = L.bind_ag(stage, params, cu_budget=budget)
+                    call = L.bind_ag(stage, params, launch=launch)
                     call.launch()
                     torch.cuda.synchronize()
                     call.close()
@@ -424,9 +441,10 @@ def test_ag_cu_exclusive_modes(gpu_available):
                         assert np.array_equal(a, b), (w, pad)
             for mode in (TIDE_AG_SDMA, TIDE_AG_COPY2D):
                 with pytest.raises(TideError, match="INVALID"):
-                    L.ag_place(stage, poisoned_params(shapes), mode=mode, cu_budget=tide_ag_cu_exclusive(4))
-            with pytest.raises(TideError, match="INVALID"):
-                L.ag_place(stage, poisoned_params(shapes), cu_budget=-1)
+                    L.ag_place(stage, poisoned_params(shapes), mode=mode, launch=Launch.cu_exclusive(4))
+            for bad in (Launch.per_cu_cap(1), Launch(TIDE_LAUNCH_CU_EXCLUSIVE, 16)):
+                with pytest.raises(TideError, match="INVALID"):
+                    L.ag_place(stage, poisoned_params(shapes), launch=bad)
 
 
 def test_destroy_with_work_in_flight(gpu_available):
@@ -440,7 +458,7 @@ def test_destroy_with_work_in_flight(gpu_available):
     say("destroy with work in flight")
     with Layout(shapes, R) as L:
         shards = poisoned_shards(R, S)
-        call = L.bind_rs(grads, shards, cu_budget=2)  # many short launches queued
+        call = L.bind_rs(grads, shards, launch=Launch.bounded(2))  # many short launches queued
         for _ in range(3):
             call.launch()
         call.close()
@@ -450,7 +468,7 @@ def test_destroy_with_work_in_flight(gpu_available):
         del scratch
     shards = poisoned_shards(R, S)
     L = Layout(shapes, R)
-    L.rs_bf16_to_fp32(grads, shards, cu_budget=2)
+    L.rs_bf16_to_fp32(grads, shards, launch=Launch.bounded(2))
     L.close()
     torch.cuda.synchronize()
     assert_rs_equal(shards_bits(shards), want)

@@ -105,7 +105,7 @@ def test_cu_mask_stream_confines_work_and_keeps_results(gpu_available):
                 got = [torch.full((L.S,), float("nan"), device="cuda") for _ in range(R)]
                 L.rs_bf16_to_fp32(grads, ref)
                 torch.cuda.synchronize()
-                call = L.bind_rs(grads, got, cu_budget=0)
+                call = L.bind_rs(grads, got)
                 call.launch(s_in)
                 torch.cuda.synchronize()
                 call.close()

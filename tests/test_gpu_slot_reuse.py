@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from oracle import geometry as ogeo
-from all_gather_placement_amd import Layout
+from all_gather_placement_amd import Launch, Layout
 from workloads import ORDERED, TINY, normal_bf16_bits, normal_bf16_cuda
 from tests.test_gpu_parity import GROUPS, POISON_BF16, assert_rs_equal, dev_bf16, host_bits_bf16, host_bits_f32, poisoned_shards, say
 
@@ -31,9 +31,9 @@ def test_slot_pack_bit_exact(gpu_available, case):
     geo, S = ogeo.group_geometry(shapes, R)
     want = oracle.pack_slot(g, shapes, R)
     with Layout(shapes, R) as L:
-        for budget in (0, 3):
+        for launch in (Launch.default(), Launch.bounded(3), Launch.cu_exclusive(6)):
             slot = poisoned_slot(R, S)
-            L.slot_pack([dev_bf16(x) for x in g], slot, cu_budget=budget)
+            L.slot_pack([dev_bf16(x) for x in g], slot, launch=launch)
             torch.cuda.synchronize()
             assert np.array_equal(host_bits_bf16(slot), want)
 
@@ -45,11 +45,11 @@ def test_slot_pack_alignment(gpu_available, g_off, s_off):
     g = [normal_bf16_bits(s, 1.0, 91, 0, p) for p, s in enumerate(shapes)]
     geo, S = ogeo.group_geometry(shapes, R)
     with Layout(shapes, R) as L:
-        for budget in (0, 3):
+        for launch in (Launch.default(), Launch.bounded(3)):
             slot = poisoned_slot(R, S, s_off)
-            L.slot_pack([dev_bf16(x, (g_off * (p + 1)) % 8) for p, x in enumerate(g)], slot, cu_budget=budget)
+            L.slot_pack([dev_bf16(x, (g_off * (p + 1)) % 8) for p, x in enumerate(g)], slot, launch=launch)
             torch.cuda.synchronize()
-            assert np.array_equal(host_bits_bf16(slot), oracle.pack_slot(g, shapes, R)), budget
+            assert np.array_equal(host_bits_bf16(slot), oracle.pack_slot(g, shapes, R)), launch
 
 
 @pytest.mark.parametrize("case", range(len(GROUPS)))
@@ -69,9 +69,11 @@ def test_rs_from_slots_bit_exact(gpu_available, case):
     want = oracle.rs_from_slots(slots_bits, shapes, R)
     assert np.array_equal(want.view(np.uint32), oracle.reduce_scatter(g, shapes, R).view(np.uint32))
     with Layout(shapes, R) as L:
-        for budget in (0, 5):
+        forms = [Launch.default(), Launch.bounded(5), Launch.per_cu_cap(4), Launch.cu_exclusive(2)]
+        forms += [Launch.cu_exclusive(16)] if C <= 4 else []
+        for launch in forms:
             shards = poisoned_shards(R, S)
-            L.rs_slots_bf16_to_fp32([dev_bf16(x) for x in slots_bits], shards, cu_budget=budget)
+            L.rs_slots_bf16_to_fp32([dev_bf16(x) for x in slots_bits], shards, launch=launch)
             torch.cuda.synchronize()
             assert_rs_equal(np.stack([host_bits_f32(x) for x in shards]), want)
 
