@@ -19,7 +19,7 @@
 namespace tide {
 namespace {
 
-static_assert(TIDE_CU_EXCLUSIVE_MAX_ITEMS == 2 * kRsCuMaxGroups && rs_cu_items_ok(4, 2) && !rs_cu_items_ok(5, 2),
+static_assert(TIDE_CU_EXCLUSIVE_MAX_ITEMS == 2 * kRsCuMaxGroups && rs_cu_items_ok(4, 2),
               "header and kernels agree on the widest CU-exclusive RS workgroup");
 
 struct Range {

@@ -210,14 +210,38 @@ __device__ __forceinline__ void full_item_store(const f32x4* xfer, float* dst, i
 #endif
 }
 
+// Wave-local form of the exchange: a full item's wave w computed outputs 512*w .. 512*w + 511
+// itself, so it can redistribute them through its own 2 KiB of the group's slot and store them as
+// two 1 KiB wave instructions with no workgroup barrier: every wave stores as soon as its sums are
+// done.  LDS instructions of one wave execute in order; the wavefront-scope fences only keep the
+// compiler from moving the reads above the writes (or the next item's writes above these reads).
+// Measured on MI355X against the workgroup-wide exchange (one barrier, then every group's stores):
+// single-item workgroups (bounded launches, per-CU caps) +0.9% / +-0%; CU-exclusive workgroups of
+// W = 2 / 3 / 4 groups +1.8 / +2.0 / +2.5%, 5 +-0%, 6 / 7 / 8 -4 / -4 / -1.4% (Llama-3.1-70B group,
+// two runs each): wide workgroups stream better when all their stores leave together.
+constexpr int kRsCuWaveMaxGroups = 4;  // CU-exclusive workgroups of at most this many groups store wave by wave
+__device__ __forceinline__ void full_item_wave_store(const float a[8], f32x4* xfer, float* dst, int tid) {
+  const int w = tid >> 6, l = tid & 63;
+  f32x4* xw = xfer + w * 128;
+  xw[2 * l] = f32x4{a[0], a[1], a[2], a[3]};
+  xw[2 * l + 1] = f32x4{a[4], a[5], a[6], a[7]};
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const f32x4 v0 = xw[l], v1 = xw[64 + l];
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(dst + 512 * w, 0, 2048, 0x00020000);
+  constexpr int aux = TIDE_RS_STORE_AUX >= 0 ? TIDE_RS_STORE_AUX : 18;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v0), rsrc, 16 * l, 0, aux);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v1), rsrc, 16 * (64 + l), 0, aux);
+  // the next item's writes to this slot come after these reads (program order within the wave)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+}
+
 template <int CT>
 __device__ __forceinline__ void full_item_finish(const u32x4 x[CT], float* dst, f32x4* xfer, int tid) {
   float a[8];
   full_item_sums<CT>(x, a);
-  __syncthreads();  // the previous item's readers are done with xfer
-  full_item_put(a, xfer, tid);
-  __syncthreads();
-  full_item_store(xfer, dst, tid);
+  full_item_wave_store(a, xfer, dst, tid);
 }
 
 // Full work item, runtime contributor count (C > kRsMaxCt): contributors in blocks of 8, each
@@ -273,10 +297,7 @@ __device__ __forceinline__ void full_item_rt(void* const* gptr, int32_t P, const
                                              f32x4* xfer, int tid) {
   float a[8];
   full_item_rt_sums(gptr, P, ch, C, tid, a);
-  __syncthreads();  // the previous item's readers are done with xfer
-  full_item_put(a, xfer, tid);
-  __syncthreads();
-  full_item_rt_store(xfer, dst, tid);
+  full_item_wave_store(a, xfer, dst, tid);
 }
 
 // RS kernel.  CT in 1..kRsMaxCt: contributor count fixed at compile time; CT == 0: any C >= 1.
@@ -390,13 +411,14 @@ __device__ __forceinline__ void load_bases(const unsigned short* const* __restri
   }
 }
 
-// One RS work item of a CU-exclusive workgroup's group (the per-item work of rs_kernel): a full item
-// leaves its sums in the group's exchange slot `xfer` and returns the destination to store them to
-// after the workgroup barrier; any other item is written directly and returns nullptr.
+// One RS work item of a CU-exclusive workgroup's group (the per-item work of rs_kernel): with `wave`,
+// a full item is stored through the wave-local exchange and nullptr returned; otherwise it leaves its
+// sums in the group's exchange slot `xfer` and returns the destination to store them to after the
+// workgroup barrier.  Any other item is written directly and returns nullptr.
 template <int CT, bool VEC, bool FLAT>
 __device__ __forceinline__ float* rs_cu_item(const RsChunk* __restrict__ chunks, int64_t item,
                                              void* const* __restrict__ ptrs, int32_t P, int32_t C, int64_t S,
-                                             f32x4* xfer, int tid) {
+                                             f32x4* xfer, int tid, bool wave) {
   const unsigned short* const* __restrict__ gptr = reinterpret_cast<const unsigned short* const*>(ptrs);
   float* const* __restrict__ sptr = reinterpret_cast<float* const*>(ptrs + static_cast<int64_t>(C) * P);
   const int nc = CT > 0 ? CT : C;
@@ -426,8 +448,12 @@ __device__ __forceinline__ float* rs_cu_item(const RsChunk* __restrict__ chunks,
         float a[8];
         full_item_load<CT>(src, tid, x);
         full_item_sums<CT>(x, a);
-        full_item_put(a, xfer, tid);
-        full_dst = dst;
+        if (wave) {
+          full_item_wave_store(a, xfer, dst, tid);
+        } else {
+          full_item_put(a, xfer, tid);
+          full_dst = dst;
+        }
       } else
 #endif
       {
@@ -447,8 +473,12 @@ __device__ __forceinline__ float* rs_cu_item(const RsChunk* __restrict__ chunks,
       if (full_item(ch)) {
         float a[8];
         full_item_rt_sums(ptrs, P, ch, nc, tid, a);
-        full_item_put(a, xfer, tid);
-        full_dst = dst;
+        if (wave) {
+          full_item_wave_store(a, xfer, dst, tid);
+        } else {
+          full_item_put(a, xfer, tid);
+          full_dst = dst;
+        }
       } else
 #endif
       {
@@ -480,9 +510,10 @@ __device__ __forceinline__ float* rs_cu_item(const RsChunk* __restrict__ chunks,
 // for instance) takes it within one RS workgroup lifetime, while the RS itself runs as one launch
 // with W*KI items resident per CU.  With KI > 1 (few contributors, whose items carry few bytes), a
 // group whose KI items are all full issues every load of all of them before its first sum, so the
-// CU keeps as many bytes in flight as with more contributors.  There is one workgroup barrier,
-// outside every per-group branch: full items leave their sums in their exchange slots and are
-// stored after it; the others are finished before it.
+// CU keeps as many bytes in flight as with more contributors.  Workgroups of more than
+// kRsCuWaveMaxGroups groups have one workgroup barrier, outside every per-group branch: full items
+// leave their sums in their exchange slots and are stored after it, all together; the others are
+// finished before it.  Narrower workgroups store each full item wave by wave, with no barrier.
 template <int CT, int KI, bool VEC, bool FLAT>
 __global__ __launch_bounds__(kThreads * kRsCuMaxGroups) void rs_cu_kernel(const RsChunk* __restrict__ chunks,
                                                                           int64_t count,
@@ -500,6 +531,7 @@ __global__ __launch_bounds__(kThreads * kRsCuMaxGroups) void rs_cu_kernel(const 
   }
   const int64_t first = (slot * W + grp) * KI;
   f32x4* xfer = xfer_dyn + static_cast<int64_t>(grp) * KI * 2 * kThreads;
+  const bool wave = W <= kRsCuWaveMaxGroups;  // uniform over the workgroup
   float* full_dst[KI];
 #pragma unroll
   for (int k = 0; k < KI; ++k) full_dst[k] = nullptr;
@@ -537,7 +569,12 @@ __global__ __launch_bounds__(kThreads * kRsCuMaxGroups) void rs_cu_kernel(const 
         for (int k = 0; k < KI; ++k) {
           float a[8];
           full_item_sums<CT>(x[k], a);
-          full_item_put(a, xfer + k * 2 * kThreads, tid);
+          if (wave) {
+            full_item_wave_store(a, xfer + k * 2 * kThreads, full_dst[k], tid);
+            full_dst[k] = nullptr;
+          } else {
+            full_item_put(a, xfer + k * 2 * kThreads, tid);
+          }
         }
         done = true;
       }
@@ -548,19 +585,21 @@ __global__ __launch_bounds__(kThreads * kRsCuMaxGroups) void rs_cu_kernel(const 
 #pragma unroll
     for (int k = 0; k < KI; ++k) {
       if (first + k < count)
-        full_dst[k] = rs_cu_item<CT, VEC, FLAT>(chunks, first + k, ptrs, P, C, S, xfer + k * 2 * kThreads, tid);
+        full_dst[k] = rs_cu_item<CT, VEC, FLAT>(chunks, first + k, ptrs, P, C, S, xfer + k * 2 * kThreads, tid, wave);
     }
   }
 
 #if TIDE_RS_WIDE
-  __syncthreads();  // every group's exchange slots are written
+  if (!wave) {
+    __syncthreads();  // every group's exchange slots are written
 #pragma unroll
-  for (int k = 0; k < KI; ++k) {
-    if (full_dst[k] != nullptr) {
-      if (CT > 0)
-        full_item_store(xfer + k * 2 * kThreads, full_dst[k], tid);
-      else
-        full_item_rt_store(xfer + k * 2 * kThreads, full_dst[k], tid);
+    for (int k = 0; k < KI; ++k) {
+      if (full_dst[k] != nullptr) {
+        if (CT > 0)
+          full_item_store(xfer + k * 2 * kThreads, full_dst[k], tid);
+        else
+          full_item_rt_store(xfer + k * 2 * kThreads, full_dst[k], tid);
+      }
     }
   }
 #endif
@@ -781,7 +820,7 @@ hipError_t launch_rs_cu_ct(const RsChunk* chunks, int64_t count, int grid, int t
 template <int CT, bool FLAT>
 hipError_t launch_rs_cu_ki(int ki, const RsChunk* chunks, int64_t count, int grid, int threads, void* const* ptrs,
                            int32_t P, int32_t C, int64_t S, bool vec, int lds, hipStream_t s) {
-  if constexpr (CT >= 1 && CT <= 4) {
+  if constexpr (CT >= 1 && CT <= kRsCuKi2MaxC) {
     if (ki == 2) return launch_rs_cu_ct<CT, 2, FLAT>(chunks, count, grid, threads, ptrs, P, C, S, vec, lds, s);
   }
   if (ki != 1) return hipErrorInvalidValue;

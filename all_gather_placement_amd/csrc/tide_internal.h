@@ -156,8 +156,10 @@ static_assert(kThreads * kRsCuMaxGroups <= 1024, "a CU-exclusive workgroup fits 
 // Items per group of a CU-exclusive RS workgroup: 1, or 2 for C <= 4 (compiled contributor counts):
 // all of a group's loads stay in registers at once.  Measured on MI355X (Llama-3.1-8B shapes, one
 // 8-group workgroup per CU): 2 items per group over 1 at C = 1 / 2 / 3 / 4: 5.9 / 6.12 / 6.17 / 6.19
-// against 4.76 / 5.54 / 6.03 / 6.14 TB/s; 4 items per group at C = 1 / 2: 5.66 / 5.78, not kept.
-constexpr bool rs_cu_items_ok(int C, int ki) { return ki == 1 || (ki == 2 && C >= 1 && C <= 4); }
+// against 4.76 / 5.54 / 6.03 / 6.14 TB/s; 4 items per group at C = 1 / 2: 5.66 / 5.78, and 2 items per
+// group at C = 8 (16 in flight per CU): 6.02 against 6.34 TB/s for 8 items (Llama-3.1-70B), not kept.
+constexpr int kRsCuKi2MaxC = 4;
+constexpr bool rs_cu_items_ok(int C, int ki) { return ki == 1 || (ki == 2 && C >= 1 && C <= kRsCuKi2MaxC); }
 // Local memory of the exchange slots of a CU-exclusive RS workgroup: 4 KiB per item in flight.
 constexpr int rs_cu_xfer_bytes(int groups, int ki) { return groups * ki * 2 * kThreads * 16; }
 static_assert(rs_cu_xfer_bytes(kRsCuMaxGroups, 2) <= 64 * 1024, "the widest CU-exclusive RS workgroup fits a CU");
