@@ -121,6 +121,8 @@ def build(verbose: bool = False, extra=(), out: str = LIB, sources=SOURCES, prob
     tmp = out + ".tmp"
     link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
             "-Wl,-rpath,/opt/rocm/lib", "-L/opt/rocm/lib", "-lamdhip64"]
+    if out == PROBE_LIB:
+        link.append("-lhsa-runtime64")  # the DMA engines' rectangular copy (tide_probe_dma_rect_copies)
     if verbose:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)

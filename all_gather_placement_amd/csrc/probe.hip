@@ -1,6 +1,9 @@
 // Occupancy and interference probes for gfx950 (libtide_probe.so); see include/tide_probe.h.
 #include <hip/hip_runtime.h>
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
 
+#include <chrono>
 #include <vector>
 
 #include "../../include/tide_probe.h"
@@ -154,9 +157,106 @@ int launch_mix_c(int32_t mode, const unsigned short* const* src, float* dst, int
   }
 }
 
+// The HSA agent of HIP device `dev`, matched by PCI domain, bus and device.
+struct AgentMatch {
+  uint32_t domain, bdf;
+  hsa_agent_t agent;
+  bool found;
+};
+
+hsa_status_t match_agent(hsa_agent_t a, void* data) {
+  auto* m = static_cast<AgentMatch*>(data);
+  hsa_device_type_t t;
+  if (hsa_agent_get_info(a, HSA_AGENT_INFO_DEVICE, &t) != HSA_STATUS_SUCCESS || t != HSA_DEVICE_TYPE_GPU)
+    return HSA_STATUS_SUCCESS;
+  uint32_t domain = 0, bdf = 0;
+  if (hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_DOMAIN), &domain) != HSA_STATUS_SUCCESS ||
+      hsa_agent_get_info(a, static_cast<hsa_agent_info_t>(HSA_AMD_AGENT_INFO_BDFID), &bdf) != HSA_STATUS_SUCCESS)
+    return HSA_STATUS_SUCCESS;
+  if (domain == m->domain && (bdf & ~7u) == (m->bdf & ~7u)) {  // function bits ignored
+    m->agent = a;
+    m->found = true;
+    return HSA_STATUS_INFO_BREAK;
+  }
+  return HSA_STATUS_SUCCESS;
+}
+
+bool current_gpu_agent(hsa_agent_t* out) {
+  int dev = 0, bus = 0, device = 0, domain = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&bus, hipDeviceAttributePciBusId, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&device, hipDeviceAttributePciDeviceId, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&domain, hipDeviceAttributePciDomainID, dev) != hipSuccess)
+    return false;
+  if (hsa_init() != HSA_STATUS_SUCCESS) return false;  // reference counted: HIP holds the runtime open too
+  AgentMatch m{static_cast<uint32_t>(domain), (static_cast<uint32_t>(bus) << 8) | (static_cast<uint32_t>(device) << 3),
+               {0}, false};
+  hsa_iterate_agents(match_agent, &m);
+  if (m.found) *out = m.agent;
+  return m.found;
+}
+
 }  // namespace
 
 extern "C" {
+
+int32_t tide_probe_dma_rect_copies(int32_t n, const tide_probe_rect* rects, int64_t timeout_ms, double* elapsed_us) {
+  if (n < 1 || rects == nullptr || timeout_ms < 0) return -1;
+  const int64_t u32max = 0xffffffffll;
+  for (int32_t i = 0; i < n; ++i) {
+    const tide_probe_rect& r = rects[i];
+    if (r.dst == nullptr || r.src == nullptr || r.width <= 0 || r.rows <= 0 || r.width > u32max || r.rows > u32max ||
+        r.width % 4 || r.dst_pitch % 4 || r.src_pitch % 4 || r.width > r.dst_pitch || r.width > r.src_pitch ||
+        (reinterpret_cast<uintptr_t>(r.dst) & 3) || (reinterpret_cast<uintptr_t>(r.src) & 3))
+      return -1;
+  }
+  hsa_agent_t gpu;
+  if (!current_gpu_agent(&gpu)) return -2;
+  std::vector<hsa_signal_t> sig;
+  sig.reserve(n);
+  int32_t rc = 0;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int32_t i = 0; i < n && rc == 0; ++i) {
+    const tide_probe_rect& r = rects[i];
+    hsa_signal_t s;
+    if (hsa_signal_create(1, 0, nullptr, &s) != HSA_STATUS_SUCCESS) {
+      rc = -1;
+      break;
+    }
+    hsa_pitched_ptr_t dst{r.dst, static_cast<size_t>(r.dst_pitch), static_cast<size_t>(r.dst_pitch * r.rows)};
+    hsa_pitched_ptr_t src{const_cast<void*>(r.src), static_cast<size_t>(r.src_pitch),
+                          static_cast<size_t>(r.src_pitch * r.rows)};
+    const hsa_dim3_t zero{0, 0, 0};
+    const hsa_dim3_t range{static_cast<uint32_t>(r.width), static_cast<uint32_t>(r.rows), 1};
+    const hsa_status_t st =
+        hsa_amd_memory_async_copy_rect(&dst, &zero, &src, &zero, &range, gpu, hsaDeviceToDevice, 0, nullptr, s);
+    if (st != HSA_STATUS_SUCCESS) {
+      hsa_signal_destroy(s);
+      rc = static_cast<int32_t>(st);
+      break;
+    }
+    sig.push_back(s);
+  }
+  // wait for every issued copy, against one deadline
+  const auto deadline = t0 + std::chrono::milliseconds(timeout_ms);
+  for (hsa_signal_t s : sig) {
+    while (hsa_signal_load_scacquire(s) != 0) {
+      const auto now = std::chrono::steady_clock::now();
+      if (now >= deadline) {
+        rc = -3;
+        break;
+      }
+      const uint64_t left_ns =
+          static_cast<uint64_t>(std::chrono::duration_cast<std::chrono::nanoseconds>(deadline - now).count());
+      hsa_signal_wait_scacquire(s, HSA_SIGNAL_CONDITION_LT, 1, left_ns, HSA_WAIT_STATE_BLOCKED);
+    }
+    if (rc == -3) break;
+  }
+  const auto t1 = std::chrono::steady_clock::now();
+  if (elapsed_us) *elapsed_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+  if (rc != -3)
+    for (hsa_signal_t s : sig) hsa_signal_destroy(s);  // after a timeout they may still be signalled: kept
+  return rc;
+}
 
 int32_t tide_probe_mix(int32_t C, int32_t mode, const void* const* src, float* dst, int64_t items, int32_t lds_bytes,
                        void* stream) {

@@ -18,6 +18,13 @@ RECORD_BYTES = 32
 _lib = None
 
 
+class Rect(ctypes.Structure):
+    """tide_probe_rect: `rows` rows of `width` bytes from src + i*src_pitch to dst + i*dst_pitch."""
+
+    _fields_ = [("dst", ctypes.c_void_p), ("src", ctypes.c_void_p), ("dst_pitch", ctypes.c_int64),
+                ("src_pitch", ctypes.c_int64), ("width", ctypes.c_int64), ("rows", ctypes.c_int64)]
+
+
 def load_probe_library():
     global _lib
     if _lib is None:
@@ -42,6 +49,9 @@ def load_probe_library():
         lib.tide_probe_stream_destroy.argtypes = [ctypes.c_void_p]
         lib.tide_probe_wall_clock_khz.restype = ctypes.c_int64
         lib.tide_probe_wall_clock_khz.argtypes = []
+        lib.tide_probe_dma_rect_copies.restype = ctypes.c_int32
+        lib.tide_probe_dma_rect_copies.argtypes = [ctypes.c_int32, ctypes.POINTER(Rect), ctypes.c_int64,
+                                                   ctypes.POINTER(ctypes.c_double)]
         _lib = lib
     return _lib
 
@@ -136,3 +146,17 @@ def decode(records_host):
     se = (hw >> 13) & 0x3
     return {"start": r[:, 0].astype(np.int64), "end": r[:, 1].astype(np.int64), "xcc": xcc, "se": se, "sh": sh,
             "cu": cu, "cu_key": ((xcc * 4 + se) * 2 + sh) * 16 + cu}
+
+
+def dma_rect_copies(rects, timeout_ms: int = 10000) -> float:
+    """Run rectangular copies on the DMA engines (tide_probe_dma_rect_copies): `rects` is a sequence of
+    (dst, src, dst_pitch, src_pitch, width, rows) with device addresses and byte sizes.  The copies
+    are not stream-ordered: synchronise the device before the call.  Returns the host time from the
+    first issue to the last completion, in microseconds."""
+    lib = load_probe_library()
+    arr = (Rect * max(len(rects), 1))(*[Rect(*r) for r in rects])
+    us = ctypes.c_double()
+    rc = lib.tide_probe_dma_rect_copies(len(rects), arr, int(timeout_ms), ctypes.byref(us))
+    if rc != 0:
+        raise RuntimeError(f"tide_probe_dma_rect_copies failed: {rc}")
+    return us.value

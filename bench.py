@@ -85,6 +85,9 @@ def parse():
                     help="the RS's access shape with reads or writes left out, beside the library RS (C = 1-8)")
     ap.add_argument("--copy-sizes", action="store_true",
                     help="placement of one flat parameter of 1-256 MiB over R = 1 and 8 ranks on each engine")
+    ap.add_argument("--dma-rect", action="store_true",
+                    help="placement on the four layer groups: kernel, DMA engines per segment, and one DMA-engine "
+                         "rectangular copy per parameter (the copy-engine form of a strided copy per parameter)")
     ap.add_argument("--slot-reuse", action="store_true",
                     help="instead of the step benchmark: Slot-Reuse (pack into slots + RS from slots) vs in-place RS")
     return ap.parse_args()
@@ -867,6 +870,89 @@ def overlap(args, log):
           flush=True)
 
 
+def rect_plan(L, stage, params):
+    """One rectangular copy per parameter of the placement (rows = the ranks whose slice is full,
+    source pitch = one stage slot, destination contiguous) plus one single-row copy for the rank whose
+    slice is part padding, from the library's layout.  (dst, src, dst_pitch, src_pitch, width, rows)."""
+    S = L.S
+    base = stage.data_ptr()
+    rects = []
+    for p, q in enumerate(params):
+        rows, Lp, m, o = L.param(p)
+        if rows * Lp == 0:
+            continue
+        e = m * Lp
+        full = rows // m
+        if full:
+            rects.append((q.data_ptr(), base + 2 * o, 2 * e, 2 * S, 2 * e, full))
+        v = rows - full * m
+        if v:
+            rects.append((q.data_ptr() + 2 * full * e, base + 2 * (full * S + o), 2 * v * Lp, 2 * v * Lp, 2 * v * Lp, 1))
+    return rects
+
+
+def dma_rect(args, log):
+    """AG placement of each layer group three ways, timed on the same stage and parameters: the
+    placement kernel (default launch), the DMA engines with one 1-D copy per (parameter, rank) segment
+    (TIDE_AG_SDMA), and the DMA engines with one rectangular copy per parameter (libtide_probe's
+    tide_probe_dma_rect_copies, all issued before waiting; host-synchronous, not stream-ordered).
+    The rectangular placement is checked bit for bit against the kernel's.  GB/s = 4 * numel / t."""
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import Layout, TIDE_AG_KERNEL, TIDE_AG_SDMA
+    from all_gather_placement_amd import probe as pr
+    from workloads import CONFIGS, normal_bf16_cuda
+
+    dev = torch.device("cuda:0")
+    rows = []
+    for name in ("llama3_1_8b_layer", "llama3_1_70b_layer", "qwen3_30b_a3b", "wan2_2_block"):
+        cfg = CONFIGS[name]
+        L = Layout(cfg.shapes, cfg.R)
+        L.prepare()
+        stage = normal_bf16_cuda((cfg.R * L.S,), cfg.sigma, cfg.cfg_id, 1 << 20, 0)
+        ref = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in cfg.shapes]
+        out = [torch.full(s, float("nan"), dtype=torch.bfloat16, device=dev) for s in cfg.shapes]
+        nbytes = 4 * cfg.numel()
+
+        def timed(fn, n):
+            ts = []
+            for _ in range(n):
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return statistics.median(ts)
+
+        L.ag_place(stage, ref, mode=TIDE_AG_KERNEL)
+        t_kernel = timed(lambda: L.ag_place(stage, ref, mode=TIDE_AG_KERNEL), 9)
+        L.ag_place(stage, out, mode=TIDE_AG_SDMA)
+        t_sdma = timed(lambda: L.ag_place(stage, out, mode=TIDE_AG_SDMA), 3)
+        segments = sum(1 for p in range(L.P) for r in range(L.R) if L.segment(p, r)[1] > 0)
+        rects = rect_plan(L, stage, out)
+        for q in out:
+            q.view(torch.int16).fill_(0x7FC1)
+        torch.cuda.synchronize()
+        t_rect = [pr.dma_rect_copies(rects) / 1e3 for _ in range(3)]
+        exact = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(out, ref))
+        row = {"workload": name, "P": cfg.P, "R": cfg.R, "bytes": nbytes,
+               "kernel_ms": round(t_kernel, 4), "kernel_gbps": round(nbytes / t_kernel / 1e6, 1),
+               "sdma_segments": segments, "sdma_ms": round(t_sdma, 3), "sdma_gbps": round(nbytes / t_sdma / 1e6, 1),
+               "rect_copies": len(rects), "rect_ms_median": round(statistics.median(t_rect), 3),
+               "rect_gbps": round(nbytes / statistics.median(t_rect) / 1e6, 1), "rect_bit_exact": exact}
+        log(json.dumps(row))
+        rows.append(row)
+        L.close()
+        del stage, ref, out
+        torch.cuda.empty_cache()
+    print(json.dumps({"experiment": "AG placement: kernel vs DMA engines per segment vs one DMA rectangular copy "
+                                    "per parameter", "rows": rows}), flush=True)
+
+
 def mix_bound(args, log):
     """The RS's access shape with its writes or its reads left out (the mix probe of libtide_probe.so),
     beside the library RS on the same buffers: one flat parameter of 2^27 elements, R = 1, C = 1, 2,
@@ -964,6 +1050,10 @@ def main():
     if args.slot_reuse:
         torch.cuda.set_device(0)
         slot_reuse(args, log)
+        return
+    if args.dma_rect:
+        torch.cuda.set_device(0)
+        dma_rect(args, log)
         return
     if args.probes:
         torch.cuda.set_device(0)

@@ -108,6 +108,35 @@ int32_t tide_probe_stream_create_cu_mask(int32_t first_cu, int32_t n_cus, void**
 /* Destroy a stream made by tide_probe_stream_create_cu_mask.  Returns 0 or a hipError_t value; -1 for NULL. */
 int32_t tide_probe_stream_destroy(void* stream);
 
+/* One rectangular copy for tide_probe_dma_rect_copies: `rows` rows of `width` bytes, row i read from
+ * src + i*src_pitch and written to dst + i*dst_pitch (device addresses; every address, pitch and
+ * width a multiple of 4 bytes). */
+typedef struct tide_probe_rect {
+  void* dst;
+  const void* src;
+  int64_t dst_pitch;
+  int64_t src_pitch;
+  int64_t width;
+  int64_t rows;
+} tide_probe_rect;
+
+/*
+ * Rectangular copies on the DMA engines, the copy-engine form of [Endgame] Figure 5b's placement
+ * (each parameter filled from the stage slots by one strided copy).  HIP's 2-D copies between device
+ * buffers run as shader kernels on ROCm; the DMA engines' rectangular copy is reached through the HSA
+ * runtime's provisional hsa_amd_memory_async_copy_rect on the current device's GPU agent.  All n
+ * copies are issued before any is waited for, then the host waits for every one (at most timeout_ms
+ * in all).  The copies are not ordered with any HIP stream: the caller synchronises the device
+ * first and reads the results after the call returns.
+ *   elapsed_us  may be NULL; receives the host time from the first issue to the last completion.
+ * Returns 0; -1 for bad arguments (n < 1, NULL rects, a NULL pointer, a size or pitch not a
+ * positive multiple of 4, width beyond a pitch, more than 2^32-1 rows or width bytes); -2 when the
+ * current device's GPU agent is not found; -3 when the copies did not all finish within timeout_ms
+ * (some may still be running); otherwise the hsa_status_t of the first copy the runtime refused
+ * (the copies issued before it have finished when the call returns).
+ */
+int32_t tide_probe_dma_rect_copies(int32_t n, const tide_probe_rect* rects, int64_t timeout_ms, double* elapsed_us);
+
 /* Device wall-clock rate in kHz (hipDeviceAttributeWallClockRate of the current device), or -1. */
 int64_t tide_probe_wall_clock_khz(void);
 

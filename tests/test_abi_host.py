@@ -350,8 +350,9 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     text = open(os.path.join(ROOT, "include", "tide_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(tide_probe_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["tide_probe_build_id", "tide_probe_clock", "tide_probe_launch", "tide_probe_mix",
-                     "tide_probe_stream_create_cu_mask", "tide_probe_stream_destroy", "tide_probe_wall_clock_khz"]
+    assert names == ["tide_probe_build_id", "tide_probe_clock", "tide_probe_dma_rect_copies", "tide_probe_launch",
+                     "tide_probe_mix", "tide_probe_stream_create_cu_mask", "tide_probe_stream_destroy",
+                     "tide_probe_wall_clock_khz"]
     for n in names:
         assert hasattr(lib, n)
     assert lib.tide_probe_launch(0, 0, 10, None, None) == -1
@@ -374,6 +375,15 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert lib.tide_probe_stream_destroy(None) == -1
     assert h.value is None
     assert pr.clock_mhz([0, 100000, 5, 5 + 2_400_000], 100000) == 2400.0  # 1 ms of wall clock, 2.4M cycles
+    # rectangular DMA copies: argument checks come before any HSA or HIP call
+    a, b = 1 << 40, 1 << 41
+    bad_rects = [(a, b, 64, 64, 0, 1), (a, b, 64, 64, 6, 1), (a, b, 64, 66, 8, 1), (a, b, 32, 64, 64, 1),
+                 (a + 2, b, 64, 64, 8, 1), (None, b, 64, 64, 8, 1), (a, b, 64, 64, 8, 0), (a, b, 1 << 34, 1 << 34, 1 << 33, 1)]
+    for r in bad_rects:
+        arr = (pr.Rect * 1)(pr.Rect(*r))
+        assert lib.tide_probe_dma_rect_copies(1, arr, 100, None) == -1, r
+    assert lib.tide_probe_dma_rect_copies(0, (pr.Rect * 1)(), 100, None) == -1
+    assert lib.tide_probe_dma_rect_copies(1, None, 100, None) == -1
 
 
 def test_binding_checks_pointer_array_lengths_before_the_call():

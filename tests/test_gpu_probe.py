@@ -115,3 +115,26 @@ def test_cu_mask_stream_confines_work_and_keeps_results(gpu_available):
             torch.cuda.synchronize()
             pr.destroy_stream(h_in)
             pr.destroy_stream(h_out)
+
+
+def test_dma_rect_copies_place_a_group_like_the_oracle(gpu_available):
+    """The DMA engines' rectangular copy, one per parameter plus one per partly padded rank (the
+    placement shape of bench.py --dma-rect), lands every parameter element as the oracle's copy-out."""
+    import oracle
+    from all_gather_placement_amd import Layout
+    from bench import rect_plan
+    from workloads import normal_bf16_bits
+
+    shapes, R = [(64, 8), (33, 6), (16,), (3, 2, 4)], 4  # every slice and offset a whole 4-byte word
+    with Layout(shapes, R) as L:
+        stage_bits = normal_bf16_bits((R * L.S,), 1.0, 250, 0)
+        stage = torch.from_numpy(stage_bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+        params = [torch.full(s, -1, dtype=torch.int16, device="cuda").view(torch.bfloat16) for s in shapes]
+        rects = rect_plan(L, stage, params)
+        assert len(rects) == 5  # (33, 6) has a partly padded rank: 33 rows = 3 full slices of 9 + 6
+        torch.cuda.synchronize()
+        us = pr.dma_rect_copies(rects)
+        assert us > 0
+        want = oracle.all_gather_place(stage_bits, shapes, R)
+        for q, w in zip(params, want):
+            assert np.array_equal(q.view(torch.int16).cpu().numpy().view(np.uint16), w)
