@@ -248,27 +248,6 @@ int ensure_dma(DeviceState* st) {
 // Enqueueing validated work
 // ---------------------------------------------------------------------------------------------
 
-// Launch plan for `count` work items: bounded = grids of at most `max_wgs` workgroups, each taking
-// `bounded_items` items and exiting (bounded_items 0: one launch, workgroups walk every item);
-// otherwise one launch of single-item workgroups (or kPersistentWorkgroups walking them).
-struct Plan {
-  int grid;
-  int items;
-  int64_t per_launch;
-};
-
-Plan plan_for(int64_t count, bool bounded, int64_t max_wgs, int bounded_items) {
-  if (!bounded) {
-    const int64_t cap = kPersistentWorkgroups > 0 ? kPersistentWorkgroups : (int64_t(1) << 30);
-    const int64_t g = std::min<int64_t>(count, cap);
-    const int items = int((count + g - 1) / g);
-    return Plan{int(g), items, int64_t(g) * items};
-  }
-  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(count, max_wgs));
-  const int64_t items = bounded_items > 0 ? bounded_items : (count + grid - 1) / grid;
-  return Plan{int(grid), int(items), grid * items};
-}
-
 // Kernels of a table-driven request (RS, RS from slots, AG kernel, slot pack), reading the device
 // pointer table `dev_table`.  Only kernel launches: nothing is allocated, copied or recorded.
 int enqueue_kernels(const tide_layout* L, const DeviceState* st, const Request& q, void* const* dev_table,
@@ -437,6 +416,9 @@ namespace {
 int mark_launch(tide_call* call, hipStream_t hs) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   const hipError_t q = hipStreamIsCapturing(hs, &cs);
+  // a failed query (the legacy stream while another stream captures, say) leaves the thread's last
+  // error set, which the next launch would report as its own: clear it, and wait for the device then
+  if (q != hipSuccess) (void)hipGetLastError();
   std::lock_guard<std::mutex> lock(call->mu);
   if (q != hipSuccess || cs != hipStreamCaptureStatusNone) {
     call->untracked = true;

@@ -81,21 +81,10 @@ __device__ __forceinline__ void store4(float* d, const float a[4], bool dst16) {
   }
 }
 
-// Work item taken by this workgroup.  Workgroups are dispatched round-robin over the XCDs
-// (workgroup b runs on XCD b mod kXcds).  With REMAP, when the grid has one workgroup per item, the
-// items are renumbered so that every XCD walks one contiguous range of the table, keeping its L2 and
-// TLB on one stream of pages; the map is a bijection on [0, count).  Such a grid has no item for
-// j > 0 (a launch may still pass items_per_wg > 1, e.g. a bounded launch's short tail), so the
-// caller's loop ends there and every item is taken exactly once.
+// Work item taken by this workgroup at step j of its loop (item_index, tide_internal.h).
 template <bool REMAP>
 __device__ __forceinline__ int64_t item_of(int j, int64_t count) {
-  if (REMAP && gridDim.x == count) {
-    if (j > 0) return count;
-    const int64_t b = blockIdx.x;
-    const int64_t x = b % kXcds, i = b / kXcds;
-    return x * (count / kXcds) + min<int64_t>(x, count % kXcds) + i;
-  }
-  return static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(j) * gridDim.x;
+  return item_index(REMAP, gridDim.x, blockIdx.x, j, count);
 }
 
 // One output element, fixed ascending contributor order (heads, tails, unaligned bases).
@@ -524,11 +513,7 @@ __global__ __launch_bounds__(kThreads * kRsCuMaxGroups) void rs_cu_kernel(const 
   const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kThreads);
   const int tid = static_cast<int>(threadIdx.x) % kThreads;
   // workgroup slots, one per grid position: each XCD walks one contiguous range of them
-  int64_t slot = blockIdx.x;
-  if (TIDE_RS_XCD_REMAP != 0) {
-    const int64_t n = gridDim.x, x = slot % kXcds, i = slot / kXcds;
-    slot = x * (n / kXcds) + min<int64_t>(x, n % kXcds) + i;
-  }
+  const int64_t slot = TIDE_RS_XCD_REMAP != 0 ? xcd_slot(gridDim.x, blockIdx.x) : static_cast<int64_t>(blockIdx.x);
   const int64_t first = (slot * W + grp) * KI;
   f32x4* xfer = xfer_dyn + static_cast<int64_t>(grp) * KI * 2 * kThreads;
   const bool wave = W <= kRsCuWaveMaxGroups;  // uniform over the workgroup

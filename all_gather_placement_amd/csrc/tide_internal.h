@@ -165,6 +165,60 @@ constexpr int rs_cu_xfer_bytes(int groups, int ki) { return groups * ki * 2 * kT
 static_assert(rs_cu_xfer_bytes(kRsCuMaxGroups, 2) <= 64 * 1024, "the widest CU-exclusive RS workgroup fits a CU");
 constexpr int kAgBoundedItems = TIDE_AG_BOUNDED_ITEMS;
 
+// Index maps shared by the kernels and the host (one definition, so host-side checks see exactly
+// what the kernels compute).
+#if defined(__HIP__)
+#define TIDE_HD __attribute__((host)) __attribute__((device))
+#else
+#define TIDE_HD
+#endif
+
+// Work item taken by workgroup `block` of a `grid`-workgroup launch over `count` items, at step j of
+// its loop (it takes items while the result is below `count`).  Workgroups are dispatched
+// round-robin over the XCDs (workgroup b runs on XCD b mod kXcds).  With `remap`, when the grid has
+// one workgroup per item, the items are renumbered so that every XCD walks one contiguous range of
+// the table, keeping its L2 and TLB on one stream of pages (a bijection on [0, count)); such a grid
+// has no item for j > 0 (a launch may still pass more items per workgroup, e.g. a bounded launch's
+// short tail), so every item is taken exactly once.  Otherwise items stride by the grid.
+TIDE_HD inline int64_t item_index(bool remap, int64_t grid, int64_t block, int j, int64_t count) {
+  if (remap && grid == count) {
+    if (j > 0) return count;
+    const int64_t x = block % kXcds, i = block / kXcds;
+    return x * (count / kXcds) + (x < count % kXcds ? x : count % kXcds) + i;
+  }
+  return block + static_cast<int64_t>(j) * grid;
+}
+
+// Workgroup slot of workgroup `block` in a one-launch grid of `grid` workgroups: each XCD walks one
+// contiguous range of slots (a bijection on [0, grid)).
+TIDE_HD inline int64_t xcd_slot(int64_t grid, int64_t block) {
+  const int64_t x = block % kXcds, i = block / kXcds;
+  return x * (grid / kXcds) + (x < grid % kXcds ? x : grid % kXcds) + i;
+}
+
+// Launch plan for `count` work items: bounded = grids of at most `max_wgs` workgroups, each taking
+// `bounded_items` items and exiting (bounded_items 0: one launch, workgroups walk every item);
+// otherwise one launch of single-item workgroups (or kPersistentWorkgroups walking them).  Launch k
+// covers items [k*per_launch, min((k+1)*per_launch, count)) with min(grid, its item count) workgroups.
+struct Plan {
+  int grid;
+  int items;
+  int64_t per_launch;
+};
+
+inline Plan plan_for(int64_t count, bool bounded, int64_t max_wgs, int bounded_items) {
+  if (!bounded) {
+    const int64_t cap = kPersistentWorkgroups > 0 ? kPersistentWorkgroups : (int64_t(1) << 30);
+    const int64_t g = count < cap ? count : cap;
+    const int items = int((count + g - 1) / g);
+    return Plan{int(g), items, int64_t(g) * items};
+  }
+  const int64_t lim = count < max_wgs ? count : max_wgs;
+  const int64_t grid = lim > 1 ? lim : 1;
+  const int64_t items = bounded_items > 0 ? bounded_items : (count + grid - 1) / grid;
+  return Plan{int(grid), int(items), grid * items};
+}
+
 // One RS work item: nvalid summed elements of parameter p, starting at element `src` of the
 // parameter's storage, written to shard r at element `dst`; then npad zeros at dst + nvalid.
 struct RsChunk {

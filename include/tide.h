@@ -104,7 +104,10 @@ enum {
                          only the tiniest segments as a small copy kernel).  On one MI355X a call
                          costs ~65 us before any byte moves and large copies stream 1.1-1.6 TB/s:
                          0.9-2 TB/s of traffic for large segments, 0.03-0.1 TB/s for thousands of
-                         small ones.  For callers that must leave the CUs to compute. */
+                         small ones.  For callers that must leave the CUs to compute.  (The DMA
+                         engines' rectangular copy, which would fill each parameter in one copy,
+                         streams 0.10-0.12 TB/s on MI355X and is not ordered with HIP streams, so it
+                         is not used.) */
   TIDE_AG_COPY2D = 2  /* one runtime 2-D copy per parameter (row pitch = one stage slot) plus one
                          copy for the rank whose slice is part padding; the HIP runtime picks the
                          engine (on ROCm 7.2 a shader blit kernel, i.e. it uses CUs). */
@@ -131,12 +134,14 @@ tide_status tide_layout_create(int32_t num_params, const int32_t* ndims, const i
  * be destroyed first and must not be launched afterwards.  NULL is ignored. */
 void tide_layout_destroy(tide_layout* layout);
 
-/* Upload the layout's device tables to the current device (idempotent).  After this, RS and AG
- * calls on that device allocate nothing except when a call passes more pointers than any earlier
- * one.  An immediate call stages its table of buffer addresses in one of 8 slots per device; when
- * all 8 hold tables of calls still in flight, it waits on the host for the oldest to finish
- * (prepared calls own their tables and never wait).  Errors: TIDE_ERR_INVALID (null),
- * TIDE_ERR_NOMEM, TIDE_ERR_HIP. */
+/* Upload the layout's device tables to the current device (idempotent).  The library's device
+ * memory (these tables, pointer-table slots, prepared calls' tables) comes from the device's
+ * stream-ordered memory pool on an internal stream, so freeing it never waits for the whole device.
+ * After this, RS and AG calls on that device allocate nothing except when a call passes more
+ * pointers than any earlier one.  An immediate call writes its table of buffer addresses into one
+ * of 8 slots per device with a small kernel on its stream; when all 8 hold tables of calls still in
+ * flight, it waits on the host for the oldest to finish (prepared calls own their tables and never
+ * wait).  Errors: TIDE_ERR_INVALID (null), TIDE_ERR_NOMEM, TIDE_ERR_HIP. */
 tide_status tide_layout_prepare(const tide_layout* layout);
 
 /* Geometry queries (host only).  Return -1 for a NULL layout. */

@@ -2,6 +2,7 @@
 // Built with g++ (no device code): the kernel launchers are stubs that abort, and every call made
 // here returns before any HIP call (layouts never reach a device; invalid arguments are rejected
 // first).  Exit status 0 = all checks passed.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -195,6 +196,53 @@ int main() {
   CHECK(tide_call_launch(nullptr, nullptr) == TIDE_ERR_INVALID);
   int32_t th = 0, it = 0, out = 0, lds = 0;
   CHECK(tide_rs_launch_shape(0, D, 0, &th, &it, &out, &lds) == TIDE_ERR_INVALID);
+  // Every work item is taken exactly once by the kernels' own index maps (item_index, xcd_slot) under
+  // every launch plan the entry points make: single-item launches, bounded launches (RS 4 and
+  // placement 8 items per workgroup, budgets of 2B workgroups), with and without the XCD remap, and
+  // CU-exclusive workgroups of W groups taking KI items each.
+  {
+    std::vector<int> seen;
+    int64_t bad_plans = 0;
+    auto check_plan = [&](int64_t count, bool bounded, int64_t max_wgs, int items, bool remap) {
+      seen.assign(size_t(count), 0);
+      const tide::Plan plan = tide::plan_for(count, bounded, max_wgs, items);
+      for (int64_t first = 0; first < count; first += plan.per_launch) {
+        const int64_t n = std::min<int64_t>(plan.per_launch, count - first);
+        const int64_t grid = std::min<int64_t>(plan.grid, n);
+        for (int64_t b = 0; b < grid; ++b)
+          for (int j = 0; j < plan.items; ++j) {
+            const int64_t it = tide::item_index(remap, grid, b, j, n);
+            if (it >= n) break;  // the kernels' loops end at the first item past their launch
+            ++seen[size_t(first + it)];
+          }
+      }
+      for (int64_t i = 0; i < count; ++i) bad_plans += seen[size_t(i)] != 1;
+    };
+    auto check_cu = [&](int64_t count, int W, int KI) {
+      seen.assign(size_t(count), 0);
+      const int64_t grid = (count + int64_t(W) * KI - 1) / (int64_t(W) * KI);
+      for (int64_t b = 0; b < grid; ++b)
+        for (int g = 0; g < W; ++g)
+          for (int k = 0; k < KI; ++k) {
+            const int64_t it = (tide::xcd_slot(grid, b) * W + g) * KI + k;
+            if (it < count) ++seen[size_t(it)];
+          }
+      for (int64_t i = 0; i < count; ++i) bad_plans += seen[size_t(i)] != 1;
+    };
+    const int64_t counts[] = {1, 2, 3, 7, 8, 9, 15, 16, 17, 63, 100, 1023, 1024, 1025, 4097, 70001};
+    for (int64_t count : counts) {
+      for (bool remap : {false, true}) {
+        check_plan(count, false, 0, 0, remap);
+        for (int64_t B : {1, 2, 3, 7, 64, 512, 5000}) {
+          check_plan(count, true, B * tide::kBudgetThreads / tide::kThreads, tide::kRsBoundedItems, remap);
+          check_plan(count, true, B * tide::kBudgetThreads / tide::kAgThreads, tide::kAgBoundedItems, remap);
+        }
+      }
+      for (int W = 1; W <= tide::kRsCuMaxGroups; ++W)
+        for (int KI : {1, 2}) check_cu(count, W, KI);
+    }
+    CHECK(bad_plans == 0);
+  }
   tide_call_destroy(nullptr);
   CHECK(tide_last_hip_error() == 0);
   tide_layout_destroy(L);
