@@ -956,15 +956,17 @@ def dma_rect(args, log):
 def mix_bound(args, log):
     """The RS's access shape with its writes or its reads left out (the mix probe of libtide_probe.so),
     beside the library RS on the same buffers: one flat parameter of 2^27 elements, R = 1, C = 1, 2,
-    4 and 8 separate contributor buffers, each launch at the library's RS launch shape for that C.
-    The HBM bus carries reads and writes in turn, so reads-only + writes-only time bounds the RS from
-    below.  Medians of 21 HIP-event timings per row, three interleaved rounds; the row keeps the
-    round medians' median."""
+    4 and 8 separate contributor buffers.  The probe runs one item per workgroup, so it is launched
+    with as many items resident per CU as the library's default RS launch keeps (its items per
+    CU-exclusive workgroup); the library RS is timed in its default launch and in the per-CU cap of
+    the same item count, which is the probe's own launch shape.  The HBM bus carries reads and
+    writes in turn, so reads-only + writes-only time bounds the RS from below.  Medians of 21
+    HIP-event timings per row, three interleaved rounds; the row keeps the round medians' median."""
     import statistics
 
     import torch
 
-    from all_gather_placement_amd import Layout, tide_rs_launch_shape
+    from all_gather_placement_amd import Launch, Layout, tide_rs_launch_shape
     from all_gather_placement_amd import probe as pr
 
     items = 1 << 17
@@ -990,28 +992,32 @@ def mix_bound(args, log):
             ts.append(a.elapsed_time(b))
         return statistics.median(ts)
 
+    kinds = ("reads_only", "writes_only", "both", "library_rs", "library_rs_per_cu_cap")
+    per_cu = {C: tide_rs_launch_shape(C)["items_per_workgroup"] for C in (1, 2, 4, 8)}
+    cap = {C: Launch.per_cu_cap(per_cu[C]) for C in per_cu}
     times = {}
     for rnd in range(3):
         for C in (1, 2, 4, 8):
-            lds = tide_rs_launch_shape(C)["lds_bytes"]
+            lds = tide_rs_launch_shape(C, cap[C])["lds_bytes"]
             for name, mode in modes:
                 t = med(lambda: pr.mix_launch(C, mode, src, dst, items, lds))
                 times.setdefault((C, name), []).append(t)
-            call = L.bind_rs([[g] for g in grads[:C]], [dst])
-            times.setdefault((C, "library_rs"), []).append(med(call.launch))
-            call.close()
-            log(f"round {rnd} C={C}: " + ", ".join(f"{k} {times[(C, k)][-1]:.4f} ms"
-                                                    for k in ("reads_only", "writes_only", "both", "library_rs")))
+            for name, launch in (("library_rs", Launch.default()), ("library_rs_per_cu_cap", cap[C])):
+                call = L.bind_rs([[g] for g in grads[:C]], [dst], launch=launch)
+                times.setdefault((C, name), []).append(med(call.launch))
+                call.close()
+            log(f"round {rnd} C={C}: " + ", ".join(f"{k} {times[(C, k)][-1]:.4f} ms" for k in kinds))
     rows = []
     for C in (1, 2, 4, 8):
-        t = {k: statistics.median(times[(C, k)]) for k in ("reads_only", "writes_only", "both", "library_rs")}
+        t = {k: statistics.median(times[(C, k)]) for k in kinds}
         rb, wb = 2 * C * n, 4 * n
-        row = {"C": C, "rs_lds_bytes": tide_rs_launch_shape(C)["lds_bytes"]}
+        row = {"C": C, "items_resident_per_cu": per_cu[C],
+               "probe_lds_bytes": tide_rs_launch_shape(C, cap[C])["lds_bytes"]}
         for k, v in t.items():
             row[f"{k}_ms"] = round(v, 4)
         row["reads_only_gbps"] = round(rb / (t["reads_only"] * 1e-3) / 1e9, 1)
         row["writes_only_gbps"] = round(wb / (t["writes_only"] * 1e-3) / 1e9, 1)
-        for k in ("both", "library_rs"):
+        for k in ("both", "library_rs", "library_rs_per_cu_cap"):
             row[f"{k}_gbps"] = round((rb + wb) / (t[k] * 1e-3) / 1e9, 1)
         bound = t["reads_only"] + t["writes_only"]
         row["sum_bound_ms"] = round(bound, 4)

@@ -17,17 +17,17 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_traffic_only_from_counters_taken_on_this_kernel_source(tmp_path, monkeypatch):
-    text = open(os.path.join(ROOT, "profiles", "rs_kernel_llama3_1_8b_layer_pmc.md")).read()
+    text = open(os.path.join(ROOT, "profiles", "rs_kernel_llama3_1_70b_layer_pmc.md")).read()
     recorded = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text).group(1)
     kernel = re.search(r"rs_kernel_name:\s*(.+)", text).group(1).strip()
     hbm = float(re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text).group(1))
     # the committed summary is read when its hash matches the kernel source and its kernel the launch's...
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: recorded)
-    assert bench.read_traffic("llama3_1_8b_layer", kernel) == hbm
+    assert bench.read_traffic("llama3_1_70b_layer", kernel) == hbm
     # ...and ignored (null) for another kernel or any other source
-    assert bench.read_traffic("llama3_1_8b_layer", "some_other_kernel<8>") is None
+    assert bench.read_traffic("llama3_1_70b_layer", "some_other_kernel<8>") is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
-    assert bench.read_traffic("llama3_1_8b_layer", kernel) is None
+    assert bench.read_traffic("llama3_1_70b_layer", kernel) is None
     assert bench.read_traffic("no_such_workload", kernel) is None
     # the counters moved every algorithmic byte about once (reads + writes within 1% of 20 B per output)
     algorithmic = int(re.search(r"algorithmic_bytes_per_launch:\s*([0-9]+)", text).group(1))
