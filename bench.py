@@ -444,7 +444,7 @@ def interference(args, log):
 def slot_reuse(args, log):
     """Slot-Reuse against In-Place on one workload: times, GB/s and the bytes live during the RS.
 
-    Slot-Reuse packs each contributor's gradients into a vacated all-gather slot (R*S bf16, the
+    Slot-Reuse packs each contributor's gradients into an all-gather slot that is free again (R*S bf16, the
     stage layout) and reduces from the slots; the per-parameter gradients can be released after
     their pack.  In-Place reads the gradients where they are.  Bytes: pack = 2*numel read +
     2*R*S written per contributor; RS from slots = 2*C*R*S read + 4*R*S written.
@@ -501,7 +501,7 @@ def slot_reuse(args, log):
         "slot_reuse_total_ms": round(t_pack + t_rs_slots, 4),
         "bytes_live_during_rs_in_place": 2 * cfg.C * numel + 4 * cfg.R * S,
         "bytes_live_during_rs_slot_reuse": 2 * cfg.C * cfg.R * S + 4 * cfg.R * S,
-        "note": "Slot-Reuse's slots are vacated all-gather buffers (already allocated); the gradients can be "
+        "note": "Slot-Reuse's slots are all-gather buffers that are free again (already allocated); the gradients can be "
                 "released once packed, so their 2*C*numel bytes are not live during its RS.",
     }
     log(json.dumps(out))

@@ -18,7 +18,7 @@ but lost every math symbol, so the definitions here are the plainest reading of 
                in-place path reaches the same values while skipping the pack (abstract; Table 1,
                the in-place input mode of the RS; Figure 1, every piece stored once, directly in
                its destination);
-* Slot-Reuse staging -- gradients packed into a vacated all-gather slot, then reduced from the
+* Slot-Reuse staging -- gradients packed into an all-gather slot that is free again, then reduced from the
                slots (abstract; Figure 7); see oracle/slot.py;
 * all-gather placement -- FSDP2's copy-out of the rank-major all-gather output into
                per-parameter storage (Table 7 caption: split_with_sizes_copy), which TIDE-AG

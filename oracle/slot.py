@@ -1,4 +1,4 @@
-"""Slot-Reuse staging: gradients packed into a vacated all-gather slot (oracle; test infrastructure).
+"""Slot-Reuse staging: gradients packed into an all-gather slot that is free again (oracle; test infrastructure).
 
 In TIDE's optional Slot-Reuse mode ([Endgame] abstract; Figure 7) a contributor's gradients are first
 copied into an all-gather buffer that is no longer needed, and the reduce-scatter reads them from there;

@@ -1,4 +1,4 @@
-"""GPU parity of the Slot-Reuse path (pack into a vacated all-gather slot, reduce from the slots).
+"""GPU parity of the Slot-Reuse path (pack into an all-gather slot that is free again, reduce from the slots).
 
 Packing is compared bit for bit with the oracle's pack (padding must become +0 whatever the slot
 held); the reduce-scatter from slots with the oracle's slot reduction (padding in the slots is

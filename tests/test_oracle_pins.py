@@ -452,7 +452,7 @@ def test_mutants_are_caught():
 
 
 # ---------------------------------------------------------------------------------------------
-# Slot-Reuse staging (pack into a vacated all-gather slot, then reduce from the slots)
+# Slot-Reuse staging (pack into an all-gather slot that is free again, then reduce from the slots)
 # ---------------------------------------------------------------------------------------------
 
 @settings(max_examples=40, deadline=None)
