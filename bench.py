@@ -39,7 +39,7 @@ METRIC = "RS effective HBM GB/s (bf16 in + fp32 out) and % of 8 TB/s peak, 1 GPU
 HBM_PEAK_GBPS = 8000.0
 
 
-def parse():
+def parser() -> argparse.ArgumentParser:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -90,7 +90,11 @@ def parse():
                          "rectangular copy per parameter (the copy-engine form of a strided copy per parameter)")
     ap.add_argument("--slot-reuse", action="store_true",
                     help="instead of the step benchmark: Slot-Reuse (pack into slots + RS from slots) vs in-place RS")
-    return ap.parse_args()
+    return ap
+
+
+def parse():
+    return parser().parse_args()
 
 
 def parse_launch(text: str):

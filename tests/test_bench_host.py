@@ -65,3 +65,22 @@ def test_oracle_only_in_the_cpu_baseline_leg_and_never_in_the_package():
         for f in sorted(os.listdir(os.path.join(ROOT, d))):
             if f.endswith(".py"):
                 assert _oracle_imports(os.path.join(ROOT, d, f)) == [], (d, f)
+
+
+def test_profile_commands_use_flags_bench_py_knows():
+    """Every bench.py command a committed profile summary gives uses only options bench.py accepts,
+    so each summary can be re-made from the committed files."""
+    known = set(bench.parser()._option_string_actions)
+    seen = 0
+    for name in sorted(os.listdir(os.path.join(ROOT, "profiles"))):
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        for block in re.findall(r"```\n(.*?)```", text, flags=re.S):
+            for line in block.splitlines():
+                if "bench.py" not in line:
+                    continue
+                cmd = line.split("bench.py", 1)[1].split("#", 1)[0]
+                flags = re.findall(r"(?<!\S)(--[a-z0-9][a-z0-9-]*)", cmd)
+                unknown = [f for f in flags if f not in known]
+                assert not unknown, (name, line, unknown)
+                seen += 1
+    assert seen >= 15
