@@ -64,6 +64,8 @@ def parser() -> argparse.ArgumentParser:
         ["default", "per_cu_cap:1", "per_cu_cap:2", "per_cu_cap:4"] + [f"cu_exclusive:{n}" for n in (1, 2, 4, 6, 8)]
         + [f"bounded:{b}" for b in (8, 16, 32, 64, 128, 256, 512, 768, 1024, 1536, 2048)]),
         help="--interference / --overlap: the launch forms to measure (comma list)")
+    ap.add_argument("--ag-launches", default="default,bounded:512,bounded:768,cu_exclusive:2,cu_exclusive:4,cu_exclusive:6",
+                    help="--interference: the launch forms of the placement kernel's rows (comma list)")
     ap.add_argument("--gemm", default="4096,4096,4096", help="victim GEMM M,N,K (bf16)")
     ap.add_argument("--probe-launches",
                     default="none,default,bounded:16,bounded:64,bounded:256,bounded:512,bounded:768,bounded:1024,"
@@ -407,9 +409,8 @@ def interference(args, log):
     log(f"victim GEMM {M}x{N}x{K} bf16 alone: {alone * 1e3:.1f} us (median of {len(alone_all)})")
     rows = []
     cases = [("rs", parse_launch(x)) for x in args.launches.split(",") if x.strip()]
-    cases += [("ag_kernel", Launch.default()), ("ag_kernel", Launch.bounded(512)), ("ag_kernel", Launch.bounded(768)),
-              ("ag_kernel", Launch.cu_exclusive(2)), ("ag_kernel", Launch.cu_exclusive(4)),
-              ("ag_kernel", Launch.cu_exclusive(6)), ("ag_copy2d", Launch.default()), ("ag_sdma", Launch.default())]
+    cases += [("ag_kernel", parse_launch(x)) for x in args.ag_launches.split(",") if x.strip()]
+    cases += [("ag_copy2d", Launch.default()), ("ag_sdma", Launch.default())]
     for kind, launch in cases:
         t_alone = comm_alone(kind, launch)
         conc, outlast = [], 0
