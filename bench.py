@@ -85,6 +85,8 @@ def parser() -> argparse.ArgumentParser:
     ap.add_argument("--overlap-comm", choices=["rs", "ag_kernel", "ag_sdma", "ag_copy2d"], default="rs")
     ap.add_argument("--mix-bound", action="store_true",
                     help="the RS's access shape with reads or writes left out, beside the library RS (C = 1-8)")
+    ap.add_argument("--group-sizes", action="store_true",
+                    help="RS and placement on Llama-shaped layer groups of hidden size 256-8192 (17 MB to 17 GB)")
     ap.add_argument("--copy-sizes", action="store_true",
                     help="placement of one flat parameter of 1-256 MiB over R = 1 and 8 ranks on each engine")
     ap.add_argument("--dma-rect", action="store_true",
@@ -737,6 +739,56 @@ def engines(args, log):
     print(json.dumps({"experiment": "placement engines vs victims", "workload": cfg.name, "rows": rows}), flush=True)
 
 
+def group_sizes(args, log):
+    """RS and placement across group sizes: Llama-shaped layer groups (q, o h x h; k, v h/4 x h; gate,
+    up 3.5h x h; down h x 3.5h; two norms; R = 8, C = 8) for h = 256 .. 8192, i.e. 17 MB to 17 GB of RS
+    traffic per call, each collective in its default launch through a prepared call; mean of 20
+    HIP-event timings after 3 warm-up launches.  Shows where launch overhead stops mattering."""
+    import statistics
+
+    import torch
+
+    from all_gather_placement_amd import Layout, TIDE_AG_KERNEL
+
+    def mean_ms(call, n=20):
+        for _ in range(3):
+            call.launch()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in evs:
+            a.record()
+            call.launch()
+            b.record()
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(b) for a, b in evs)
+
+    R, C = 8, 8
+    rows = []
+    for h in (256, 512, 1024, 2048, 4096, 8192):
+        f = h * 7 // 2
+        shapes = [(h, h), (h // 4, h), (h // 4, h), (h, h), (f, h), (f, h), (h, f), (h,), (h,)]
+        numel = sum(int(torch.tensor(s).prod()) for s in shapes)
+        with Layout(shapes, R) as L:
+            grads = [[torch.randn(s, device="cuda").to(torch.bfloat16) for s in shapes] for _ in range(C)]
+            shards = [torch.empty(L.S, dtype=torch.float32, device="cuda") for _ in range(R)]
+            stage = torch.randn(R * L.S, device="cuda").to(torch.bfloat16)
+            params = [torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes]
+            rs_b, ag_b = 2 * C * numel + 4 * R * L.S, 4 * numel
+            rs = L.bind_rs(grads, shards)
+            ag = L.bind_ag(stage, params, mode=TIDE_AG_KERNEL)
+            t_rs, t_ag = mean_ms(rs), mean_ms(ag)
+            rs.close()
+            ag.close()
+            row = {"h": h, "numel": numel, "rs_bytes": rs_b, "rs_us": round(t_rs * 1e3, 1),
+                   "rs_gbps": round(rs_b / t_rs / 1e6, 1), "rs_frac": round(rs_b / t_rs / 1e6 / 8000, 4),
+                   "ag_bytes": ag_b, "ag_us": round(t_ag * 1e3, 1), "ag_gbps": round(ag_b / t_ag / 1e6, 1)}
+            log(json.dumps(row))
+            rows.append(row)
+            del grads, shards, stage, params
+        torch.cuda.empty_cache()
+    print(json.dumps({"experiment": "RS and placement vs group size", "R": R, "C": C, "rows": rows}), flush=True)
+
+
 def copy_sizes(args, log):
     """Per-copy cost of the placement engines: one flat bf16 parameter of 1, 8, 64 and 256 MiB placed
     from a stage over R = 1 (one copy) and R = 8 (eight copies), on the DMA engines, the runtime 2-D
@@ -1077,6 +1129,10 @@ def main():
     if args.copy_sizes:
         torch.cuda.set_device(0)
         copy_sizes(args, log)
+        return
+    if args.group_sizes:
+        torch.cuda.set_device(0)
+        group_sizes(args, log)
         return
     if args.mix_bound:
         torch.cuda.set_device(0)
